@@ -1,0 +1,239 @@
+"""Plain fp64 definitions of RoPE, causal attention and the KV cache.
+
+TEST INFRASTRUCTURE ONLY (see ``oracle/__init__.py``): the product path
+never imports this module.
+
+Shapes follow the head-split form of multi-head attention ([Scratch] §3.1;
+[Guide] §5.1): Q is [B, Hq, S, D]; K and V are [B, Hkv, S, D].  A contiguous
+cache holds K and V as separate tensors [B, Hkv, max_seq, D] ([NanoVLLM] §05,
+5.2: K and V are separate tensors; [Intuition] §5: head-major layout).  A
+paged cache holds K and V pools [num_blocks, Hkv, block_size, D] plus an
+int32 block table [B, max_blocks_per_seq] ([NanoVLLM] §05, 5.3: logical
+block -> physical block, offset inside the block).
+
+Pins (tests under ``tests/test_oracle_*.py``, none reuses this code):
+
+* ``rope_inv_freq`` / ``rope_rotate``: identity at position 0; exact norm
+  preservation; scores depend only on relative position; hand values
+  (cos 1, sin 1) for D = 2 and the i = 1 frequency 10000^(-2/4) = 0.01
+  for D = 4, which also separates adjacent from half-split pairing.
+* ``causal_attention``: rows of P sum to 1; K = 0 gives the causal prefix
+  mean; causality under perturbation of later positions; a scalar
+  brute force on tiny shapes; a hand-worked 2-token example; an fp64
+  blockwise online softmax in the test agrees to 1e-12.
+* ``kv_cache_append`` / ``cache_rows`` / ``paged_slot``: paged under random
+  block tables equals contiguous; written slots hold exactly the values.
+* ``attn_decode``: L = 0 gives O = v_new; step t equals the last row of a
+  full-recompute prefill over the same tokens; GQA equals MHA with each
+  KV head repeated.
+
+Convention choices with no pin on synthetic data ("parity unpinned"):
+adjacent pairs (2i, 2i+1) for RoPE, and contiguous GQA groups.
+"""
+
+from __future__ import annotations
+
+import numpy as np
+
+__all__ = [
+    "rope_inv_freq",
+    "rope_rotate",
+    "causal_attention",
+    "attn_prefill",
+    "kv_cache_append",
+    "cache_rows",
+    "attn_decode",
+    "paged_slot",
+]
+
+
+def _f64(x) -> np.ndarray:
+    return np.asarray(x, dtype=np.float64)
+
+
+# --------------------------------------------------------------------------
+# RoPE  ([Intuition] §4, the Transformer core and RoPE)
+# --------------------------------------------------------------------------
+
+def rope_inv_freq(D: int, theta: float = 10000.0) -> np.ndarray:
+    """Per-pair angular frequency theta_i = theta^(-2i/D), i in [0, D/2).
+
+    [Intuition] §4 gives theta_i as 10000 raised to -2i/d and builds i with an
+    arange over d//2 in floating point (not integer) arithmetic.
+    """
+    if D % 2:
+        raise ValueError("head dimension must be even for RoPE pairs")
+    i = np.arange(D // 2, dtype=np.float64)
+    return np.power(np.float64(theta), -2.0 * i / D)
+
+
+def rope_rotate(x, positions, theta: float = 10000.0) -> np.ndarray:
+    """Rotate each pair (x[2i], x[2i+1]) by the angle m * theta_i.
+
+    ``x`` is [..., S, D]; ``positions`` (m) broadcasts against [..., S].  Each
+    pair is multiplied by the 2x2 matrix [[cos, -sin], [sin, cos]] of its
+    angle, the rotation [Intuition] §4 writes out for the pairs (q0,q1),
+    (q2,q3), ..., with m the token's position index.
+    """
+    x = _f64(x)
+    D = x.shape[-1]
+    m = _f64(positions)[..., None]                      # [..., S, 1]
+    ang = m * rope_inv_freq(D, theta)                   # [..., S, D/2]
+    c, s = np.cos(ang), np.sin(ang)
+    R = np.stack([np.stack([c, -s], axis=-1),
+                  np.stack([s, c], axis=-1)], axis=-2)  # [..., S, D/2, 2, 2]
+    pairs = x.reshape(x.shape[:-1] + (D // 2, 2))       # [..., S, D/2, 2]
+    out = np.einsum("...ij,...j->...i", R, pairs)
+    return out.reshape(x.shape)
+
+
+# --------------------------------------------------------------------------
+# Scaled dot-product attention with the causal mask
+# ([Guide] §2.3 and §5.1; [Scratch] §3.1 and §3.3)
+# --------------------------------------------------------------------------
+
+def causal_attention(q, k, v, positions, scale: float) -> np.ndarray:
+    """softmax(q k^T * scale + mask) v for one (sequence, head).
+
+    q is [Sq, D]; k and v are [Sk, D]; ``positions`` is a pair
+    (query positions [Sq], key positions [Sk]).  Key j is masked (-inf) for
+    query i when its position is later ([Guide] §5.1: the upper-right triangle
+    is set to -inf; [Scratch] §3.3: a position sees itself and earlier ones,
+    -inf marks a blocked entry).  The full score matrix is formed on purpose.
+    """
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    qpos, kpos = (np.asarray(p) for p in positions)
+    scores = (q @ k.T) * scale
+    blocked = kpos[None, :] > qpos[:, None]
+    scores = np.where(blocked, -np.inf, scores)
+    rowmax = scores.max(axis=1, keepdims=True)
+    e = np.exp(scores - rowmax)
+    p = e / e.sum(axis=1, keepdims=True)
+    return p @ v
+
+
+def attn_prefill(q, k, v, positions, theta: float = 10000.0,
+                 scale: float | None = None):
+    """Prefill over a whole prompt: RoPE on Q and K, then causal attention.
+
+    q [B, Hq, S, D], k/v [B, Hkv, S, D], positions [B, S].  Query head hq
+    reads KV head hq // (Hq // Hkv) (contiguous GQA groups; a convention, the
+    pages only name GQA).  The scale defaults to 1/sqrt(D), applied to the
+    scores before the softmax ([Intuition] §4: 1/sqrt(d_k) with d_k the head
+    dimension; [Scratch] §3.1).
+
+    Returns (out [B, Hq, S, D], k_rot [B, Hkv, S, D]); V is not rotated.
+    """
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    positions = np.asarray(positions)
+    B, Hq, S, D = q.shape
+    Hkv = k.shape[1]
+    if Hq % Hkv:
+        raise ValueError("Hq must be a multiple of Hkv")
+    group = Hq // Hkv
+    if scale is None:
+        scale = 1.0 / np.sqrt(D)
+    pos_b = positions[:, None, :]
+    q_rot = rope_rotate(q, pos_b, theta)
+    k_rot = rope_rotate(k, pos_b, theta)
+    out = np.empty_like(q_rot)
+    for b in range(B):
+        for hq in range(Hq):
+            hk = hq // group
+            out[b, hq] = causal_attention(q_rot[b, hq], k_rot[b, hk], v[b, hk],
+                                          (positions[b], positions[b]), scale)
+    return out, k_rot
+
+
+# --------------------------------------------------------------------------
+# KV cache  ([Guide] §2.5; [Scratch] §3.2; [NanoVLLM] §05)
+# --------------------------------------------------------------------------
+
+def paged_slot(block_table, b: int, t: int, block_size: int):
+    """Physical (block, offset) of token t of sequence b in a paged cache.
+
+    [NanoVLLM] §05 (5.3) looks the physical block up in the block table at
+    t // block_size and takes t % block_size as the offset inside it.
+    """
+    return int(block_table[b, t // block_size]), t % block_size
+
+
+def kv_cache_append(cache_k, cache_v, k_rot, v, positions,
+                    block_table=None, block_size: int = 16):
+    """Write rotated keys and raw values at cache index == position.
+
+    [Scratch] §3.2: each new token's K and V go to the cache slot of its
+    absolute position, which must equal the cache index.  ``cache_k`` and
+    ``cache_v`` are modified in place (contiguous [B, Hkv, max_seq, D] or
+    paged pools [num_blocks, Hkv, block_size, D]); k_rot and v are
+    [B, Hkv, S, D] with positions [B, S].
+    """
+    positions = np.asarray(positions)
+    B, Hkv, S, _ = np.shape(k_rot)
+    for b in range(B):
+        for s in range(S):
+            t = int(positions[b, s])
+            if block_table is None:
+                cache_k[b, :, t, :] = k_rot[b, :, s, :]
+                cache_v[b, :, t, :] = v[b, :, s, :]
+            else:
+                blk, off = paged_slot(block_table, b, t, block_size)
+                cache_k[blk, :, off, :] = k_rot[b, :, s, :]
+                cache_v[blk, :, off, :] = v[b, :, s, :]
+
+
+def cache_rows(cache, b: int, hk: int, n: int, block_table=None,
+               block_size: int = 16) -> np.ndarray:
+    """Rows 0..n-1 of sequence b, KV head hk, as an [n, D] float64 array."""
+    if block_table is None:
+        return _f64(cache[b, hk, :n, :])
+    rows = []
+    for t in range(n):
+        blk, off = paged_slot(block_table, b, t, block_size)
+        rows.append(_f64(cache[blk, hk, off, :]))
+    return np.stack(rows) if rows else np.zeros((0, cache.shape[-1]))
+
+
+def attn_decode(q, k_new, v_new, cache_k, cache_v, seq_lens,
+                theta: float = 10000.0, scale: float | None = None,
+                block_table=None, block_size: int = 16):
+    """One decode step: a single new query token per sequence.
+
+    For sequence b with L = seq_lens[b] tokens already cached, the new
+    token's position is L.  q [B, Hq, D] and k_new [B, Hkv, D] are rotated
+    at position L; the rotated key and raw value are written to cache index
+    L ([Scratch] §3.2); the query then attends over cache rows 0..L, the L
+    cached tokens plus itself ([Guide] §2.5: only the new token's Q, K, V
+    are computed; K and V of earlier tokens never change).  With the cache
+    there is no further mask: the (1, S) row is all visible ([Scratch] §3.3).
+
+    The caches are updated in place (float64 copies are the caller's
+    choice).  Returns out [B, Hq, D].
+    """
+    q, k_new, v_new = _f64(q), _f64(k_new), _f64(v_new)
+    B, Hq, D = q.shape
+    Hkv = k_new.shape[1]
+    group = Hq // Hkv
+    if scale is None:
+        scale = 1.0 / np.sqrt(D)
+    seq_lens = np.asarray(seq_lens)
+    out = np.empty((B, Hq, D))
+    for b in range(B):
+        L = int(seq_lens[b])
+        q_rot = rope_rotate(q[b][:, None, :], np.array([L]), theta)[:, 0, :]
+        k_rot = rope_rotate(k_new[b][:, None, :], np.array([L]), theta)  # [Hkv, 1, D]
+        v_one = v_new[b][None, :, None, :]                                # [1, Hkv, 1, D]
+        if block_table is None:
+            kv_cache_append(cache_k[b:b + 1], cache_v[b:b + 1], k_rot[None], v_one,
+                            np.array([[L]]))
+        else:
+            kv_cache_append(cache_k, cache_v, k_rot[None], v_one, np.array([[L]]),
+                            block_table=block_table[b:b + 1], block_size=block_size)
+        pos = np.arange(L + 1)
+        for hq in range(Hq):
+            hk = hq // group
+            keys = cache_rows(cache_k, b, hk, L + 1, block_table, block_size)
+            vals = cache_rows(cache_v, b, hk, L + 1, block_table, block_size)
+            out[b, hq] = causal_attention(q_rot[hq][None, :], keys, vals,
+                                          (np.array([L]), pos), scale)[0]
+    return out
