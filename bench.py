@@ -1,6 +1,37 @@
-"""Benchmark of the attention hot path on one MI355X (filled in below)."""
+#!/usr/bin/env python3
+"""Benchmark of the attention hot path on one MI355X.
+
+One step is one pass of every stage of the path over the synthetic workloads:
+
+  1. prefill of the Qwen-shaped prompt (B=1, H=32, D=128, S=4096, bf16):
+     RoPE on K and the cache store (one pass), then the tiled online-softmax
+     attention kernel (RoPE on Q fused), writing a [1, 32, 4096, 128] cache;
+  2. one decode step over the contiguous cache (B=32, H=32, D=128, cached
+     lengths uniform in [1, 4095]);
+  3. one decode step over the paged cache with GQA (B=64, Hq=32, Hkv=8,
+     16-token blocks, lengths uniform in [512, 8192]).
+
+All inputs are resident in HBM before timing.  The headline ``value`` is the
+prefill's algorithmic TFLOP/s over the whole prefill call; the decode steps'
+KV GB/s and tokens/s are reported beside it.  The main kernel of every call
+is also timed alone with HIP events recorded on its stream around the launch,
+which gives the roofline fractions.  The fp64 oracle, timed on the host
+cores on a bounded sample of the same workloads, is reported as a baseline.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--only NAME] [--no-cpu-baseline]
+"""
 
 from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+METRIC = "prefill TFLOP/s (% MFMA peak); decode KV GB/s (% HBM peak) + tokens/s"
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_HBM_GBPS = 8000.0      # MI355X HBM3E
 
 
 def prefill_flops(B: int, H: int, S: int, D: int) -> int:
@@ -13,3 +44,233 @@ def decode_kv_bytes(lens, Hkv: int, D: int, elem_bytes: int) -> int:
     """Algorithmic KV bytes one decode step reads: every cached K and V row
     of every KV head once (GQA query heads share their KV head's read)."""
     return sum(int(L) for L in lens) * Hkv * D * 2 * elem_bytes
+
+
+def decode_io_bytes(B: int, Hq: int, Hkv: int, D: int, elem_bytes: int) -> int:
+    """Per-step bytes besides the cache read: q in, out, k_new/v_new in, and
+    the appended K/V row written."""
+    return B * (2 * Hq + 4 * Hkv) * D * elem_bytes
+
+
+def parse_args(argv=None):
+    p = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=30)
+    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--only", choices=["prefill", "contiguous", "paged"], default=None,
+                   help="time one stage only (profiling runs)")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cpu-heads", type=int, default=4,
+                   help="prefill heads in the oracle's timed sample")
+    return p.parse_args(argv)
+
+
+def cpu_baseline(pf, c4, heads: int):
+    """Time the fp64 oracle on the host on a bounded sample of the workloads."""
+    import numpy as np
+    import threadpoolctl
+    import oracle
+    info = threadpoolctl.threadpool_info()
+    threads = max([d.get("num_threads", 1) for d in info] or [1])
+    S, D = pf.S, pf.D
+    q = pf.q[:, :heads].float().cpu().double().numpy()
+    k = pf.k[:, :heads].float().cpu().double().numpy()
+    v = pf.v[:, :heads].float().cpu().double().numpy()
+    pos = pf.positions.cpu().numpy()
+    t0 = time.perf_counter()
+    oracle.attn_prefill(q, k, v, pos, pf.theta, pf.scale)
+    t_pf = time.perf_counter() - t0
+    flops = prefill_flops(1, heads, S, D)
+    # decode sample: the first 8 sequences of the contiguous workload
+    bsel = list(range(8))
+    lens = np.array([c4.lens_host[b] for b in bsel])
+    n = int(lens.max()) + 1
+    dq = c4.q[bsel].float().cpu().double().numpy()
+    dk = c4.k_new[bsel].float().cpu().double().numpy()
+    dv = c4.v_new[bsel].float().cpu().double().numpy()
+    ck = c4.cache_k[bsel][:, :, :n].float().cpu().double().numpy()
+    cv = c4.cache_v[bsel][:, :, :n].float().cpu().double().numpy()
+    t0 = time.perf_counter()
+    oracle.attn_decode(dq, dk, dv, ck, cv, lens, c4.theta, c4.scale)
+    t_dec = time.perf_counter() - t0
+    dbytes = decode_kv_bytes(lens, c4.Hkv, c4.D, 2)
+    return {
+        "value": flops / t_pf / 1e12,
+        "unit": "TFLOP/s",
+        "cores": threads,
+        "kind": "oracle",
+        "sample": (f"fp64 oracle prefill of {heads} of the 32 heads of the S=4096 prompt "
+                   f"({t_pf:.1f} s); decode of 8 of the 32 contiguous-cache sequences "
+                   f"({t_dec:.2f} s)"),
+        "decode_GBps": dbytes / t_dec / 1e9,
+        "decode_tokens_per_s": len(bsel) / t_dec,
+        "host_cores_visible": len(os.sched_getaffinity(0)),
+    }
+
+
+def main(argv=None) -> int:
+    args = parse_args(argv)
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path "
+              "(run with --gpus 1)", file=sys.stderr)
+        return 2
+
+    import torch
+    import causal_attention_rope_amd as car
+    import workloads as W
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream(dev)
+
+    stages = ["prefill", "contiguous", "paged"] if args.only is None else [args.only]
+
+    # ---------------- inputs, resident in HBM ----------------
+    pf = W.qwen_prefill(dev)
+    c4 = W.contiguous_decode(dev)
+    c5 = W.paged_decode(dev)
+    pf_cache = car.KVCache(torch.zeros((1, 32, 4096, 128), dtype=torch.bfloat16, device=dev),
+                           torch.zeros((1, 32, 4096, 128), dtype=torch.bfloat16, device=dev))
+    pf_out = torch.empty_like(pf.q)
+    pf_ws = torch.empty(car.prefill_workspace_bytes(torch.bfloat16, 1, 32, 4096, 128),
+                        dtype=torch.uint8, device=dev)
+    c4_cache = car.KVCache(c4.cache_k, c4.cache_v)
+    c5_cache = car.KVCache(c5.cache_k, c5.cache_v, c5.block_table)
+    c4_out, c5_out = torch.empty_like(c4.q), torch.empty_like(c5.q)
+    c4_ws = torch.empty(car.decode_workspace_bytes(c4.B, c4.Hq, c4.D, c4.max_seq_len),
+                        dtype=torch.uint8, device=dev)
+    c5_ws = torch.empty(car.decode_workspace_bytes(c5.B, c5.Hq, c5.D, c5.max_seq_len),
+                        dtype=torch.uint8, device=dev)
+
+    def new_event():
+        e = torch.cuda.Event(enable_timing=True)
+        e.record(stream)  # creates the underlying HIP event
+        return e
+
+    n_ev = args.steps
+    ev = {s: {"call": [(new_event(), new_event()) for _ in range(n_ev)],
+              "kernel": [(new_event(), new_event()) for _ in range(n_ev)]} for s in stages}
+
+    def run_stage(s, i=None):
+        if i is not None:
+            car.set_timing_events(*ev[s]["kernel"][i])
+            ev[s]["call"][i][0].record(stream)
+        if s == "prefill":
+            car.attn_prefill(pf.q, pf.k, pf.v, pf.positions, pf.theta, pf.scale,
+                             cache=pf_cache, out=pf_out, workspace=pf_ws)
+        elif s == "contiguous":
+            car.attn_decode(c4.q, c4.k_new, c4.v_new, c4.seq_lens, c4_cache, c4.max_seq_len,
+                            c4.theta, c4.scale, out=c4_out, workspace=c4_ws)
+        else:
+            car.attn_decode(c5.q, c5.k_new, c5.v_new, c5.seq_lens, c5_cache, c5.max_seq_len,
+                            c5.theta, c5.scale, out=c5_out, workspace=c5_ws)
+        if i is not None:
+            ev[s]["call"][i][1].record(stream)
+            car.set_timing_events(None, None)
+
+    for _ in range(args.warmup):
+        for s in stages:
+            run_stage(s)
+    torch.cuda.synchronize()
+
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        for s in stages:
+            run_stage(s, i)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_per_step = wall / args.steps * 1e3
+
+    def avg_ms(pairs):
+        return sum(a.elapsed_time(b) for a, b in pairs) / len(pairs)
+
+    res = {}
+    for s in stages:
+        res[s] = {"call_ms": avg_ms(ev[s]["call"]), "kernel_ms": avg_ms(ev[s]["kernel"])}
+
+    for out in (pf_out, c4_out, c5_out):
+        if not torch.isfinite(out.float()).all():
+            print("non-finite output", file=sys.stderr)
+            return 1
+
+    # ---------------- figures ----------------
+    kernels = {}
+    pf_flops = prefill_flops(pf.B, pf.Hq, pf.S, pf.D)
+    line_extra = {}
+    if "prefill" in res:
+        r = res["prefill"]
+        r["TFLOPs_call"] = pf_flops / (r["call_ms"] * 1e-3) / 1e12
+        r["TFLOPs_kernel"] = pf_flops / (r["kernel_ms"] * 1e-3) / 1e12
+        kernels["prefill_attention"] = {
+            "bound": "mfma", "achieved": r["TFLOPs_kernel"], "peak": PEAK_BF16_TFLOPS,
+            "unit": "TFLOP/s", "frac": r["TFLOPs_kernel"] / PEAK_BF16_TFLOPS,
+            "traffic": None, "avg_us": r["kernel_ms"] * 1e3,
+            "per_launch": f"{pf_flops} flops (2*B*H*D*S*(S+1), B=1 H=32 D=128 S=4096)"}
+    for s, c in (("contiguous", c4), ("paged", c5)):
+        if s not in res:
+            continue
+        r = res[s]
+        kv = decode_kv_bytes(c.lens_host, c.Hkv, c.D, 2)
+        r["GBps_call"] = kv / (r["call_ms"] * 1e-3) / 1e9
+        r["GBps_kernel"] = kv / (r["kernel_ms"] * 1e-3) / 1e9
+        r["tokens_per_s"] = c.B / (r["call_ms"] * 1e-3)
+        r["hbm_frac_call"] = r["GBps_call"] / PEAK_HBM_GBPS
+        r["kv_bytes"] = kv
+        r["io_bytes"] = decode_io_bytes(c.B, c.Hq, c.Hkv, c.D, 2)
+        kernels[f"decode_{s}_split"] = {
+            "bound": "hbm", "achieved": r["GBps_kernel"], "peak": PEAK_HBM_GBPS,
+            "unit": "GB/s", "frac": r["GBps_kernel"] / PEAK_HBM_GBPS, "traffic": None,
+            "avg_us": r["kernel_ms"] * 1e3,
+            "per_launch": f"{kv} bytes (sum_b L_b * Hkv * D * 2 (K,V) * 2 B)"}
+
+    dominant = max(kernels, key=lambda k: kernels[k]["avg_us"])
+    roofline = {k: v for k, v in kernels[dominant].items() if k in
+                ("bound", "achieved", "peak", "unit", "frac", "traffic")}
+    roofline["kernel"] = dominant
+
+    if "prefill" in res:
+        value, unit = res["prefill"]["TFLOPs_call"], "TFLOP/s"
+    elif "contiguous" in res:
+        value, unit = res["contiguous"]["GBps_call"], "GB/s"
+    else:
+        value, unit = res["paged"]["GBps_call"], "GB/s"
+
+    line = {
+        "metric": METRIC,
+        "value": value,
+        "unit": unit,
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": "+".join(
+                {"prefill": "qwen_prefill(B=1,H=32,D=128,S=4096,cache 4096)",
+                 "contiguous": "contiguous_decode(B=32,H=32,D=128,L~U[1,4095])",
+                 "paged": "paged_decode(B=64,Hq=32,Hkv=8,D=128,block 16,L~U[512,8192])"}[s]
+                for s in stages),
+            "parallelism": "single GPU",
+        },
+        "roofline": roofline,
+        "stages": res,
+        "kernels": kernels,
+        "prefill_mfma_frac_call": (res["prefill"]["TFLOPs_call"] / PEAK_BF16_TFLOPS
+                                   if "prefill" in res else None),
+    }
+    line.update(line_extra)
+    if not args.no_cpu_baseline and args.only is None:
+        line["cpu_baseline"] = cpu_baseline(pf, c4, args.cpu_heads)
+    else:
+        line["cpu_baseline"] = None
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,336 @@
+"""Causal attention with RoPE and a KV cache on AMD MI355X (gfx950).
+
+A thin binding over ``libcar.so``, the C ABI declared in ``include/car.h``.
+Every step of the computation runs in the library's HIP kernels; this module
+only checks tensors, allocates outputs and workspaces through torch, and
+passes raw device pointers and torch's current HIP stream.  There is no CPU
+fallback: importing fails if the library has not been built.
+
+Entry points (same names as the C ABI without the ``car_`` prefix):
+``rope_apply``, ``kv_cache_append``, ``attn_prefill``, ``attn_decode``,
+plus ``KVCache``, the workspace size queries and ``set_timing_events``.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+from typing import Optional
+
+import torch
+
+__all__ = [
+    "CarError", "KVCache", "rope_apply", "kv_cache_append", "attn_prefill", "attn_decode",
+    "prefill_workspace_bytes", "decode_workspace_bytes", "set_timing_events", "library_path",
+]
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+library_path = os.path.join(_HERE, "libcar.so")
+
+F32, BF16 = 0, 1
+_DTYPES = {torch.float32: F32, torch.bfloat16: BF16}
+
+
+class CarError(RuntimeError):
+    """A non-zero car_status returned by the library."""
+
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {_lib.car_status_string(status).decode()}")
+
+
+class _CarKVCache(ctypes.Structure):
+    _fields_ = [
+        ("k", ctypes.c_void_p),
+        ("v", ctypes.c_void_p),
+        ("block_table", ctypes.c_void_p),
+        ("max_seq", ctypes.c_int32),
+        ("num_blocks", ctypes.c_int32),
+        ("block_size", ctypes.c_int32),
+        ("max_blocks_per_seq", ctypes.c_int32),
+    ]
+
+
+def _load() -> ctypes.CDLL:
+    if not os.path.exists(library_path):
+        raise ImportError(
+            f"{library_path} is missing; build it first with "
+            "`python -m causal_attention_rope_amd.build`")
+    lib = ctypes.CDLL(library_path)
+    vp, i32, f32, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+    cache_p = ctypes.POINTER(_CarKVCache)
+    sigs = {
+        "car_rope_apply": (i32, [vp, i32, i32, i32, i32, i32, vp, f32, vp]),
+        "car_kv_cache_append": (i32, [cache_p, i32, vp, vp, i32, i32, i32, i32, vp, vp]),
+        "car_attn_prefill_workspace_bytes": (sz, [i32, i32, i32, i32, i32, cache_p]),
+        "car_attn_prefill": (i32, [vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, vp, f32, f32,
+                                   cache_p, vp, sz, vp]),
+        "car_attn_decode_workspace_bytes": (sz, [i32, i32, i32, i32]),
+        "car_attn_decode": (i32, [vp, vp, vp, vp, i32, i32, i32, i32, i32, vp, i32, f32, f32,
+                                  cache_p, vp, sz, vp]),
+        "car_status_string": (ctypes.c_char_p, [i32]),
+        "car_set_timing_events": (i32, [vp, vp]),
+    }
+    for name, (res, args) in sigs.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    return lib
+
+
+def _check_single_hip_runtime() -> None:
+    """The library must share torch's HIP runtime (one libamdhip64 mapped)."""
+    try:
+        with open("/proc/self/maps") as f:
+            paths = {ln.split()[-1] for ln in f if "libamdhip64" in ln}
+    except OSError:
+        return
+    real = {os.path.realpath(p) for p in paths}
+    if len(real) > 1:
+        raise ImportError(f"two HIP runtimes are loaded ({sorted(real)}); libcar.so must "
+                          "resolve libamdhip64 to torch's copy")
+
+
+_lib = _load()
+_check_single_hip_runtime()
+
+
+# --------------------------------------------------------------------------
+# helpers
+# --------------------------------------------------------------------------
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(t: torch.Tensor):
+    return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+
+
+def _need(t: torch.Tensor, name: str, dtype=None, dim=None, device=None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be on a GPU device")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if dim is not None and t.dim() != dim:
+        raise ValueError(f"{name} must have {dim} dimensions, got shape {tuple(t.shape)}")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype not in _DTYPES:
+        raise ValueError(f"unsupported dtype {t.dtype}; use float32 or bfloat16")
+    return _DTYPES[t.dtype]
+
+
+def _check(status: int, where: str) -> None:
+    if status != 0:
+        raise CarError(status, where)
+
+
+class KVCache:
+    """One layer's KV cache (separate K and V tensors).
+
+    Contiguous: ``k`` and ``v`` are [B, Hkv, max_seq, D].
+    Paged: ``k`` and ``v`` are pools [num_blocks, Hkv, 16, D] and
+    ``block_table`` is int32 [B, max_blocks_per_seq].
+    """
+
+    def __init__(self, k: torch.Tensor, v: torch.Tensor,
+                 block_table: Optional[torch.Tensor] = None):
+        _need(k, "cache k", dim=4)
+        _need(v, "cache v", dtype=k.dtype, dim=4, device=k.device)
+        if k.shape != v.shape:
+            raise ValueError("cache k and v must have the same shape")
+        self.k, self.v, self.block_table = k, v, block_table
+        if block_table is not None:
+            _need(block_table, "block_table", dtype=torch.int32, dim=2, device=k.device)
+            if k.shape[2] != 16:
+                raise ValueError("paged cache blocks must hold 16 tokens")
+        self.Hkv, self.D = k.shape[1], k.shape[3]
+
+    @property
+    def paged(self) -> bool:
+        return self.block_table is not None
+
+    def check_batch(self, B: int) -> None:
+        """The cache must hold (or map) at least B sequences."""
+        rows = self.block_table.shape[0] if self.paged else self.k.shape[0]
+        if rows < B:
+            raise ValueError(f"cache holds {rows} sequences, the call has {B}")
+
+    @property
+    def capacity(self) -> int:
+        """Tokens one sequence can hold."""
+        return self.block_table.shape[1] * 16 if self.paged else self.k.shape[2]
+
+    def _c(self) -> _CarKVCache:
+        c = _CarKVCache()
+        c.k, c.v = self.k.data_ptr(), self.v.data_ptr()
+        if self.paged:
+            c.block_table = self.block_table.data_ptr()
+            c.max_seq = 0
+            c.num_blocks = self.k.shape[0]
+            c.block_size = 16
+            c.max_blocks_per_seq = self.block_table.shape[1]
+        else:
+            c.block_table = None
+            c.max_seq = self.k.shape[2]
+        return c
+
+
+# --------------------------------------------------------------------------
+# entry points
+# --------------------------------------------------------------------------
+
+def set_timing_events(start: Optional[torch.cuda.Event], stop: Optional[torch.cuda.Event]):
+    """Record ``start``/``stop`` around the main attention kernel of the
+    following attn_prefill / attn_decode calls (None, None switches off).
+    The events must already exist (recorded once)."""
+    if start is None or stop is None:
+        _check(_lib.car_set_timing_events(None, None), "set_timing_events")
+    else:
+        _check(_lib.car_set_timing_events(ctypes.c_void_p(start.cuda_event),
+                                          ctypes.c_void_p(stop.cuda_event)),
+               "set_timing_events")
+
+
+def rope_apply(x: torch.Tensor, positions: torch.Tensor, theta: float = 10000.0) -> torch.Tensor:
+    """Rotate x [B, H, S, D] in place by RoPE at positions int32 [B, S]."""
+    _need(x, "x", dim=4)
+    B, H, S, D = x.shape
+    _need(positions, "positions", dtype=torch.int32, dim=2, device=x.device)
+    if tuple(positions.shape) != (B, S):
+        raise ValueError("positions must be [B, S]")
+    _check(_lib.car_rope_apply(_ptr(x), _dtype_code(x), B, H, S, D, _ptr(positions),
+                               float(theta), _stream(x)), "rope_apply")
+    return x
+
+
+def kv_cache_append(cache: KVCache, k: torch.Tensor, v: torch.Tensor,
+                    positions: torch.Tensor) -> None:
+    """Store rotated keys k and values v [B, Hkv, S, D] at cache index == position."""
+    _need(k, "k", dtype=cache.k.dtype, dim=4, device=cache.k.device)
+    _need(v, "v", dtype=cache.k.dtype, dim=4, device=cache.k.device)
+    if k.shape != v.shape:
+        raise ValueError("k and v must have the same shape")
+    B, Hkv, S, D = k.shape
+    if Hkv != cache.Hkv or D != cache.D:
+        raise ValueError("k/v heads or head dim do not match the cache")
+    cache.check_batch(B)
+    _need(positions, "positions", dtype=torch.int32, dim=2, device=k.device)
+    if tuple(positions.shape) != (B, S):
+        raise ValueError("positions must be [B, S]")
+    c = cache._c()
+    _check(_lib.car_kv_cache_append(ctypes.byref(c), _dtype_code(k), _ptr(k), _ptr(v), B, Hkv,
+                                    S, D, _ptr(positions), _stream(k)), "kv_cache_append")
+
+
+def prefill_workspace_bytes(dtype: torch.dtype, B: int, Hkv: int, S: int, D: int) -> int:
+    return int(_lib.car_attn_prefill_workspace_bytes(_DTYPES[dtype], B, Hkv, S, D, None))
+
+
+def decode_workspace_bytes(B: int, Hq: int, D: int, max_seq_len: int) -> int:
+    return int(_lib.car_attn_decode_workspace_bytes(B, Hq, D, max_seq_len))
+
+
+def _workspace(nbytes: int, device, workspace: Optional[torch.Tensor]) -> torch.Tensor:
+    if workspace is None:
+        return torch.empty(max(nbytes, 16), dtype=torch.uint8, device=device)
+    _need(workspace, "workspace", device=device)
+    if workspace.numel() * workspace.element_size() < nbytes:
+        raise ValueError(f"workspace holds fewer than the {nbytes} bytes required")
+    return workspace
+
+
+def attn_prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, positions: torch.Tensor,
+                 theta: float = 10000.0, scale: Optional[float] = None,
+                 cache: Optional[KVCache] = None, out: Optional[torch.Tensor] = None,
+                 workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Causal attention over a prompt with RoPE on q and k (see car_attn_prefill).
+
+    q [B, Hq, S, D]; k, v [B, Hkv, S, D]; positions int32 [B, S], strictly
+    increasing per sequence.  With ``cache`` the rotated keys and the values
+    are also stored at index == position.  Returns out [B, Hq, S, D].
+    """
+    _need(q, "q", dim=4)
+    _need(k, "k", dtype=q.dtype, dim=4, device=q.device)
+    _need(v, "v", dtype=q.dtype, dim=4, device=q.device)
+    B, Hq, S, D = q.shape
+    if k.shape != v.shape or k.shape[0] != B or k.shape[2] != S or k.shape[3] != D:
+        raise ValueError("k and v must be [B, Hkv, S, D] matching q")
+    Hkv = k.shape[1]
+    _need(positions, "positions", dtype=torch.int32, dim=2, device=q.device)
+    if tuple(positions.shape) != (B, S):
+        raise ValueError("positions must be [B, S]")
+    if out is None:
+        out = torch.empty_like(q)
+    _need(out, "out", dtype=q.dtype, dim=4, device=q.device)
+    if out.shape != q.shape:
+        raise ValueError("out must have q's shape")
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    c = None
+    if cache is not None:
+        if cache.k.dtype != q.dtype or cache.k.device != q.device:
+            raise ValueError("cache dtype/device must match q")
+        if cache.Hkv != Hkv or cache.D != D:
+            raise ValueError("cache heads or head dim do not match k")
+        cache.check_batch(B)
+        c = cache._c()
+    dt = _dtype_code(q)
+    need = int(_lib.car_attn_prefill_workspace_bytes(dt, B, Hkv, S, D, None))
+    ws = _workspace(need, q.device, workspace)
+    _check(_lib.car_attn_prefill(_ptr(q), _ptr(k), _ptr(v), _ptr(out), dt, B, Hq, Hkv, S, D,
+                                 _ptr(positions), float(theta), float(scale),
+                                 ctypes.byref(c) if c is not None else None, _ptr(ws),
+                                 ws.numel() * ws.element_size(), _stream(q)), "attn_prefill")
+    return out
+
+
+def attn_decode(q: torch.Tensor, k_new: torch.Tensor, v_new: torch.Tensor,
+                seq_lens: torch.Tensor, cache: KVCache, max_seq_len: int,
+                theta: float = 10000.0, scale: Optional[float] = None,
+                out: Optional[torch.Tensor] = None,
+                workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """One decode step (see car_attn_decode).
+
+    q [B, Hq, D]; k_new, v_new [B, Hkv, D] (not rotated); seq_lens int32 [B]
+    (tokens already cached = position of the new token); ``max_seq_len`` is a
+    host bound on seq_lens + 1.  Writes the new key/value into the cache and
+    returns out [B, Hq, D].
+    """
+    _need(q, "q", dim=3)
+    _need(k_new, "k_new", dtype=q.dtype, dim=3, device=q.device)
+    _need(v_new, "v_new", dtype=q.dtype, dim=3, device=q.device)
+    B, Hq, D = q.shape
+    if k_new.shape != v_new.shape or k_new.shape[0] != B or k_new.shape[2] != D:
+        raise ValueError("k_new and v_new must be [B, Hkv, D] matching q")
+    Hkv = k_new.shape[1]
+    _need(seq_lens, "seq_lens", dtype=torch.int32, dim=1, device=q.device)
+    if seq_lens.shape[0] != B:
+        raise ValueError("seq_lens must be [B]")
+    if cache.k.dtype != q.dtype or cache.k.device != q.device:
+        raise ValueError("cache dtype/device must match q")
+    if cache.Hkv != Hkv or cache.D != D:
+        raise ValueError("cache heads or head dim do not match k_new")
+    cache.check_batch(B)
+    if out is None:
+        out = torch.empty_like(q)
+    _need(out, "out", dtype=q.dtype, dim=3, device=q.device)
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    need = int(_lib.car_attn_decode_workspace_bytes(B, Hq, D, int(max_seq_len)))
+    ws = _workspace(need, q.device, workspace)
+    c = cache._c()
+    _check(_lib.car_attn_decode(_ptr(q), _ptr(k_new), _ptr(v_new), _ptr(out), _dtype_code(q),
+                                B, Hq, Hkv, D, _ptr(seq_lens), int(max_seq_len), float(theta),
+                                float(scale), ctypes.byref(c), _ptr(ws),
+                                ws.numel() * ws.element_size(), _stream(q)), "attn_decode")
+    return out

@@ -1,0 +1,207 @@
+// C-ABI entry points (include/car.h): argument validation, RoPE frequency
+// table, workspace sizing and dispatch to the HIP kernels.  Every check runs
+// before any launch; a failed check returns its status with nothing
+// enqueued.
+#include <math.h>
+#include <stdint.h>
+
+#include <atomic>
+
+#include "car.h"
+#include "launch.hpp"
+
+using namespace car;
+
+namespace {
+
+std::atomic<hipEvent_t> g_ev_start{nullptr};
+std::atomic<hipEvent_t> g_ev_stop{nullptr};
+
+TimedLaunch timing() {
+  TimedLaunch t{g_ev_start.load(), g_ev_stop.load()};
+  if (t.start == nullptr || t.stop == nullptr) t.start = t.stop = nullptr;
+  return t;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool dtype_ok(car_dtype dt) { return dt == CAR_DTYPE_F32 || dt == CAR_DTYPE_BF16; }
+bool head_dim_ok(int D) { return D == 64 || D == 128; }
+size_t elem_bytes(car_dtype dt) { return dt == CAR_DTYPE_F32 ? 4 : 2; }
+bool positive_finite(float x) { return isfinite(x) && x > 0.f; }
+
+car_status from_hip(hipError_t e) { return e == hipSuccess ? CAR_OK : CAR_ERR_HIP; }
+
+// theta^(-2i/D) for i < D/2, in double, split into float hi + lo.
+RopeFreq make_freq(int D, float theta) {
+  RopeFreq f{};
+  for (int i = 0; i < D / 2; ++i) {
+    const double x = pow((double)theta, -2.0 * i / (double)D);
+    f.hi[i] = (float)x;
+    f.lo[i] = (float)(x - (double)f.hi[i]);
+  }
+  return f;
+}
+
+// Validates a cache description; fills the device view and its capacity.
+car_status check_cache(const car_kv_cache* c, CacheArgs* out, int64_t* capacity) {
+  if (c == nullptr || c->k == nullptr || c->v == nullptr) return CAR_ERR_INVALID_ARGUMENT;
+  if (!aligned16(c->k) || !aligned16(c->v)) return CAR_ERR_INVALID_ARGUMENT;
+  CacheArgs a{};
+  a.k = c->k;
+  a.v = c->v;
+  a.table = c->block_table;
+  if (c->block_table != nullptr) {
+    if (c->block_size != 16) return CAR_ERR_UNSUPPORTED;
+    if (c->num_blocks <= 0 || c->max_blocks_per_seq <= 0) return CAR_ERR_INVALID_ARGUMENT;
+    if ((int64_t)c->max_blocks_per_seq * 16 > INT32_MAX) return CAR_ERR_INVALID_ARGUMENT;
+    a.num_blocks = c->num_blocks;
+    a.mbps = c->max_blocks_per_seq;
+    *capacity = (int64_t)c->max_blocks_per_seq * 16;
+  } else {
+    if (c->max_seq <= 0) return CAR_ERR_INVALID_ARGUMENT;
+    a.max_seq = c->max_seq;
+    *capacity = c->max_seq;
+  }
+  *out = a;
+  return CAR_OK;
+}
+
+int64_t prefill_ws_bytes(car_dtype dt, int B, int Hkv, int S, int D) {
+  return (int64_t)B * Hkv * S * D * (int64_t)elem_bytes(dt);
+}
+
+int decode_nsplit(int max_seq_len) { return (max_seq_len + DECODE_SPLIT - 1) / DECODE_SPLIT; }
+
+}  // namespace
+
+extern "C" {
+
+const char* car_status_string(car_status s) {
+  switch (s) {
+    case CAR_OK: return "CAR_OK";
+    case CAR_ERR_INVALID_ARGUMENT: return "CAR_ERR_INVALID_ARGUMENT: invalid argument";
+    case CAR_ERR_UNSUPPORTED: return "CAR_ERR_UNSUPPORTED: configuration not built";
+    case CAR_ERR_WORKSPACE: return "CAR_ERR_WORKSPACE: workspace missing or too small";
+    case CAR_ERR_HIP: return "CAR_ERR_HIP: HIP runtime error at launch";
+  }
+  return "unknown car_status";
+}
+
+car_status car_set_timing_events(hipEvent_t start, hipEvent_t stop) {
+  g_ev_start.store(start);
+  g_ev_stop.store(stop);
+  return CAR_OK;
+}
+
+car_status car_rope_apply(void* x, car_dtype dtype, int B, int H, int S, int D,
+                          const int32_t* positions, float theta, hipStream_t stream) {
+  if (!dtype_ok(dtype) || !head_dim_ok(D)) return CAR_ERR_UNSUPPORTED;
+  if (B < 0 || H < 0 || S < 0 || !positive_finite(theta)) return CAR_ERR_INVALID_ARGUMENT;
+  if ((int64_t)B * H * S == 0) return CAR_OK;
+  if (x == nullptr || positions == nullptr || !aligned16(x)) return CAR_ERR_INVALID_ARGUMENT;
+  return from_hip(launch_rope_apply(dtype == CAR_DTYPE_F32 ? F32 : BF16, D, x, B, H, S,
+                                    positions, make_freq(D, theta), stream));
+}
+
+car_status car_kv_cache_append(const car_kv_cache* cache, car_dtype dtype, const void* k,
+                               const void* v, int B, int Hkv, int S, int D,
+                               const int32_t* positions, hipStream_t stream) {
+  if (!dtype_ok(dtype) || !head_dim_ok(D)) return CAR_ERR_UNSUPPORTED;
+  if (B < 0 || Hkv < 0 || S < 0) return CAR_ERR_INVALID_ARGUMENT;
+  if (cache != nullptr && cache->block_table != nullptr && cache->block_size != 16)
+    return CAR_ERR_UNSUPPORTED;
+  if ((int64_t)B * Hkv * S == 0) return CAR_OK;
+  if (k == nullptr || v == nullptr || positions == nullptr || !aligned16(k) || !aligned16(v))
+    return CAR_ERR_INVALID_ARGUMENT;
+  CacheArgs c;
+  int64_t cap = 0;
+  const car_status cs = check_cache(cache, &c, &cap);
+  if (cs != CAR_OK) return cs;
+  return from_hip(launch_kv_append(dtype == CAR_DTYPE_F32 ? F32 : BF16, D,
+                                   cache->block_table != nullptr, c, k, v, B, Hkv, S, positions,
+                                   stream));
+}
+
+size_t car_attn_prefill_workspace_bytes(car_dtype dtype, int B, int Hkv, int S, int D,
+                                        const car_kv_cache* cache) {
+  (void)cache;
+  if (!dtype_ok(dtype) || !head_dim_ok(D) || B < 0 || Hkv < 0 || S < 0) return 0;
+  return (size_t)prefill_ws_bytes(dtype, B, Hkv, S, D);
+}
+
+car_status car_attn_prefill(const void* q, const void* k, const void* v, void* out,
+                            car_dtype dtype, int B, int Hq, int Hkv, int S, int D,
+                            const int32_t* positions, float theta, float scale,
+                            const car_kv_cache* cache, void* workspace, size_t workspace_bytes,
+                            hipStream_t stream) {
+  if (!dtype_ok(dtype) || !head_dim_ok(D)) return CAR_ERR_UNSUPPORTED;
+  if (cache != nullptr && cache->block_table != nullptr && cache->block_size != 16)
+    return CAR_ERR_UNSUPPORTED;
+  if (B < 0 || Hq < 0 || Hkv < 0 || S < 0) return CAR_ERR_INVALID_ARGUMENT;
+  if (!positive_finite(theta) || !positive_finite(scale)) return CAR_ERR_INVALID_ARGUMENT;
+  if (Hkv == 0 ? Hq != 0 : (Hq % Hkv) != 0) return CAR_ERR_INVALID_ARGUMENT;
+  if ((int64_t)B * Hq * S == 0) return CAR_OK;
+  if (q == nullptr || k == nullptr || v == nullptr || out == nullptr || positions == nullptr)
+    return CAR_ERR_INVALID_ARGUMENT;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out))
+    return CAR_ERR_INVALID_ARGUMENT;
+  CacheArgs c{};
+  int64_t cap = 0;
+  if (cache != nullptr) {
+    const car_status cs = check_cache(cache, &c, &cap);
+    if (cs != CAR_OK) return cs;
+  }
+  const int64_t need = prefill_ws_bytes(dtype, B, Hkv, S, D);
+  if (workspace == nullptr || !aligned16(workspace) || (int64_t)workspace_bytes < need)
+    return CAR_ERR_WORKSPACE;
+
+  const Dtype dt = dtype == CAR_DTYPE_F32 ? F32 : BF16;
+  const RopeFreq fr = make_freq(D, theta);
+  hipError_t e = launch_prefill_prep(dt, D, cache != nullptr && cache->block_table != nullptr,
+                                     cache != nullptr ? &c : nullptr, k, v, workspace, B, Hkv, S,
+                                     positions, fr, stream);
+  if (e != hipSuccess) return CAR_ERR_HIP;
+  return from_hip(launch_prefill_attention(dt, D, q, workspace, v, out, B, Hq, Hkv, S,
+                                           positions, fr, scale, stream, timing()));
+}
+
+size_t car_attn_decode_workspace_bytes(int B, int Hq, int D, int max_seq_len) {
+  if (B < 0 || Hq < 0 || !head_dim_ok(D) || max_seq_len < 1) return 0;
+  return (size_t)B * Hq * decode_nsplit(max_seq_len) * decode_partial_words(D) * sizeof(float);
+}
+
+car_status car_attn_decode(const void* q, const void* k_new, const void* v_new, void* out,
+                           car_dtype dtype, int B, int Hq, int Hkv, int D,
+                           const int32_t* seq_lens, int max_seq_len, float theta, float scale,
+                           const car_kv_cache* cache, void* workspace, size_t workspace_bytes,
+                           hipStream_t stream) {
+  if (!dtype_ok(dtype) || !head_dim_ok(D)) return CAR_ERR_UNSUPPORTED;
+  if (cache != nullptr && cache->block_table != nullptr && cache->block_size != 16)
+    return CAR_ERR_UNSUPPORTED;
+  if (B < 0 || Hq < 0 || Hkv < 0 || max_seq_len < 1) return CAR_ERR_INVALID_ARGUMENT;
+  if (!positive_finite(theta) || !isfinite(scale)) return CAR_ERR_INVALID_ARGUMENT;
+  if (Hkv == 0 ? Hq != 0 : (Hq % Hkv) != 0) return CAR_ERR_INVALID_ARGUMENT;
+  if ((int64_t)B * Hq == 0) return CAR_OK;
+  const int group = Hq / Hkv;
+  if (group != 1 && group != 2 && group != 4 && group != 8) return CAR_ERR_UNSUPPORTED;
+  if (q == nullptr || k_new == nullptr || v_new == nullptr || out == nullptr ||
+      seq_lens == nullptr)
+    return CAR_ERR_INVALID_ARGUMENT;
+  if (!aligned16(q) || !aligned16(k_new) || !aligned16(v_new) || !aligned16(out))
+    return CAR_ERR_INVALID_ARGUMENT;
+  CacheArgs c;
+  int64_t cap = 0;
+  const car_status cs = check_cache(cache, &c, &cap);
+  if (cs != CAR_OK) return cs;
+  if (max_seq_len > cap) return CAR_ERR_INVALID_ARGUMENT;
+  const size_t need = car_attn_decode_workspace_bytes(B, Hq, D, max_seq_len);
+  if (workspace == nullptr || !aligned16(workspace) || workspace_bytes < need)
+    return CAR_ERR_WORKSPACE;
+  return from_hip(launch_decode(dtype == CAR_DTYPE_F32 ? F32 : BF16, D, group,
+                                cache->block_table != nullptr, q, k_new, v_new, out, B, Hq, Hkv,
+                                seq_lens, decode_nsplit(max_seq_len), c,
+                                static_cast<float*>(workspace), make_freq(D, theta), scale,
+                                stream, timing()));
+}
+
+}  // extern "C"

@@ -1,0 +1,67 @@
+// Internal interface between the C-ABI shim (car_api.cpp) and the kernel
+// translation units.  Plain structs passed by value as kernel arguments.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace car {
+
+// Per-pair RoPE frequency theta^(-2i/D) as an unevaluated float sum hi + lo.
+struct RopeFreq {
+  float hi[64];
+  float lo[64];
+};
+
+// Device view of one layer's KV cache (see car_kv_cache in car.h).
+struct CacheArgs {
+  void* k;
+  void* v;
+  const int32_t* table;  // nullptr when contiguous
+  int max_seq;           // contiguous: slots per sequence
+  int num_blocks;        // paged: pool size in blocks
+  int mbps;              // paged: row length of the block table
+};
+
+enum Dtype { F32 = 0, BF16 = 1 };
+
+// Launch-time timing events (benchmark hook); both null when unused.
+struct TimedLaunch {
+  hipEvent_t start;
+  hipEvent_t stop;
+};
+
+// Tokens handled by one decode workgroup (one split of the sequence).
+constexpr int DECODE_SPLIT = 256;
+// fp32 words per decode partial: running max, running sum, 2 pad, D values.
+__host__ __device__ constexpr int decode_partial_words(int D) { return D + 4; }
+
+// ---- rope_cache.hip -------------------------------------------------------
+hipError_t launch_rope_apply(Dtype dt, int D, void* x, int B, int H, int S,
+                             const int32_t* positions, const RopeFreq& fr, hipStream_t s);
+
+hipError_t launch_kv_append(Dtype dt, int D, bool paged, const CacheArgs& c, const void* k,
+                            const void* v, int B, int Hkv, int S, const int32_t* positions,
+                            hipStream_t s);
+
+// Rotates k into k_rot (dense [B,Hkv,S,D]) and, if cache != nullptr, also
+// stores the rotated keys and raw values into the cache.
+hipError_t launch_prefill_prep(Dtype dt, int D, bool paged, const CacheArgs* cache,
+                               const void* k, const void* v, void* k_rot, int B, int Hkv,
+                               int S, const int32_t* positions, const RopeFreq& fr,
+                               hipStream_t s);
+
+// ---- prefill.hip -----------------------------------------------------------
+hipError_t launch_prefill_attention(Dtype dt, int D, const void* q, const void* k_rot,
+                                    const void* v, void* out, int B, int Hq, int Hkv, int S,
+                                    const int32_t* positions, const RopeFreq& fr, float scale,
+                                    hipStream_t s, const TimedLaunch& tl);
+
+// ---- decode.hip ------------------------------------------------------------
+hipError_t launch_decode(Dtype dt, int D, int group, bool paged, const void* q,
+                         const void* k_new, const void* v_new, void* out, int B, int Hq,
+                         int Hkv, const int32_t* seq_lens, int nsplit, const CacheArgs& c,
+                         float* partials, const RopeFreq& fr, float scale, hipStream_t s,
+                         const TimedLaunch& tl);
+
+}  // namespace car

@@ -1,0 +1,189 @@
+// RoPE and KV-cache stores: the bandwidth-bound elementwise kernels.
+//
+// Each thread moves 16-byte vectors (8 bf16 or 4 fp32 values, i.e. 4 or 2
+// RoPE pairs) in a grid-stride loop; consecutive threads take consecutive
+// vectors of a row, so every wave reads and writes whole 256-512 byte rows.
+//
+// RoPE follows [Intuition] ("手写LLM推理引擎：重建对Tokenizer、KV Cache与RoPE的底层直觉")
+// §4: adjacent pairs (x[2i], x[2i+1]) rotated by m * theta^(-2i/D).  The cache
+// store follows [Scratch] ("从零手搓AI推理引擎") §3.2: a token is written at the
+// cache index equal to its position; paged caches resolve the index through
+// the block table as in [NanoVLLM] ("以 Nano-vLLM 为例，深入理解 LLM 推理引擎（Part 2）")
+// §05, 5.3.
+#include "common.hpp"
+
+namespace car {
+
+namespace {
+
+constexpr int kThreads = 256;
+
+inline int grid_for(int64_t nvec) {
+  const int64_t blocks = (nvec + kThreads - 1) / kThreads;
+  return (int)(blocks < 16384 ? (blocks > 0 ? blocks : 1) : 16384);
+}
+
+template <typename T, int D>
+__global__ __launch_bounds__(kThreads) void rope_apply_kernel(T* __restrict__ x,
+                                                              const int32_t* __restrict__ positions,
+                                                              int H, int S, int64_t nvec,
+                                                              RopeFreq fr) {
+  constexpr int N = Vec16<T>::N;
+  constexpr int VPR = D / N;  // vectors per row
+  for (int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x; i < nvec;
+       i += (int64_t)gridDim.x * kThreads) {
+    const int64_t row = i / VPR;
+    const int col = (int)(i % VPR) * N;
+    const int s = (int)(row % S);
+    const int b = (int)(row / ((int64_t)S * H));
+    const int pos = positions[(int64_t)b * S + s];
+    T* p = x + row * D + col;
+    float f[N];
+    load16<T>(p, f);
+    rope_rotate_regs<N>(f, pos, col / 2, fr);
+    store16<T>(p, f);
+  }
+}
+
+template <typename T, int D, bool PAGED>
+__global__ __launch_bounds__(kThreads) void kv_append_kernel(CacheArgs c,
+                                                             const T* __restrict__ k,
+                                                             const T* __restrict__ v, int Hkv,
+                                                             int S,
+                                                             const int32_t* __restrict__ positions,
+                                                             int64_t nvec) {
+  constexpr int N = Vec16<T>::N;
+  constexpr int VPR = D / N;
+  const int last = cache_last_slot<PAGED>(c);
+  for (int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x; i < nvec;
+       i += (int64_t)gridDim.x * kThreads) {
+    const int64_t row = i / VPR;
+    const int col = (int)(i % VPR) * N;
+    const int s = (int)(row % S);
+    const int64_t bh = row / S;
+    const int hk = (int)(bh % Hkv);
+    const int b = (int)(bh / Hkv);
+    const int pos = min(max(positions[(int64_t)b * S + s], 0), last);
+    const int64_t dst = cache_row<PAGED>(c, b, hk, Hkv, pos) * D + col;
+    *reinterpret_cast<uint4*>(static_cast<T*>(c.k) + dst) =
+        *reinterpret_cast<const uint4*>(k + row * D + col);
+    *reinterpret_cast<uint4*>(static_cast<T*>(c.v) + dst) =
+        *reinterpret_cast<const uint4*>(v + row * D + col);
+  }
+}
+
+// Rotate the prompt's keys once (dense copy for the attention kernel) and,
+// with a cache, store rotated keys and raw values at their positions.
+template <typename T, int D, bool PAGED, bool CACHE>
+__global__ __launch_bounds__(kThreads) void prefill_prep_kernel(
+    CacheArgs c, const T* __restrict__ k, const T* __restrict__ v, T* __restrict__ k_rot,
+    int Hkv, int S, const int32_t* __restrict__ positions, int64_t nvec, RopeFreq fr) {
+  constexpr int N = Vec16<T>::N;
+  constexpr int VPR = D / N;
+  for (int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x; i < nvec;
+       i += (int64_t)gridDim.x * kThreads) {
+    const int64_t row = i / VPR;
+    const int col = (int)(i % VPR) * N;
+    const int s = (int)(row % S);
+    const int64_t bh = row / S;
+    const int b = (int)(bh / Hkv);
+    const int pos = positions[(int64_t)b * S + s];
+    float f[N];
+    load16<T>(k + row * D + col, f);
+    rope_rotate_regs<N>(f, pos, col / 2, fr);
+    store16<T>(k_rot + row * D + col, f);
+    if constexpr (CACHE) {
+      const int hk = (int)(bh % Hkv);
+      const int slot = min(max(pos, 0), cache_last_slot<PAGED>(c));
+      const int64_t dst = cache_row<PAGED>(c, b, hk, Hkv, slot) * D + col;
+      store16<T>(static_cast<T*>(c.k) + dst, f);
+      *reinterpret_cast<uint4*>(static_cast<T*>(c.v) + dst) =
+          *reinterpret_cast<const uint4*>(v + row * D + col);
+    }
+  }
+}
+
+template <typename T, int D>
+hipError_t rope_apply_t(void* x, int B, int H, int S, const int32_t* positions,
+                        const RopeFreq& fr, hipStream_t st) {
+  const int64_t nvec = (int64_t)B * H * S * (D / Vec16<T>::N);
+  hipLaunchKernelGGL((rope_apply_kernel<T, D>), dim3(grid_for(nvec)), dim3(kThreads), 0, st,
+                     static_cast<T*>(x), positions, H, S, nvec, fr);
+  return hipGetLastError();
+}
+
+template <typename T, int D>
+hipError_t kv_append_t(bool paged, const CacheArgs& c, const void* k, const void* v, int B,
+                       int Hkv, int S, const int32_t* positions, hipStream_t st) {
+  const int64_t nvec = (int64_t)B * Hkv * S * (D / Vec16<T>::N);
+  const T* kk = static_cast<const T*>(k);
+  const T* vv = static_cast<const T*>(v);
+  if (paged)
+    hipLaunchKernelGGL((kv_append_kernel<T, D, true>), dim3(grid_for(nvec)), dim3(kThreads), 0,
+                       st, c, kk, vv, Hkv, S, positions, nvec);
+  else
+    hipLaunchKernelGGL((kv_append_kernel<T, D, false>), dim3(grid_for(nvec)), dim3(kThreads),
+                       0, st, c, kk, vv, Hkv, S, positions, nvec);
+  return hipGetLastError();
+}
+
+template <typename T, int D>
+hipError_t prefill_prep_t(bool paged, const CacheArgs* cache, const void* k, const void* v,
+                          void* k_rot, int B, int Hkv, int S, const int32_t* positions,
+                          const RopeFreq& fr, hipStream_t st) {
+  const int64_t nvec = (int64_t)B * Hkv * S * (D / Vec16<T>::N);
+  const T* kk = static_cast<const T*>(k);
+  const T* vv = static_cast<const T*>(v);
+  T* kr = static_cast<T*>(k_rot);
+  const dim3 grid(grid_for(nvec)), block(kThreads);
+  if (cache == nullptr) {
+    CacheArgs none{};
+    hipLaunchKernelGGL((prefill_prep_kernel<T, D, false, false>), grid, block, 0, st, none, kk,
+                       vv, kr, Hkv, S, positions, nvec, fr);
+  } else if (paged) {
+    hipLaunchKernelGGL((prefill_prep_kernel<T, D, true, true>), grid, block, 0, st, *cache, kk,
+                       vv, kr, Hkv, S, positions, nvec, fr);
+  } else {
+    hipLaunchKernelGGL((prefill_prep_kernel<T, D, false, true>), grid, block, 0, st, *cache,
+                       kk, vv, kr, Hkv, S, positions, nvec, fr);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_rope_apply(Dtype dt, int D, void* x, int B, int H, int S,
+                             const int32_t* positions, const RopeFreq& fr, hipStream_t s) {
+  if (dt == F32)
+    return D == 64 ? rope_apply_t<float, 64>(x, B, H, S, positions, fr, s)
+                   : rope_apply_t<float, 128>(x, B, H, S, positions, fr, s);
+  return D == 64 ? rope_apply_t<bf16_t, 64>(x, B, H, S, positions, fr, s)
+                 : rope_apply_t<bf16_t, 128>(x, B, H, S, positions, fr, s);
+}
+
+hipError_t launch_kv_append(Dtype dt, int D, bool paged, const CacheArgs& c, const void* k,
+                            const void* v, int B, int Hkv, int S, const int32_t* positions,
+                            hipStream_t s) {
+  if (dt == F32)
+    return D == 64 ? kv_append_t<float, 64>(paged, c, k, v, B, Hkv, S, positions, s)
+                   : kv_append_t<float, 128>(paged, c, k, v, B, Hkv, S, positions, s);
+  return D == 64 ? kv_append_t<bf16_t, 64>(paged, c, k, v, B, Hkv, S, positions, s)
+                 : kv_append_t<bf16_t, 128>(paged, c, k, v, B, Hkv, S, positions, s);
+}
+
+hipError_t launch_prefill_prep(Dtype dt, int D, bool paged, const CacheArgs* cache,
+                               const void* k, const void* v, void* k_rot, int B, int Hkv,
+                               int S, const int32_t* positions, const RopeFreq& fr,
+                               hipStream_t s) {
+  if (dt == F32)
+    return D == 64
+               ? prefill_prep_t<float, 64>(paged, cache, k, v, k_rot, B, Hkv, S, positions, fr, s)
+               : prefill_prep_t<float, 128>(paged, cache, k, v, k_rot, B, Hkv, S, positions, fr,
+                                            s);
+  return D == 64
+             ? prefill_prep_t<bf16_t, 64>(paged, cache, k, v, k_rot, B, Hkv, S, positions, fr, s)
+             : prefill_prep_t<bf16_t, 128>(paged, cache, k, v, k_rot, B, Hkv, S, positions, fr,
+                                           s);
+}
+
+}  // namespace car

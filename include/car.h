@@ -1,0 +1,201 @@
+/*
+ * car.h -- causal attention with rotary position embedding (RoPE) and a KV
+ * cache, as a C ABI over plain device pointers, for AMD MI355X (gfx950).
+ *
+ * What is computed is defined on these pages (titles as published):
+ *   [Guide]     "手写LLM推理引擎：从黑盒到白盒的底层实现指南"
+ *   [Intuition] "手写LLM推理引擎：重建对Tokenizer、KV Cache与RoPE的底层直觉"
+ *   [Scratch]   "从零手搓AI推理引擎：告别调包思维，深入底层构建与优化"
+ *   [NanoVLLM]  "以 Nano-vLLM 为例，深入理解 LLM 推理引擎（Part 2）"
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * Layout.  Row-major, densely packed, head-major tensors ([Scratch] §3.1:
+ *   the head split gives Q, K, V of shape (B, H, S, D); [Intuition] §5:
+ *   a batch, head, sequence, dim order for the cache):
+ *     q, out      [B, Hq,  S, D]      (decode: [B, Hq, D])
+ *     k, v        [B, Hkv, S, D]      (decode: [B, Hkv, D])
+ *     positions   int32 [B, S]        (decode uses seq_lens instead)
+ *   Query head hq reads KV head hq / (Hq / Hkv) (contiguous GQA groups).
+ * Element type.  CAR_DTYPE_F32 or CAR_DTYPE_BF16 for every float tensor of
+ *   one call, caches included.  Arithmetic is fp32 (MFMA accumulation in
+ *   fp32 for bf16); outputs are rounded to the element type, nearest-even.
+ * Head dimension.  D must be 64 or 128; otherwise CAR_ERR_UNSUPPORTED.
+ * RoPE ([Intuition] §4).  Each adjacent pair (x[2i], x[2i+1]) is rotated by
+ *   the angle m * theta^(-2i/D), m the token's position:
+ *   x'[2i] = x[2i] cos - x[2i+1] sin,  x'[2i+1] = x[2i] sin + x[2i+1] cos.
+ *   V is never rotated.  `theta` is the base (10000 on the pages).
+ * Positions and the cache.  A token's position equals its cache index
+ *   ([Scratch] §3.2); positions are 0-based.
+ * Ownership.  The caller owns every buffer.  The library never allocates,
+ *   frees or keeps a pointer after a call returns, and holds no state
+ *   except the benchmark event pair of car_set_timing_events().
+ * Asynchrony.  Each call only enqueues kernels on `stream` (0 = the null
+ *   stream) and returns; results are ready when the stream reaches them.
+ * Errors.  Everything the host can check (null pointers, sizes, D, Hq/Hkv,
+ *   16-byte alignment of every float tensor, block size, workspace size) is
+ *   checked before any launch, and a failed check returns its status with
+ *   nothing enqueued.  Nothing throws or aborts across the ABI.  Values in
+ *   device memory (positions, seq_lens, block_table) cannot be checked by
+ *   the host: the kernels clamp indices so that memory outside the given
+ *   buffers is never touched, but results for out-of-range values are
+ *   unspecified.
+ */
+#ifndef CAR_H_
+#define CAR_H_
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum car_dtype {
+  CAR_DTYPE_F32 = 0,
+  CAR_DTYPE_BF16 = 1
+} car_dtype;
+
+typedef enum car_status {
+  CAR_OK = 0,
+  CAR_ERR_INVALID_ARGUMENT = 1, /* null pointer, negative size, Hq % Hkv != 0,
+                                   pointer not 16-byte aligned, bad cache shape */
+  CAR_ERR_UNSUPPORTED = 2,      /* well formed but not built: D not in {64, 128},
+                                   block_size != 16, Hq/Hkv not in {1, 2, 4, 8},
+                                   unknown dtype */
+  CAR_ERR_WORKSPACE = 3,        /* workspace missing or smaller than required */
+  CAR_ERR_HIP = 4               /* the HIP runtime reported an error at launch */
+} car_status;
+
+/*
+ * One layer's KV cache.  K and V are separate tensors ([NanoVLLM] §05, 5.2).
+ *   contiguous (block_table == NULL): k, v are [B, Hkv, max_seq, D];
+ *     token t of sequence b, head hk is row (b*Hkv + hk)*max_seq + t.
+ *   paged (block_table != NULL): k, v are pools [num_blocks, Hkv, block_size, D]
+ *     and block_table is int32 [B, max_blocks_per_seq]; token t of sequence b
+ *     lives in physical block block_table[b][t / block_size] at offset
+ *     t % block_size ([NanoVLLM] §05, 5.3; [Intuition] §5: pages of 16 tokens).
+ *     block_size must be 16.
+ * The caller keeps the table entries of every block a call touches in
+ * [0, num_blocks) and distinct across sequences.
+ */
+typedef struct car_kv_cache {
+  void* k;
+  void* v;
+  const int32_t* block_table;
+  int32_t max_seq;            /* contiguous: slots per sequence; ignored if paged */
+  int32_t num_blocks;         /* paged only */
+  int32_t block_size;         /* paged only; must be 16 */
+  int32_t max_blocks_per_seq; /* paged only: row length of block_table */
+} car_kv_cache;
+
+/*
+ * car_rope_apply -- rotate x in place by RoPE ([Intuition] §4).
+ *   x          [B, H, S, D] device, read and written.
+ *   positions  int32 [B, S] device: position m of token s of sequence b.
+ * Every pair of every head and token is rotated by its own angle.
+ */
+car_status car_rope_apply(void* x, car_dtype dtype, int B, int H, int S, int D,
+                          const int32_t* positions, float theta, hipStream_t stream);
+
+/*
+ * car_kv_cache_append -- store already-rotated keys and raw values in the
+ * cache at index == position ([Scratch] §3.2; [Guide] §2.5: K and V of a
+ * token never change once computed, so they are written once and kept).
+ *   k, v       [B, Hkv, S, D] device, read only.
+ *   positions  int32 [B, S] device: cache index of each token; every index
+ *              must lie below the cache capacity (max_seq, or
+ *              max_blocks_per_seq * 16 when paged).
+ *   cache      host pointer to the cache description; its k, v are written.
+ */
+car_status car_kv_cache_append(const car_kv_cache* cache, car_dtype dtype,
+                               const void* k, const void* v, int B, int Hkv, int S,
+                               int D, const int32_t* positions, hipStream_t stream);
+
+/*
+ * Bytes of device workspace car_attn_prefill needs for these sizes: room for
+ * the rotated keys [B, Hkv, S, D] in `dtype`.  Returns 0 for invalid sizes.
+ * `cache` may be NULL; the size does not depend on it.
+ */
+size_t car_attn_prefill_workspace_bytes(car_dtype dtype, int B, int Hkv, int S, int D,
+                                        const car_kv_cache* cache);
+
+/*
+ * car_attn_prefill -- causal multi-head attention over a whole prompt.
+ *   out[b, hq, i] = sum_j softmax_j(scale * q'[b,hq,i] . k'[b,hk,j]) v[b,hk,j]
+ * over keys j with positions[b][j] <= positions[b][i], where q' and k' are q
+ * and k rotated by RoPE at their positions ([Guide] §2.3 and §5.1: scaled
+ * dot product, the upper-right triangle masked to -inf; [Scratch] §3.1 and
+ * §3.3).  It runs as a tiled online softmax ([Scratch] §3.4: a running
+ * maximum m and sum l per query row, the earlier accumulation corrected at
+ * each key block) and never stores the S x S score matrix.
+ *   q          [B, Hq, S, D] device;   k, v  [B, Hkv, S, D] device (k not rotated).
+ *   out        [B, Hq, S, D] device, written.
+ *   positions  int32 [B, S] device, strictly increasing along s for every b
+ *              (so that the position order equals the index order).
+ *   scale      multiplies the scores before the softmax; 1/sqrt(D) on the
+ *              pages ([Intuition] §4).
+ *   cache      NULL: nothing is stored.  Otherwise every rotated key and raw
+ *              value is also stored at index positions[b][s], as by
+ *              car_kv_cache_append.
+ *   workspace  device scratch of at least car_attn_prefill_workspace_bytes();
+ *              its contents on entry are ignored and on exit unspecified.
+ * S == 0 is a no-op returning CAR_OK.
+ */
+car_status car_attn_prefill(const void* q, const void* k, const void* v, void* out,
+                            car_dtype dtype, int B, int Hq, int Hkv, int S, int D,
+                            const int32_t* positions, float theta, float scale,
+                            const car_kv_cache* cache, void* workspace,
+                            size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * Bytes of device workspace car_attn_decode needs: per (sequence, query head)
+ * one partial (running max, running sum, D accumulators) in fp32 for every
+ * 256-token split of max_seq_len tokens.  Returns 0 for invalid sizes.
+ */
+size_t car_attn_decode_workspace_bytes(int B, int Hq, int D, int max_seq_len);
+
+/*
+ * car_attn_decode -- one decode step: one new query token per sequence.
+ * With L = seq_lens[b] tokens already cached, the new token's position is L
+ * ([Scratch] §3.2).  q and k_new are rotated at position L; the rotated key
+ * and raw value are written to cache index L; the query then attends over
+ * cache indices 0..L, the cached tokens and itself ([Guide] §2.5: only the
+ * new token's Q, K, V are computed; [Scratch] §3.3: with a cache the mask is
+ * a single row, all visible).
+ *   q           [B, Hq, D] device;  k_new, v_new  [B, Hkv, D] device (not rotated).
+ *   out         [B, Hq, D] device, written.
+ *   seq_lens    int32 [B] device; L + 1 must fit the cache capacity and
+ *               must not exceed max_seq_len.
+ *   max_seq_len host bound on seq_lens[b] + 1 over the batch; it sizes the
+ *               launch (tokens beyond it are not read).
+ *   cache       contiguous or paged, written at index L for every sequence.
+ *   workspace   device scratch of at least car_attn_decode_workspace_bytes();
+ *               contents on entry ignored, on exit unspecified.
+ * Calls that share a workspace must be ordered on one stream.
+ */
+car_status car_attn_decode(const void* q, const void* k_new, const void* v_new,
+                           void* out, car_dtype dtype, int B, int Hq, int Hkv, int D,
+                           const int32_t* seq_lens, int max_seq_len, float theta,
+                           float scale, const car_kv_cache* cache, void* workspace,
+                           size_t workspace_bytes, hipStream_t stream);
+
+/* Human-readable name of a status code (static storage). */
+const char* car_status_string(car_status status);
+
+/*
+ * Benchmark hook.  When both events are non-NULL, the main attention kernel
+ * of each following car_attn_prefill / car_attn_decode call is launched with
+ * `start` recorded immediately before it and `stop` immediately after it on
+ * the call's stream, so that hipEventElapsedTime(start, stop) is that
+ * kernel's duration.  Pass NULL, NULL to switch it off.  Process-wide; not
+ * meant for concurrent use from several threads.
+ */
+car_status car_set_timing_events(hipEvent_t start, hipEvent_t stop);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* CAR_H_ */

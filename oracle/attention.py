@@ -187,11 +187,9 @@ def cache_rows(cache, b: int, hk: int, n: int, block_table=None,
     """Rows 0..n-1 of sequence b, KV head hk, as an [n, D] float64 array."""
     if block_table is None:
         return _f64(cache[b, hk, :n, :])
-    rows = []
-    for t in range(n):
-        blk, off = paged_slot(block_table, b, t, block_size)
-        rows.append(_f64(cache[blk, hk, off, :]))
-    return np.stack(rows) if rows else np.zeros((0, cache.shape[-1]))
+    t = np.arange(n)
+    blocks = np.asarray(block_table)[b, t // block_size]   # paged_slot, all tokens at once
+    return _f64(cache[blocks, hk, t % block_size, :])
 
 
 def attn_decode(q, k_new, v_new, cache_k, cache_v, seq_lens,

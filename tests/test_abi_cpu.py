@@ -1,0 +1,167 @@
+"""The C-ABI library without a GPU: it loads, exports every symbol that
+include/car.h declares, and its host-side checks reject bad arguments with
+the documented status before anything is launched.
+
+Every call here fails a host check (null or misaligned pointer, bad size,
+unsupported configuration, short workspace), so no kernel is ever enqueued;
+the non-null pointers passed are never dereferenced by the host.
+"""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "car.h")
+
+OK, INVALID, UNSUPPORTED, WORKSPACE, HIP = 0, 1, 2, 3, 4
+F32, BF16 = 0, 1
+FAKE = 0x10000  # aligned, non-null, never dereferenced (every call below fails first)
+
+
+@pytest.fixture(scope="module")
+def car():
+    import causal_attention_rope_amd as m
+    return m
+
+
+@pytest.fixture(scope="module")
+def lib(car):
+    return car._lib
+
+
+def declared_functions():
+    text = open(HEADER, encoding="utf-8").read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(car_[a-z_]+)\s*\(", text)))
+
+
+def test_header_declares_the_four_entry_points():
+    names = declared_functions()
+    for n in ("car_rope_apply", "car_kv_cache_append", "car_attn_prefill", "car_attn_decode"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol(car):
+    lib = ctypes.CDLL(car.library_path)
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+
+
+def test_status_strings(lib):
+    for code in (OK, INVALID, UNSUPPORTED, WORKSPACE, HIP):
+        s = lib.car_status_string(code).decode()
+        assert s.startswith("CAR_")
+    assert "unknown" in lib.car_status_string(99).decode()
+
+
+def _cache(car, paged=False, block_size=16, max_seq=64, k=FAKE, v=FAKE):
+    c = car._CarKVCache()
+    c.k, c.v = k, v
+    if paged:
+        c.block_table = FAKE
+        c.num_blocks, c.block_size, c.max_blocks_per_seq = 8, block_size, 4
+    else:
+        c.block_table = None
+        c.max_seq = max_seq
+    return c
+
+
+def test_rope_apply_rejects(lib):
+    f = lib.car_rope_apply
+    assert f(FAKE, BF16, 1, 1, 1, 96, FAKE, 1e4, None) == UNSUPPORTED     # D
+    assert f(FAKE, 7, 1, 1, 1, 64, FAKE, 1e4, None) == UNSUPPORTED        # dtype
+    assert f(None, BF16, 1, 1, 1, 64, FAKE, 1e4, None) == INVALID         # null x
+    assert f(FAKE + 8, BF16, 1, 1, 1, 64, FAKE, 1e4, None) == INVALID     # misaligned
+    assert f(FAKE, BF16, -1, 1, 1, 64, FAKE, 1e4, None) == INVALID        # size
+    assert f(FAKE, BF16, 1, 1, 1, 64, FAKE, -1.0, None) == INVALID        # theta
+    assert f(FAKE, BF16, 1, 1, 1, 64, None, 1e4, None) == INVALID         # positions
+    assert f(None, BF16, 0, 4, 4, 64, None, 1e4, None) == OK              # empty: no-op
+
+
+def test_kv_cache_append_rejects(car, lib):
+    f = lib.car_kv_cache_append
+    c = _cache(car)
+    assert f(ctypes.byref(c), BF16, FAKE, FAKE, 1, 1, 1, 80, FAKE, None) == UNSUPPORTED
+    assert f(None, BF16, FAKE, FAKE, 1, 1, 1, 64, FAKE, None) == INVALID
+    assert f(ctypes.byref(c), BF16, None, FAKE, 1, 1, 1, 64, FAKE, None) == INVALID
+    bad = _cache(car, paged=True, block_size=32)
+    assert f(ctypes.byref(bad), BF16, FAKE, FAKE, 1, 1, 1, 64, FAKE, None) == UNSUPPORTED
+    zero = _cache(car, max_seq=0)
+    assert f(ctypes.byref(zero), BF16, FAKE, FAKE, 1, 1, 1, 64, FAKE, None) == INVALID
+    mis = _cache(car, k=FAKE + 4)
+    assert f(ctypes.byref(mis), BF16, FAKE, FAKE, 1, 1, 1, 64, FAKE, None) == INVALID
+    assert f(ctypes.byref(c), BF16, None, None, 0, 1, 1, 64, None, None) == OK
+
+
+def test_prefill_rejects(car, lib):
+    f = lib.car_attn_prefill
+    need = lib.car_attn_prefill_workspace_bytes(BF16, 2, 2, 8, 64, None)
+    assert need == 2 * 2 * 8 * 64 * 2
+    args = dict(q=FAKE, k=FAKE, v=FAKE, out=FAKE, dt=BF16, B=2, Hq=4, Hkv=2, S=8, D=64,
+                pos=FAKE, theta=1e4, scale=0.125, cache=None, ws=FAKE, wsb=need)
+
+    def call(**kw):
+        a = dict(args, **kw)
+        return f(a["q"], a["k"], a["v"], a["out"], a["dt"], a["B"], a["Hq"], a["Hkv"], a["S"],
+                 a["D"], a["pos"], a["theta"], a["scale"], a["cache"], a["ws"], a["wsb"], None)
+
+    assert call(D=80) == UNSUPPORTED
+    assert call(Hq=3) == INVALID                     # Hq % Hkv
+    assert call(scale=0.0) == INVALID
+    assert call(scale=float("nan")) == INVALID
+    assert call(q=None) == INVALID
+    assert call(out=FAKE + 2) == INVALID
+    assert call(ws=None) == WORKSPACE
+    assert call(wsb=need - 1) == WORKSPACE
+    bad = _cache(car, paged=True, block_size=8)
+    assert call(cache=ctypes.byref(bad)) == UNSUPPORTED
+    zero = _cache(car, max_seq=0)
+    assert call(cache=ctypes.byref(zero), wsb=0) == INVALID
+    assert call(S=0, q=None, ws=None) == OK          # empty prompt: no-op
+
+
+def test_decode_rejects(car, lib):
+    f = lib.car_attn_decode
+    need = lib.car_attn_decode_workspace_bytes(2, 8, 128, 300)
+    assert need == 2 * 8 * 2 * (128 + 4) * 4        # two 256-token splits
+    c = _cache(car, max_seq=512)
+    args = dict(q=FAKE, kn=FAKE, vn=FAKE, out=FAKE, dt=BF16, B=2, Hq=8, Hkv=2, D=128,
+                lens=FAKE, msl=300, theta=1e4, scale=0.088, cache=ctypes.byref(c), ws=FAKE,
+                wsb=need - 16)
+
+    def call(**kw):
+        a = dict(args, **kw)
+        return f(a["q"], a["kn"], a["vn"], a["out"], a["dt"], a["B"], a["Hq"], a["Hkv"], a["D"],
+                 a["lens"], a["msl"], a["theta"], a["scale"], a["cache"], a["ws"], a["wsb"], None)
+
+    assert call() == WORKSPACE                       # everything valid but the workspace
+    assert call(ws=None) == WORKSPACE
+    assert call(D=96) == UNSUPPORTED
+    assert call(Hq=5) == INVALID                     # Hq % Hkv
+    assert call(Hq=6) == UNSUPPORTED                 # group of 3 not built
+    assert call(Hq=32) == UNSUPPORTED                # group of 16 not built
+    assert call(lens=None) == INVALID
+    assert call(msl=0) == INVALID
+    assert call(msl=513) == INVALID                  # beyond the cache capacity
+    assert call(cache=None) == INVALID
+    bad = _cache(car, paged=True, block_size=32)
+    assert call(cache=ctypes.byref(bad)) == UNSUPPORTED
+    assert call(B=0, q=None, ws=None) == OK          # empty batch: no-op
+
+
+def test_workspace_sizes(lib):
+    assert lib.car_attn_decode_workspace_bytes(32, 32, 128, 4096) == 32 * 32 * 16 * 132 * 4
+    assert lib.car_attn_decode_workspace_bytes(64, 32, 128, 8193) == 64 * 32 * 33 * 132 * 4
+    assert lib.car_attn_decode_workspace_bytes(1, 1, 96, 10) == 0
+    assert lib.car_attn_prefill_workspace_bytes(F32, 1, 4, 128, 64, None) == 4 * 128 * 64 * 4
+    assert lib.car_attn_prefill_workspace_bytes(BF16, 1, 4, 128, 72, None) == 0
+
+
+def test_binding_refuses_cpu_tensors(car):
+    import torch
+    x = torch.zeros(1, 1, 4, 64)
+    with pytest.raises(ValueError):
+        car.rope_apply(x, torch.zeros(1, 4, dtype=torch.int32))

@@ -1,0 +1,136 @@
+"""GPU parity: attn_prefill against the oracle's full-matrix masked attention
+with explicit RoPE rotations, element by element, at sizes spanning several
+tiles with ragged tails, plus the cache it writes; the two full-size prefill
+workloads on sampled heads."""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads as W
+from helpers import TOL, bits, f64, log_case, max_abs
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+
+
+@pytest.fixture(scope="module")
+def car():
+    import causal_attention_rope_amd as m
+    return m
+
+
+def make_cache(car, case, paged, cap):
+    if case.cache_max_seq is None and not paged and cap is None:
+        return None, None
+    B, Hkv, D = case.B, case.Hkv, case.D
+    if paged:
+        mbps = (cap + 15) // 16
+        nb = B * mbps + 3
+        table = np.random.default_rng(cap).permutation(nb)[: B * mbps].reshape(B, mbps)
+        table = table.astype(np.int32)
+        ck = torch.full((nb, Hkv, 16, D), float("nan"), dtype=case.dtype, device=DEV)
+        return car.KVCache(ck, ck.clone(), torch.from_numpy(table).to(DEV)), table
+    ck = torch.full((B, Hkv, cap, D), float("nan"), dtype=case.dtype, device=DEV)
+    return car.KVCache(ck, ck.clone()), None
+
+
+def check_prefill(car, case, paged=False, cap=None, heads=None):
+    """Run the GPU prefill and compare with the oracle (on ``heads`` only if given)."""
+    cache, table = make_cache(car, case, paged, cap)
+    out = car.attn_prefill(case.q, case.k, case.v, case.positions, theta=case.theta,
+                           scale=case.scale, cache=cache)
+    torch.cuda.synchronize()
+    pos = case.positions.cpu().numpy()
+    tol = TOL[case.dtype]
+    hq_list = range(case.Hq) if heads is None else heads
+    group = case.Hq // case.Hkv
+    hk_list = sorted({hq // group for hq in hq_list})
+    worst = 0.0
+    for b in range(case.B):
+        q = f64(case.q[b:b + 1, list(hq_list)])
+        k = f64(case.k[b:b + 1, hk_list])
+        v = f64(case.v[b:b + 1, hk_list])
+        # regroup: query heads hq read KV head hq // group, i.e. index hk_list.index(...)
+        ref_out = np.empty(q.shape)
+        for i, hq in enumerate(hq_list):
+            j = hk_list.index(hq // group)
+            o, _ = oracle.attn_prefill(q[:, i:i + 1], k[:, j:j + 1], v[:, j:j + 1],
+                                       pos[b:b + 1], case.theta, case.scale)
+            ref_out[:, i] = o[:, 0]
+        got = f64(out[b:b + 1, list(hq_list)])
+        worst = max(worst, max_abs(got, ref_out))
+        if cache is not None:
+            k_rot = oracle.rope_rotate(k, pos[b:b + 1][:, None, :], case.theta)
+            for j, hk in enumerate(hk_list):
+                if table is None:
+                    gk = f64(cache.k[b, hk, pos[b]])
+                    gv = cache.v[b, hk, torch.as_tensor(pos[b], device=DEV, dtype=torch.long)]
+                else:
+                    t = pos[b]
+                    blk = torch.as_tensor(table[b, t // 16], device=DEV, dtype=torch.long)
+                    off = torch.as_tensor(t % 16, device=DEV, dtype=torch.long)
+                    gk = f64(cache.k[blk, hk, off])
+                    gv = cache.v[blk, hk, off]
+                worst = max(worst, max_abs(gk, k_rot[0, j]))
+                assert torch.equal(bits(gv.cpu()), bits(case.v[b, hk].cpu())), "cached V"
+    log_case(f"{case.name}: max-abs error {worst:.3e} (tol {tol})")
+    assert worst <= tol
+    return out, cache
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16], ids=["f32", "bf16"])
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("S", [1, 2, 63, 130, 333])
+def test_prefill_shapes(car, dtype, D, S):
+    log_case(f"prefill {dtype} D={D} S={S}")
+    case = W.prefill_case(f"prefill_S{S}", 2, 4, 4, S, D, dtype, 100 + S, DEV)
+    check_prefill(car, case)
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16], ids=["f32", "bf16"])
+@pytest.mark.parametrize("group", [2, 4])
+def test_prefill_gqa(car, dtype, group):
+    log_case(f"prefill gqa group={group} {dtype}")
+    case = W.prefill_case("gqa", 1, 8, 8 // group, 200, 128, dtype, 7 + group, DEV)
+    check_prefill(car, case)
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16], ids=["f32", "bf16"])
+@pytest.mark.parametrize("paged", [False, True], ids=["contiguous", "paged"])
+def test_prefill_writes_cache_at_offset_positions(car, dtype, paged):
+    log_case(f"prefill into cache {dtype} paged={paged}")
+    case = W.prefill_case("offset", 2, 4, 2, 150, 64, dtype, 55, DEV, pos_offset=9)
+    check_prefill(car, case, paged=paged, cap=200)
+
+
+def test_prefill_many_tiles_bf16(car):
+    """Long enough for 8-wave workgroups (>= 256 of them) and several KV tiles."""
+    log_case("prefill bf16 8-wave path")
+    case = W.prefill_case("long", 1, 64, 64, 1100, 128, torch.bfloat16, 77, DEV)
+    check_prefill(car, case, heads=[0, 31, 63])
+
+
+def test_prefill_empty_prompt_is_noop(car):
+    q = torch.empty((1, 2, 0, 64), dtype=torch.bfloat16, device=DEV)
+    out = car.attn_prefill(q, q[:, :1], q[:, :1], torch.empty((1, 0), dtype=torch.int32,
+                                                              device=DEV))
+    assert out.shape == q.shape
+
+
+def test_tiny_workload_prefill_fp32(car):
+    """Workload 1's prefill: B=1, H=4, D=64, S=128, fp32, cache of 144 slots."""
+    pre, _ = W.tiny(DEV)
+    check_prefill(car, pre, cap=144)
+
+
+def test_gpt2_workload_prefill(car):
+    """Workload 2 at full size, every head: B=4, H=12, D=64, S=512, bf16."""
+    check_prefill(car, W.gpt2_prefill(DEV))
+
+
+def test_qwen_workload_prefill_sampled_heads(car):
+    """Workload 3 at full size (B=1, H=32, D=128, S=4096, cache 4096), in the
+    launch configuration the benchmark times; the oracle checks 3 heads."""
+    check_prefill(car, W.qwen_prefill(DEV), cap=4096, heads=[0, 17, 31])
