@@ -60,9 +60,40 @@ def parse_args(argv=None):
     p.add_argument("--only", choices=["prefill", "contiguous", "paged"], default=None,
                    help="time one stage only (profiling runs)")
     p.add_argument("--no-cpu-baseline", action="store_true")
-    p.add_argument("--cpu-heads", type=int, default=4,
+    p.add_argument("--cpu-heads", type=int, default=32,
                    help="prefill heads in the oracle's timed sample")
+    p.add_argument("--copy-calibration", action="store_true",
+                   help="first run one plain 1 GiB device copy (HBM counter calibration)")
     return p.parse_args(argv)
+
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+KERNEL_SOURCES = ["rope_cache.hip", "decode.hip", "prefill.hip", "common.hpp", "launch.hpp"]
+COPY_BYTES = 1 << 30
+
+
+def kernel_source_sha() -> str:
+    """Hash of the kernel sources; HBM traffic figures are valid only for it."""
+    import hashlib
+    h = hashlib.sha256()
+    for name in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "causal_attention_rope_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic():
+    """Per-launch HBM bytes per kernel from profiles/traffic.json, if they were
+    taken on the current kernel sources (else {})."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    try:
+        with open(path) as f:
+            t = json.load(f)
+    except OSError:
+        return {}
+    if t.get("source_sha") != kernel_source_sha():
+        return {}
+    return t.get("kernels", {})
 
 
 def cpu_baseline(pf, c4, heads: int):
@@ -169,6 +200,13 @@ def main(argv=None) -> int:
             ev[s]["call"][i][1].record(stream)
             car.set_timing_events(None, None)
 
+    if args.copy_calibration:
+        src = torch.empty(COPY_BYTES, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+
     for _ in range(args.warmup):
         for s in stages:
             run_stage(s)
@@ -223,6 +261,11 @@ def main(argv=None) -> int:
             "unit": "GB/s", "frac": r["GBps_kernel"] / PEAK_HBM_GBPS, "traffic": None,
             "avg_us": r["kernel_ms"] * 1e3,
             "per_launch": f"{kv} bytes (sum_b L_b * Hkv * D * 2 (K,V) * 2 B)"}
+
+    traffic = measured_traffic()
+    for name, k in kernels.items():
+        t = traffic.get(name)
+        k["traffic"] = None if t is None else t["fetch_bytes"] + t["write_bytes"]
 
     dominant = max(kernels, key=lambda k: kernels[k]["avg_us"])
     roofline = {k: v for k, v in kernels[dominant].items() if k in

@@ -31,13 +31,55 @@ namespace {
 
 constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
+constexpr int kTokensPerWave = DECODE_SPLIT / kWaves;  // 64
 
-// Rows per lane loaded at once: at most 16 (128 VGPRs of raw K/V) and at
-// most 16 score registers across the G query heads, so that 2 waves fit per
-// SIMD with the query and accumulator registers of all G heads.
-constexpr int decode_steps(int all, int G) {
-  const int s = all < 16 ? all : 16;
-  return s < 16 / G ? s : 16 / G;
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a),
+                                         __builtin_bit_cast(bf16x2_t, b), c, false);
+}
+
+__device__ __forceinline__ uint32_t perm_lo(uint32_t a, uint32_t b) {
+  return __builtin_amdgcn_perm(b, a, 0x05040100u);  // (a.lo16, b.lo16)
+}
+__device__ __forceinline__ uint32_t perm_hi(uint32_t a, uint32_t b) {
+  return __builtin_amdgcn_perm(b, a, 0x07060302u);  // (a.hi16, b.hi16)
+}
+
+constexpr uint32_t kOnePair = 0x3F803F80u;  // (1.0, 1.0) in bf16
+
+// Per-lane geometry of the decode split kernel.  A round is R rows per lane
+// (two register buffers of R rows are live): 8 rows, or 4 where the query and
+// accumulator registers are large (fp32 with D = 128, or 8 query heads).
+template <typename T, int D, int G>
+struct DecodeGeom {
+  static constexpr int N = Vec16<T>::N;        // elements per 16-byte load
+  static constexpr int LPR = D / N;            // lanes per cache row
+  static constexpr int NG = 64 / LPR;          // rows per wave load instruction
+  static constexpr int STEPS = kTokensPerWave / NG;
+  static constexpr int R_MAX = (sizeof(T) == 4 && D == 128) || G >= 8 ? 4 : 8;
+  static constexpr int R = STEPS < R_MAX ? STEPS : R_MAX;  // steps per round
+  static constexpr int ROUNDS = STEPS / R;
+  static_assert(R % 2 == 0 && ROUNDS * R == STEPS, "rounds must tile the wave's tokens");
+  static_assert(ROUNDS == 1 || ROUNDS % 2 == 0, "rounds are consumed in pairs");
+};
+
+// Score of one row for query head g: the lane's part of q . k, reduced over
+// the LPR lanes of the row.  bf16: packed dot2 on raw words.
+template <typename T, int D>
+__device__ __forceinline__ float row_score(const uint32_t* qw, const u32x4_t& k) {
+  using Gm = DecodeGeom<T, D, 1>;
+  float p = 0.f;
+  if constexpr (sizeof(T) == 2) {
+#pragma unroll
+    for (int w = 0; w < 4; ++w) p = dot2_bf16(qw[w], k[w], p);
+  } else {
+#pragma unroll
+    for (int w = 0; w < 4; ++w) p = fmaf(__uint_as_float(qw[w]), __uint_as_float(k[w]), p);
+  }
+  return group_sum<Gm::LPR>(p);
 }
 
 template <typename T, int D, int G, bool PAGED>
@@ -45,15 +87,10 @@ __global__ __launch_bounds__(kThreads, 2) void decode_split_kernel(
     const T* __restrict__ q, const T* __restrict__ k_new, const T* __restrict__ v_new,
     const int32_t* __restrict__ seq_lens, CacheArgs c, float* __restrict__ part, int Hkv,
     int nsplit, RopeFreq fr, float qk_scale) {
-  constexpr int N = Vec16<T>::N;      // elements per 16-byte load
-  constexpr int LPR = D / N;          // lanes per cache row
-  constexpr int NG = 64 / LPR;        // rows per wave load instruction
-  constexpr int TPW = DECODE_SPLIT / kWaves;  // tokens per wave
-  constexpr int STEPS_ALL = TPW / NG;
-  constexpr int STEPS = decode_steps(STEPS_ALL, G);
-  constexpr int PASSES = STEPS_ALL / STEPS;
+  using Gm = DecodeGeom<T, D, G>;
+  constexpr int N = Gm::N, LPR = Gm::LPR, NG = Gm::NG, R = Gm::R, ROUNDS = Gm::ROUNDS;
   constexpr int PW = decode_partial_words(D);
-  static_assert(STEPS * PASSES == STEPS_ALL, "split must divide evenly");
+  constexpr bool BF = sizeof(T) == 2;
 
   __shared__ float sm_acc[kWaves][G][D];
   __shared__ float sm_ml[kWaves][G][2];
@@ -65,36 +102,48 @@ __global__ __launch_bounds__(kThreads, 2) void decode_split_kernel(
   if (t0 > L) return;  // uniform over the workgroup
 
   const int lane = threadIdx.x & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform per wave
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int grp = lane / LPR;
   const int col = (lane % LPR) * N;
+  const int tw = t0 + wave * kTokensPerWave;  // first token of this wave
 
-  // Query heads of this KV head, rotated at position L, pre-scaled so that
-  // exp2 of a score difference is the softmax weight.
-  float qv[G][N];
+  // Query heads of this KV head, rotated at position L and pre-scaled so
+  // that exp2 of a score difference is the softmax weight; as 4 raw words
+  // (packed bf16 pairs, or fp32 bit patterns).
+  uint32_t qw[G][4];
 #pragma unroll
   for (int g = 0; g < G; ++g) {
-    load16<T>(q + ((int64_t)b * Hq + hk * G + g) * D + col, qv[g]);
-    rope_rotate_regs<N>(qv[g], L, col / 2, fr);
+    float f[N];
+    load16<T>(q + ((int64_t)b * Hq + hk * G + g) * D + col, f);
+    rope_rotate_regs<N>(f, L, col / 2, fr);
 #pragma unroll
-    for (int e = 0; e < N; ++e) qv[g][e] *= qk_scale;
+    for (int w = 0; w < 4; ++w) {
+      if constexpr (BF)
+        qw[g][w] = pack_bf16x2(f[2 * w] * qk_scale, f[2 * w + 1] * qk_scale);
+      else
+        qw[g][w] = __float_as_uint(f[w] * qk_scale);
+    }
   }
 
-  // The new token (index L) lives in this split's range only for one split.
-  float kn[N], vn[N];
-#pragma unroll
-  for (int e = 0; e < N; ++e) kn[e] = vn[e] = 0.f;
+  // The new token (index L): rotated key and raw value, stored into the cache
+  // by the split that holds L; in the cache's element type it is also the
+  // row this split uses for token L.
   T* const Kc = static_cast<T*>(c.k);
   T* const Vc = static_cast<T*>(c.v);
+  u32x4_t kn = {0, 0, 0, 0}, vn = {0, 0, 0, 0};
   if (L < t0 + DECODE_SPLIT) {
     const int64_t src = ((int64_t)b * Hkv + hk) * D + col;
-    load16<T>(k_new + src, kn);
-    rope_rotate_regs<N>(kn, L, col / 2, fr);
-    load16<T>(v_new + src, vn);
+    float f[N];
+    load16<T>(k_new + src, f);
+    rope_rotate_regs<N>(f, L, col / 2, fr);
+    T kt[N];
+    store16<T>(kt, f);
+    kn = *reinterpret_cast<const u32x4_t*>(kt);
+    vn = *reinterpret_cast<const u32x4_t*>(v_new + src);
     if (wave == 0 && grp == 0) {
       const int64_t dst = cache_row<PAGED>(c, b, hk, Hkv, L) * D + col;
-      store16<T>(Kc + dst, kn);
-      *reinterpret_cast<uint4*>(Vc + dst) = *reinterpret_cast<const uint4*>(v_new + src);
+      *reinterpret_cast<u32x4_t*>(Kc + dst) = kn;
+      *reinterpret_cast<u32x4_t*>(Vc + dst) = vn;
     }
   }
 
@@ -107,62 +156,136 @@ __global__ __launch_bounds__(kThreads, 2) void decode_split_kernel(
     for (int e = 0; e < N; ++e) acc[g][e] = 0.f;
   }
 
-  const int tw = t0 + wave * TPW;
-  const int t_hi = L > 0 ? L - 1 : 0;  // last cached row (clamp target)
-#pragma unroll 1
-  for (int pass = 0; pass < PASSES; ++pass) {
-    // Issue every K and V load of the pass first (memory-level parallelism);
-    // rows are kept as raw 16-byte vectors and widened where they are used.
-    uint4 kraw[STEPS], vraw[STEPS];
-#pragma unroll
-    for (int st = 0; st < STEPS; ++st) {
-      const int t = tw + (pass * STEPS + st) * NG + grp;
-      const int64_t row = cache_row<PAGED>(c, b, hk, Hkv, min(t, t_hi));
-      kraw[st] = *reinterpret_cast<const uint4*>(Kc + row * D + col);
-      vraw[st] = *reinterpret_cast<const uint4*>(Vc + row * D + col);
+  if (tw <= L) {  // uniform per wave: this wave holds at least one token
+    // Physical blocks of the wave's 64 tokens (wave-uniform), clamped to the
+    // sequence's last block so that the table is never read past its row.
+    int blk0 = 0, blk1 = 0, blk2 = 0, blk3 = 0;
+    if constexpr (PAGED) {
+      static_assert(kTokensPerWave == 64, "four 16-token blocks per wave");
+      const int32_t* trow = c.table + (int64_t)b * c.mbps;
+      const int last_blk = L >> 4, nb = c.num_blocks - 1;
+      blk0 = min(max(trow[min((tw >> 4) + 0, last_blk)], 0), nb);
+      blk1 = min(max(trow[min((tw >> 4) + 1, last_blk)], 0), nb);
+      blk2 = min(max(trow[min((tw >> 4) + 2, last_blk)], 0), nb);
+      blk3 = min(max(trow[min((tw >> 4) + 3, last_blk)], 0), nb);
     }
-    float sc[STEPS][G];
-    float mx[G];
-#pragma unroll
-    for (int g = 0; g < G; ++g) mx[g] = -INFINITY;
-#pragma unroll
-    for (int st = 0; st < STEPS; ++st) {
-      const int t = tw + (pass * STEPS + st) * NG + grp;
-      float kf[N];
-#pragma unroll
-      for (int e = 0; e < N; ++e) kf[e] = t < L ? elem<T>(kraw[st], e) : kn[e];
-#pragma unroll
-      for (int g = 0; g < G; ++g) {
-        float p = 0.f;
-#pragma unroll
-        for (int e = 0; e < N; ++e) p = fmaf(qv[g][e], kf[e], p);
-        p = group_sum<LPR>(p);
-        sc[st][g] = t <= L ? p : -INFINITY;
-        mx[g] = fmaxf(mx[g], sc[st][g]);
+    const int t_hi = L > 0 ? L - 1 : 0;  // last cached row
+
+    // Row (element offset / D) of step x for this lane; rows at or past L are
+    // clamped to a cached row (their data is replaced or masked).
+    auto row_of = [&](int x, bool full) -> int64_t {
+      const int t = tw + x * NG + grp;
+      if constexpr (PAGED) {
+        if (full) {
+          const int j = (x * NG) >> 4;  // which of the wave's blocks
+          const int blk = j == 0 ? blk0 : j == 1 ? blk1 : j == 2 ? blk2 : blk3;
+          return (((int64_t)blk * Hkv + hk) << 4) + (t & 15);
+        }
+        return cache_row<true>(c, b, hk, Hkv, min(t, t_hi));
+      } else {
+        return cache_row<false>(c, b, hk, Hkv, full ? t : min(t, t_hi));
       }
-    }
+    };
+
+    u32x4_t kb[2][R], vb[2][R];
+    // Loads of round r into register buffer BUF (a compile-time index).
+    auto issue = [&](int r, auto BUF) {
+      constexpr int buf = decltype(BUF)::value;
+      const bool full = tw + (r + 1) * R * NG - 1 < L;  // every row of the round cached
 #pragma unroll
-    for (int g = 0; g < G; ++g) {
-      const float m_new = fmaxf(m_run[g], strided_max<LPR>(mx[g]));
-      // m_new is -inf only while no valid token has been seen by this wave.
-      const float alpha = m_new == -INFINITY ? 1.f : fast_exp2(m_run[g] - m_new);
-      l_run[g] *= alpha;
+      for (int st = 0; st < R; ++st) {
+        const int64_t row = row_of(r * R + st, full);
+        kb[buf][st] = *reinterpret_cast<const u32x4_t*>(Kc + row * D + col);
+        vb[buf][st] = *reinterpret_cast<const u32x4_t*>(Vc + row * D + col);
+      }
+    };
+
+    // Online-softmax update with the rows of round r held in buffer BUF.
+    auto consume = [&](int r, auto BUF) {
+      constexpr int buf = decltype(BUF)::value;
+      const bool full = tw + (r + 1) * R * NG - 1 < L;
+      if (!full) {
+        // the round reaches index L: token L from registers, later rows zeroed
 #pragma unroll
-      for (int e = 0; e < N; ++e) acc[g][e] *= alpha;
-      m_run[g] = m_new;
-    }
+        for (int st = 0; st < R; ++st) {
+          const int t = tw + (r * R + st) * NG + grp;
 #pragma unroll
-    for (int st = 0; st < STEPS; ++st) {
-      const int t = tw + (pass * STEPS + st) * NG + grp;
-      float vf[N];
+          for (int w = 0; w < 4; ++w) {
+            kb[buf][st][w] = t < L ? kb[buf][st][w] : kn[w];
+            vb[buf][st][w] = t < L ? vb[buf][st][w] : (t == L ? vn[w] : 0u);
+          }
+        }
+      }
+      float sc[R][G];
 #pragma unroll
-      for (int e = 0; e < N; ++e) vf[e] = t < L ? elem<T>(vraw[st], e) : (t == L ? vn[e] : 0.f);
+      for (int st = 0; st < R; ++st) {
+        const int t = tw + (r * R + st) * NG + grp;
+#pragma unroll
+        for (int g = 0; g < G; ++g) {
+          const float sv = row_score<T, D>(qw[g], kb[buf][st]);
+          sc[st][g] = (full || t <= L) ? sv : -INFINITY;
+        }
+      }
 #pragma unroll
       for (int g = 0; g < G; ++g) {
-        const float p = t <= L ? fast_exp2(sc[st][g] - m_run[g]) : 0.f;
-        l_run[g] += p;
+        float mx = sc[0][g];
 #pragma unroll
-        for (int e = 0; e < N; ++e) acc[g][e] = fmaf(p, vf[e], acc[g][e]);
+        for (int st = 1; st < R; ++st) mx = fmaxf(mx, sc[st][g]);
+        // round 0 always holds token tw <= L, so m_new is finite from here on
+        const float m_new = fmaxf(m_run[g], strided_max<LPR>(mx));
+        const float alpha = fast_exp2(m_run[g] - m_new);
+        m_run[g] = m_new;
+        l_run[g] *= alpha;
+#pragma unroll
+        for (int e = 0; e < N; ++e) acc[g][e] *= alpha;
+      }
+#pragma unroll
+      for (int st = 0; st < R; st += 2) {
+        if constexpr (BF) {
+          // P V over a pair of rows with packed dot2: (p_a, p_b) . (v_a[e], v_b[e])
+          uint32_t vp[N];
+#pragma unroll
+          for (int e = 0; e < N; ++e)
+            vp[e] = (e & 1) ? perm_hi(vb[buf][st][e >> 1], vb[buf][st + 1][e >> 1])
+                            : perm_lo(vb[buf][st][e >> 1], vb[buf][st + 1][e >> 1]);
+#pragma unroll
+          for (int g = 0; g < G; ++g) {
+            const uint32_t pp = pack_bf16x2(fast_exp2(sc[st][g] - m_run[g]),
+                                            fast_exp2(sc[st + 1][g] - m_run[g]));
+            l_run[g] = dot2_bf16(pp, kOnePair, l_run[g]);
+#pragma unroll
+            for (int e = 0; e < N; ++e) acc[g][e] = dot2_bf16(pp, vp[e], acc[g][e]);
+          }
+        } else {
+#pragma unroll
+          for (int h = 0; h < 2; ++h) {
+#pragma unroll
+            for (int g = 0; g < G; ++g) {
+              const float pr = fast_exp2(sc[st + h][g] - m_run[g]);
+              l_run[g] += pr;
+#pragma unroll
+              for (int e = 0; e < N; ++e)
+                acc[g][e] = fmaf(pr, __uint_as_float(vb[buf][st + h][e]), acc[g][e]);
+            }
+          }
+        }
+      }
+    };
+
+    // Double-buffered rounds: round r+1's loads are in flight while round r
+    // is consumed.
+    using B0 = std::integral_constant<int, 0>;
+    using B1 = std::integral_constant<int, 1>;
+    issue(0, B0{});
+    if constexpr (ROUNDS == 1) {
+      consume(0, B0{});
+    } else {
+#pragma unroll 1
+      for (int r = 0; r < ROUNDS; r += 2) {
+        issue(r + 1, B1{});
+        consume(r, B0{});
+        if (r + 2 < ROUNDS) issue(r + 2, B0{});
+        consume(r + 1, B1{});
       }
     }
   }
@@ -210,8 +333,10 @@ __global__ __launch_bounds__(kThreads, 2) void decode_split_kernel(
   }
 }
 
-// One wave per (sequence, query head): merge the partials of all splits that
-// hold tokens 0..L and write the normalised output.
+// One wave per (sequence, query head): merge the partials of the splits that
+// hold tokens 0..L (log-sum-exp rule) and write the normalised output.  Lane s
+// reads split s's maximum and sum; the accumulators are read split by split,
+// 4 splits at a time.
 template <typename T, int D>
 __global__ __launch_bounds__(64) void decode_combine_kernel(const float* __restrict__ part,
                                                             const int32_t* __restrict__ seq_lens,
@@ -225,15 +350,40 @@ __global__ __launch_bounds__(64) void decode_combine_kernel(const float* __restr
   const int L = min(max(seq_lens[b], 0), last_slot);
   const int n = min(L / DECODE_SPLIT + 1, nsplit);
   const float* p = part + (int64_t)bh * nsplit * PW;
+
+  // max and weighted sum over splits, 64 splits per pass
   float M = -INFINITY;
-  for (int s = 0; s < n; ++s) M = fmaxf(M, p[(int64_t)s * PW]);
-  float l = 0.f, a[E];
+  for (int s = lane; s < n; s += 64) M = fmaxf(M, p[(int64_t)s * PW]);
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) M = fmaxf(M, __shfl_xor(M, o));
+  float l = 0.f;
+  for (int s = lane; s < n; s += 64) l += fast_exp2(p[(int64_t)s * PW] - M) * p[(int64_t)s * PW + 1];
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) l += __shfl_xor(l, o);
+
+  float a[E];
 #pragma unroll
   for (int e = 0; e < E; ++e) a[e] = 0.f;
-  for (int s = 0; s < n; ++s) {
+  int s = 0;
+  for (; s + 4 <= n; s += 4) {
+    float w[4], v[4][E];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const float* ps = p + (int64_t)(s + u) * PW;
+      w[u] = ps[0];
+#pragma unroll
+      for (int e = 0; e < E; ++e) v[u][e] = ps[4 + lane + 64 * e];
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const float f = fast_exp2(w[u] - M);
+#pragma unroll
+      for (int e = 0; e < E; ++e) a[e] = fmaf(f, v[u][e], a[e]);
+    }
+  }
+  for (; s < n; ++s) {
     const float* ps = p + (int64_t)s * PW;
     const float f = fast_exp2(ps[0] - M);
-    l = fmaf(f, ps[1], l);
 #pragma unroll
     for (int e = 0; e < E; ++e) a[e] = fmaf(f, ps[4 + lane + 64 * e], a[e]);
   }

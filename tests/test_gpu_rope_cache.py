@@ -69,14 +69,17 @@ def test_kv_cache_append_bit_exact(car, dtype, D, paged):
         table_np = None
         ck = torch.full((B, Hkv, cap, D), float("nan"), dtype=dtype, device=DEV)
         cache = car.KVCache(ck, ck.clone())
+    before_k, before_v = cache.k.cpu(), cache.v.cpu()
     want_k, want_v = f64(cache.k).copy(), f64(cache.v).copy()
     oracle.kv_cache_append(want_k, want_v, f64(k), f64(v), pos_np, block_table=table_np)
     car.kv_cache_append(cache, k, v, pos)
     torch.cuda.synchronize()
-    exp_k = torch.from_numpy(want_k).to(dtype)
-    exp_v = torch.from_numpy(want_v).to(dtype)
-    assert torch.equal(bits(cache.k.cpu()), bits(exp_k))
-    assert torch.equal(bits(cache.v.cpu()), bits(exp_v))
+    for got, want, before in ((cache.k, want_k, before_k), (cache.v, want_v, before_v)):
+        written = torch.from_numpy(~np.isnan(want))
+        # written slots: the stored values exactly; all others: the canaries untouched
+        exp = torch.where(written, torch.from_numpy(want).to(dtype), before)
+        assert torch.equal(bits(got.cpu()), bits(exp))
+        assert int(written.sum()) == B * Hkv * S * D
 
 
 def test_kv_cache_append_empty_is_noop(car):
