@@ -227,9 +227,10 @@ def main(argv=None) -> int:
     for s in stages:
         res[s] = {"call_ms": avg_ms(ev[s]["call"]), "kernel_ms": avg_ms(ev[s]["kernel"])}
 
-    for out in (pf_out, c4_out, c5_out):
-        if not torch.isfinite(out.float()).all():
-            print("non-finite output", file=sys.stderr)
+    outs = {"prefill": pf_out, "contiguous": c4_out, "paged": c5_out}
+    for s in stages:
+        if not torch.isfinite(outs[s].float()).all():
+            print(f"non-finite output in stage {s}", file=sys.stderr)
             return 1
 
     # ---------------- figures ----------------

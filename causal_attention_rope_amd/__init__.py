@@ -56,8 +56,12 @@ def _load() -> ctypes.CDLL:
     if not os.path.exists(library_path):
         raise ImportError(
             f"{library_path} is missing; build it first with "
-            "`python -m causal_attention_rope_amd.build`")
-    lib = ctypes.CDLL(library_path)
+            "`python causal_attention_rope_amd/build.py`")
+    try:
+        lib = ctypes.CDLL(library_path)
+    except OSError as e:
+        raise ImportError(f"cannot load {library_path}: {e}; rebuild it with "
+                          "`python causal_attention_rope_amd/build.py`") from e
     vp, i32, f32, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
     cache_p = ctypes.POINTER(_CarKVCache)
     sigs = {

@@ -1,6 +1,9 @@
 """Build libcar.so (the HIP kernels and the C-ABI shim) for gfx950, in-tree.
 
-    python -m causal_attention_rope_amd.build
+    python causal_attention_rope_amd/build.py
+
+(Run as a script: importing the package loads libcar.so, which the build
+creates.)
 
 Compiles every source under ``csrc/`` with hipcc for ``--offload-arch=gfx950``
 into ``_build/`` and links ``libcar.so`` next to this file.  Always rebuilds.
@@ -58,6 +61,17 @@ def _compile(src: str, extra) -> str:
     return obj
 
 
+def check_defined(lib: str) -> None:
+    """Fail if the library leaves any of its own symbols undefined (a kernel
+    whose host launch stub was not emitted would only fail at load time)."""
+    r = subprocess.run(["nm", "-C", "-u", lib], capture_output=True, text=True)
+    if r.returncode != 0:
+        return  # nm unavailable: the load test in tests/ still catches it
+    missing = [ln.strip() for ln in r.stdout.splitlines() if "car::" in ln]
+    if missing:
+        raise RuntimeError("libcar.so has undefined symbols:\n" + "\n".join(missing))
+
+
 def build(verbose: bool = False, extra_flags=()) -> str:
     os.makedirs(BUILD, exist_ok=True)
     with concurrent.futures.ThreadPoolExecutor(max_workers=len(SOURCES)) as ex:
@@ -67,6 +81,7 @@ def build(verbose: bool = False, extra_flags=()) -> str:
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
+    check_defined(tmp)
     os.replace(tmp, LIB)
     if verbose:
         print(f"built {LIB}")

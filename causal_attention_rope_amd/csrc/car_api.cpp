@@ -31,11 +31,13 @@ bool positive_finite(float x) { return isfinite(x) && x > 0.f; }
 
 car_status from_hip(hipError_t e) { return e == hipSuccess ? CAR_OK : CAR_ERR_HIP; }
 
-// theta^(-2i/D) for i < D/2, in double, split into float hi + lo.
+// theta^(-2i/D) / (2 pi) (revolutions per position) for i < D/2, in double,
+// split into float hi + lo.
 RopeFreq make_freq(int D, float theta) {
   RopeFreq f{};
+  const double two_pi = 6.283185307179586476925286766559;
   for (int i = 0; i < D / 2; ++i) {
-    const double x = pow((double)theta, -2.0 * i / (double)D);
+    const double x = pow((double)theta, -2.0 * i / (double)D) / two_pi;
     f.hi[i] = (float)x;
     f.lo[i] = (float)(x - (double)f.hi[i]);
   }

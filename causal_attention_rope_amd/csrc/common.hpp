@@ -82,50 +82,27 @@ __device__ __forceinline__ void store16<bf16_t>(bf16_t* p, const float (&f)[8]) 
 }
 
 // ---------------------------------------------------------------------------
-// RoPE angle.  The angle of pair i at position m is m * f_i with
-// f_i = theta^(-2i/D) supplied as an unevaluated sum hi + lo of two floats
-// (computed once on the host in double precision).  The product is formed
-// with an exact FMA residual, a = a_hi + a_lo.
-//
-// cos/sin use Cody and Waite's argument reduction: k = rint(a_hi * 2/pi),
-// r = a_hi - k*(P1 + P2 + P3) + a_lo with pi/2 = P1 + P2 + P3 split into
-// floats and each step an FMA; then Taylor polynomials on |r| <= pi/4
-// (truncation below 3e-9) and the quadrant k mod 4.  Branch free.  The
-// reduction keeps the absolute error near 1e-7 for |a| up to ~1e5 rad,
-// i.e. every position a 32-bit cache index can hold at theta_0 = 1 up to
-// 1e5 tokens; beyond that the error grows linearly with |a|.
+// RoPE angle.  The angle of pair i at position m is m * theta_i with
+// theta_i = base^(-2i/D).  It is handled in revolutions: the host supplies
+// f_i = theta_i / (2 pi) as an unevaluated sum hi + lo of two floats (from a
+// double), the product m * f_i is formed with an exact FMA residual, and its
+// integer part is removed exactly, which leaves r in [-1/2, 1/2] revolutions
+// with an absolute error near 2^-40.  cos and sin of 2 pi r come from the
+// hardware v_cos_f32 / v_sin_f32, which take revolutions (measured max
+// absolute error 1.24e-7 on [-1/2, 1/2)).  Branch free; valid for every
+// position below 2^24.
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ void rope_cos_sin(int pos, float f_hi, float f_lo, float& c,
                                              float& s) {
+  // No FMA contraction here: fusing m * f_hi into a - rint(a) would add the
+  // product's rounding residual a second time.
+#pragma clang fp contract(off)
   const float m = (float)pos;
   const float a = m * f_hi;
-  const float a_lo = fmaf(m, f_hi, -a) + m * f_lo;
-  constexpr float TWO_OVER_PI = 0.636619772367581343f;
-  constexpr float P1 = 1.57079637050628662109e+00f;   // float(pi/2)
-  constexpr float P2 = -4.37113882867379288655e-08f;  // float(pi/2 - P1)
-  constexpr float P3 = -1.71512451000588187280e-15f;  // float(pi/2 - P1 - P2)
-  const float k = rintf(a * TWO_OVER_PI);
-  float r = fmaf(-k, P1, a);
-  r = fmaf(-k, P2, r);
-  r = fmaf(-k, P3, r);
-  r += a_lo;
-  const float r2 = r * r;
-  // sin r = r - r^3/3! + r^5/5! - r^7/7! + r^9/9!
-  float ps = fmaf(r2, 2.75573192239858906526e-06f, -1.98412698412698412526e-04f);
-  ps = fmaf(r2, ps, 8.33333333333333321769e-03f);
-  ps = fmaf(r2, ps, -1.66666666666666657415e-01f);
-  const float sr = fmaf(r * r2, ps, r);
-  // cos r = 1 - r^2/2! + r^4/4! - r^6/6! + r^8/8! - r^10/10!
-  float pc = fmaf(r2, -2.75573192239858906526e-07f, 2.48015873015873015658e-05f);
-  pc = fmaf(r2, pc, -1.38888888888888894189e-03f);
-  pc = fmaf(r2, pc, 4.16666666666666643537e-02f);
-  pc = fmaf(r2, pc, -0.5f);
-  const float cr = fmaf(r2, pc, 1.0f);
-  const int quadrant = ((int)k) & 3;
-  const float s0 = (quadrant & 1) ? cr : sr;
-  const float c0 = (quadrant & 1) ? sr : cr;
-  s = (quadrant & 2) ? -s0 : s0;
-  c = ((quadrant + 1) & 2) ? -c0 : c0;
+  const float e = fmaf(m, f_hi, -a) + m * f_lo;  // exact residual + low part
+  const float r = (a - rintf(a)) + e;            // a - rint(a) is exact
+  s = __builtin_amdgcn_sinf(r);
+  c = __builtin_amdgcn_cosf(r);
 }
 
 // Rotate the adjacent pairs held in f[0..N) whose first pair index is p0.

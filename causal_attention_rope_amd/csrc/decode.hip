@@ -195,8 +195,9 @@ __global__ __launch_bounds__(kThreads, 2) void decode_split_kernel(
 #pragma unroll
       for (int st = 0; st < R; ++st) {
         const int64_t row = row_of(r * R + st, full);
-        kb[buf][st] = *reinterpret_cast<const u32x4_t*>(Kc + row * D + col);
-        vb[buf][st] = *reinterpret_cast<const u32x4_t*>(Vc + row * D + col);
+        // streamed once: non-temporal loads keep the rows out of the caches
+        kb[buf][st] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(Kc + row * D + col));
+        vb[buf][st] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(Vc + row * D + col));
       }
     };
 

@@ -7,7 +7,8 @@
 
 namespace car {
 
-// Per-pair RoPE frequency theta^(-2i/D) as an unevaluated float sum hi + lo.
+// Per-pair RoPE frequency in revolutions per position, theta^(-2i/D) / (2 pi),
+// as an unevaluated float sum hi + lo.
 struct RopeFreq {
   float hi[64];
   float lo[64];

@@ -125,100 +125,72 @@ __global__ __launch_bounds__(F32_ROWS) void prefill_f32_kernel(
 
 // ------------------------------------------------------------ bf16 MFMA ---
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+typedef short s16x4_t __attribute__((ext_vector_type(4)));
 
-template <int D, int WAVES>
+constexpr uint32_t kOnePair = 0x3F803F80u;  // (1.0, 1.0) in bf16
+constexpr float kRescaleLog2 = 8.f;          // largest exp2 argument allowed before rescaling
+
+__device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a),
+                                         __builtin_bit_cast(bf16x2_t, b), c, false);
+}
+
+// Two floats to a packed bf16 pair with one v_cvt_pk_bf16_f32 (round to nearest even).
+__device__ __forceinline__ uint32_t cvt_pk_bf16(float a, float b) {
+  typedef float f32x2_t __attribute__((ext_vector_type(2)));
+  const f32x2_t f = {a, b};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f, bf16x2_t));
+}
+
+// One direct global -> LDS load: every lane moves its 16 bytes from `src` to
+// lds_base + 16 * lane (lds_base uniform over the wave).  Kept in a separate
+// device function: a kernel body that names the builtin directly loses its
+// host-side launch stub in the host compilation pass.
+__device__ __forceinline__ void dma16(const void* src, void* lds_base) {
+  __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)lds_base, 16, 0, 0);
+}
+
+template <int D>
 struct Tile {
+  static constexpr int WAVES = 4;
   static constexpr int THREADS = 64 * WAVES;
-  static constexpr int BM = 32 * WAVES;          // query rows per workgroup
-  static constexpr int BN = D == 128 ? 64 : 128; // keys per tile
-  static constexpr int KSTR = D + 8;             // K row stride in LDS (elements)
-  static constexpr int VSTR = BN + 4;            // V^T row stride in LDS (elements)
-  static constexpr int K_ELEMS = BN * KSTR;
-  static constexpr int V_ELEMS = D * VSTR;
-  static constexpr int STAGE = K_ELEMS + V_ELEMS;
-  static constexpr int CH = BN * D / (THREADS * 8);  // 16-byte chunks per thread per tensor
-  static constexpr int NKB = BN / 32;            // 32-key blocks of S^T
-  static constexpr int NDB = D / 32;             // 32-wide head-dim blocks of O^T
-  static constexpr int QKS = D / 16;             // k-steps of Q K^T
-  static constexpr int PKS = BN / 16;            // k-steps of P V
-  static_assert(CH == 2 || CH == 4, "V is transposed 2 or 4 keys per thread");
+  static constexpr int BM = 32 * WAVES;           // query rows per workgroup
+  static constexpr int BN = D == 128 ? 64 : 128;  // keys per tile
+  static constexpr int ROWB = D * 2;              // bytes per K or V row
+  static constexpr int CPR = ROWB / 16;           // 16-byte chunks per row
+  static constexpr int TILEB = BN * ROWB;         // bytes of one K (or V) tile
+  static constexpr int STAGEB = 2 * TILEB;        // K tile then V tile
+  static constexpr int RPI = 64 / CPR;            // rows per 1 KB direct-to-LDS load
+  static constexpr int IPW = TILEB / 1024 / WAVES;  // such loads per wave per tensor
+  static constexpr int NKB = BN / 32;             // 32-key blocks of S^T
+  static constexpr int NDB = D / 32;              // 32-wide head-dim blocks of O^T
+  static constexpr int QKS = D / 16;              // k-steps of Q K^T
+  static constexpr int PKS = BN / 16;             // k-steps of P V
+  static_assert(TILEB % (1024 * WAVES) == 0, "tiles split evenly into 1 KB loads");
 };
 
-// Physical key column of logical key `key` in V^T row d (XOR swizzle in
-// groups of 4 keys, selected by d / 16).
-__device__ __forceinline__ int vt_col(int d, int key) { return key ^ (((d >> 4) & 7) << 2); }
-
-__device__ __forceinline__ uint32_t perm_lo(uint32_t a, uint32_t b) {
-  return __builtin_amdgcn_perm(b, a, 0x05040100u);  // (a.lo16, b.lo16)
-}
-__device__ __forceinline__ uint32_t perm_hi(uint32_t a, uint32_t b) {
-  return __builtin_amdgcn_perm(b, a, 0x07060302u);  // (a.hi16, b.hi16)
-}
-
-__device__ __forceinline__ uint32_t word_of(const u32x4_t& u, int w) { return u[w]; }
-
-// Global -> register staging of the K and V tiles that start at key j0
-// (rows past the sequence end are clamped to the last row; they are masked).
-template <int D, int WAVES, int CH>
-__device__ __forceinline__ void load_tile(u32x4_t (&kreg)[CH], u32x4_t (&vreg)[CH],
-                                          const bf16_t* kbase, const bf16_t* vbase, int j0,
-                                          int S, int tid) {
-  using C = Tile<D, WAVES>;
-  const int v_dc = tid % (D / 8), v_kg = tid / (D / 8);
-  static_for<0, CH>([&](auto P) {
-    constexpr int p = decltype(P)::value;
-    const int ch = tid + p * C::THREADS;
-    const int key = ch / (D / 8), dc = ch % (D / 8);
-    const int64_t krow = min(j0 + key, S - 1);
-    kreg[p] = *reinterpret_cast<const u32x4_t*>(kbase + krow * D + dc * 8);
-    const int64_t vrow = min(j0 + v_kg * CH + p, S - 1);
-    vreg[p] = *reinterpret_cast<const u32x4_t*>(vbase + vrow * D + v_dc * 8);
-  });
+// LDS layout of a K or V tile: rows of D bf16 in key order; the 16-byte chunk
+// c of row r sits at position c ^ swz(r).  swz is one-to-one on 16 (or 8)
+// consecutive rows, so the 32 rows of a K operand read fall on distinct
+// banks, and its bits 1..2 follow r % 4, so the 4 rows that one 16-lane group
+// of a transposing V read touches never share a chunk position.
+template <int CPR>
+__device__ __forceinline__ int swz(int r) {
+  const int s = ((r & 3) << 1) | ((r >> 2) & 1);
+  return CPR == 16 ? (s | (((r >> 3) & 1) << 3)) : s;
 }
 
-// Register -> LDS: K row-major, V transposed into V^T[d][key] (swizzled).
-template <int D, int WAVES, int CH>
-__device__ __forceinline__ void store_tile(const u32x4_t (&kreg)[CH], const u32x4_t (&vreg)[CH],
-                                           bf16_t* ks, int tid) {
-  using C = Tile<D, WAVES>;
-  bf16_t* vs = ks + C::K_ELEMS;
-  static_for<0, CH>([&](auto P) {
-    constexpr int p = decltype(P)::value;
-    const int ch = tid + p * C::THREADS;
-    const int key = ch / (D / 8), dc = ch % (D / 8);
-    *reinterpret_cast<u32x4_t*>(ks + key * C::KSTR + dc * 8) = kreg[p];
-  });
-  const int v_dc = tid % (D / 8), v_kg = tid / (D / 8);
-#pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    const int w = e >> 1;
-    const int d = v_dc * 8 + e;
-    bf16_t* dst = vs + d * C::VSTR + vt_col(d, v_kg * C::CH);
-    if constexpr (C::CH == 4) {
-      u32x2_t t;
-      t[0] = (e & 1) ? perm_hi(word_of(vreg[0], w), word_of(vreg[1], w))
-                     : perm_lo(word_of(vreg[0], w), word_of(vreg[1], w));
-      t[1] = (e & 1) ? perm_hi(word_of(vreg[2], w), word_of(vreg[3], w))
-                     : perm_lo(word_of(vreg[2], w), word_of(vreg[3], w));
-      *reinterpret_cast<u32x2_t*>(dst) = t;
-    } else {
-      *reinterpret_cast<uint32_t*>(dst) =
-          (e & 1) ? perm_hi(word_of(vreg[0], w), word_of(vreg[1], w))
-                  : perm_lo(word_of(vreg[0], w), word_of(vreg[1], w));
-    }
-  }
-}
-
-template <int D, int WAVES>
-__global__ __launch_bounds__(64 * WAVES, 2) void prefill_bf16_kernel(
+template <int D>
+__global__ __launch_bounds__(Tile<D>::THREADS, 2) void prefill_bf16_kernel(
     const bf16_t* __restrict__ q, const bf16_t* __restrict__ kr, const bf16_t* __restrict__ v,
     bf16_t* __restrict__ out, const int32_t* __restrict__ positions, int Hq, int Hkv, int S,
     int nqt, RopeFreq fr, float sm_scale_log2) {
-  using C = Tile<D, WAVES>;
-  __shared__ __attribute__((aligned(16))) bf16_t smem[2 * C::STAGE];
+  using C = Tile<D>;
+  __shared__ __attribute__((aligned(1024))) char smem[2 * C::STAGEB];
 
   // ---- work assignment: one head per XCD at a time, longest tiles first ----
   const int nbh = gridDim.x / nqt;
@@ -255,114 +227,192 @@ __global__ __launch_bounds__(64 * WAVES, 2) void prefill_bf16_kernel(
       float f[8];
       load16<bf16_t>(qp + d0, f);
       rope_rotate_regs<8>(f, pos, d0 / 2, fr);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) qf[ks][e] = (__bf16)f[e];
+      const u32x4_t u = {cvt_pk_bf16(f[0], f[1]), cvt_pk_bf16(f[2], f[3]),
+                         cvt_pk_bf16(f[4], f[5]), cvt_pk_bf16(f[6], f[7])};
+      qf[ks] = __builtin_bit_cast(bf16x8_t, u);
     }
   }
 
   const bf16_t* kbase = kr + ((int64_t)b * Hkv + hk) * S * D;
   const bf16_t* vbase = v + ((int64_t)b * Hkv + hk) * S * D;
 
-  // ---- global -> register staging of one K tile and one V tile ----
-  // K: chunk ch = tid + p*THREADS is (key ch / (D/8), dims (ch % (D/8))*8..+8).
-  // V: thread holds keys (tid / (D/8))*CH .. +CH of dims (tid % (D/8))*8 .. +8,
-  // transposed on the way into LDS.
-  u32x4_t kreg[C::CH], vreg[C::CH];
+  // ---- direct global -> LDS loads of K and V tiles ----
+  // Load i of this wave fills LDS bytes [n KB, (n+1) KB) of a tile (n =
+  // wave*IPW + i): lane l lands at position l%CPR of row n*RPI + l/CPR and so
+  // fetches the logical chunk (l%CPR) ^ swz(row).  K and V have two buffers
+  // each: K holds tiles t+1 and t+2 while V holds t and t+1 (the QK^T of tile
+  // t+1 is issued before the softmax of tile t).
+  int dma_row[C::IPW], dma_col[C::IPW];
+#pragma unroll
+  for (int i = 0; i < C::IPW; ++i) {
+    const int n = wave * C::IPW + i;
+    const int row = n * C::RPI + lane / C::CPR;
+    dma_row[i] = row;
+    dma_col[i] = ((lane % C::CPR) ^ swz<C::CPR>(row)) * 8;
+  }
+  auto issue = [&](const bf16_t* base, int j0, char* dst) {
+    const bool full = j0 + C::BN <= S;  // uniform
+#pragma unroll
+    for (int i = 0; i < C::IPW; ++i) {
+      const int n = wave * C::IPW + i;
+      const int r = full ? j0 + dma_row[i] : min(j0 + dma_row[i], S - 1);
+      dma16(base + (int64_t)r * D + dma_col[i], dst + n * 1024);
+    }
+  };
+  char* const kbuf = smem;                    // [2][TILEB]
+  char* const vbuf = smem + 2 * C::TILEB;     // [2][TILEB]
+
+  // ---- per-lane LDS read offsets (bytes within a tile) ----
+  // K operand (S^T = K Q^T, A = K rows): row kb*32 + l32, chunk 2*kk + g.
+  int koff[C::QKS];
+#pragma unroll
+  for (int kk = 0; kk < C::QKS; ++kk)
+    koff[kk] = l32 * C::ROWB + (((2 * kk + g) ^ swz<C::CPR>(l32)) << 4);
+  // V operand (O^T = V^T P^T, A = V^T) by transposing reads: lane 16*qd + s
+  // points at row kk*16 + 8h + 4*(lane/32) + s/4, dims db*32 + 16*(qd%2) + 4*(s%4)
+  // (4 values); after the transpose the lane holds V[kk*16 + 8h + 4g + j][db*32 + l32].
+  int voff[C::NDB][2];
+  {
+    const int qd = lane >> 4, s = lane & 15;
+#pragma unroll
+    for (int db = 0; db < C::NDB; ++db)
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int row = 8 * h + 4 * g + (s >> 2);     // + kk*16 (swz does not depend on kk)
+        const int col = db * 32 + 16 * (qd & 1) + 4 * (s & 3);
+        const int chunk = col >> 3;
+        voff[db][h] = row * C::ROWB + ((chunk ^ swz<C::CPR>(row)) << 4) + ((col & 7) << 1);
+      }
+  }
+
   f32x16_t oacc[C::NDB];
 #pragma unroll
   for (int db = 0; db < C::NDB; ++db)
 #pragma unroll
     for (int r = 0; r < 16; ++r) oacc[db][r] = 0.f;
   float m_run = -INFINITY, l_run = 0.f;
+  f32x16_t sacc[2][C::NKB];  // S^T of the tile being consumed and of the next one
 
   const int q_end = min(q0 + C::BM, S);  // exclusive
   const int ntiles = (q_end + C::BN - 1) / C::BN;
+  // tiles 0..wlast hold keys visible to this wave (uniform per wave)
+  const int wlast = min(ntiles - 1, (qw + 31) / C::BN);
 
-  load_tile<D, WAVES>(kreg, vreg, kbase, vbase, 0, S, tid);
-  store_tile<D, WAVES>(kreg, vreg, smem, tid);
-  __syncthreads();
-
-  for (int t = 0; t < ntiles; ++t) {
-    const int j0 = t * C::BN;
-    if (t + 1 < ntiles) load_tile<D, WAVES>(kreg, vreg, kbase, vbase, j0 + C::BN, S, tid);
-
-    if (j0 <= qw + 31) {  // some key of this tile is visible to this wave
-      const bf16_t* ks = smem + (t & 1) * C::STAGE;
-      const bf16_t* vs = ks + C::K_ELEMS;
-
-      // S^T = K Q^T : lane holds keys kb*32 + 8*(r/4) + 4*g + r%4 of query qrow
-      f32x16_t sacc[C::NKB];
+  // S^T = K Q^T for the tile in K buffer kb_i: lane holds keys
+  // kb*32 + 8*(r/4) + 4*g + r%4 of query qrow.  The two 32-key blocks are
+  // interleaved so that consecutive MFMAs are independent.
+  auto qk = [&](int kbi, auto SI) {
+    constexpr int si = decltype(SI)::value;
+    const char* kt = kbuf + kbi * C::TILEB;
+#pragma unroll
+    for (int kb = 0; kb < C::NKB; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) sacc[si][kb][r] = 0.f;
+#pragma unroll
+    for (int kk = 0; kk < C::QKS; ++kk)
 #pragma unroll
       for (int kb = 0; kb < C::NKB; ++kb) {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) sacc[kb][r] = 0.f;
-#pragma unroll
-        for (int kk = 0; kk < C::QKS; ++kk) {
-          const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(
-              ks + (kb * 32 + l32) * C::KSTR + kk * 16 + g * 8);
-          sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[kk], sacc[kb], 0, 0, 0);
-        }
+        const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(kt + kb * 32 * C::ROWB + koff[kk]);
+        sacc[si][kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[kk], sacc[si][kb], 0, 0, 0);
       }
+  };
 
-      // causal mask, only where the tile reaches past this wave's first row
-      if (j0 + C::BN - 1 > qw) {
-#pragma unroll
-        for (int kb = 0; kb < C::NKB; ++kb)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int key = j0 + kb * 32 + 8 * (r >> 2) + 4 * g + (r & 3);
-            if (key > qrow) sacc[kb][r] = -INFINITY;
-          }
-      }
-
-      // online softmax update (base 2, scale folded into the exponent)
-      float mt = -INFINITY;
+  // Online softmax of tile t (scores in sacc[si]) and O^T += V^T P^T with the
+  // V tile in V buffer t&1.  The reference maximum m_run is only raised when
+  // some row of the wave would otherwise see exp2 arguments above
+  // kRescaleLog2 (weights up to 2^8): O and l always share the same
+  // reference, so the result is exact while the rescale of O is skipped for
+  // most tiles.
+  auto softmax_pv = [&](int t, auto SI) {
+    constexpr int si = decltype(SI)::value;
+    const int j0 = t * C::BN;
+    if (j0 + C::BN - 1 > qw) {  // causal mask where the tile passes this wave's first row
 #pragma unroll
       for (int kb = 0; kb < C::NKB; ++kb)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) mt = fmaxf(mt, sacc[kb][r]);
-      mt = fmaxf(mt, __shfl_xor(mt, 32));
+        for (int r = 0; r < 16; ++r) {
+          const int key = j0 + kb * 32 + 8 * (r >> 2) + 4 * g + (r & 3);
+          if (key > qrow) sacc[si][kb][r] = -INFINITY;
+        }
+    }
+    float mt = -INFINITY;
+#pragma unroll
+    for (int kb = 0; kb < C::NKB; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mt = fmaxf(mt, sacc[si][kb][r]);
+    mt = fmaxf(mt, __shfl_xor(mt, 32));
+    const bool grow = (mt - m_run) * sm_scale_log2 > kRescaleLog2;
+    if (__builtin_amdgcn_ballot_w64(grow) != 0) {  // wave-uniform branch
       const float m_new = fmaxf(m_run, mt);
-      const float mc = m_new * sm_scale_log2;
-      const float alpha = fast_exp2(m_run * sm_scale_log2 - mc);
+      const float alpha = fast_exp2((m_run - m_new) * sm_scale_log2);
       m_run = m_new;
       l_run *= alpha;
 #pragma unroll
       for (int db = 0; db < C::NDB; ++db)
 #pragma unroll
         for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
+    }
+    const float mc = m_run * sm_scale_log2;
 
-      bf16x8_t pf[C::PKS];
+    // P (bf16) in the B-operand layout of O^T = V^T P^T; l sums the rounded P
+    bf16x8_t pf[C::PKS];
 #pragma unroll
-      for (int kk = 0; kk < C::PKS; ++kk) {
+    for (int kk = 0; kk < C::PKS; ++kk) {
+      uint32_t pw[4];
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          const float p = fast_exp2(fmaf(sacc[kk >> 1][8 * (kk & 1) + i], sm_scale_log2, -mc));
-          l_run += p;
-          pf[kk][i] = (__bf16)p;
-        }
+      for (int i = 0; i < 4; ++i) {
+        const float p0 = fast_exp2(fmaf(sacc[si][kk >> 1][8 * (kk & 1) + 2 * i], sm_scale_log2, -mc));
+        const float p1 = fast_exp2(fmaf(sacc[si][kk >> 1][8 * (kk & 1) + 2 * i + 1], sm_scale_log2, -mc));
+        pw[i] = cvt_pk_bf16(p0, p1);
+        l_run = dot2_bf16(pw[i], kOnePair, l_run);
       }
-
-      // O^T += V^T P^T : A operand = V^T rows d, keys {4g..4g+3, 8+4g..8+4g+3}
-#pragma unroll
-      for (int kk = 0; kk < C::PKS; ++kk) {
-#pragma unroll
-        for (int db = 0; db < C::NDB; ++db) {
-          const int d = db * 32 + l32;
-          const int key = kk * 16 + 4 * g;
-          const u32x2_t lo =
-              *reinterpret_cast<const u32x2_t*>(vs + d * C::VSTR + vt_col(d, key));
-          const u32x2_t hi =
-              *reinterpret_cast<const u32x2_t*>(vs + d * C::VSTR + vt_col(d, key + 8));
-          const u32x4_t u = {lo[0], lo[1], hi[0], hi[1]};
-          const bf16x8_t a = __builtin_bit_cast(bf16x8_t, u);
-          oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pf[kk], oacc[db], 0, 0, 0);
-        }
-      }
+      const u32x4_t u = {pw[0], pw[1], pw[2], pw[3]};
+      pf[kk] = __builtin_bit_cast(bf16x8_t, u);
     }
 
-    if (t + 1 < ntiles) store_tile<D, WAVES>(kreg, vreg, smem + ((t + 1) & 1) * C::STAGE, tid);
-    __syncthreads();
+    const char* vt = vbuf + (t & 1) * C::TILEB;
+#pragma unroll
+    for (int kk = 0; kk < C::PKS; ++kk) {
+#pragma unroll
+      for (int db = 0; db < C::NDB; ++db) {
+        typedef __attribute__((address_space(3))) s16x4_t lds_s16x4_t;
+        const s16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (lds_s16x4_t*)(vt + kk * 16 * C::ROWB + voff[db][0]));
+        const s16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (lds_s16x4_t*)(vt + kk * 16 * C::ROWB + voff[db][1]));
+        const u32x2_t ul = __builtin_bit_cast(u32x2_t, lo);
+        const u32x2_t uh = __builtin_bit_cast(u32x2_t, hi);
+        const u32x4_t u = {ul[0], ul[1], uh[0], uh[1]};
+        oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, u),
+                                                           pf[kk], oacc[db], 0, 0, 0);
+      }
+    }
+  };
+
+  // One pipeline step for tile t (S^T of tile t already issued into
+  // sacc[SC]): make K(t+1) and V(t) visible, start the loads of K(t+2) and
+  // V(t+1), issue QK^T of tile t+1 into sacc[SN], then softmax and P V of t.
+  auto step = [&](int t, auto SC, auto SN) {
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's loads landed
+    __syncthreads();                     // everyone's loads landed; old buffers free
+    if (t + 2 < ntiles) issue(kbase, (t + 2) * C::BN, kbuf + (t & 1) * C::TILEB);
+    if (t + 1 < ntiles) issue(vbase, (t + 1) * C::BN, vbuf + ((t + 1) & 1) * C::TILEB);
+    if (t + 1 <= wlast) qk((t + 1) & 1, SN);
+    if (t <= wlast) softmax_pv(t, SC);
+  };
+
+  using S0 = std::integral_constant<int, 0>;
+  using S1 = std::integral_constant<int, 1>;
+  issue(kbase, 0, kbuf);
+  issue(vbase, 0, vbuf);
+  if (ntiles > 1) issue(kbase, C::BN, kbuf + C::TILEB);
+  __builtin_amdgcn_s_waitcnt(0x0F70);
+  __syncthreads();
+  // K(0) is visible; K(1) and V(0) may still be in flight (waited for in step 0)
+  qk(0, S0{});
+  for (int t = 0; t < ntiles; t += 2) {
+    step(t, S0{}, S1{});
+    if (t + 1 < ntiles) step(t + 1, S1{}, S0{});
   }
 
   // ---- normalise and store: lane holds query qrow, dims db*32+8*(r/4)+4g+r%4 ----
@@ -374,10 +424,10 @@ __global__ __launch_bounds__(64 * WAVES, 2) void prefill_bf16_kernel(
     for (int db = 0; db < C::NDB; ++db)
 #pragma unroll
       for (int r4 = 0; r4 < 4; ++r4) {
-        uint2 u;
-        u.x = pack_bf16x2(oacc[db][4 * r4] * inv, oacc[db][4 * r4 + 1] * inv);
-        u.y = pack_bf16x2(oacc[db][4 * r4 + 2] * inv, oacc[db][4 * r4 + 3] * inv);
-        *reinterpret_cast<uint2*>(op + db * 32 + 8 * r4 + 4 * g) = u;
+        u32x2_t u;
+        u[0] = cvt_pk_bf16(oacc[db][4 * r4] * inv, oacc[db][4 * r4 + 1] * inv);
+        u[1] = cvt_pk_bf16(oacc[db][4 * r4 + 2] * inv, oacc[db][4 * r4 + 3] * inv);
+        *reinterpret_cast<u32x2_t*>(op + db * 32 + 8 * r4 + 4 * g) = u;
       }
   }
 }
@@ -394,33 +444,18 @@ hipError_t prefill_f32_t(const void* q, const void* k_rot, const void* v, void* 
   return hipGetLastError();
 }
 
-template <int D, int WAVES>
-hipError_t prefill_bf16_launch(const void* q, const void* k_rot, const void* v, void* out,
-                               int B, int Hq, int Hkv, int S, const int32_t* positions,
-                               const RopeFreq& fr, float scale, hipStream_t st,
-                               const TimedLaunch& tl) {
-  using C = Tile<D, WAVES>;
-  const int nqt = (S + C::BM - 1) / C::BM;
-  hipExtLaunchKernelGGL((prefill_bf16_kernel<D, WAVES>), dim3(nqt * B * Hq), dim3(C::THREADS),
-                        0, st, tl.start, tl.stop, 0, static_cast<const bf16_t*>(q),
-                        static_cast<const bf16_t*>(k_rot), static_cast<const bf16_t*>(v),
-                        static_cast<bf16_t*>(out), positions, Hq, Hkv, S, nqt, fr,
-                        scale * 1.4426950408889634f);
-  return hipGetLastError();
-}
-
-// 8-wave workgroups (256 query rows) when they alone fill the 256 CUs;
-// otherwise 4-wave workgroups (128 rows) for more parallelism.
 template <int D>
 hipError_t prefill_bf16_t(const void* q, const void* k_rot, const void* v, void* out, int B,
                           int Hq, int Hkv, int S, const int32_t* positions, const RopeFreq& fr,
                           float scale, hipStream_t st, const TimedLaunch& tl) {
-  const int64_t big = (int64_t)((S + 255) / 256) * B * Hq;
-  if (big >= 256)
-    return prefill_bf16_launch<D, 8>(q, k_rot, v, out, B, Hq, Hkv, S, positions, fr, scale, st,
-                                     tl);
-  return prefill_bf16_launch<D, 4>(q, k_rot, v, out, B, Hq, Hkv, S, positions, fr, scale, st,
-                                   tl);
+  using C = Tile<D>;
+  const int nqt = (S + C::BM - 1) / C::BM;
+  hipExtLaunchKernelGGL((prefill_bf16_kernel<D>), dim3(nqt * B * Hq), dim3(C::THREADS), 0, st,
+                        tl.start, tl.stop, 0, static_cast<const bf16_t*>(q),
+                        static_cast<const bf16_t*>(k_rot), static_cast<const bf16_t*>(v),
+                        static_cast<bf16_t*>(out), positions, Hq, Hkv, S, nqt, fr,
+                        scale * 1.4426950408889634f);
+  return hipGetLastError();
 }
 
 }  // namespace
