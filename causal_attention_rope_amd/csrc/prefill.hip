@@ -12,18 +12,21 @@
 // Two kernels:
 //  * fp32: one thread per query row, key tiles staged in LDS; plain fp32
 //    arithmetic for the 1e-4 accuracy of fp32 inputs.
-//  * bf16: MFMA 32x32x16 bf16 with fp32 accumulation.  A workgroup owns 128
-//    query rows (4 waves x 32) and walks key tiles of 64 (D = 128) or 128
-//    (D = 64) keys up to the diagonal.  Each wave computes S^T = K Q^T so that
-//    a lane holds one query's scores in its accumulator registers: the row
-//    maximum and sum need only in-lane work plus one exchange with lane^32,
-//    and the probabilities already sit in the operand layout of the second
-//    product O^T = V^T P^T.  K tiles are staged row-major in LDS, V tiles
-//    transposed (keys contiguous per head-dim row) with an XOR swizzle that
-//    keeps both the transposing stores and the operand loads free of bank
-//    conflicts; tiles are double-buffered so the next tile's global loads
-//    overlap the current tile's MFMA work.  Workgroups of one head go to one
-//    XCD (shared L2) and the longest (latest) query tiles start first.
+//  * bf16: MFMA 32x32x16 bf16 with fp32 accumulation.  A workgroup of 8
+//    waves (two per SIMD) owns 256 query rows (32 per wave) and walks key
+//    tiles of 64 (D = 128) or 128 (D = 64) keys up to the diagonal.  Each
+//    wave computes S^T = K Q^T so that a lane holds one query's scores in its
+//    accumulator registers: the row maximum and sum need only in-lane work
+//    plus one exchange between the two wave halves, and the probabilities
+//    already sit in the operand layout of the second product O^T = V^T P^T.
+//    K and V tiles are copied row-major from global memory straight into LDS
+//    (buffer loads with an LDS destination), chunk-permuted so that the K
+//    operand reads and the transposing V operand reads are free of bank
+//    conflicts; tiles are double-buffered so the next tiles' loads overlap
+//    the current tile's MFMA work.  A workgroup takes one long and one short
+//    query tile of a head (equal work for every workgroup of the causal
+//    triangle), and the heads are pinned to XCDs so that a KV head's tiles
+//    stay in one L2.
 #include <math.h>
 
 #include "common.hpp"
@@ -146,17 +149,35 @@ __device__ __forceinline__ uint32_t cvt_pk_bf16(float a, float b) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector(f, bf16x2_t));
 }
 
-// One direct global -> LDS load: every lane moves its 16 bytes from `src` to
-// lds_base + 16 * lane (lds_base uniform over the wave).  Kept in a separate
-// device function: a kernel body that names the builtin directly loses its
-// host-side launch stub in the host compilation pass.
-__device__ __forceinline__ void dma16(const void* src, void* lds_base) {
-  __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)lds_base, 16, 0, 0);
+// One direct buffer -> LDS load: every lane moves the 16 bytes at
+// rsrc.base + soff + voff to lds_base + 16 * lane (lds_base and soff uniform
+// over the wave).  Kept in a separate device function: a kernel body that
+// names the builtin directly loses its host-side launch stub in the host
+// compilation pass.
+__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t rsrc, uint32_t voff, uint32_t soff,
+                                      void* lds_base) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (__attribute__((address_space(3))) void*)lds_base,
+                                           16, voff, soff, 0, 0);
+}
+
+// Buffer resource over `bytes` bytes at `base` (raw addressing, no stride);
+// the fourth descriptor word is the gfx9-family default data format.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
+                                           0x00020000);
+}
+
+// Swap the two 32-lane halves of the wave: lane l receives x from lane l ^ 32.
+__device__ __forceinline__ float swap_halves(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(uint32_t, x),
+                                                  __builtin_bit_cast(uint32_t, x), false, false);
+  // lanes < 32 find the upper half's value in r[1], lanes >= 32 the lower half's in r[0]
+  return __builtin_bit_cast(float, (__lane_id() < 32) ? r[1] : r[0]);
 }
 
 template <int D>
 struct Tile {
-  static constexpr int WAVES = 4;
+  static constexpr int WAVES = 8;
   static constexpr int THREADS = 64 * WAVES;
   static constexpr int BM = 32 * WAVES;           // query rows per workgroup
   static constexpr int BN = D == 128 ? 64 : 128;  // keys per tile
@@ -173,15 +194,38 @@ struct Tile {
   static_assert(TILEB % (1024 * WAVES) == 0, "tiles split evenly into 1 KB loads");
 };
 
-// LDS layout of a K or V tile: rows of D bf16 in key order; the 16-byte chunk
-// c of row r sits at position c ^ swz(r).  swz is one-to-one on 16 (or 8)
-// consecutive rows, so the 32 rows of a K operand read fall on distinct
-// banks, and its bits 1..2 follow r % 4, so the 4 rows that one 16-lane group
-// of a transposing V read touches never share a chunk position.
+// LDS layout of a K or V tile: rows of D bf16 in key order, the 16-byte
+// chunk c of row r stored at chunk position phys(c, r), a permutation of the
+// row's chunks.  LDS has 64 four-byte banks (256 bytes per cycle); a 16-byte
+// read serves 16 lanes per cycle and an 8-byte read 32 lanes, so a read is
+// conflict-free when those lanes cover each bank once.
+//  * K operand reads (16 B, rows r..r+15 of one chunk c): D = 128 rows span
+//    all banks, so phys must be one-to-one over r % 16; D = 64 rows fill half
+//    the banks (r % 2 picks the half), so phys must be one-to-one over bits
+//    1..3 of r.
+//  * V transposing reads (8 B, 32 lanes = 4 rows x chunks c0..c0+3 of dims
+//    0..31 of a 32-dim block): for D = 128, chunks c0, c0+1 (dims 0..15) and
+//    c0+2, c0+3 (dims 16..31) must land in different bank halves, hence the
+//    flip of chunk bit 3 by chunk bit 1; the row terms spread the 4 rows.
 template <int CPR>
-__device__ __forceinline__ int swz(int r) {
-  const int s = ((r & 3) << 1) | ((r >> 2) & 1);
-  return CPR == 16 ? (s | (((r >> 3) & 1) << 3)) : s;
+__device__ __forceinline__ int phys_chunk(int c, int r) {
+  if constexpr (CPR == 16) {
+    const int s = ((r & 3) << 1) | ((r >> 2) & 1) | (((r >> 3) & 1) << 3);
+    return (c ^ (((c >> 1) & 1) << 3)) ^ s;
+  } else {
+    return c ^ ((((r >> 1) & 1) << 2) | (((r >> 2) & 1) << 1) | ((r >> 3) & 1));
+  }
+}
+
+// Inverse of phys_chunk in c: the logical chunk stored at position p of row r.
+template <int CPR>
+__device__ __forceinline__ int logical_chunk(int p, int r) {
+  if constexpr (CPR == 16) {
+    const int y = p ^ (((r & 3) << 1) | ((r >> 2) & 1) | (((r >> 3) & 1) << 3));
+    return y ^ (((y >> 1) & 1) << 3);
+  } else {
+    return p ^ ((((r >> 1) & 1) << 2) | (((r >> 2) & 1) << 1) | ((r >> 3) & 1));
+  }
 }
 
 template <int D>
@@ -192,17 +236,25 @@ __global__ __launch_bounds__(Tile<D>::THREADS, 2) void prefill_bf16_kernel(
   using C = Tile<D>;
   __shared__ __attribute__((aligned(1024))) char smem[2 * C::STAGEB];
 
-  // ---- work assignment: one head per XCD at a time, longest tiles first ----
-  const int nbh = gridDim.x / nqt;
+  // ---- work assignment: balanced query-tile pairs, heads pinned to XCDs ----
+  // Query tile i needs i+1 key-tile rows of the causal triangle, so a
+  // workgroup takes the pair (nqt-1-p, p): every pair costs nqt+1 tile rows
+  // (the middle tile of an odd nqt runs alone) and all workgroups of a launch
+  // finish together.  Workgroups go to the 8 XCDs round-robin by id; when the
+  // head count is a multiple of 8, XCD x owns the consecutive heads
+  // [x*hpx, (x+1)*hpx), so query heads of one KV group share its L2.
+  const int npair = (nqt + 1) >> 1;
+  const int nbh = gridDim.x / npair;
   const int bid = blockIdx.x;
-  int bh, qt;
+  int bh, pr;
   if ((nbh & 7) == 0) {
+    const int hpx = nbh >> 3;
     const int xcd = bid & 7, slot = bid >> 3;
-    bh = (slot / nqt) * 8 + xcd;
-    qt = nqt - 1 - slot % nqt;
+    bh = xcd * hpx + slot % hpx;
+    pr = slot / hpx;
   } else {
     bh = bid % nbh;
-    qt = nqt - 1 - bid / nbh;
+    pr = bid / nbh;
   }
   const int b = bh / Hq, hq = bh % Hq;
   const int hk = hq / (Hq / Hkv);
@@ -211,52 +263,40 @@ __global__ __launch_bounds__(Tile<D>::THREADS, 2) void prefill_bf16_kernel(
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform per wave
   const int l32 = lane & 31, g = lane >> 5;
-  const int q0 = qt * C::BM;
-  const int qw = q0 + wave * 32;             // first query row of this wave
-  const int qrow = qw + l32;                 // this lane's query row
-  const int qrc = min(qrow, S - 1);
-
-  // ---- Q fragments (B operand of S^T = K Q^T), rotated, bf16 ----
-  bf16x8_t qf[C::QKS];
-  {
-    const bf16_t* qp = q + ((int64_t)bh * S + qrc) * D;
-    const int pos = positions[(int64_t)b * S + qrc];
-#pragma unroll
-    for (int ks = 0; ks < C::QKS; ++ks) {
-      const int d0 = ks * 16 + g * 8;
-      float f[8];
-      load16<bf16_t>(qp + d0, f);
-      rope_rotate_regs<8>(f, pos, d0 / 2, fr);
-      const u32x4_t u = {cvt_pk_bf16(f[0], f[1]), cvt_pk_bf16(f[2], f[3]),
-                         cvt_pk_bf16(f[4], f[5]), cvt_pk_bf16(f[6], f[7])};
-      qf[ks] = __builtin_bit_cast(bf16x8_t, u);
-    }
-  }
-
   const bf16_t* kbase = kr + ((int64_t)b * Hkv + hk) * S * D;
   const bf16_t* vbase = v + ((int64_t)b * Hkv + hk) * S * D;
 
-  // ---- direct global -> LDS loads of K and V tiles ----
+  // ---- direct buffer -> LDS loads of K and V tiles ----
   // Load i of this wave fills LDS bytes [n KB, (n+1) KB) of a tile (n =
-  // wave*IPW + i): lane l lands at position l%CPR of row n*RPI + l/CPR and so
-  // fetches the logical chunk (l%CPR) ^ swz(row).  K and V have two buffers
-  // each: K holds tiles t+1 and t+2 while V holds t and t+1 (the QK^T of tile
-  // t+1 is issued before the softmax of tile t).
-  int dma_row[C::IPW], dma_col[C::IPW];
+  // wave*IPW + i): lane l lands at chunk position l%CPR of tile row
+  // n*RPI + l/CPR and so fetches that row's logical chunk stored there.  A
+  // whole tile needs only the per-lane offsets within the tile plus the
+  // tile's start as a scalar offset; in the last, partial tile the rows past
+  // the end re-read row S-1 (finite values; those keys are masked).  K and V
+  // have two buffers each: K holds tiles t+1 and t+2 while V holds t and t+1
+  // (the QK^T of tile t+1 is issued before the softmax of tile t).
+  const uint32_t head_bytes = (uint32_t)S * C::ROWB;
+  const __amdgpu_buffer_rsrc_t krs = make_rsrc(kbase, head_bytes);
+  const __amdgpu_buffer_rsrc_t vrs = make_rsrc(vbase, head_bytes);
+  uint32_t dma_off[C::IPW];
 #pragma unroll
   for (int i = 0; i < C::IPW; ++i) {
-    const int n = wave * C::IPW + i;
-    const int row = n * C::RPI + lane / C::CPR;
-    dma_row[i] = row;
-    dma_col[i] = ((lane % C::CPR) ^ swz<C::CPR>(row)) * 8;
+    const int row = (wave * C::IPW + i) * C::RPI + lane / C::CPR;
+    dma_off[i] = row * C::ROWB + (logical_chunk<C::CPR>(lane % C::CPR, row) << 4);
   }
-  auto issue = [&](const bf16_t* base, int j0, char* dst) {
-    const bool full = j0 + C::BN <= S;  // uniform
+  auto issue = [&](__amdgpu_buffer_rsrc_t rs, int j0, char* dst) {
+    if (j0 + C::BN <= S) {  // uniform
 #pragma unroll
-    for (int i = 0; i < C::IPW; ++i) {
-      const int n = wave * C::IPW + i;
-      const int r = full ? j0 + dma_row[i] : min(j0 + dma_row[i], S - 1);
-      dma16(base + (int64_t)r * D + dma_col[i], dst + n * 1024);
+      for (int i = 0; i < C::IPW; ++i)
+        dma16(rs, dma_off[i], (uint32_t)j0 * C::ROWB, dst + (wave * C::IPW + i) * 1024);
+    } else {
+#pragma unroll
+      for (int i = 0; i < C::IPW; ++i) {
+        const int row = (wave * C::IPW + i) * C::RPI + lane / C::CPR;
+        const uint32_t off = min(j0 + row, S - 1) * C::ROWB +
+                             (logical_chunk<C::CPR>(lane % C::CPR, row) << 4);
+        dma16(rs, off, 0, dst + (wave * C::IPW + i) * 1024);
+      }
     }
   };
   char* const kbuf = smem;                    // [2][TILEB]
@@ -267,7 +307,7 @@ __global__ __launch_bounds__(Tile<D>::THREADS, 2) void prefill_bf16_kernel(
   int koff[C::QKS];
 #pragma unroll
   for (int kk = 0; kk < C::QKS; ++kk)
-    koff[kk] = l32 * C::ROWB + (((2 * kk + g) ^ swz<C::CPR>(l32)) << 4);
+    koff[kk] = l32 * C::ROWB + (phys_chunk<C::CPR>(2 * kk + g, l32) << 4);
   // V operand (O^T = V^T P^T, A = V^T) by transposing reads: lane 16*qd + s
   // points at row kk*16 + 8h + 4*(lane/32) + s/4, dims db*32 + 16*(qd%2) + 4*(s%4)
   // (4 values); after the transpose the lane holds V[kk*16 + 8h + 4g + j][db*32 + l32].
@@ -278,157 +318,188 @@ __global__ __launch_bounds__(Tile<D>::THREADS, 2) void prefill_bf16_kernel(
     for (int db = 0; db < C::NDB; ++db)
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
-        const int row = 8 * h + 4 * g + (s >> 2);     // + kk*16 (swz does not depend on kk)
+        const int row = 8 * h + 4 * g + (s >> 2);  // + kk*16 (phys_chunk ignores r >= 16)
         const int col = db * 32 + 16 * (qd & 1) + 4 * (s & 3);
         const int chunk = col >> 3;
-        voff[db][h] = row * C::ROWB + ((chunk ^ swz<C::CPR>(row)) << 4) + ((col & 7) << 1);
+        voff[db][h] = row * C::ROWB + (phys_chunk<C::CPR>(chunk, row) << 4) + ((col & 7) << 1);
       }
   }
 
-  f32x16_t oacc[C::NDB];
-#pragma unroll
-  for (int db = 0; db < C::NDB; ++db)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) oacc[db][r] = 0.f;
-  float m_run = -INFINITY, l_run = 0.f;
-  f32x16_t sacc[2][C::NKB];  // S^T of the tile being consumed and of the next one
+  // ---- the pair's two query tiles, longest first ----
+#pragma nounroll
+  for (int pass = 0; pass < 2; ++pass) {
+    const int qt = pass == 0 ? nqt - 1 - pr : pr;
+    if (pass == 1) {
+      if (qt == nqt - 1 - pr) break;  // middle tile of an odd nqt: no partner
+      __syncthreads();                // every wave is done with the LDS tiles
+    }
+    const int q0 = qt * C::BM;
+    const int qw = q0 + wave * 32;             // first query row of this wave
+    const int qrow = qw + l32;                 // this lane's query row
+    const int qrc = min(qrow, S - 1);
 
-  const int q_end = min(q0 + C::BM, S);  // exclusive
-  const int ntiles = (q_end + C::BN - 1) / C::BN;
-  // tiles 0..wlast hold keys visible to this wave (uniform per wave)
-  const int wlast = min(ntiles - 1, (qw + 31) / C::BN);
-
-  // S^T = K Q^T for the tile in K buffer kb_i: lane holds keys
-  // kb*32 + 8*(r/4) + 4*g + r%4 of query qrow.  The two 32-key blocks are
-  // interleaved so that consecutive MFMAs are independent.
-  auto qk = [&](int kbi, auto SI) {
-    constexpr int si = decltype(SI)::value;
-    const char* kt = kbuf + kbi * C::TILEB;
-#pragma unroll
-    for (int kb = 0; kb < C::NKB; ++kb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) sacc[si][kb][r] = 0.f;
-#pragma unroll
-    for (int kk = 0; kk < C::QKS; ++kk)
-#pragma unroll
-      for (int kb = 0; kb < C::NKB; ++kb) {
-        const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(kt + kb * 32 * C::ROWB + koff[kk]);
-        sacc[si][kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[kk], sacc[si][kb], 0, 0, 0);
+    // ---- Q fragments (B operand of S^T = K Q^T), rotated, bf16 ----
+    bf16x8_t qf[C::QKS];
+    {
+      const bf16_t* qp = q + ((int64_t)bh * S + qrc) * D;
+      const int pos = positions[(int64_t)b * S + qrc];
+  #pragma unroll
+      for (int ks = 0; ks < C::QKS; ++ks) {
+        const int d0 = ks * 16 + g * 8;
+        float f[8];
+        load16<bf16_t>(qp + d0, f);
+        rope_rotate_regs<8>(f, pos, d0 / 2, fr);
+        const u32x4_t u = {cvt_pk_bf16(f[0], f[1]), cvt_pk_bf16(f[2], f[3]),
+                           cvt_pk_bf16(f[4], f[5]), cvt_pk_bf16(f[6], f[7])};
+        qf[ks] = __builtin_bit_cast(bf16x8_t, u);
       }
-  };
+    }
 
-  // Online softmax of tile t (scores in sacc[si]) and O^T += V^T P^T with the
-  // V tile in V buffer t&1.  The reference maximum m_run is only raised when
-  // some row of the wave would otherwise see exp2 arguments above
-  // kRescaleLog2 (weights up to 2^8): O and l always share the same
-  // reference, so the result is exact while the rescale of O is skipped for
-  // most tiles.
-  auto softmax_pv = [&](int t, auto SI) {
-    constexpr int si = decltype(SI)::value;
-    const int j0 = t * C::BN;
-    if (j0 + C::BN - 1 > qw) {  // causal mask where the tile passes this wave's first row
-#pragma unroll
+    f32x16_t oacc[C::NDB];
+  #pragma unroll
+    for (int db = 0; db < C::NDB; ++db)
+  #pragma unroll
+      for (int r = 0; r < 16; ++r) oacc[db][r] = 0.f;
+    float m_run = -INFINITY, l_run = 0.f;
+    f32x16_t sacc[2][C::NKB];  // S^T of the tile being consumed and of the next one
+
+    const int q_end = min(q0 + C::BM, S);  // exclusive
+    const int ntiles = (q_end + C::BN - 1) / C::BN;
+    // tiles 0..wlast hold keys visible to this wave (uniform per wave)
+    const int wlast = min(ntiles - 1, (qw + 31) / C::BN);
+
+    // S^T = K Q^T for the tile in K buffer kb_i: lane holds keys
+    // kb*32 + 8*(r/4) + 4*g + r%4 of query qrow.  The two 32-key blocks are
+    // interleaved so that consecutive MFMAs are independent.
+    auto qk = [&](int kbi, auto SI) {
+      constexpr int si = decltype(SI)::value;
+      const char* kt = kbuf + kbi * C::TILEB;
+  #pragma unroll
       for (int kb = 0; kb < C::NKB; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int key = j0 + kb * 32 + 8 * (r >> 2) + 4 * g + (r & 3);
-          if (key > qrow) sacc[si][kb][r] = -INFINITY;
+  #pragma unroll
+        for (int r = 0; r < 16; ++r) sacc[si][kb][r] = 0.f;
+  #pragma unroll
+      for (int kk = 0; kk < C::QKS; ++kk)
+  #pragma unroll
+        for (int kb = 0; kb < C::NKB; ++kb) {
+          const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(kt + kb * 32 * C::ROWB + koff[kk]);
+          sacc[si][kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[kk], sacc[si][kb], 0, 0, 0);
+        }
+    };
+
+    // Online softmax of tile t (scores in sacc[si]) and O^T += V^T P^T with the
+    // V tile in V buffer t&1.  The reference maximum m_run is only raised when
+    // some row of the wave would otherwise see exp2 arguments above
+    // kRescaleLog2 (weights up to 2^8): O and l always share the same
+    // reference, so the result is exact while the rescale of O is skipped for
+    // most tiles.
+    auto softmax_pv = [&](int t, auto SI) {
+      constexpr int si = decltype(SI)::value;
+      const int j0 = t * C::BN;
+      if (j0 + C::BN - 1 > qw) {  // causal mask where the tile passes this wave's first row
+  #pragma unroll
+        for (int kb = 0; kb < C::NKB; ++kb)
+  #pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int key = j0 + kb * 32 + 8 * (r >> 2) + 4 * g + (r & 3);
+            if (key > qrow) sacc[si][kb][r] = -INFINITY;
+          }
+      }
+      float mt = -INFINITY;
+  #pragma unroll
+      for (int kb = 0; kb < C::NKB; ++kb)
+  #pragma unroll
+        for (int r = 0; r < 16; ++r) mt = fmaxf(mt, sacc[si][kb][r]);
+      mt = fmaxf(mt, swap_halves(mt));
+      const bool grow = (mt - m_run) * sm_scale_log2 > kRescaleLog2;
+      if (__builtin_amdgcn_ballot_w64(grow) != 0) {  // wave-uniform branch
+        const float m_new = fmaxf(m_run, mt);
+        const float alpha = fast_exp2((m_run - m_new) * sm_scale_log2);
+        m_run = m_new;
+        l_run *= alpha;
+  #pragma unroll
+        for (int db = 0; db < C::NDB; ++db)
+  #pragma unroll
+          for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
+      }
+      const float mc = m_run * sm_scale_log2;
+
+      // P (bf16) in the B-operand layout of O^T = V^T P^T; l sums the rounded P
+      bf16x8_t pf[C::PKS];
+  #pragma unroll
+      for (int kk = 0; kk < C::PKS; ++kk) {
+        uint32_t pw[4];
+  #pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float p0 = fast_exp2(fmaf(sacc[si][kk >> 1][8 * (kk & 1) + 2 * i], sm_scale_log2, -mc));
+          const float p1 = fast_exp2(fmaf(sacc[si][kk >> 1][8 * (kk & 1) + 2 * i + 1], sm_scale_log2, -mc));
+          pw[i] = cvt_pk_bf16(p0, p1);
+          l_run = dot2_bf16(pw[i], kOnePair, l_run);
+        }
+        const u32x4_t u = {pw[0], pw[1], pw[2], pw[3]};
+        pf[kk] = __builtin_bit_cast(bf16x8_t, u);
+      }
+
+      const char* vt = vbuf + (t & 1) * C::TILEB;
+  #pragma unroll
+      for (int kk = 0; kk < C::PKS; ++kk) {
+  #pragma unroll
+        for (int db = 0; db < C::NDB; ++db) {
+          typedef __attribute__((address_space(3))) s16x4_t lds_s16x4_t;
+          const s16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (lds_s16x4_t*)(vt + kk * 16 * C::ROWB + voff[db][0]));
+          const s16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (lds_s16x4_t*)(vt + kk * 16 * C::ROWB + voff[db][1]));
+          const u32x2_t ul = __builtin_bit_cast(u32x2_t, lo);
+          const u32x2_t uh = __builtin_bit_cast(u32x2_t, hi);
+          const u32x4_t u = {ul[0], ul[1], uh[0], uh[1]};
+          oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, u),
+                                                             pf[kk], oacc[db], 0, 0, 0);
+        }
+      }
+    };
+
+    // One pipeline step for tile t (S^T of tile t already issued into
+    // sacc[SC]): make K(t+1) and V(t) visible, start the loads of K(t+2) and
+    // V(t+1), issue QK^T of tile t+1 into sacc[SN], then softmax and P V of t.
+    auto step = [&](int t, auto SC, auto SN) {
+      __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's loads landed
+      __syncthreads();                     // everyone's loads landed; old buffers free
+      if (t + 2 < ntiles) issue(krs, (t + 2) * C::BN, kbuf + (t & 1) * C::TILEB);
+      if (t + 1 < ntiles) issue(vrs, (t + 1) * C::BN, vbuf + ((t + 1) & 1) * C::TILEB);
+      if (t + 1 <= wlast) qk((t + 1) & 1, SN);
+      if (t <= wlast) softmax_pv(t, SC);
+    };
+
+    using S0 = std::integral_constant<int, 0>;
+    using S1 = std::integral_constant<int, 1>;
+    issue(krs, 0, kbuf);
+    issue(vrs, 0, vbuf);
+    if (ntiles > 1) issue(krs, C::BN, kbuf + C::TILEB);
+    __builtin_amdgcn_s_waitcnt(0x0F70);
+    __syncthreads();
+    // K(0) is visible; K(1) and V(0) may still be in flight (waited for in step 0)
+    qk(0, S0{});
+    for (int t = 0; t < ntiles; t += 2) {
+      step(t, S0{}, S1{});
+      if (t + 1 < ntiles) step(t + 1, S1{}, S0{});
+    }
+
+    // ---- normalise and store: lane holds query qrow, dims db*32+8*(r/4)+4g+r%4 ----
+    const float l_tot = l_run + swap_halves(l_run);
+    if (qrow < S) {
+      const float inv = 1.f / l_tot;
+      bf16_t* op = out + ((int64_t)bh * S + qrow) * D;
+  #pragma unroll
+      for (int db = 0; db < C::NDB; ++db)
+  #pragma unroll
+        for (int r4 = 0; r4 < 4; ++r4) {
+          u32x2_t u;
+          u[0] = cvt_pk_bf16(oacc[db][4 * r4] * inv, oacc[db][4 * r4 + 1] * inv);
+          u[1] = cvt_pk_bf16(oacc[db][4 * r4 + 2] * inv, oacc[db][4 * r4 + 3] * inv);
+          *reinterpret_cast<u32x2_t*>(op + db * 32 + 8 * r4 + 4 * g) = u;
         }
     }
-    float mt = -INFINITY;
-#pragma unroll
-    for (int kb = 0; kb < C::NKB; ++kb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) mt = fmaxf(mt, sacc[si][kb][r]);
-    mt = fmaxf(mt, __shfl_xor(mt, 32));
-    const bool grow = (mt - m_run) * sm_scale_log2 > kRescaleLog2;
-    if (__builtin_amdgcn_ballot_w64(grow) != 0) {  // wave-uniform branch
-      const float m_new = fmaxf(m_run, mt);
-      const float alpha = fast_exp2((m_run - m_new) * sm_scale_log2);
-      m_run = m_new;
-      l_run *= alpha;
-#pragma unroll
-      for (int db = 0; db < C::NDB; ++db)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
-    }
-    const float mc = m_run * sm_scale_log2;
-
-    // P (bf16) in the B-operand layout of O^T = V^T P^T; l sums the rounded P
-    bf16x8_t pf[C::PKS];
-#pragma unroll
-    for (int kk = 0; kk < C::PKS; ++kk) {
-      uint32_t pw[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float p0 = fast_exp2(fmaf(sacc[si][kk >> 1][8 * (kk & 1) + 2 * i], sm_scale_log2, -mc));
-        const float p1 = fast_exp2(fmaf(sacc[si][kk >> 1][8 * (kk & 1) + 2 * i + 1], sm_scale_log2, -mc));
-        pw[i] = cvt_pk_bf16(p0, p1);
-        l_run = dot2_bf16(pw[i], kOnePair, l_run);
-      }
-      const u32x4_t u = {pw[0], pw[1], pw[2], pw[3]};
-      pf[kk] = __builtin_bit_cast(bf16x8_t, u);
-    }
-
-    const char* vt = vbuf + (t & 1) * C::TILEB;
-#pragma unroll
-    for (int kk = 0; kk < C::PKS; ++kk) {
-#pragma unroll
-      for (int db = 0; db < C::NDB; ++db) {
-        typedef __attribute__((address_space(3))) s16x4_t lds_s16x4_t;
-        const s16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (lds_s16x4_t*)(vt + kk * 16 * C::ROWB + voff[db][0]));
-        const s16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (lds_s16x4_t*)(vt + kk * 16 * C::ROWB + voff[db][1]));
-        const u32x2_t ul = __builtin_bit_cast(u32x2_t, lo);
-        const u32x2_t uh = __builtin_bit_cast(u32x2_t, hi);
-        const u32x4_t u = {ul[0], ul[1], uh[0], uh[1]};
-        oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, u),
-                                                           pf[kk], oacc[db], 0, 0, 0);
-      }
-    }
-  };
-
-  // One pipeline step for tile t (S^T of tile t already issued into
-  // sacc[SC]): make K(t+1) and V(t) visible, start the loads of K(t+2) and
-  // V(t+1), issue QK^T of tile t+1 into sacc[SN], then softmax and P V of t.
-  auto step = [&](int t, auto SC, auto SN) {
-    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's loads landed
-    __syncthreads();                     // everyone's loads landed; old buffers free
-    if (t + 2 < ntiles) issue(kbase, (t + 2) * C::BN, kbuf + (t & 1) * C::TILEB);
-    if (t + 1 < ntiles) issue(vbase, (t + 1) * C::BN, vbuf + ((t + 1) & 1) * C::TILEB);
-    if (t + 1 <= wlast) qk((t + 1) & 1, SN);
-    if (t <= wlast) softmax_pv(t, SC);
-  };
-
-  using S0 = std::integral_constant<int, 0>;
-  using S1 = std::integral_constant<int, 1>;
-  issue(kbase, 0, kbuf);
-  issue(vbase, 0, vbuf);
-  if (ntiles > 1) issue(kbase, C::BN, kbuf + C::TILEB);
-  __builtin_amdgcn_s_waitcnt(0x0F70);
-  __syncthreads();
-  // K(0) is visible; K(1) and V(0) may still be in flight (waited for in step 0)
-  qk(0, S0{});
-  for (int t = 0; t < ntiles; t += 2) {
-    step(t, S0{}, S1{});
-    if (t + 1 < ntiles) step(t + 1, S1{}, S0{});
-  }
-
-  // ---- normalise and store: lane holds query qrow, dims db*32+8*(r/4)+4g+r%4 ----
-  const float l_tot = l_run + __shfl_xor(l_run, 32);
-  if (qrow < S) {
-    const float inv = 1.f / l_tot;
-    bf16_t* op = out + ((int64_t)bh * S + qrow) * D;
-#pragma unroll
-    for (int db = 0; db < C::NDB; ++db)
-#pragma unroll
-      for (int r4 = 0; r4 < 4; ++r4) {
-        u32x2_t u;
-        u[0] = cvt_pk_bf16(oacc[db][4 * r4] * inv, oacc[db][4 * r4 + 1] * inv);
-        u[1] = cvt_pk_bf16(oacc[db][4 * r4 + 2] * inv, oacc[db][4 * r4 + 3] * inv);
-        *reinterpret_cast<u32x2_t*>(op + db * 32 + 8 * r4 + 4 * g) = u;
-      }
   }
 }
 
@@ -450,7 +521,8 @@ hipError_t prefill_bf16_t(const void* q, const void* k_rot, const void* v, void*
                           float scale, hipStream_t st, const TimedLaunch& tl) {
   using C = Tile<D>;
   const int nqt = (S + C::BM - 1) / C::BM;
-  hipExtLaunchKernelGGL((prefill_bf16_kernel<D>), dim3(nqt * B * Hq), dim3(C::THREADS), 0, st,
+  const int npair = (nqt + 1) / 2;
+  hipExtLaunchKernelGGL((prefill_bf16_kernel<D>), dim3(npair * B * Hq), dim3(C::THREADS), 0, st,
                         tl.start, tl.stop, 0, static_cast<const bf16_t*>(q),
                         static_cast<const bf16_t*>(k_rot), static_cast<const bf16_t*>(v),
                         static_cast<bf16_t*>(out), positions, Hq, Hkv, S, nqt, fr,

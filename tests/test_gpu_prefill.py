@@ -106,10 +106,21 @@ def test_prefill_writes_cache_at_offset_positions(car, dtype, paged):
 
 
 def test_prefill_many_tiles_bf16(car):
-    """Long enough for 8-wave workgroups (>= 256 of them) and several KV tiles."""
-    log_case("prefill bf16 8-wave path")
+    """Many KV tiles and an odd number of 256-row query tiles (5): two
+    workgroups per head take a long and a short tile, the middle tile runs
+    alone."""
+    log_case("prefill bf16 many tiles, odd query-tile count")
     case = W.prefill_case("long", 1, 64, 64, 1100, 128, torch.bfloat16, 77, DEV)
     check_prefill(car, case, heads=[0, 31, 63])
+
+
+@pytest.mark.parametrize("D", [64, 128])
+def test_prefill_head_count_not_multiple_of_8(car, D):
+    """B*Hq = 6 (the head-to-XCD pinning needs a multiple of 8): the
+    round-robin assignment, with GQA and an odd query-tile count (3)."""
+    log_case(f"prefill bf16 6 heads D={D}")
+    case = W.prefill_case("heads6", 1, 6, 3, 700, D, torch.bfloat16, 31 + D, DEV)
+    check_prefill(car, case)
 
 
 def test_prefill_empty_prompt_is_noop(car):
