@@ -201,7 +201,7 @@ car_status car_attn_decode(const void* q, const void* k_new, const void* v_new, 
     return CAR_ERR_WORKSPACE;
   return from_hip(launch_decode(dtype == CAR_DTYPE_F32 ? F32 : BF16, D, group,
                                 cache->block_table != nullptr, q, k_new, v_new, out, B, Hq, Hkv,
-                                seq_lens, decode_nsplit(max_seq_len), c,
+                                seq_lens, max_seq_len, c,
                                 static_cast<float*>(workspace), make_freq(D, theta), scale,
                                 stream, timing()));
 }

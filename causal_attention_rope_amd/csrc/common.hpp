@@ -173,6 +173,49 @@ __device__ __forceinline__ float group_sum(float x) {
   return x;
 }
 
+// All-reduce over the lanes that share lane % STRIDE, STRIDE in {4, 8, 16, 32},
+// without LDS traffic: rotations by 4 and 8 inside each row of 16 lanes (DPP
+// row_ror), then the swaps of 16-lane rows and of 32-lane halves
+// (v_permlane16_swap / v_permlane32_swap).
+constexpr int DPP_ROW_ROR4 = 0x124;
+constexpr int DPP_ROW_ROR8 = 0x128;
+
+// The two results of a permlane swap of x with itself hold, on every lane,
+// the lane's own x and its partner's (lane ^ 16, resp. lane ^ 32), in an
+// order that depends on the lane; a symmetric combine needs no select.
+template <bool MAX>
+__device__ __forceinline__ float combine16(float x) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                  false);
+  const float a = __uint_as_float(r[0]), b = __uint_as_float(r[1]);
+  return MAX ? fmaxf(a, b) : a + b;
+}
+template <bool MAX>
+__device__ __forceinline__ float combine32(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                  false);
+  const float a = __uint_as_float(r[0]), b = __uint_as_float(r[1]);
+  return MAX ? fmaxf(a, b) : a + b;
+}
+
+template <int STRIDE>
+__device__ __forceinline__ float class_max(float x) {
+  static_assert(STRIDE == 4 || STRIDE == 8 || STRIDE == 16 || STRIDE == 32, "stride");
+  if constexpr (STRIDE <= 4) x = fmaxf(x, dpp_mov<DPP_ROW_ROR4>(x));
+  if constexpr (STRIDE <= 8) x = fmaxf(x, dpp_mov<DPP_ROW_ROR8>(x));
+  if constexpr (STRIDE <= 16) x = combine16<true>(x);
+  return combine32<true>(x);
+}
+
+template <int STRIDE>
+__device__ __forceinline__ float class_sum(float x) {
+  static_assert(STRIDE == 4 || STRIDE == 8 || STRIDE == 16 || STRIDE == 32, "stride");
+  if constexpr (STRIDE <= 4) x += dpp_mov<DPP_ROW_ROR4>(x);
+  if constexpr (STRIDE <= 8) x += dpp_mov<DPP_ROW_ROR8>(x);
+  if constexpr (STRIDE <= 16) x = combine16<false>(x);
+  return combine32<false>(x);
+}
+
 // Reductions across the lanes that share lane % STRIDE (STRIDE a power of
 // two dividing 64): combines lane, lane ^ STRIDE, lane ^ 2*STRIDE, ...
 template <int STRIDE>

@@ -31,7 +31,6 @@ namespace {
 
 constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
-constexpr int kTokensPerWave = DECODE_SPLIT / kWaves;  // 64
 
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
@@ -49,46 +48,65 @@ __device__ __forceinline__ uint32_t perm_hi(uint32_t a, uint32_t b) {
 }
 
 constexpr uint32_t kOnePair = 0x3F803F80u;  // (1.0, 1.0) in bf16
+constexpr float kRescaleLog2 = 8.f;          // largest exp2 argument allowed before rescaling
 
-// Per-lane geometry of the decode split kernel.  A round is R rows per lane
-// (two register buffers of R rows are live): 8 rows, or 4 where the query and
-// accumulator registers are large (fp32 with D = 128, or 8 query heads).
-template <typename T, int D, int G>
+// Per-lane geometry of the decode split kernel.  A lane holds C = 2 chunks
+// of 16 bytes of a cache row, chunks c*LPR + lane%LPR for c < C, so LPR =
+// D*sizeof(T)/32 lanes cover a row and each load instruction (one chunk per
+// lane) moves 64/LPR rows, each as a contiguous half row.  Two chunks per lane
+// halve the lanes per row against one chunk: a score needs one fewer
+// reduction step and every per-row step (exp, pack, max) runs on half as many
+// lanes.  A round is R row steps (two register buffers of R steps are live).
+#ifndef CAR_DECODE_RMAX
+#define CAR_DECODE_RMAX 2
+#endif
+#ifndef CAR_DECODE_C
+#define CAR_DECODE_C 1
+#endif
+template <typename T, int D, int G, int SPLIT = DECODE_SPLIT>
 struct DecodeGeom {
-  static constexpr int N = Vec16<T>::N;        // elements per 16-byte load
-  static constexpr int LPR = D / N;            // lanes per cache row
-  static constexpr int NG = 64 / LPR;          // rows per wave load instruction
-  static constexpr int STEPS = kTokensPerWave / NG;
-  static constexpr int R_MAX = (sizeof(T) == 4 && D == 128) || G >= 8 ? 4 : 8;
+  static constexpr int TPW = SPLIT / kWaves;   // tokens per wave
+  static constexpr int N = Vec16<T>::N;        // elements per 16-byte chunk
+  static constexpr int C = CAR_DECODE_C;       // chunks per lane per row
+  static constexpr int LPR = D / N / C;        // lanes per cache row
+  static constexpr int NG = 64 / LPR;          // rows per load instruction
+  static constexpr int STEPS = TPW / NG;
+  static_assert(SPLIT % DECODE_SPLIT == 0 && TPW % 64 == 0, "whole 16-token blocks per wave");
+  static constexpr int R_MAX = CAR_DECODE_RMAX;
   static constexpr int R = STEPS < R_MAX ? STEPS : R_MAX;  // steps per round
   static constexpr int ROUNDS = STEPS / R;
+  static_assert(LPR == 4 || LPR == 8 || LPR == 16 || LPR == 32, "lanes per row");
+  static_assert(NG <= 16 && 16 % NG == 0, "a row step stays inside one 16-token block");
   static_assert(R % 2 == 0 && ROUNDS * R == STEPS, "rounds must tile the wave's tokens");
   static_assert(ROUNDS == 1 || ROUNDS % 2 == 0, "rounds are consumed in pairs");
 };
 
-// Score of one row for query head g: the lane's part of q . k, reduced over
-// the LPR lanes of the row.  bf16: packed dot2 on raw words.
-template <typename T, int D>
-__device__ __forceinline__ float row_score(const uint32_t* qw, const u32x4_t& k) {
+// Score of one row for one query head: the lane's part of q . k, reduced
+// over the LPR lanes of the row.  bf16: packed dot2 on raw words.
+template <typename T, int D, int C>
+__device__ __forceinline__ float row_score(const uint32_t (&qw)[C][4], const u32x4_t (&k)[C]) {
   using Gm = DecodeGeom<T, D, 1>;
   float p = 0.f;
-  if constexpr (sizeof(T) == 2) {
 #pragma unroll
-    for (int w = 0; w < 4; ++w) p = dot2_bf16(qw[w], k[w], p);
-  } else {
+  for (int c = 0; c < C; ++c)
 #pragma unroll
-    for (int w = 0; w < 4; ++w) p = fmaf(__uint_as_float(qw[w]), __uint_as_float(k[w]), p);
-  }
+    for (int w = 0; w < 4; ++w) {
+      if constexpr (sizeof(T) == 2)
+        p = dot2_bf16(qw[c][w], k[c][w], p);
+      else
+        p = fmaf(__uint_as_float(qw[c][w]), __uint_as_float(k[c][w]), p);
+    }
   return group_sum<Gm::LPR>(p);
 }
 
-template <typename T, int D, int G, bool PAGED>
-__global__ __launch_bounds__(kThreads, 2) void decode_split_kernel(
+template <typename T, int D, int G, bool PAGED, int SPLIT>
+__global__ __launch_bounds__(kThreads, (G <= 4 ? 4 : 2)) void decode_split_kernel(
     const T* __restrict__ q, const T* __restrict__ k_new, const T* __restrict__ v_new,
     const int32_t* __restrict__ seq_lens, CacheArgs c, float* __restrict__ part, int Hkv,
     int nsplit, RopeFreq fr, float qk_scale) {
-  using Gm = DecodeGeom<T, D, G>;
-  constexpr int N = Gm::N, LPR = Gm::LPR, NG = Gm::NG, R = Gm::R, ROUNDS = Gm::ROUNDS;
+  using Gm = DecodeGeom<T, D, G, SPLIT>;
+  constexpr int N = Gm::N, C = Gm::C, LPR = Gm::LPR, NG = Gm::NG, R = Gm::R,
+                ROUNDS = Gm::ROUNDS, TPW = Gm::TPW;
   constexpr int PW = decode_partial_words(D);
   constexpr bool BF = sizeof(T) == 2;
 
@@ -98,76 +116,87 @@ __global__ __launch_bounds__(kThreads, 2) void decode_split_kernel(
   const int split = blockIdx.x, hk = blockIdx.y, b = blockIdx.z;
   const int Hq = Hkv * G;
   const int L = min(max(seq_lens[b], 0), cache_last_slot<PAGED>(c));
-  const int t0 = split * DECODE_SPLIT;
+  const int t0 = split * SPLIT;
   if (t0 > L) return;  // uniform over the workgroup
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int grp = lane / LPR;
-  const int col = (lane % LPR) * N;
-  const int tw = t0 + wave * kTokensPerWave;  // first token of this wave
+  const int grp = lane / LPR;  // row of the step
+  int col[C];                  // first element of the lane's chunks
+#pragma unroll
+  for (int ch = 0; ch < C; ++ch) col[ch] = (ch * LPR + lane % LPR) * N;
+  const int tw = t0 + wave * TPW;  // first token of this wave
 
   // Query heads of this KV head, rotated at position L and pre-scaled so
-  // that exp2 of a score difference is the softmax weight; as 4 raw words
-  // (packed bf16 pairs, or fp32 bit patterns).
-  uint32_t qw[G][4];
+  // that exp2 of a score difference is the softmax weight; as raw words
+  // (packed bf16 pairs, or fp32 bit patterns), 4 per chunk.
+  uint32_t qw[G][C][4];
 #pragma unroll
-  for (int g = 0; g < G; ++g) {
-    float f[N];
-    load16<T>(q + ((int64_t)b * Hq + hk * G + g) * D + col, f);
-    rope_rotate_regs<N>(f, L, col / 2, fr);
+  for (int g = 0; g < G; ++g)
 #pragma unroll
-    for (int w = 0; w < 4; ++w) {
-      if constexpr (BF)
-        qw[g][w] = pack_bf16x2(f[2 * w] * qk_scale, f[2 * w + 1] * qk_scale);
-      else
-        qw[g][w] = __float_as_uint(f[w] * qk_scale);
+    for (int ch = 0; ch < C; ++ch) {
+      float f[N];
+      load16<T>(q + ((int64_t)b * Hq + hk * G + g) * D + col[ch], f);
+      rope_rotate_regs<N>(f, L, col[ch] / 2, fr);
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        if constexpr (BF)
+          qw[g][ch][w] = pack_bf16x2(f[2 * w] * qk_scale, f[2 * w + 1] * qk_scale);
+        else
+          qw[g][ch][w] = __float_as_uint(f[w] * qk_scale);
+      }
     }
-  }
 
   // The new token (index L): rotated key and raw value, stored into the cache
   // by the split that holds L; in the cache's element type it is also the
   // row this split uses for token L.
   T* const Kc = static_cast<T*>(c.k);
   T* const Vc = static_cast<T*>(c.v);
-  u32x4_t kn = {0, 0, 0, 0}, vn = {0, 0, 0, 0};
-  if (L < t0 + DECODE_SPLIT) {
-    const int64_t src = ((int64_t)b * Hkv + hk) * D + col;
-    float f[N];
-    load16<T>(k_new + src, f);
-    rope_rotate_regs<N>(f, L, col / 2, fr);
-    T kt[N];
-    store16<T>(kt, f);
-    kn = *reinterpret_cast<const u32x4_t*>(kt);
-    vn = *reinterpret_cast<const u32x4_t*>(v_new + src);
-    if (wave == 0 && grp == 0) {
-      const int64_t dst = cache_row<PAGED>(c, b, hk, Hkv, L) * D + col;
-      *reinterpret_cast<u32x4_t*>(Kc + dst) = kn;
-      *reinterpret_cast<u32x4_t*>(Vc + dst) = vn;
+  u32x4_t kn[C], vn[C];
+#pragma unroll
+  for (int ch = 0; ch < C; ++ch) kn[ch] = vn[ch] = u32x4_t{0u, 0u, 0u, 0u};
+  if (L < t0 + SPLIT) {
+#pragma unroll
+    for (int ch = 0; ch < C; ++ch) {
+      const int64_t src = ((int64_t)b * Hkv + hk) * D + col[ch];
+      float f[N];
+      load16<T>(k_new + src, f);
+      rope_rotate_regs<N>(f, L, col[ch] / 2, fr);
+      T kt[N];
+      store16<T>(kt, f);
+      kn[ch] = *reinterpret_cast<const u32x4_t*>(kt);
+      vn[ch] = *reinterpret_cast<const u32x4_t*>(v_new + src);
+      if (wave == 0 && grp == 0) {
+        const int64_t dst = cache_row<PAGED>(c, b, hk, Hkv, L) * D + col[ch];
+        *reinterpret_cast<u32x4_t*>(Kc + dst) = kn[ch];
+        *reinterpret_cast<u32x4_t*>(Vc + dst) = vn[ch];
+      }
     }
   }
 
-  float m_run[G], l_run[G], acc[G][N];
+  float m_run[G], l_run[G], acc[G][C][N];
 #pragma unroll
   for (int g = 0; g < G; ++g) {
     m_run[g] = -INFINITY;
     l_run[g] = 0.f;
 #pragma unroll
-    for (int e = 0; e < N; ++e) acc[g][e] = 0.f;
+    for (int ch = 0; ch < C; ++ch)
+#pragma unroll
+      for (int e = 0; e < N; ++e) acc[g][ch][e] = 0.f;
   }
 
   if (tw <= L) {  // uniform per wave: this wave holds at least one token
-    // Physical blocks of the wave's 64 tokens (wave-uniform), clamped to the
-    // sequence's last block so that the table is never read past its row.
-    int blk0 = 0, blk1 = 0, blk2 = 0, blk3 = 0;
+    // Physical blocks of the wave's tokens: lane j holds the id of the wave's
+    // j-th 16-token block, clamped to the sequence's last block so that the
+    // table is never read past its row; a row step picks its id with a
+    // wave-uniform lane read.
+    constexpr int NBLK = TPW / 16;
+    static_assert(NBLK <= 64, "one block id per lane");
+    int myblk = 0;
     if constexpr (PAGED) {
-      static_assert(kTokensPerWave == 64, "four 16-token blocks per wave");
       const int32_t* trow = c.table + (int64_t)b * c.mbps;
-      const int last_blk = L >> 4, nb = c.num_blocks - 1;
-      blk0 = min(max(trow[min((tw >> 4) + 0, last_blk)], 0), nb);
-      blk1 = min(max(trow[min((tw >> 4) + 1, last_blk)], 0), nb);
-      blk2 = min(max(trow[min((tw >> 4) + 2, last_blk)], 0), nb);
-      blk3 = min(max(trow[min((tw >> 4) + 3, last_blk)], 0), nb);
+      if (lane < NBLK)
+        myblk = min(max(trow[min((tw >> 4) + lane, L >> 4)], 0), c.num_blocks - 1);
     }
     const int t_hi = L > 0 ? L - 1 : 0;  // last cached row
 
@@ -177,8 +206,7 @@ __global__ __launch_bounds__(kThreads, 2) void decode_split_kernel(
       const int t = tw + x * NG + grp;
       if constexpr (PAGED) {
         if (full) {
-          const int j = (x * NG) >> 4;  // which of the wave's blocks
-          const int blk = j == 0 ? blk0 : j == 1 ? blk1 : j == 2 ? blk2 : blk3;
+          const int blk = __builtin_amdgcn_readlane(myblk, (x * NG) >> 4);  // uniform index
           return (((int64_t)blk * Hkv + hk) << 4) + (t & 15);
         }
         return cache_row<true>(c, b, hk, Hkv, min(t, t_hi));
@@ -187,7 +215,7 @@ __global__ __launch_bounds__(kThreads, 2) void decode_split_kernel(
       }
     };
 
-    u32x4_t kb[2][R], vb[2][R];
+    u32x4_t kb[2][R][C], vb[2][R][C];
     // Loads of round r into register buffer BUF (a compile-time index).
     auto issue = [&](int r, auto BUF) {
       constexpr int buf = decltype(BUF)::value;
@@ -195,9 +223,14 @@ __global__ __launch_bounds__(kThreads, 2) void decode_split_kernel(
 #pragma unroll
       for (int st = 0; st < R; ++st) {
         const int64_t row = row_of(r * R + st, full);
-        // streamed once: non-temporal loads keep the rows out of the caches
-        kb[buf][st] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(Kc + row * D + col));
-        vb[buf][st] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(Vc + row * D + col));
+#pragma unroll
+        for (int ch = 0; ch < C; ++ch) {
+          // streamed once: non-temporal loads keep the rows out of the caches
+          kb[buf][st][ch] = __builtin_nontemporal_load(
+              reinterpret_cast<const u32x4_t*>(Kc + row * D + col[ch]));
+          vb[buf][st][ch] = __builtin_nontemporal_load(
+              reinterpret_cast<const u32x4_t*>(Vc + row * D + col[ch]));
+        }
       }
     };
 
@@ -211,10 +244,12 @@ __global__ __launch_bounds__(kThreads, 2) void decode_split_kernel(
         for (int st = 0; st < R; ++st) {
           const int t = tw + (r * R + st) * NG + grp;
 #pragma unroll
-          for (int w = 0; w < 4; ++w) {
-            kb[buf][st][w] = t < L ? kb[buf][st][w] : kn[w];
-            vb[buf][st][w] = t < L ? vb[buf][st][w] : (t == L ? vn[w] : 0u);
-          }
+          for (int ch = 0; ch < C; ++ch)
+#pragma unroll
+            for (int w = 0; w < 4; ++w) {
+              kb[buf][st][ch][w] = t < L ? kb[buf][st][ch][w] : kn[ch][w];
+              vb[buf][st][ch][w] = t < L ? vb[buf][st][ch][w] : (t == L ? vn[ch][w] : 0u);
+            }
         }
       }
       float sc[R][G];
@@ -223,39 +258,52 @@ __global__ __launch_bounds__(kThreads, 2) void decode_split_kernel(
         const int t = tw + (r * R + st) * NG + grp;
 #pragma unroll
         for (int g = 0; g < G; ++g) {
-          const float sv = row_score<T, D>(qw[g], kb[buf][st]);
+          const float sv = row_score<T, D, C>(qw[g], kb[buf][st]);
           sc[st][g] = (full || t <= L) ? sv : -INFINITY;
         }
       }
+      // Lazy rescale: the reference maximum m_run of a head only moves when
+      // a score exceeds it by more than kRescaleLog2 (weights up to 2^8); O
+      // and l always share the reference, so the result is exact while the
+      // cross-lane maximum, the exp and the rescale of O are skipped for most
+      // rounds.  m_run is the same on every lane of the wave.
 #pragma unroll
       for (int g = 0; g < G; ++g) {
         float mx = sc[0][g];
 #pragma unroll
         for (int st = 1; st < R; ++st) mx = fmaxf(mx, sc[st][g]);
-        // round 0 always holds token tw <= L, so m_new is finite from here on
-        const float m_new = fmaxf(m_run[g], strided_max<LPR>(mx));
-        const float alpha = fast_exp2(m_run[g] - m_new);
-        m_run[g] = m_new;
-        l_run[g] *= alpha;
+        if (__builtin_amdgcn_ballot_w64(mx - m_run[g] > kRescaleLog2) != 0) {  // uniform
+          // round 0 always holds token tw <= L, so m_new is finite from here on
+          const float m_new = fmaxf(m_run[g], class_max<LPR>(mx));
+          const float alpha = fast_exp2(m_run[g] - m_new);
+          m_run[g] = m_new;
+          l_run[g] *= alpha;
 #pragma unroll
-        for (int e = 0; e < N; ++e) acc[g][e] *= alpha;
+          for (int ch = 0; ch < C; ++ch)
+#pragma unroll
+            for (int e = 0; e < N; ++e) acc[g][ch][e] *= alpha;
+        }
       }
 #pragma unroll
       for (int st = 0; st < R; st += 2) {
         if constexpr (BF) {
           // P V over a pair of rows with packed dot2: (p_a, p_b) . (v_a[e], v_b[e])
-          uint32_t vp[N];
+          uint32_t vp[C][N];
 #pragma unroll
-          for (int e = 0; e < N; ++e)
-            vp[e] = (e & 1) ? perm_hi(vb[buf][st][e >> 1], vb[buf][st + 1][e >> 1])
-                            : perm_lo(vb[buf][st][e >> 1], vb[buf][st + 1][e >> 1]);
+          for (int ch = 0; ch < C; ++ch)
+#pragma unroll
+            for (int e = 0; e < N; ++e)
+              vp[ch][e] = (e & 1) ? perm_hi(vb[buf][st][ch][e >> 1], vb[buf][st + 1][ch][e >> 1])
+                                  : perm_lo(vb[buf][st][ch][e >> 1], vb[buf][st + 1][ch][e >> 1]);
 #pragma unroll
           for (int g = 0; g < G; ++g) {
             const uint32_t pp = pack_bf16x2(fast_exp2(sc[st][g] - m_run[g]),
                                             fast_exp2(sc[st + 1][g] - m_run[g]));
             l_run[g] = dot2_bf16(pp, kOnePair, l_run[g]);
 #pragma unroll
-            for (int e = 0; e < N; ++e) acc[g][e] = dot2_bf16(pp, vp[e], acc[g][e]);
+            for (int ch = 0; ch < C; ++ch)
+#pragma unroll
+              for (int e = 0; e < N; ++e) acc[g][ch][e] = dot2_bf16(pp, vp[ch][e], acc[g][ch][e]);
           }
         } else {
 #pragma unroll
@@ -265,8 +313,10 @@ __global__ __launch_bounds__(kThreads, 2) void decode_split_kernel(
               const float pr = fast_exp2(sc[st + h][g] - m_run[g]);
               l_run[g] += pr;
 #pragma unroll
-              for (int e = 0; e < N; ++e)
-                acc[g][e] = fmaf(pr, __uint_as_float(vb[buf][st + h][e]), acc[g][e]);
+              for (int ch = 0; ch < C; ++ch)
+#pragma unroll
+                for (int e = 0; e < N; ++e)
+                  acc[g][ch][e] = fmaf(pr, __uint_as_float(vb[buf][st + h][ch][e]), acc[g][ch][e]);
             }
           }
         }
@@ -294,15 +344,19 @@ __global__ __launch_bounds__(kThreads, 2) void decode_split_kernel(
   // Merge the rows of the wave (lanes that share the same columns).
 #pragma unroll
   for (int g = 0; g < G; ++g) {
-    l_run[g] = strided_sum<LPR>(l_run[g]);
+    l_run[g] = class_sum<LPR>(l_run[g]);
 #pragma unroll
-    for (int e = 0; e < N; ++e) acc[g][e] = strided_sum<LPR>(acc[g][e]);
+    for (int ch = 0; ch < C; ++ch)
+#pragma unroll
+      for (int e = 0; e < N; ++e) acc[g][ch][e] = class_sum<LPR>(acc[g][ch][e]);
   }
   if (grp == 0) {
 #pragma unroll
     for (int g = 0; g < G; ++g) {
 #pragma unroll
-      for (int e = 0; e < N; ++e) sm_acc[wave][g][col + e] = acc[g][e];
+      for (int ch = 0; ch < C; ++ch)
+#pragma unroll
+        for (int e = 0; e < N; ++e) sm_acc[wave][g][col[ch] + e] = acc[g][ch][e];
       if (lane == 0) {
         sm_ml[wave][g][0] = m_run[g];
         sm_ml[wave][g][1] = l_run[g];
@@ -342,14 +396,15 @@ template <typename T, int D>
 __global__ __launch_bounds__(64) void decode_combine_kernel(const float* __restrict__ part,
                                                             const int32_t* __restrict__ seq_lens,
                                                             T* __restrict__ out, int Hq,
-                                                            int nsplit, int last_slot) {
+                                                            int nsplit, int split_tokens,
+                                                            int last_slot) {
   constexpr int PW = decode_partial_words(D);
   constexpr int E = D / 64;
   const int bh = blockIdx.x;
   const int b = bh / Hq;
   const int lane = threadIdx.x;
   const int L = min(max(seq_lens[b], 0), last_slot);
-  const int n = min(L / DECODE_SPLIT + 1, nsplit);
+  const int n = min(L / split_tokens + 1, nsplit);
   const float* p = part + (int64_t)bh * nsplit * PW;
 
   // max and weighted sum over splits, 64 splits per pass
@@ -401,13 +456,21 @@ __global__ __launch_bounds__(64) void decode_combine_kernel(const float* __restr
   }
 }
 
+// Tokens per workgroup: 256 with one query head per KV head; with several,
+// each workgroup carries the per-head setup (rotated queries, partials) G
+// times and longer splits amortise it (measured on the paged GQA workload).
+template <int G>
+constexpr int split_tokens() { return G == 1 ? DECODE_SPLIT : 2 * DECODE_SPLIT; }
+
 template <typename T, int D, int G, bool PAGED>
 hipError_t decode_t(const void* q, const void* k_new, const void* v_new, void* out, int B,
-                    int Hkv, const int32_t* seq_lens, int nsplit, const CacheArgs& c,
+                    int Hkv, const int32_t* seq_lens, int max_seq_len, const CacheArgs& c,
                     float* partials, const RopeFreq& fr, float scale, hipStream_t st,
                     const TimedLaunch& tl) {
+  constexpr int SPLIT = split_tokens<G>();
+  const int nsplit = (max_seq_len + SPLIT - 1) / SPLIT;  // <= the workspace's split count
   const float qk_scale = scale * 1.4426950408889634f;  // log2(e): softmax in base 2
-  hipExtLaunchKernelGGL((decode_split_kernel<T, D, G, PAGED>), dim3(nsplit, Hkv, B),
+  hipExtLaunchKernelGGL((decode_split_kernel<T, D, G, PAGED, SPLIT>), dim3(nsplit, Hkv, B),
                         dim3(kThreads), 0, st, tl.start, tl.stop, 0,
                         static_cast<const T*>(q), static_cast<const T*>(k_new),
                         static_cast<const T*>(v_new), seq_lens, c, partials, Hkv, nsplit, fr,
@@ -416,31 +479,31 @@ hipError_t decode_t(const void* q, const void* k_new, const void* v_new, void* o
   if (e != hipSuccess) return e;
   const int last = PAGED ? c.mbps * 16 - 1 : c.max_seq - 1;
   hipLaunchKernelGGL((decode_combine_kernel<T, D>), dim3(B * Hkv * G), dim3(64), 0, st,
-                     partials, seq_lens, static_cast<T*>(out), Hkv * G, nsplit, last);
+                     partials, seq_lens, static_cast<T*>(out), Hkv * G, nsplit, SPLIT, last);
   return hipGetLastError();
 }
 
 template <typename T, int D, int G>
 hipError_t decode_paged(bool paged, const void* q, const void* kn, const void* vn, void* out,
-                        int B, int Hkv, const int32_t* sl, int nsplit, const CacheArgs& c,
+                        int B, int Hkv, const int32_t* sl, int max_seq_len, const CacheArgs& c,
                         float* part, const RopeFreq& fr, float scale, hipStream_t st,
                         const TimedLaunch& tl) {
-  return paged ? decode_t<T, D, G, true>(q, kn, vn, out, B, Hkv, sl, nsplit, c, part, fr, scale,
+  return paged ? decode_t<T, D, G, true>(q, kn, vn, out, B, Hkv, sl, max_seq_len, c, part, fr, scale,
                                          st, tl)
-               : decode_t<T, D, G, false>(q, kn, vn, out, B, Hkv, sl, nsplit, c, part, fr,
+               : decode_t<T, D, G, false>(q, kn, vn, out, B, Hkv, sl, max_seq_len, c, part, fr,
                                           scale, st, tl);
 }
 
 template <typename T, int D>
 hipError_t decode_group(int group, bool paged, const void* q, const void* kn, const void* vn,
-                        void* out, int B, int Hkv, const int32_t* sl, int nsplit,
+                        void* out, int B, int Hkv, const int32_t* sl, int max_seq_len,
                         const CacheArgs& c, float* part, const RopeFreq& fr, float scale,
                         hipStream_t st, const TimedLaunch& tl) {
   switch (group) {
-    case 1: return decode_paged<T, D, 1>(paged, q, kn, vn, out, B, Hkv, sl, nsplit, c, part, fr, scale, st, tl);
-    case 2: return decode_paged<T, D, 2>(paged, q, kn, vn, out, B, Hkv, sl, nsplit, c, part, fr, scale, st, tl);
-    case 4: return decode_paged<T, D, 4>(paged, q, kn, vn, out, B, Hkv, sl, nsplit, c, part, fr, scale, st, tl);
-    case 8: return decode_paged<T, D, 8>(paged, q, kn, vn, out, B, Hkv, sl, nsplit, c, part, fr, scale, st, tl);
+    case 1: return decode_paged<T, D, 1>(paged, q, kn, vn, out, B, Hkv, sl, max_seq_len, c, part, fr, scale, st, tl);
+    case 2: return decode_paged<T, D, 2>(paged, q, kn, vn, out, B, Hkv, sl, max_seq_len, c, part, fr, scale, st, tl);
+    case 4: return decode_paged<T, D, 4>(paged, q, kn, vn, out, B, Hkv, sl, max_seq_len, c, part, fr, scale, st, tl);
+    case 8: return decode_paged<T, D, 8>(paged, q, kn, vn, out, B, Hkv, sl, max_seq_len, c, part, fr, scale, st, tl);
     default: return hipErrorInvalidValue;
   }
 }
@@ -449,19 +512,19 @@ hipError_t decode_group(int group, bool paged, const void* q, const void* kn, co
 
 hipError_t launch_decode(Dtype dt, int D, int group, bool paged, const void* q,
                          const void* k_new, const void* v_new, void* out, int B, int Hq,
-                         int Hkv, const int32_t* seq_lens, int nsplit, const CacheArgs& c,
+                         int Hkv, const int32_t* seq_lens, int max_seq_len, const CacheArgs& c,
                          float* partials, const RopeFreq& fr, float scale, hipStream_t s,
                          const TimedLaunch& tl) {
   (void)Hq;
   if (dt == F32)
     return D == 64 ? decode_group<float, 64>(group, paged, q, k_new, v_new, out, B, Hkv, seq_lens,
-                                             nsplit, c, partials, fr, scale, s, tl)
+                                             max_seq_len, c, partials, fr, scale, s, tl)
                    : decode_group<float, 128>(group, paged, q, k_new, v_new, out, B, Hkv,
-                                              seq_lens, nsplit, c, partials, fr, scale, s, tl);
+                                              seq_lens, max_seq_len, c, partials, fr, scale, s, tl);
   return D == 64 ? decode_group<bf16_t, 64>(group, paged, q, k_new, v_new, out, B, Hkv, seq_lens,
-                                            nsplit, c, partials, fr, scale, s, tl)
+                                            max_seq_len, c, partials, fr, scale, s, tl)
                  : decode_group<bf16_t, 128>(group, paged, q, k_new, v_new, out, B, Hkv,
-                                             seq_lens, nsplit, c, partials, fr, scale, s, tl);
+                                             seq_lens, max_seq_len, c, partials, fr, scale, s, tl);
 }
 
 }  // namespace car

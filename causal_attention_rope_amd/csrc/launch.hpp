@@ -32,7 +32,9 @@ struct TimedLaunch {
   hipEvent_t stop;
 };
 
-// Tokens handled by one decode workgroup (one split of the sequence).
+// Smallest number of tokens one decode workgroup handles (one split of the
+// sequence; the launch may use a multiple of it).  It sizes the partials
+// workspace.
 constexpr int DECODE_SPLIT = 256;
 // fp32 words per decode partial: running max, running sum, 2 pad, D values.
 __host__ __device__ constexpr int decode_partial_words(int D) { return D + 4; }
@@ -59,9 +61,11 @@ hipError_t launch_prefill_attention(Dtype dt, int D, const void* q, const void* 
                                     hipStream_t s, const TimedLaunch& tl);
 
 // ---- decode.hip ------------------------------------------------------------
+// Partials: [B, Hq, nsplit, decode_partial_words(D)] fp32 with nsplit =
+// ceil(max_seq_len / split) <= ceil(max_seq_len / DECODE_SPLIT).
 hipError_t launch_decode(Dtype dt, int D, int group, bool paged, const void* q,
                          const void* k_new, const void* v_new, void* out, int B, int Hq,
-                         int Hkv, const int32_t* seq_lens, int nsplit, const CacheArgs& c,
+                         int Hkv, const int32_t* seq_lens, int max_seq_len, const CacheArgs& c,
                          float* partials, const RopeFreq& fr, float scale, hipStream_t s,
                          const TimedLaunch& tl);
 
