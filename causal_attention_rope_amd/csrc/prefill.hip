@@ -373,18 +373,28 @@ __global__ __launch_bounds__(Tile<D>::THREADS, 2) void prefill_bf16_kernel(
     // interleaved so that consecutive MFMAs are independent.
     auto qk = [&](int kbi, auto SI) {
       constexpr int si = decltype(SI)::value;
+      constexpr int NQ = C::QKS * C::NKB;
       const char* kt = kbuf + kbi * C::TILEB;
-  #pragma unroll
-      for (int kb = 0; kb < C::NKB; ++kb)
-  #pragma unroll
-        for (int r = 0; r < 16; ++r) sacc[si][kb][r] = 0.f;
-  #pragma unroll
-      for (int kk = 0; kk < C::QKS; ++kk)
-  #pragma unroll
-        for (int kb = 0; kb < C::NKB; ++kb) {
-          const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(kt + kb * 32 * C::ROWB + koff[kk]);
-          sacc[si][kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[kk], sacc[si][kb], 0, 0, 0);
-        }
+      // MFMA i: k-step i / NKB of 32-key block i % NKB; its K rows are read
+      // two MFMAs ahead (a ring of three operand slots), in exactly this order
+      auto load = [&](int i) {
+        return *reinterpret_cast<const bf16x8_t*>(kt + (i % C::NKB) * 32 * C::ROWB +
+                                                  koff[i / C::NKB]);
+      };
+      bf16x8_t ka[3];
+      ka[0] = load(0);
+      ka[1] = load(1);
+      static_for<0, NQ>([&](auto I) {
+        constexpr int i = decltype(I)::value;
+        if constexpr (i + 2 < NQ) ka[(i + 2) % 3] = load(i + 2);
+        __builtin_amdgcn_sched_barrier(0);
+        constexpr int kk = i / C::NKB, kb = i % C::NKB;
+        if constexpr (kk == 0)
+          sacc[si][kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[i % 3], qf[0], f32x16_t{}, 0, 0, 0);
+        else
+          sacc[si][kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[i % 3], qf[kk], sacc[si][kb], 0, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
+      });
     };
 
     // Online softmax of tile t (scores in sacc[si]) and O^T += V^T P^T with the
