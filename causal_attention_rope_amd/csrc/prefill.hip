@@ -450,22 +450,42 @@ __global__ __launch_bounds__(Tile<D>::THREADS, 2) void prefill_bf16_kernel(
         pf[kk] = __builtin_bit_cast(bf16x8_t, u);
       }
 
+      // O^T += V^T P^T: operand i is k-step i / NDB (16 keys) of head-dim
+      // block i % NDB, from two transposing reads.  At D = 128 the operands
+      // are read two ahead (a ring of three slots) in exactly this order; at
+      // D = 64 the compiler's order needs fewer registers.
       const char* vt = vbuf + (t & 1) * C::TILEB;
+      constexpr int NP = C::PKS * C::NDB;
+      auto load_v = [&](int i) {
+        typedef __attribute__((address_space(3))) s16x4_t lds_s16x4_t;
+        const char* base = vt + (i / C::NDB) * 16 * C::ROWB;
+        const s16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (lds_s16x4_t*)(base + voff[i % C::NDB][0]));
+        const s16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (lds_s16x4_t*)(base + voff[i % C::NDB][1]));
+        const u32x2_t ul = __builtin_bit_cast(u32x2_t, lo);
+        const u32x2_t uh = __builtin_bit_cast(u32x2_t, hi);
+        const u32x4_t u = {ul[0], ul[1], uh[0], uh[1]};
+        return __builtin_bit_cast(bf16x8_t, u);
+      };
+      auto mma_v = [&](bf16x8_t a, int i) {
+        oacc[i % C::NDB] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pf[i / C::NDB],
+                                                                   oacc[i % C::NDB], 0, 0, 0);
+      };
+      if constexpr (D == 128) {
+        bf16x8_t va[3];
+        va[0] = load_v(0);
+        va[1] = load_v(1);
+        static_for<0, NP>([&](auto I) {
+          constexpr int i = decltype(I)::value;
+          if constexpr (i + 2 < NP) va[(i + 2) % 3] = load_v(i + 2);
+          __builtin_amdgcn_sched_barrier(0);
+          mma_v(va[i % 3], i);
+          __builtin_amdgcn_sched_barrier(0);
+        });
+      } else {
   #pragma unroll
-      for (int kk = 0; kk < C::PKS; ++kk) {
-  #pragma unroll
-        for (int db = 0; db < C::NDB; ++db) {
-          typedef __attribute__((address_space(3))) s16x4_t lds_s16x4_t;
-          const s16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-              (lds_s16x4_t*)(vt + kk * 16 * C::ROWB + voff[db][0]));
-          const s16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-              (lds_s16x4_t*)(vt + kk * 16 * C::ROWB + voff[db][1]));
-          const u32x2_t ul = __builtin_bit_cast(u32x2_t, lo);
-          const u32x2_t uh = __builtin_bit_cast(u32x2_t, hi);
-          const u32x4_t u = {ul[0], ul[1], uh[0], uh[1]};
-          oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, u),
-                                                             pf[kk], oacc[db], 0, 0, 0);
-        }
+        for (int i = 0; i < NP; ++i) mma_v(load_v(i), i);
       }
     };
 
