@@ -459,8 +459,11 @@ __global__ __launch_bounds__(64) void decode_combine_kernel(const float* __restr
 // Tokens per workgroup: 256 with one query head per KV head; with several,
 // each workgroup carries the per-head setup (rotated queries, partials) G
 // times and longer splits amortise it (measured on the paged GQA workload).
+#ifndef CAR_DECODE_GQA_SPLIT_MULT
+#define CAR_DECODE_GQA_SPLIT_MULT 2
+#endif
 template <int G>
-constexpr int split_tokens() { return G == 1 ? DECODE_SPLIT : 2 * DECODE_SPLIT; }
+constexpr int split_tokens() { return G == 1 ? DECODE_SPLIT : CAR_DECODE_GQA_SPLIT_MULT * DECODE_SPLIT; }
 
 template <typename T, int D, int G, bool PAGED>
 hipError_t decode_t(const void* q, const void* k_new, const void* v_new, void* out, int B,
