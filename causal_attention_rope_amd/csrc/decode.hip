@@ -198,38 +198,37 @@ __global__ __launch_bounds__(kThreads, (G <= 4 ? 4 : 2)) void decode_split_kerne
       if (lane < NBLK)
         myblk = min(max(trow[min((tw >> 4) + lane, L >> 4)], 0), c.num_blocks - 1);
     }
-    const int t_hi = L > 0 ? L - 1 : 0;  // last cached row
-
-    // Row (element offset / D) of step x for this lane; rows at or past L are
-    // clamped to a cached row (their data is replaced or masked).
-    auto row_of = [&](int x, bool full) -> int64_t {
-      const int t = tw + x * NG + grp;
-      if constexpr (PAGED) {
-        if (full) {
-          const int blk = __builtin_amdgcn_readlane(myblk, (x * NG) >> 4);  // uniform index
-          return (((int64_t)blk * Hkv + hk) << 4) + (t & 15);
-        }
-        return cache_row<true>(c, b, hk, Hkv, min(t, t_hi));
-      } else {
-        return cache_row<false>(c, b, hk, Hkv, full ? t : min(t, t_hi));
-      }
-    };
 
     u32x4_t kb[2][R][C], vb[2][R][C];
-    // Loads of round r into register buffer BUF (a compile-time index).
+    // Loads of round r into register buffer BUF (a compile-time index).  The
+    // NG rows of a step are consecutive cache rows (a step never straddles a
+    // 16-token block), so each step needs one wave-uniform base and the lane's
+    // chunk offset.  Rows at or past L are only ever replaced (consume), so
+    // they just have to stay inside the cache: the paged block ids are
+    // clamped to the sequence's last block, and contiguous rows to L.
+    const int64_t cbase = PAGED ? 0 : ((int64_t)b * Hkv + hk) * c.max_seq + tw;
     auto issue = [&](int r, auto BUF) {
       constexpr int buf = decltype(BUF)::value;
-      const bool full = tw + (r + 1) * R * NG - 1 < L;  // every row of the round cached
 #pragma unroll
       for (int st = 0; st < R; ++st) {
-        const int64_t row = row_of(r * R + st, full);
+        const int x = r * R + st;
+        int64_t row0;
+        int lrow = grp;  // lane's row within the step
+        if constexpr (PAGED) {
+          const int blk = __builtin_amdgcn_readlane(myblk, (x * NG) >> 4);  // uniform index
+          row0 = (((int64_t)blk * Hkv + hk) << 4) + ((x * NG) & 15);
+        } else {
+          row0 = cbase + x * NG;
+          lrow = min(grp, L - tw - x * NG);  // never past row L (may be negative)
+        }
+        const T* kp = Kc + row0 * D;
+        const T* vp = Vc + row0 * D;
 #pragma unroll
         for (int ch = 0; ch < C; ++ch) {
+          const int off = lrow * D + col[ch];
           // streamed once: non-temporal loads keep the rows out of the caches
-          kb[buf][st][ch] = __builtin_nontemporal_load(
-              reinterpret_cast<const u32x4_t*>(Kc + row * D + col[ch]));
-          vb[buf][st][ch] = __builtin_nontemporal_load(
-              reinterpret_cast<const u32x4_t*>(Vc + row * D + col[ch]));
+          kb[buf][st][ch] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(kp + off));
+          vb[buf][st][ch] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(vp + off));
         }
       }
     };
