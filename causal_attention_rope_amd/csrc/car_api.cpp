@@ -186,6 +186,8 @@ car_status car_attn_decode(const void* q, const void* k_new, const void* v_new, 
   if ((int64_t)B * Hq == 0) return CAR_OK;
   const int group = Hq / Hkv;
   if (group != 1 && group != 2 && group != 4 && group != 8) return CAR_ERR_UNSUPPORTED;
+  // launch grid: B * Hkv workgroups in x, one row per 256-token split in y
+  if ((int64_t)B * Hkv > INT32_MAX || decode_nsplit(max_seq_len) > 65535) return CAR_ERR_UNSUPPORTED;
   if (q == nullptr || k_new == nullptr || v_new == nullptr || out == nullptr ||
       seq_lens == nullptr)
     return CAR_ERR_INVALID_ARGUMENT;

@@ -113,11 +113,20 @@ __global__ __launch_bounds__(kThreads, (G <= 4 ? 4 : 2)) void decode_split_kerne
   __shared__ float sm_acc[kWaves][G][D];
   __shared__ float sm_ml[kWaves][G][2];
 
-  const int split = blockIdx.x, hk = blockIdx.y, b = blockIdx.z;
+  // Workgroups are numbered split-major with (sequence, KV head) fastest:
+  // consecutive workgroup ids go to the 8 XCDs in turn, so every XCD gets
+  // the same mix of sequences and splits and they all drain together.  The
+  // splits of a sequence are aligned to the last row of the grid, so the
+  // shorter last splits (0..L ends anywhere inside one) are dispatched last
+  // and fill the end of the launch; rows before a sequence's first split
+  // exit at once.
+  const int hk = blockIdx.x % Hkv, b = blockIdx.x / Hkv;
   const int Hq = Hkv * G;
   const int L = min(max(seq_lens[b], 0), cache_last_slot<PAGED>(c));
+  const int nsb = min(L / SPLIT + 1, nsplit);  // splits that hold tokens 0..L
+  const int split = (int)blockIdx.y - (nsplit - nsb);
+  if (split < 0) return;  // uniform over the workgroup
   const int t0 = split * SPLIT;
-  if (t0 > L) return;  // uniform over the workgroup
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -472,7 +481,7 @@ hipError_t decode_t(const void* q, const void* k_new, const void* v_new, void* o
   constexpr int SPLIT = split_tokens<G>();
   const int nsplit = (max_seq_len + SPLIT - 1) / SPLIT;  // <= the workspace's split count
   const float qk_scale = scale * 1.4426950408889634f;  // log2(e): softmax in base 2
-  hipExtLaunchKernelGGL((decode_split_kernel<T, D, G, PAGED, SPLIT>), dim3(nsplit, Hkv, B),
+  hipExtLaunchKernelGGL((decode_split_kernel<T, D, G, PAGED, SPLIT>), dim3(Hkv * B, nsplit),
                         dim3(kThreads), 0, st, tl.start, tl.stop, 0,
                         static_cast<const T*>(q), static_cast<const T*>(k_new),
                         static_cast<const T*>(v_new), seq_lens, c, partials, Hkv, nsplit, fr,

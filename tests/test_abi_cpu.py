@@ -150,6 +150,8 @@ def test_decode_rejects(car, lib):
     bad = _cache(car, paged=True, block_size=32)
     assert call(cache=ctypes.byref(bad)) == UNSUPPORTED
     assert call(B=0, q=None, ws=None) == OK          # empty batch: no-op
+    assert call(B=1 << 30) == UNSUPPORTED            # B * Hkv workgroups exceed the grid
+    assert call(msl=65535 * 256 + 1) == UNSUPPORTED  # more than 65535 splits
 
 
 def test_workspace_sizes(lib):
