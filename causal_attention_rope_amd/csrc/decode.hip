@@ -9,13 +9,15 @@
 //
 // How it maps to MI355X.  Decode reads every cached K/V row once and does
 // ~1 flop per byte, so it is bound by HBM bandwidth.  The sequence is split
-// into 256-token pieces; workgroup (split, kv head, sequence) streams its
-// piece with 16-byte loads, LPR = D*sizeof(T)/16 lanes covering one row, so a
+// into pieces of 256 tokens (1024 when several query heads share a KV head);
+// workgroup (kv head, sequence, split) streams its piece with 16-byte loads,
+// LPR = D*sizeof(T)/16 lanes covering one row, so a
 // wave load instruction moves 64/LPR whole rows (4 rows of 256 bytes for
 // bf16, D = 128).  All G = Hq/Hkv query heads of a KV head are served from the
 // same loads (GQA).  Dot products are reduced across the LPR lanes of a row
 // with DPP moves; the softmax maximum and sums are combined across the rows
-// of a wave with lane shuffles and across the 4 waves through LDS.  Each
+// of a wave with lane shuffles and across the waves (4, or 8 with GQA)
+// through LDS.  Each
 // workgroup leaves one partial (max, sum, D accumulators) per query head; a
 // second small kernel merges the partials of a sequence with the
 // log-sum-exp rule of the online softmax ([Scratch] §3.4).  The workgroup
@@ -29,8 +31,11 @@ namespace car {
 
 namespace {
 
-constexpr int kWaves = 4;
-constexpr int kThreads = 64 * kWaves;
+// Waves per workgroup: 4 with one query head per KV head; 8 with several,
+// whose per-workgroup setup and merge (G heads each) are then shared by
+// twice the tokens (measured on the paged GQA workload).
+template <int G>
+constexpr int decode_waves() { return G > 1 ? 8 : 4; }
 
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
@@ -65,7 +70,8 @@ constexpr float kRescaleLog2 = 8.f;          // largest exp2 argument allowed be
 #endif
 template <typename T, int D, int G, int SPLIT = DECODE_SPLIT>
 struct DecodeGeom {
-  static constexpr int TPW = SPLIT / kWaves;   // tokens per wave
+  static constexpr int WAVES = decode_waves<G>();
+  static constexpr int TPW = SPLIT / WAVES;    // tokens per wave
   static constexpr int N = Vec16<T>::N;        // elements per 16-byte chunk
   static constexpr int C = CAR_DECODE_C;       // chunks per lane per row
   static constexpr int LPR = D / N / C;        // lanes per cache row
@@ -100,7 +106,8 @@ __device__ __forceinline__ float row_score(const uint32_t (&qw)[C][4], const u32
 }
 
 template <typename T, int D, int G, bool PAGED, int SPLIT>
-__global__ __launch_bounds__(kThreads, (G <= 4 ? 4 : 2)) void decode_split_kernel(
+__global__ __launch_bounds__(64 * decode_waves<G>())
+__attribute__((amdgpu_waves_per_eu(G <= 4 ? 4 : 2))) void decode_split_kernel(
     const T* __restrict__ q, const T* __restrict__ k_new, const T* __restrict__ v_new,
     const int32_t* __restrict__ seq_lens, CacheArgs c, float* __restrict__ part, int Hkv,
     int nsplit, RopeFreq fr, float qk_scale) {
@@ -110,6 +117,7 @@ __global__ __launch_bounds__(kThreads, (G <= 4 ? 4 : 2)) void decode_split_kerne
   constexpr int PW = decode_partial_words(D);
   constexpr bool BF = sizeof(T) == 2;
 
+  constexpr int kWaves = Gm::WAVES, kThreads = 64 * kWaves;
   __shared__ float sm_acc[kWaves][G][D];
   __shared__ float sm_ml[kWaves][G][2];
 
@@ -464,14 +472,12 @@ __global__ __launch_bounds__(64) void decode_combine_kernel(const float* __restr
   }
 }
 
-// Tokens per workgroup: 256 with one query head per KV head; with several,
-// each workgroup carries the per-head setup (rotated queries, partials) G
-// times and longer splits amortise it (measured on the paged GQA workload).
-#ifndef CAR_DECODE_GQA_SPLIT_MULT
-#define CAR_DECODE_GQA_SPLIT_MULT 2
-#endif
+// Tokens per workgroup: 256 with one query head per KV head (64 per wave);
+// with several, 1024 (128 per wave of 8): each workgroup carries the
+// per-head setup (rotated queries, partials) G times, and longer splits
+// amortise it (measured on the paged GQA workload).
 template <int G>
-constexpr int split_tokens() { return G == 1 ? DECODE_SPLIT : CAR_DECODE_GQA_SPLIT_MULT * DECODE_SPLIT; }
+constexpr int split_tokens() { return G == 1 ? DECODE_SPLIT : 4 * DECODE_SPLIT; }
 
 template <typename T, int D, int G, bool PAGED>
 hipError_t decode_t(const void* q, const void* k_new, const void* v_new, void* out, int B,
@@ -482,7 +488,7 @@ hipError_t decode_t(const void* q, const void* k_new, const void* v_new, void* o
   const int nsplit = (max_seq_len + SPLIT - 1) / SPLIT;  // <= the workspace's split count
   const float qk_scale = scale * 1.4426950408889634f;  // log2(e): softmax in base 2
   hipExtLaunchKernelGGL((decode_split_kernel<T, D, G, PAGED, SPLIT>), dim3(Hkv * B, nsplit),
-                        dim3(kThreads), 0, st, tl.start, tl.stop, 0,
+                        dim3(64 * decode_waves<G>()), 0, st, tl.start, tl.stop, 0,
                         static_cast<const T*>(q), static_cast<const T*>(k_new),
                         static_cast<const T*>(v_new), seq_lens, c, partials, Hkv, nsplit, fr,
                         qk_scale);

@@ -1,6 +1,6 @@
 """GPU parity: attn_decode against the oracle (RoPE at position L, append at
 index L, attention over indices 0..L) for contiguous and paged caches, GQA
-groups, lengths around the 256- and 512-token split boundaries, L = 0, NaN canaries in
+groups, lengths around the 256- and 1024-token split boundaries, L = 0, NaN canaries in
 every slot that must not be read; workload 1's 16 decode steps after its
 prefill; workloads 4 and 5 at full size on sampled sequences."""
 
@@ -69,10 +69,11 @@ def test_decode_lengths(car, dtype, D, paged):
 @pytest.mark.parametrize("group", [1, 2, 4, 8])
 @pytest.mark.parametrize("paged", [False, True], ids=["contiguous", "paged"])
 def test_decode_gqa_groups(car, dtype, group, paged):
-    """Groups above 1 run 512-token splits: lengths on both sides of 512 and
-    1024, and one inside the first split."""
+    """Groups above 1 run 1024-token splits over 8 waves of 128 tokens:
+    lengths on both sides of the wave boundaries 128 and 512 and of the split
+    boundaries 1024 and 2048, and one inside the first wave."""
     log_case(f"decode gqa group={group} {dtype} paged={paged}")
-    lens = [3, 290, 511, 512, 513, 1023, 1024, 1030]
+    lens = [3, 127, 128, 290, 511, 512, 1023, 1024, 1025, 2047, 2048, 2049]
     case = W.decode_case("gqa", len(lens), 8, 8 // group, 128, dtype, lens, 400 + group, DEV,
                          paged=paged, poison_unused=True, extra_blocks=2)
     run_and_check(car, case)
@@ -80,9 +81,9 @@ def test_decode_gqa_groups(car, dtype, group, paged):
 
 @pytest.mark.parametrize("group", [2, 4])
 def test_decode_gqa_lengths_d64(car, group):
-    """D = 64 with groups (16-row load steps, 512-token splits)."""
+    """D = 64 with groups (16-row load steps, 1024-token splits)."""
     log_case(f"decode gqa D=64 group={group}")
-    lens = [0, 1, 255, 511, 512, 513, 700]
+    lens = [0, 1, 127, 255, 511, 700, 1023, 1024, 1025]
     case = W.decode_case("gqa64", len(lens), 8, 8 // group, 64, torch.bfloat16, lens,
                          450 + group, DEV, paged=True, poison_unused=True, extra_blocks=2)
     run_and_check(car, case)
