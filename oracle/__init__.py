@@ -37,5 +37,6 @@ from .attention import (  # noqa: F401
     kv_cache_append,
     cache_rows,
     attn_decode,
+    attn_prefill_cached,
     paged_slot,
 )

@@ -26,6 +26,12 @@ Pins (tests under ``tests/test_oracle_*.py``, none reuses this code):
 * ``attn_decode``: L = 0 gives O = v_new; step t equals the last row of a
   full-recompute prefill over the same tokens; GQA equals MHA with each
   KV head repeated.
+* ``attn_prefill_cached``: a prompt taken as one chunk equals the same
+  prompt taken as two chunks over the cache (outputs and cache contents); a
+  one-token chunk equals a decode step; an empty prefix and a one-token
+  chunk give O = v; outputs of earlier queries do not move when later chunk
+  tokens change, and all of them move when the cached prefix changes; GQA
+  equals MHA with each KV head repeated.
 
 Convention choices with no pin on synthetic data ("parity unpinned"):
 adjacent pairs (2i, 2i+1) for RoPE, and contiguous GQA groups.
@@ -43,6 +49,7 @@ __all__ = [
     "kv_cache_append",
     "cache_rows",
     "attn_decode",
+    "attn_prefill_cached",
     "paged_slot",
 ]
 
@@ -234,4 +241,47 @@ def attn_decode(q, k_new, v_new, cache_k, cache_v, seq_lens,
             vals = cache_rows(cache_v, b, hk, L + 1, block_table, block_size)
             out[b, hq] = causal_attention(q_rot[hq][None, :], keys, vals,
                                           (np.array([L]), pos), scale)[0]
+    return out
+
+
+def attn_prefill_cached(q, k, v, cache_k, cache_v, seq_lens,
+                        theta: float = 10000.0, scale: float | None = None,
+                        block_table=None, block_size: int = 16):
+    """A prompt chunk that continues a cached prefix.
+
+    For sequence b with P = seq_lens[b] tokens already cached, the chunk's S
+    tokens sit at positions P..P+S-1, which are also their cache indices
+    ([Scratch] §3.2).  q [B, Hq, S, D] and k [B, Hkv, S, D] are rotated at
+    those positions; the rotated keys and raw values v are written to cache
+    indices P..P+S-1; chunk query i then attends over cache rows 0..P+i, the
+    cached prefix plus the chunk up to itself ([Scratch] §3.3: a position
+    sees itself and earlier ones; the earlier ones come from the cache).
+
+    The caches are updated in place.  Returns out [B, Hq, S, D].
+    """
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    B, Hq, S, D = q.shape
+    Hkv = k.shape[1]
+    group = Hq // Hkv
+    if scale is None:
+        scale = 1.0 / np.sqrt(D)
+    seq_lens = np.asarray(seq_lens)
+    out = np.empty((B, Hq, S, D))
+    for b in range(B):
+        P = int(seq_lens[b])
+        pos = P + np.arange(S)
+        q_rot = rope_rotate(q[b], pos, theta)           # [Hq, S, D]
+        k_rot = rope_rotate(k[b], pos, theta)           # [Hkv, S, D]
+        if block_table is None:
+            kv_cache_append(cache_k[b:b + 1], cache_v[b:b + 1], k_rot[None], v[b:b + 1],
+                            pos[None, :])
+        else:
+            kv_cache_append(cache_k, cache_v, k_rot[None], v[b:b + 1], pos[None, :],
+                            block_table=block_table[b:b + 1], block_size=block_size)
+        kpos = np.arange(P + S)
+        for hq in range(Hq):
+            hk = hq // group
+            keys = cache_rows(cache_k, b, hk, P + S, block_table, block_size)
+            vals = cache_rows(cache_v, b, hk, P + S, block_table, block_size)
+            out[b, hq] = causal_attention(q_rot[hq], keys, vals, (pos, kpos), scale)
     return out

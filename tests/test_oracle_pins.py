@@ -529,6 +529,166 @@ def test_paged_pin_catches_swapped_block_and_offset():
 
 
 # ==========================================================================
+# Chunked prefill against a cache ([Scratch] §3.2-§3.3)
+# ==========================================================================
+
+def _chunk_case(B, Hq, Hkv, D, seed):
+    r = rng(seed)
+    n = 23
+    q = r.standard_normal((B, Hq, n, D))
+    k, v = r.standard_normal((B, Hkv, n, D)), r.standard_normal((B, Hkv, n, D))
+    return q, k, v, n
+
+
+def _two_chunks(impl, q, k, v, n, split, paged=False):
+    """The prompt as chunk [0, split) then chunk [split, n) over one cache."""
+    B, Hkv, D = q.shape[0], k.shape[1], q.shape[-1]
+    cap = 32
+    ck, cv = np.full((B, Hkv, cap, D), np.nan), np.full((B, Hkv, cap, D), np.nan)
+    table = None
+    if paged:
+        nb = B * 2 + 3
+        table = rng(99).permutation(nb)[: B * 2].reshape(B, 2)
+        ck, cv = np.full((nb, Hkv, 16, D), np.nan), np.full((nb, Hkv, 16, D), np.nan)
+    o1 = impl(q[:, :, :split], k[:, :, :split], v[:, :, :split], ck, cv, np.zeros(B, int),
+              block_table=table)
+    o2 = impl(q[:, :, split:], k[:, :, split:], v[:, :, split:], ck, cv, np.full(B, split),
+              block_table=table)
+    return np.concatenate([o1, o2], axis=2), ck, cv, table
+
+
+def check_chunks_equal_whole_prompt(impl, paged=False):
+    """A prompt taken in two chunks over the cache equals the prompt taken
+    whole: same outputs, and the cache holds the rotated keys and raw values
+    at indices 0..n-1 either way."""
+    q, k, v, n = _chunk_case(2, 4, 2, 8, seed=31)
+    whole, k_rot = A.attn_prefill(q, k, v, np.tile(np.arange(n), (2, 1)))
+    for split in (1, 9, 16, 22):
+        got, ck, cv, table = _two_chunks(impl, q, k, v, n, split, paged)
+        if not np.allclose(got, whole, atol=1e-12):
+            return False
+        rows_k = np.stack([A.cache_rows(ck, b, h, n, table) for b in range(2) for h in range(2)])
+        rows_v = np.stack([A.cache_rows(cv, b, h, n, table) for b in range(2) for h in range(2)])
+        if not (np.allclose(rows_k, k_rot.reshape(4, n, 8), atol=1e-14)
+                and np.array_equal(rows_v, v.reshape(4, n, 8))):
+            return False
+    return True
+
+
+def test_chunked_prefill_equals_whole_prompt():
+    assert check_chunks_equal_whole_prompt(A.attn_prefill_cached)
+
+
+def test_chunked_prefill_paged_equals_whole_prompt():
+    assert check_chunks_equal_whole_prompt(A.attn_prefill_cached, paged=True)
+
+
+def test_one_token_chunk_equals_decode_step():
+    r = rng(32)
+    B, Hq, Hkv, D = 3, 4, 2, 8
+    lens = np.array([0, 5, 11])
+    q, kn, vn = r.standard_normal((B, Hq, D)), r.standard_normal((B, Hkv, D)), r.standard_normal((B, Hkv, D))
+    ck, cv = r.standard_normal((B, Hkv, 12, D)), r.standard_normal((B, Hkv, 12, D))
+    ck2, cv2 = ck.copy(), cv.copy()
+    dec = A.attn_decode(q, kn, vn, ck, cv, lens)
+    chk = A.attn_prefill_cached(q[:, :, None], kn[:, :, None], vn[:, :, None], ck2, cv2, lens)
+    assert np.allclose(chk[:, :, 0], dec, atol=1e-14)
+    assert np.array_equal(ck, ck2) and np.array_equal(cv, cv2)
+
+
+def test_one_token_chunk_on_empty_cache_returns_its_value():
+    r = rng(33)
+    B, Hq, Hkv, D = 2, 4, 4, 8
+    q, k, v = (r.standard_normal((B, h, 1, D)) for h in (Hq, Hkv, Hkv))
+    ck, cv = np.full((B, Hkv, 3, D), np.nan), np.full((B, Hkv, 3, D), np.nan)
+    out = A.attn_prefill_cached(q, k, v, ck, cv, np.zeros(B, int))
+    assert np.allclose(out, v, atol=1e-15)
+
+
+def test_chunk_causality_and_prefix_dependence():
+    """Changing chunk token j moves no output of a query before j; changing
+    one cached prefix row moves every chunk query's output."""
+    r = rng(34)
+    B, H, D, P, S = 1, 2, 8, 6, 7
+    q, k, v = (r.standard_normal((B, H, S, D)) for _ in range(3))
+    ck, cv = r.standard_normal((B, H, P + S, D)), r.standard_normal((B, H, P + S, D))
+    base = A.attn_prefill_cached(q, k, v, ck.copy(), cv.copy(), np.array([P]))
+    k2, v2 = k.copy(), v.copy()
+    k2[:, :, 4] += 1.0
+    v2[:, :, 4] += 1.0
+    pert = A.attn_prefill_cached(q, k2, v2, ck.copy(), cv.copy(), np.array([P]))
+    assert np.array_equal(pert[:, :, :4], base[:, :, :4])
+    assert not np.allclose(pert[:, :, 4:], base[:, :, 4:])
+    cv3 = cv.copy()
+    cv3[:, :, 2] += 1.0
+    pref = A.attn_prefill_cached(q, k, v, ck.copy(), cv3, np.array([P]))
+    assert not np.any(np.isclose(pref, base).all(axis=-1))
+
+
+def test_chunked_gqa_equals_mha_with_repeated_kv_heads():
+    r = rng(35)
+    B, Hq, Hkv, D, P, S = 2, 8, 2, 8, 5, 6
+    q = r.standard_normal((B, Hq, S, D))
+    k, v = r.standard_normal((B, Hkv, S, D)), r.standard_normal((B, Hkv, S, D))
+    ck, cv = r.standard_normal((B, Hkv, P + S, D)), r.standard_normal((B, Hkv, P + S, D))
+    lens = np.full(B, P)
+    gqa = A.attn_prefill_cached(q, k, v, ck.copy(), cv.copy(), lens)
+    mha = A.attn_prefill_cached(q, np.repeat(k, 4, axis=1), np.repeat(v, 4, axis=1),
+                                np.repeat(ck, 4, axis=1), np.repeat(cv, 4, axis=1), lens)
+    assert np.array_equal(gqa, mha)
+
+
+def _chunk_mask_without_offset(q, k, v, ck, cv, lens, block_table=None):
+    """Planted mistake: the mask compares chunk-local indices, so a chunk
+    query sees only the first i+1 cache rows."""
+    B, Hq, S, D = q.shape
+    out = np.empty((B, Hq, S, D))
+    for b in range(B):
+        P = int(lens[b])
+        pos = P + np.arange(S)
+        qr, kr = A.rope_rotate(q[b], pos), A.rope_rotate(k[b], pos)
+        if block_table is None:
+            A.kv_cache_append(ck[b:b + 1], cv[b:b + 1], kr[None], v[b:b + 1], pos[None])
+        else:
+            A.kv_cache_append(ck, cv, kr[None], v[b:b + 1], pos[None], block_table=block_table)
+        for h in range(Hq):
+            keys = A.cache_rows(ck, b, h, P + S, block_table)
+            vals = A.cache_rows(cv, b, h, P + S, block_table)
+            out[b, h] = A.causal_attention(qr[h], keys, vals, (np.arange(S), np.arange(P + S)),
+                                           1 / math.sqrt(D))
+    return out
+
+
+def _chunk_rope_at_local_positions(q, k, v, ck, cv, lens, block_table=None):
+    """Planted mistake: the chunk is rotated at positions 0..S-1."""
+    B, Hq, S, D = q.shape
+    out = np.empty((B, Hq, S, D))
+    for b in range(B):
+        P = int(lens[b])
+        pos = P + np.arange(S)
+        qr, kr = A.rope_rotate(q[b], np.arange(S)), A.rope_rotate(k[b], np.arange(S))
+        A.kv_cache_append(ck[b:b + 1], cv[b:b + 1], kr[None], v[b:b + 1], pos[None])
+        for h in range(Hq):
+            out[b, h] = A.causal_attention(qr[h], ck[b, h, :P + S], cv[b, h, :P + S],
+                                           (pos, np.arange(P + S)), 1 / math.sqrt(D))
+    return out
+
+
+@pytest.mark.parametrize("bad", [_chunk_mask_without_offset, _chunk_rope_at_local_positions])
+def test_chunk_pin_catches_planted_mistakes(bad):
+    def impl(q, k, v, ck, cv, lens, block_table=None):
+        B, Hq = q.shape[:2]
+        Hkv = k.shape[1]
+        # expand the KV heads so the planted copies can index by query head
+        return bad(q, k, v, ck, cv, lens) if Hq == Hkv else bad(
+            q, np.repeat(k, Hq // Hkv, axis=1), np.repeat(v, Hq // Hkv, axis=1), ck, cv, lens)
+    q, k, v, n = _chunk_case(1, 2, 2, 8, seed=36)
+    whole, _ = A.attn_prefill(q, k, v, np.arange(n)[None])
+    got, _, _, _ = _two_chunks(impl, q, k, v, n, 9)
+    assert not np.allclose(got, whole, atol=1e-6)
+
+
+# ==========================================================================
 # P14: constants the pages print
 # ==========================================================================
 
