@@ -22,6 +22,7 @@ import torch
 
 __all__ = [
     "CarError", "KVCache", "rope_apply", "kv_cache_append", "attn_prefill", "attn_decode",
+    "attn_prefill_cached",
     "prefill_workspace_bytes", "decode_workspace_bytes", "set_timing_events", "library_path",
 ]
 
@@ -70,6 +71,8 @@ def _load() -> ctypes.CDLL:
         "car_attn_prefill_workspace_bytes": (sz, [i32, i32, i32, i32, i32, cache_p]),
         "car_attn_prefill": (i32, [vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, vp, f32, f32,
                                    cache_p, vp, sz, vp]),
+        "car_attn_prefill_cached": (i32, [vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, vp, i32,
+                                          f32, f32, cache_p, vp]),
         "car_attn_decode_workspace_bytes": (sz, [i32, i32, i32, i32]),
         "car_attn_decode": (i32, [vp, vp, vp, vp, i32, i32, i32, i32, i32, vp, i32, f32, f32,
                                   cache_p, vp, sz, vp]),
@@ -295,6 +298,47 @@ def attn_prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, positions: t
                                  _ptr(positions), float(theta), float(scale),
                                  ctypes.byref(c) if c is not None else None, _ptr(ws),
                                  ws.numel() * ws.element_size(), _stream(q)), "attn_prefill")
+    return out
+
+
+def attn_prefill_cached(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
+                        seq_lens: torch.Tensor, cache: KVCache, max_seq_len: int,
+                        theta: float = 10000.0, scale: Optional[float] = None,
+                        out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """A prompt chunk continuing a cached prefix (see car_attn_prefill_cached).
+
+    q [B, Hq, S, D]; k, v [B, Hkv, S, D] (k not rotated); seq_lens int32 [B]
+    (tokens already cached = position of the chunk's first token);
+    ``max_seq_len`` is a host bound on seq_lens + S.  Writes the chunk's keys
+    and values into the cache and returns out [B, Hq, S, D].
+    """
+    _need(q, "q", dim=4)
+    _need(k, "k", dtype=q.dtype, dim=4, device=q.device)
+    _need(v, "v", dtype=q.dtype, dim=4, device=q.device)
+    B, Hq, S, D = q.shape
+    if k.shape != v.shape or k.shape[0] != B or k.shape[2] != S or k.shape[3] != D:
+        raise ValueError("k and v must be [B, Hkv, S, D] matching q")
+    Hkv = k.shape[1]
+    _need(seq_lens, "seq_lens", dtype=torch.int32, dim=1, device=q.device)
+    if seq_lens.shape[0] != B:
+        raise ValueError("seq_lens must be [B]")
+    if cache.k.dtype != q.dtype or cache.k.device != q.device:
+        raise ValueError("cache dtype/device must match q")
+    if cache.Hkv != Hkv or cache.D != D:
+        raise ValueError("cache heads or head dim do not match k")
+    cache.check_batch(B)
+    if out is None:
+        out = torch.empty_like(q)
+    _need(out, "out", dtype=q.dtype, dim=4, device=q.device)
+    if out.shape != q.shape:
+        raise ValueError("out must have q's shape")
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    c = cache._c()
+    _check(_lib.car_attn_prefill_cached(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _dtype_code(q),
+                                        B, Hq, Hkv, S, D, _ptr(seq_lens), int(max_seq_len),
+                                        float(theta), float(scale), ctypes.byref(c), _stream(q)),
+           "attn_prefill_cached")
     return out
 
 

@@ -167,6 +167,41 @@ car_status car_attn_prefill(const void* q, const void* k, const void* v, void* o
                                            positions, fr, scale, stream, timing()));
 }
 
+car_status car_attn_prefill_cached(const void* q, const void* k, const void* v, void* out,
+                                   car_dtype dtype, int B, int Hq, int Hkv, int S, int D,
+                                   const int32_t* seq_lens, int max_seq_len, float theta,
+                                   float scale, const car_kv_cache* cache, hipStream_t stream) {
+  if (!dtype_ok(dtype) || !head_dim_ok(D)) return CAR_ERR_UNSUPPORTED;
+  if (cache != nullptr && cache->block_table != nullptr && cache->block_size != 16)
+    return CAR_ERR_UNSUPPORTED;
+  if (B < 0 || Hq < 0 || Hkv < 0 || S < 0) return CAR_ERR_INVALID_ARGUMENT;
+  if (!positive_finite(theta) || !positive_finite(scale)) return CAR_ERR_INVALID_ARGUMENT;
+  if (Hkv == 0 ? Hq != 0 : (Hq % Hkv) != 0) return CAR_ERR_INVALID_ARGUMENT;
+  if ((int64_t)B * Hq * S == 0) return CAR_OK;
+  if (q == nullptr || k == nullptr || v == nullptr || out == nullptr || seq_lens == nullptr)
+    return CAR_ERR_INVALID_ARGUMENT;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out))
+    return CAR_ERR_INVALID_ARGUMENT;
+  CacheArgs c;
+  int64_t cap = 0;
+  const car_status cs = check_cache(cache, &c, &cap);
+  if (cs != CAR_OK) return cs;
+  if (max_seq_len < S || max_seq_len > cap) return CAR_ERR_INVALID_ARGUMENT;
+  // launch grids (fp32: B and Hq in grid y, z; bf16: query-tile pairs x B x Hq
+  // in x) and 32-bit byte offsets within one head of a contiguous cache
+  if (B > 65535 || Hq > 65535 || (int64_t)B * Hq * ((S + 511) / 512) > INT32_MAX ||
+      cap * D * 4 > (int64_t)UINT32_MAX)
+    return CAR_ERR_UNSUPPORTED;
+
+  const Dtype dt = dtype == CAR_DTYPE_F32 ? F32 : BF16;
+  const RopeFreq fr = make_freq(D, theta);
+  const bool paged = cache->block_table != nullptr;
+  hipError_t e = launch_chunk_prep(dt, D, paged, c, k, v, B, Hkv, S, seq_lens, fr, stream);
+  if (e != hipSuccess) return CAR_ERR_HIP;
+  return from_hip(launch_prefill_cached(dt, D, paged, q, out, B, Hq, Hkv, S, c, seq_lens, fr,
+                                        scale, stream, timing()));
+}
+
 size_t car_attn_decode_workspace_bytes(int B, int Hq, int D, int max_seq_len) {
   if (B < 0 || Hq < 0 || !head_dim_ok(D) || max_seq_len < 1) return 0;
   return (size_t)B * Hq * decode_nsplit(max_seq_len) * decode_partial_words(D) * sizeof(float);

@@ -35,15 +35,33 @@ namespace car {
 
 namespace {
 
+// Where the attention kernels read rotated keys and values.
+constexpr int KEYS_PROMPT = 0;  // the prompt's own K' and V, [B, Hkv, S, D]
+constexpr int KEYS_CONTIG = 1;  // a contiguous cache holding the prefix and the chunk
+constexpr int KEYS_PAGED = 2;   // a paged cache holding the prefix and the chunk
+
+// Tokens cached before the chunk (0 for a prompt): seq_lens[b], kept small
+// enough that the chunk's last key stays inside the cache.
+template <int SRC>
+__device__ __forceinline__ int chunk_start(const CacheArgs& c, const int32_t* seq_lens, int b,
+                                           int S) {
+  if constexpr (SRC == KEYS_PROMPT) {
+    return 0;
+  } else {
+    const int P = min(max(seq_lens[b], 0), cache_last_slot<SRC == KEYS_PAGED>(c) + 1 - S);
+    return max(P, 0);
+  }
+}
+
 // ------------------------------------------------------------------ fp32 ---
 constexpr int F32_ROWS = 64;  // query rows per workgroup (one per thread)
 constexpr int F32_KT = 32;    // keys per LDS tile
 
-template <int D>
+template <int D, int SRC>
 __global__ __launch_bounds__(F32_ROWS) void prefill_f32_kernel(
     const float* __restrict__ q, const float* __restrict__ kr, const float* __restrict__ v,
     float* __restrict__ out, const int32_t* __restrict__ positions, int Hq, int Hkv, int S,
-    RopeFreq fr, float qk_scale) {
+    RopeFreq fr, float qk_scale, CacheArgs c, const int32_t* __restrict__ seq_lens) {
   __shared__ float4 sk[F32_KT][D / 4];
   __shared__ float4 sv[F32_KT][D / 4];
   const int b = blockIdx.z, hq = blockIdx.y;
@@ -51,6 +69,8 @@ __global__ __launch_bounds__(F32_ROWS) void prefill_f32_kernel(
   const int i0 = blockIdx.x * F32_ROWS;
   const int i = i0 + threadIdx.x;
   const int ic = min(i, S - 1);
+  const int P = chunk_start<SRC>(c, seq_lens, b, S);  // keys before the chunk
+  const int nkeys = P + S;
 
   float qv[D];
   const float* qrow = q + (((int64_t)b * Hq + hq) * S + ic) * D;
@@ -58,7 +78,7 @@ __global__ __launch_bounds__(F32_ROWS) void prefill_f32_kernel(
   for (int d = 0; d < D; d += 4) {
     float f[4];
     load16<float>(qrow + d, f);
-    rope_rotate_regs<4>(f, positions[(int64_t)b * S + ic], d / 2, fr);
+    rope_rotate_regs<4>(f, SRC == KEYS_PROMPT ? positions[(int64_t)b * S + ic] : P + ic, d / 2, fr);
 #pragma unroll
     for (int e = 0; e < 4; ++e) qv[d + e] = f[e] * qk_scale;
   }
@@ -67,16 +87,23 @@ __global__ __launch_bounds__(F32_ROWS) void prefill_f32_kernel(
   for (int d = 0; d < D; ++d) acc[d] = 0.f;
   float m = -INFINITY, l = 0.f;
 
-  const float* kb = kr + ((int64_t)b * Hkv + hk) * S * D;
-  const float* vb = v + ((int64_t)b * Hkv + hk) * S * D;
-  const int jlast = min(S - 1, i0 + F32_ROWS - 1);
+  const float* kb = SRC == KEYS_PROMPT ? kr + ((int64_t)b * Hkv + hk) * S * D : nullptr;
+  const float* vb = SRC == KEYS_PROMPT ? v + ((int64_t)b * Hkv + hk) * S * D : nullptr;
+  const int jlast = min(nkeys - 1, P + i0 + F32_ROWS - 1);
   for (int j0 = 0; j0 <= jlast; j0 += F32_KT) {
     __syncthreads();
     for (int idx = threadIdx.x; idx < F32_KT * D / 4; idx += F32_ROWS) {
       const int r = idx / (D / 4), c4 = idx % (D / 4);
-      const int64_t row = min(j0 + r, S - 1);
-      sk[r][c4] = *reinterpret_cast<const float4*>(kb + row * D + c4 * 4);
-      sv[r][c4] = *reinterpret_cast<const float4*>(vb + row * D + c4 * 4);
+      const int j = min(j0 + r, nkeys - 1);
+      int64_t off;  // element offset of key row j
+      if constexpr (SRC == KEYS_PROMPT)
+        off = (int64_t)j * D;
+      else
+        off = cache_row<SRC == KEYS_PAGED>(c, b, hk, Hkv, j) * D;
+      const float* ksrc = SRC == KEYS_PROMPT ? kb : static_cast<const float*>(c.k);
+      const float* vsrc = SRC == KEYS_PROMPT ? vb : static_cast<const float*>(c.v);
+      sk[r][c4] = *reinterpret_cast<const float4*>(ksrc + off + c4 * 4);
+      sv[r][c4] = *reinterpret_cast<const float4*>(vsrc + off + c4 * 4);
     }
     __syncthreads();
     float s[F32_KT];
@@ -92,7 +119,7 @@ __global__ __launch_bounds__(F32_ROWS) void prefill_f32_kernel(
         dot = fmaf(qv[4 * c4 + 2], kk.z, dot);
         dot = fmaf(qv[4 * c4 + 3], kk.w, dot);
       }
-      s[r] = (j0 + r <= ic) ? dot : -INFINITY;
+      s[r] = (j0 + r <= P + ic) ? dot : -INFINITY;
       tmax = fmaxf(tmax, s[r]);
     }
     const float m_new = fmaxf(m, tmax);  // finite: key 0 is visible to every row
@@ -228,11 +255,11 @@ __device__ __forceinline__ int logical_chunk(int p, int r) {
   }
 }
 
-template <int D>
+template <int D, int SRC>
 __global__ __launch_bounds__(Tile<D>::THREADS, 2) void prefill_bf16_kernel(
     const bf16_t* __restrict__ q, const bf16_t* __restrict__ kr, const bf16_t* __restrict__ v,
     bf16_t* __restrict__ out, const int32_t* __restrict__ positions, int Hq, int Hkv, int S,
-    int nqt, RopeFreq fr, float sm_scale_log2) {
+    int nqt, RopeFreq fr, float sm_scale_log2, CacheArgs c, const int32_t* __restrict__ seq_lens) {
   using C = Tile<D>;
   __shared__ __attribute__((aligned(1024))) char smem[2 * C::STAGEB];
 
@@ -263,8 +290,19 @@ __global__ __launch_bounds__(Tile<D>::THREADS, 2) void prefill_bf16_kernel(
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform per wave
   const int l32 = lane & 31, g = lane >> 5;
-  const bf16_t* kbase = kr + ((int64_t)b * Hkv + hk) * S * D;
-  const bf16_t* vbase = v + ((int64_t)b * Hkv + hk) * S * D;
+  // Keys: the prompt itself, or rows 0..P+S-1 of a cache that held P tokens
+  // before this chunk; chunk query i sits at key index P+i.
+  const int P = chunk_start<SRC>(c, seq_lens, b, S);
+  const int nkeys = P + S;
+  const bf16_t* kbase = nullptr;  // the head's key rows (paged: per block, below)
+  const bf16_t* vbase = nullptr;
+  if constexpr (SRC == KEYS_CONTIG) {
+    kbase = static_cast<const bf16_t*>(c.k) + ((int64_t)b * Hkv + hk) * c.max_seq * D;
+    vbase = static_cast<const bf16_t*>(c.v) + ((int64_t)b * Hkv + hk) * c.max_seq * D;
+  } else if constexpr (SRC == KEYS_PROMPT) {
+    kbase = kr + ((int64_t)b * Hkv + hk) * S * D;
+    vbase = v + ((int64_t)b * Hkv + hk) * S * D;
+  }
 
   // ---- direct buffer -> LDS loads of K and V tiles ----
   // Load i of this wave fills LDS bytes [n KB, (n+1) KB) of a tile (n =
@@ -272,10 +310,13 @@ __global__ __launch_bounds__(Tile<D>::THREADS, 2) void prefill_bf16_kernel(
   // n*RPI + l/CPR and so fetches that row's logical chunk stored there.  A
   // whole tile needs only the per-lane offsets within the tile plus the
   // tile's start as a scalar offset; in the last, partial tile the rows past
-  // the end re-read row S-1 (finite values; those keys are masked).  K and V
-  // have two buffers each: K holds tiles t+1 and t+2 while V holds t and t+1
-  // (the QK^T of tile t+1 is issued before the softmax of tile t).
-  const uint32_t head_bytes = (uint32_t)S * C::ROWB;
+  // the end re-read the last key row (finite values; those keys are masked).
+  // K and V have two buffers each: K holds tiles t+1 and t+2 while V holds t
+  // and t+1 (the QK^T of tile t+1 is issued before the softmax of tile t).
+  // In a paged cache each load's RPI rows lie in one 16-token block (tiles
+  // and loads are aligned to RPI, which divides 16), so a load takes its
+  // block from the table as a scalar and addresses that block alone.
+  const uint32_t head_bytes = (uint32_t)nkeys * C::ROWB;
   const __amdgpu_buffer_rsrc_t krs = make_rsrc(kbase, head_bytes);
   const __amdgpu_buffer_rsrc_t vrs = make_rsrc(vbase, head_bytes);
   uint32_t dma_off[C::IPW];
@@ -284,8 +325,22 @@ __global__ __launch_bounds__(Tile<D>::THREADS, 2) void prefill_bf16_kernel(
     const int row = (wave * C::IPW + i) * C::RPI + lane / C::CPR;
     dma_off[i] = row * C::ROWB + (logical_chunk<C::CPR>(lane % C::CPR, row) << 4);
   }
-  auto issue = [&](__amdgpu_buffer_rsrc_t rs, int j0, char* dst) {
-    if (j0 + C::BN <= S) {  // uniform
+  const int32_t* const trow = SRC == KEYS_PAGED ? c.table + (int64_t)b * c.mbps : nullptr;
+  auto issue = [&](__amdgpu_buffer_rsrc_t rs, const void* pool, int j0, char* dst) {
+    if constexpr (SRC == KEYS_PAGED) {
+      static_assert(16 % C::RPI == 0 && C::BN % 16 == 0, "a load stays inside one block");
+#pragma unroll
+      for (int i = 0; i < C::IPW; ++i) {
+        const int r0 = (wave * C::IPW + i) * C::RPI;  // first tile row of this load
+        const int row = r0 + lane / C::CPR;
+        const int j = min(j0 + row, nkeys - 1);        // rows past the end: the last key
+        const int jb = min(j0 + r0, nkeys - 1);        // uniform: the load's block
+        const int blk = min(max(trow[jb >> 4], 0), c.num_blocks - 1);
+        const bf16_t* bp = static_cast<const bf16_t*>(pool) + (((int64_t)blk * Hkv + hk) << 4) * D;
+        const uint32_t off = (j & 15) * C::ROWB + (logical_chunk<C::CPR>(lane % C::CPR, row) << 4);
+        dma16(make_rsrc(bp, 16 * C::ROWB), off, 0, dst + (wave * C::IPW + i) * 1024);
+      }
+    } else if (j0 + C::BN <= nkeys) {  // uniform
 #pragma unroll
       for (int i = 0; i < C::IPW; ++i)
         dma16(rs, dma_off[i], (uint32_t)j0 * C::ROWB, dst + (wave * C::IPW + i) * 1024);
@@ -293,7 +348,7 @@ __global__ __launch_bounds__(Tile<D>::THREADS, 2) void prefill_bf16_kernel(
 #pragma unroll
       for (int i = 0; i < C::IPW; ++i) {
         const int row = (wave * C::IPW + i) * C::RPI + lane / C::CPR;
-        const uint32_t off = min(j0 + row, S - 1) * C::ROWB +
+        const uint32_t off = min(j0 + row, nkeys - 1) * C::ROWB +
                              (logical_chunk<C::CPR>(lane % C::CPR, row) << 4);
         dma16(rs, off, 0, dst + (wave * C::IPW + i) * 1024);
       }
@@ -342,7 +397,7 @@ __global__ __launch_bounds__(Tile<D>::THREADS, 2) void prefill_bf16_kernel(
     bf16x8_t qf[C::QKS];
     {
       const bf16_t* qp = q + ((int64_t)bh * S + qrc) * D;
-      const int pos = positions[(int64_t)b * S + qrc];
+      const int pos = SRC == KEYS_PROMPT ? positions[(int64_t)b * S + qrc] : P + qrc;
   #pragma unroll
       for (int ks = 0; ks < C::QKS; ++ks) {
         const int d0 = ks * 16 + g * 8;
@@ -364,9 +419,9 @@ __global__ __launch_bounds__(Tile<D>::THREADS, 2) void prefill_bf16_kernel(
     f32x16_t sacc[2][C::NKB];  // S^T of the tile being consumed and of the next one
 
     const int q_end = min(q0 + C::BM, S);  // exclusive
-    const int ntiles = (q_end + C::BN - 1) / C::BN;
+    const int ntiles = (P + q_end + C::BN - 1) / C::BN;
     // tiles 0..wlast hold keys visible to this wave (uniform per wave)
-    const int wlast = min(ntiles - 1, (qw + 31) / C::BN);
+    const int wlast = min(ntiles - 1, (P + qw + 31) / C::BN);
 
     // S^T = K Q^T for the tile in K buffer kb_i: lane holds keys
     // kb*32 + 8*(r/4) + 4*g + r%4 of query qrow.  The two 32-key blocks are
@@ -406,13 +461,13 @@ __global__ __launch_bounds__(Tile<D>::THREADS, 2) void prefill_bf16_kernel(
     auto softmax_pv = [&](int t, auto SI) {
       constexpr int si = decltype(SI)::value;
       const int j0 = t * C::BN;
-      if (j0 + C::BN - 1 > qw) {  // causal mask where the tile passes this wave's first row
+      if (j0 + C::BN - 1 > P + qw) {  // causal mask where the tile passes this wave's first row
   #pragma unroll
         for (int kb = 0; kb < C::NKB; ++kb)
   #pragma unroll
           for (int r = 0; r < 16; ++r) {
             const int key = j0 + kb * 32 + 8 * (r >> 2) + 4 * g + (r & 3);
-            if (key > qrow) sacc[si][kb][r] = -INFINITY;
+            if (key > P + qrow) sacc[si][kb][r] = -INFINITY;
           }
       }
       float mt = -INFINITY;
@@ -495,17 +550,17 @@ __global__ __launch_bounds__(Tile<D>::THREADS, 2) void prefill_bf16_kernel(
     auto step = [&](int t, auto SC, auto SN) {
       __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's loads landed
       __syncthreads();                     // everyone's loads landed; old buffers free
-      if (t + 2 < ntiles) issue(krs, (t + 2) * C::BN, kbuf + (t & 1) * C::TILEB);
-      if (t + 1 < ntiles) issue(vrs, (t + 1) * C::BN, vbuf + ((t + 1) & 1) * C::TILEB);
+      if (t + 2 < ntiles) issue(krs, c.k, (t + 2) * C::BN, kbuf + (t & 1) * C::TILEB);
+      if (t + 1 < ntiles) issue(vrs, c.v, (t + 1) * C::BN, vbuf + ((t + 1) & 1) * C::TILEB);
       if (t + 1 <= wlast) qk((t + 1) & 1, SN);
       if (t <= wlast) softmax_pv(t, SC);
     };
 
     using S0 = std::integral_constant<int, 0>;
     using S1 = std::integral_constant<int, 1>;
-    issue(krs, 0, kbuf);
-    issue(vrs, 0, vbuf);
-    if (ntiles > 1) issue(krs, C::BN, kbuf + C::TILEB);
+    issue(krs, c.k, 0, kbuf);
+    issue(vrs, c.v, 0, vbuf);
+    if (ntiles > 1) issue(krs, c.k, C::BN, kbuf + C::TILEB);
     __builtin_amdgcn_s_waitcnt(0x0F70);
     __syncthreads();
     // K(0) is visible; K(1) and V(0) may still be in flight (waited for in step 0)
@@ -533,31 +588,54 @@ __global__ __launch_bounds__(Tile<D>::THREADS, 2) void prefill_bf16_kernel(
   }
 }
 
-template <int D>
-hipError_t prefill_f32_t(const void* q, const void* k_rot, const void* v, void* out, int B,
-                         int Hq, int Hkv, int S, const int32_t* positions, const RopeFreq& fr,
-                         float scale, hipStream_t st, const TimedLaunch& tl) {
+// Keys and values of one launch: the prompt's own (k_rot, v) or a cache.
+struct KeySource {
+  const void* k_rot;
+  const void* v;
+  CacheArgs c;
+  const int32_t* seq_lens;
+};
+
+template <int D, int SRC>
+hipError_t prefill_f32_t(const void* q, const KeySource& ks, void* out, int B, int Hq, int Hkv,
+                         int S, const int32_t* positions, const RopeFreq& fr, float scale,
+                         hipStream_t st, const TimedLaunch& tl) {
   const dim3 grid((S + F32_ROWS - 1) / F32_ROWS, Hq, B);
-  hipExtLaunchKernelGGL((prefill_f32_kernel<D>), grid, dim3(F32_ROWS), 0, st, tl.start, tl.stop,
-                        0, static_cast<const float*>(q), static_cast<const float*>(k_rot),
-                        static_cast<const float*>(v), static_cast<float*>(out), positions, Hq,
-                        Hkv, S, fr, scale * 1.4426950408889634f);
+  hipExtLaunchKernelGGL((prefill_f32_kernel<D, SRC>), grid, dim3(F32_ROWS), 0, st, tl.start,
+                        tl.stop, 0, static_cast<const float*>(q),
+                        static_cast<const float*>(ks.k_rot), static_cast<const float*>(ks.v),
+                        static_cast<float*>(out), positions, Hq, Hkv, S, fr,
+                        scale * 1.4426950408889634f, ks.c, ks.seq_lens);
   return hipGetLastError();
 }
 
-template <int D>
-hipError_t prefill_bf16_t(const void* q, const void* k_rot, const void* v, void* out, int B,
-                          int Hq, int Hkv, int S, const int32_t* positions, const RopeFreq& fr,
-                          float scale, hipStream_t st, const TimedLaunch& tl) {
+template <int D, int SRC>
+hipError_t prefill_bf16_t(const void* q, const KeySource& ks, void* out, int B, int Hq, int Hkv,
+                          int S, const int32_t* positions, const RopeFreq& fr, float scale,
+                          hipStream_t st, const TimedLaunch& tl) {
   using C = Tile<D>;
   const int nqt = (S + C::BM - 1) / C::BM;
   const int npair = (nqt + 1) / 2;
-  hipExtLaunchKernelGGL((prefill_bf16_kernel<D>), dim3(npair * B * Hq), dim3(C::THREADS), 0, st,
-                        tl.start, tl.stop, 0, static_cast<const bf16_t*>(q),
-                        static_cast<const bf16_t*>(k_rot), static_cast<const bf16_t*>(v),
+  hipExtLaunchKernelGGL((prefill_bf16_kernel<D, SRC>), dim3(npair * B * Hq), dim3(C::THREADS), 0,
+                        st, tl.start, tl.stop, 0, static_cast<const bf16_t*>(q),
+                        static_cast<const bf16_t*>(ks.k_rot), static_cast<const bf16_t*>(ks.v),
                         static_cast<bf16_t*>(out), positions, Hq, Hkv, S, nqt, fr,
-                        scale * 1.4426950408889634f);
+                        scale * 1.4426950408889634f, ks.c, ks.seq_lens);
   return hipGetLastError();
+}
+
+template <int SRC>
+hipError_t prefill_dispatch(Dtype dt, int D, const void* q, const KeySource& ks, void* out,
+                            int B, int Hq, int Hkv, int S, const int32_t* positions,
+                            const RopeFreq& fr, float scale, hipStream_t s,
+                            const TimedLaunch& tl) {
+  if (dt == F32)
+    return D == 64 ? prefill_f32_t<64, SRC>(q, ks, out, B, Hq, Hkv, S, positions, fr, scale, s, tl)
+                   : prefill_f32_t<128, SRC>(q, ks, out, B, Hq, Hkv, S, positions, fr, scale, s,
+                                             tl);
+  return D == 64 ? prefill_bf16_t<64, SRC>(q, ks, out, B, Hq, Hkv, S, positions, fr, scale, s, tl)
+                 : prefill_bf16_t<128, SRC>(q, ks, out, B, Hq, Hkv, S, positions, fr, scale, s,
+                                            tl);
 }
 
 }  // namespace
@@ -566,13 +644,20 @@ hipError_t launch_prefill_attention(Dtype dt, int D, const void* q, const void* 
                                     const void* v, void* out, int B, int Hq, int Hkv, int S,
                                     const int32_t* positions, const RopeFreq& fr, float scale,
                                     hipStream_t s, const TimedLaunch& tl) {
-  if (dt == F32)
-    return D == 64 ? prefill_f32_t<64>(q, k_rot, v, out, B, Hq, Hkv, S, positions, fr, scale, s, tl)
-                   : prefill_f32_t<128>(q, k_rot, v, out, B, Hq, Hkv, S, positions, fr, scale, s,
-                                        tl);
-  return D == 64 ? prefill_bf16_t<64>(q, k_rot, v, out, B, Hq, Hkv, S, positions, fr, scale, s, tl)
-                 : prefill_bf16_t<128>(q, k_rot, v, out, B, Hq, Hkv, S, positions, fr, scale, s,
+  const KeySource ks{k_rot, v, CacheArgs{}, nullptr};
+  return prefill_dispatch<KEYS_PROMPT>(dt, D, q, ks, out, B, Hq, Hkv, S, positions, fr, scale, s,
                                        tl);
+}
+
+hipError_t launch_prefill_cached(Dtype dt, int D, bool paged, const void* q, void* out, int B,
+                                 int Hq, int Hkv, int S, const CacheArgs& c,
+                                 const int32_t* seq_lens, const RopeFreq& fr, float scale,
+                                 hipStream_t s, const TimedLaunch& tl) {
+  const KeySource ks{nullptr, nullptr, c, seq_lens};
+  return paged ? prefill_dispatch<KEYS_PAGED>(dt, D, q, ks, out, B, Hq, Hkv, S, nullptr, fr,
+                                              scale, s, tl)
+               : prefill_dispatch<KEYS_CONTIG>(dt, D, q, ks, out, B, Hq, Hkv, S, nullptr, fr,
+                                               scale, s, tl);
 }
 
 }  // namespace car

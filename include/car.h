@@ -150,6 +150,35 @@ car_status car_attn_prefill(const void* q, const void* k, const void* v, void* o
                             size_t workspace_bytes, hipStream_t stream);
 
 /*
+ * car_attn_prefill_cached -- a prompt chunk that continues a cached prefix
+ * (chunked or continued prefill).  With P = seq_lens[b] tokens already in
+ * the cache, the chunk's S tokens sit at positions P..P+S-1, which are also
+ * their cache indices ([Scratch] §3.2).  q and k are rotated at those
+ * positions; the rotated keys and raw values are stored at cache indices
+ * P..P+S-1; chunk query i then attends over cache indices 0..P+i, the cached
+ * prefix and the chunk up to itself ([Scratch] §3.3: a position sees itself
+ * and earlier ones, the earlier ones read from the cache):
+ *   out[b, hq, i] = sum_{j <= P+i} softmax_j(scale * q'[b,hq,i] . K[b,hk,j]) V[b,hk,j].
+ * S = 1 is a decode step; P = 0 is a whole-prompt prefill that fills the cache.
+ *   q            [B, Hq, S, D] device;  k, v  [B, Hkv, S, D] device (k not rotated).
+ *   out          [B, Hq, S, D] device, written.
+ *   seq_lens     int32 [B] device: tokens already cached; seq_lens[b] + S must
+ *                not exceed max_seq_len.  (A value that would not fit is
+ *                lowered until the chunk fits the cache.)
+ *   max_seq_len  host bound on seq_lens[b] + S over the batch; at least S and
+ *                at most the cache capacity.
+ *   cache        contiguous or paged; rows 0..P-1 must hold the prefix (as
+ *                written by earlier calls), rows P..P+S-1 are written.
+ * No workspace: the keys are rotated straight into the cache.  S == 0 or an
+ * empty batch is a no-op returning CAR_OK.  Sizes one launch cannot cover
+ * return CAR_ERR_UNSUPPORTED.
+ */
+car_status car_attn_prefill_cached(const void* q, const void* k, const void* v, void* out,
+                                   car_dtype dtype, int B, int Hq, int Hkv, int S, int D,
+                                   const int32_t* seq_lens, int max_seq_len, float theta,
+                                   float scale, const car_kv_cache* cache, hipStream_t stream);
+
+/*
  * Bytes of device workspace car_attn_decode needs: per (sequence, query head)
  * one partial (running max, running sum, D accumulators) in fp32 for every
  * 256-token split of max_seq_len tokens.  Returns 0 for invalid sizes.

@@ -154,6 +154,34 @@ def test_decode_rejects(car, lib):
     assert call(msl=65535 * 256 + 1) == UNSUPPORTED  # more than 65535 splits
 
 
+def test_prefill_cached_rejects(car, lib):
+    f = lib.car_attn_prefill_cached
+    c = _cache(car, max_seq=512)
+    args = dict(q=FAKE, k=FAKE, v=FAKE, out=FAKE, dt=BF16, B=2, Hq=8, Hkv=2, S=100, D=128,
+                lens=FAKE, msl=300, theta=1e4, scale=0.088, cache=ctypes.byref(c))
+
+    def call(**kw):
+        a = dict(args, **kw)
+        return f(a["q"], a["k"], a["v"], a["out"], a["dt"], a["B"], a["Hq"], a["Hkv"], a["S"],
+                 a["D"], a["lens"], a["msl"], a["theta"], a["scale"], a["cache"], None)
+
+    assert call(D=96) == UNSUPPORTED
+    assert call(dt=7) == UNSUPPORTED
+    assert call(Hq=5) == INVALID                     # Hq % Hkv
+    assert call(lens=None) == INVALID
+    assert call(q=None) == INVALID
+    assert call(out=FAKE + 8) == INVALID             # not 16-byte aligned
+    assert call(msl=99) == INVALID                   # below the chunk length
+    assert call(msl=513) == INVALID                  # beyond the cache capacity
+    assert call(cache=None) == INVALID
+    assert call(theta=0.0) == INVALID
+    assert call(B=70000) == UNSUPPORTED              # beyond the launch grid
+    bad = _cache(car, paged=True, block_size=32)
+    assert call(cache=ctypes.byref(bad)) == UNSUPPORTED
+    assert call(B=0, q=None) == OK                   # empty batch: no-op
+    assert call(S=0, q=None) == OK                   # empty chunk: no-op
+
+
 def test_workspace_sizes(lib):
     assert lib.car_attn_decode_workspace_bytes(32, 32, 128, 4096) == 32 * 32 * 16 * 132 * 4
     assert lib.car_attn_decode_workspace_bytes(64, 32, 128, 8193) == 64 * 32 * 33 * 132 * 4

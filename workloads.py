@@ -174,6 +174,90 @@ def decode_case(name, B, Hq, Hkv, D, dtype, lens, seed, device, paged: bool,
                       bt.contiguous(), 0, lens_host=lens)
 
 
+@dataclass
+class ChunkCase:
+    """A prompt chunk of S tokens per sequence continuing a cached prefix of
+    P = lens_host[b] tokens."""
+    name: str
+    B: int
+    Hq: int
+    Hkv: int
+    S: int
+    D: int
+    dtype: torch.dtype
+    q: torch.Tensor                    # [B, Hq, S, D]
+    k: torch.Tensor                    # [B, Hkv, S, D]
+    v: torch.Tensor
+    seq_lens: torch.Tensor             # int32 [B], tokens already cached
+    cache_k: torch.Tensor              # contiguous [B,Hkv,max_seq,D] or pool [nb,Hkv,16,D]
+    cache_v: torch.Tensor
+    block_table: Optional[torch.Tensor] = None
+    max_seq: int = 0
+    theta: float = 10000.0
+    lens_host: List[int] = field(default_factory=list)
+
+    @property
+    def scale(self) -> float:
+        return 1.0 / float(np.sqrt(self.D))
+
+    @property
+    def paged(self) -> bool:
+        return self.block_table is not None
+
+    @property
+    def max_seq_len(self) -> int:
+        """Host-side bound on seq_lens[b] + S."""
+        return max(self.lens_host) + self.S
+
+
+def chunk_case(name, B, Hq, Hkv, S, D, dtype, lens, seed, device, paged: bool,
+               max_seq: Optional[int] = None, extra_blocks: int = 0,
+               poison_unused: bool = False, blocks_per_seq: Optional[int] = None) -> ChunkCase:
+    """A chunk over caches whose first P_b rows hold N(0, 1) values.
+
+    Contiguous caches get ``max_seq`` slots per sequence (default
+    max(P)+S); paged pools get ``blocks_per_seq`` blocks per sequence
+    (default ceil((max(P)+S)/16)) plus ``extra_blocks`` owned by no
+    sequence, through a seeded random permutation.  With ``poison_unused``
+    every slot at or past P_b (the chunk's own slots included, which the call
+    writes before it reads them) and every unowned block holds NaN.
+    """
+    lens = [int(x) for x in lens]
+    rng = host_rng(seed)
+    q = randn((B, Hq, S, D), dtype, device, seed, 0)
+    k = randn((B, Hkv, S, D), dtype, device, seed, 1)
+    v = randn((B, Hkv, S, D), dtype, device, seed, 2)
+    seq_lens = torch.tensor(lens, dtype=torch.int32, device=device)
+    if not paged:
+        cap = max_seq if max_seq is not None else max(lens) + S
+        ck = randn((B, Hkv, cap, D), dtype, device, seed, 6)
+        cv = randn((B, Hkv, cap, D), dtype, device, seed, 7)
+        if poison_unused:
+            t = torch.arange(cap, device=device)[None, None, :, None]
+            far = t >= seq_lens.to(torch.int64)[:, None, None, None]
+            ck.masked_fill_(far, float("nan"))
+            cv.masked_fill_(far, float("nan"))
+        return ChunkCase(name, B, Hq, Hkv, S, D, dtype, q, k, v, seq_lens, ck, cv, None, cap,
+                         lens_host=lens)
+    mbps = blocks_per_seq or (max(lens) + S + BLOCK_SIZE - 1) // BLOCK_SIZE
+    nblocks = B * mbps + extra_blocks
+    perm = rng.permutation(nblocks)
+    table = perm[: B * mbps].reshape(B, mbps).astype(np.int32)
+    ck = randn((nblocks, Hkv, BLOCK_SIZE, D), dtype, device, seed, 6)
+    cv = randn((nblocks, Hkv, BLOCK_SIZE, D), dtype, device, seed, 7)
+    if poison_unused:
+        keep = np.zeros((nblocks, BLOCK_SIZE), dtype=bool)
+        for b, P in enumerate(lens):
+            t = np.arange(P)
+            keep[table[b, t // BLOCK_SIZE], t % BLOCK_SIZE] = True
+        far = torch.from_numpy(~keep).to(device)[:, None, :, None]
+        ck.masked_fill_(far, float("nan"))
+        cv.masked_fill_(far, float("nan"))
+    bt = torch.from_numpy(table).to(device)
+    return ChunkCase(name, B, Hq, Hkv, S, D, dtype, q, k, v, seq_lens, ck, cv, bt.contiguous(), 0,
+                     lens_host=lens)
+
+
 # --------------------------------------------------------------------------
 # The five named workloads
 # --------------------------------------------------------------------------
