@@ -40,6 +40,12 @@ def prefill_flops(B: int, H: int, S: int, D: int) -> int:
     return 2 * B * H * D * S * (S + 1)
 
 
+def chunk_flops(B: int, H: int, P: int, S: int, D: int) -> int:
+    """QK^T and PV of a chunk of S queries over P cached keys plus the chunk
+    (query i sees P + i + 1 keys): 4 * B * H * D * (S * P + S (S + 1) / 2)."""
+    return 4 * B * H * D * (S * P + S * (S + 1) // 2)
+
+
 def decode_kv_bytes(lens, Hkv: int, D: int, elem_bytes: int) -> int:
     """Algorithmic KV bytes one decode step reads: every cached K and V row
     of every KV head once (GQA query heads share their KV head's read)."""
@@ -62,6 +68,8 @@ def parse_args(argv=None):
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-heads", type=int, default=32,
                    help="prefill heads in the oracle's timed sample")
+    p.add_argument("--no-extras", action="store_true",
+                   help="skip the chunked-prefill measurements outside the timed step")
     p.add_argument("--copy-calibration", action="store_true",
                    help="first run one plain 1 GiB device copy (HBM counter calibration)")
     return p.parse_args(argv)
@@ -137,6 +145,50 @@ def cpu_baseline(pf, c4, heads: int):
         "decode_tokens_per_s": len(bsel) / t_dec,
         "host_cores_visible": len(os.sched_getaffinity(0)),
     }
+
+
+def measure_chunked(car, W, dev, stream, new_event, iters: int = 10) -> dict:
+    """A 1024-token chunk continuing a 3072-token cached prefix, 32 query
+    heads, D = 128, bf16: contiguous cache [1, 32, 4096, 128], and a paged
+    cache with 8 KV heads behind a random block table.  Event times of the
+    attention kernel and of the whole call (chunk store + attention)."""
+    import torch
+    out = {}
+    P, S = 3072, 1024
+    for name, paged, hkv in (("contiguous", False, 32), ("paged_gqa", True, 8)):
+        case = W.chunk_case(f"chunk_{name}", 1, 32, hkv, S, 128, torch.bfloat16, [P], 570, dev,
+                            paged=paged, max_seq=None if paged else P + S)
+        cache = car.KVCache(case.cache_k, case.cache_v, case.block_table)
+        o = torch.empty_like(case.q)
+
+        def call():
+            car.attn_prefill_cached(case.q, case.k, case.v, case.seq_lens, cache, P + S,
+                                    case.theta, case.scale, out=o)
+        for _ in range(2):
+            call()
+        pairs_k = [(new_event(), new_event()) for _ in range(iters)]
+        pairs_c = [(new_event(), new_event()) for _ in range(iters)]
+        for i in range(iters):
+            car.set_timing_events(*pairs_k[i])
+            pairs_c[i][0].record(stream)
+            call()
+            pairs_c[i][1].record(stream)
+            car.set_timing_events(None, None)
+        torch.cuda.synchronize()
+        if not torch.isfinite(o.float()).all():
+            raise RuntimeError(f"non-finite output in chunked prefill ({name})")
+        kms = sum(a.elapsed_time(b) for a, b in pairs_k) / iters
+        cms = sum(a.elapsed_time(b) for a, b in pairs_c) / iters
+        fl = chunk_flops(1, 32, P, S, 128)
+        out[f"chunked_prefill_{name}"] = {
+            "workload": f"B=1,Hq=32,Hkv={hkv},D=128,cached={P},chunk={S},bf16,"
+                        + ("paged 16-token blocks" if paged else "contiguous cache 4096"),
+            "kernel_ms": kms, "call_ms": cms,
+            "TFLOPs_kernel": fl / (kms * 1e-3) / 1e12, "TFLOPs_call": fl / (cms * 1e-3) / 1e12,
+            "mfma_frac_kernel": fl / (kms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
+            "per_launch": f"{fl} flops (4*B*H*D*(S*P + S(S+1)/2))"}
+        del case, cache, o
+    return out
 
 
 def main(argv=None) -> int:
@@ -233,6 +285,11 @@ def main(argv=None) -> int:
             print(f"non-finite output in stage {s}", file=sys.stderr)
             return 1
 
+    # ---------------- chunked prefill (outside the timed step) ----------------
+    extras = {}
+    if args.only is None and not args.no_extras:
+        extras = measure_chunked(car, W, dev, stream, new_event)
+
     # ---------------- figures ----------------
     kernels = {}
     pf_flops = prefill_flops(pf.B, pf.Hq, pf.S, pf.D)
@@ -308,6 +365,8 @@ def main(argv=None) -> int:
                                    if "prefill" in res else None),
     }
     line.update(line_extra)
+    if extras:
+        line["extras"] = extras
     if not args.no_cpu_baseline and args.only is None:
         line["cpu_baseline"] = cpu_baseline(pf, c4, args.cpu_heads)
     else:

@@ -270,7 +270,9 @@ __global__ __launch_bounds__(Tile<D>::THREADS, 2) void prefill_bf16_kernel(
   // finish together.  Workgroups go to the 8 XCDs round-robin by id; when the
   // head count is a multiple of 8, XCD x owns the consecutive heads
   // [x*hpx, (x+1)*hpx), so query heads of one KV group share its L2.
-  const int npair = (nqt + 1) >> 1;
+  // With a cached prefix every query tile costs about the same (the prefix
+  // dominates), so a workgroup then takes a single tile: twice the workgroups.
+  const int npair = SRC == KEYS_PROMPT ? (nqt + 1) >> 1 : nqt;
   const int nbh = gridDim.x / npair;
   const int bid = blockIdx.x;
   int bh, pr;
@@ -383,9 +385,9 @@ __global__ __launch_bounds__(Tile<D>::THREADS, 2) void prefill_bf16_kernel(
   // ---- the pair's two query tiles, longest first ----
 #pragma nounroll
   for (int pass = 0; pass < 2; ++pass) {
-    const int qt = pass == 0 ? nqt - 1 - pr : pr;
+    const int qt = SRC != KEYS_PROMPT ? pr : (pass == 0 ? nqt - 1 - pr : pr);
     if (pass == 1) {
-      if (qt == nqt - 1 - pr) break;  // middle tile of an odd nqt: no partner
+      if (SRC != KEYS_PROMPT || qt == nqt - 1 - pr) break;  // one tile, or no partner
       __syncthreads();                // every wave is done with the LDS tiles
     }
     const int q0 = qt * C::BM;
@@ -615,7 +617,7 @@ hipError_t prefill_bf16_t(const void* q, const KeySource& ks, void* out, int B, 
                           hipStream_t st, const TimedLaunch& tl) {
   using C = Tile<D>;
   const int nqt = (S + C::BM - 1) / C::BM;
-  const int npair = (nqt + 1) / 2;
+  const int npair = SRC == KEYS_PROMPT ? (nqt + 1) / 2 : nqt;  // workgroups per head
   hipExtLaunchKernelGGL((prefill_bf16_kernel<D, SRC>), dim3(npair * B * Hq), dim3(C::THREADS), 0,
                         st, tl.start, tl.stop, 0, static_cast<const bf16_t*>(q),
                         static_cast<const bf16_t*>(ks.k_rot), static_cast<const bf16_t*>(ks.v),
