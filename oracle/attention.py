@@ -31,7 +31,9 @@ Pins (tests under ``tests/test_oracle_*.py``, none reuses this code):
   one-token chunk equals a decode step; an empty prefix and a one-token
   chunk give O = v; outputs of earlier queries do not move when later chunk
   tokens change, and all of them move when the cached prefix changes; GQA
-  equals MHA with each KV head repeated.
+  equals MHA with each KV head repeated.  With ``chunk_lens``: a padded
+  batch equals each sequence run alone at its own length, whatever the
+  padding holds; padding rows are zero and padding tokens are not stored.
 
 Convention choices with no pin on synthetic data ("parity unpinned"):
 adjacent pairs (2i, 2i+1) for RoPE, and contiguous GQA groups.
@@ -246,7 +248,7 @@ def attn_decode(q, k_new, v_new, cache_k, cache_v, seq_lens,
 
 def attn_prefill_cached(q, k, v, cache_k, cache_v, seq_lens,
                         theta: float = 10000.0, scale: float | None = None,
-                        block_table=None, block_size: int = 16):
+                        block_table=None, block_size: int = 16, chunk_lens=None):
     """A prompt chunk that continues a cached prefix.
 
     For sequence b with P = seq_lens[b] tokens already cached, the chunk's S
@@ -257,6 +259,11 @@ def attn_prefill_cached(q, k, v, cache_k, cache_v, seq_lens,
     cached prefix plus the chunk up to itself ([Scratch] §3.3: a position
     sees itself and earlier ones; the earlier ones come from the cache).
 
+    With ``chunk_lens`` (a batch of chunks of different lengths padded to
+    S; [Scratch] §3.3 names the padding mask) sequence b has only its first
+    chunk_lens[b] chunk tokens: the padding tokens are neither stored nor
+    attended to, and their output rows are zero.
+
     The caches are updated in place.  Returns out [B, Hq, S, D].
     """
     q, k, v = _f64(q), _f64(k), _f64(v)
@@ -266,22 +273,25 @@ def attn_prefill_cached(q, k, v, cache_k, cache_v, seq_lens,
     if scale is None:
         scale = 1.0 / np.sqrt(D)
     seq_lens = np.asarray(seq_lens)
-    out = np.empty((B, Hq, S, D))
+    out = np.zeros((B, Hq, S, D))
     for b in range(B):
         P = int(seq_lens[b])
-        pos = P + np.arange(S)
-        q_rot = rope_rotate(q[b], pos, theta)           # [Hq, S, D]
-        k_rot = rope_rotate(k[b], pos, theta)           # [Hkv, S, D]
+        n = S if chunk_lens is None else int(chunk_lens[b])
+        if n == 0:
+            continue
+        pos = P + np.arange(n)
+        q_rot = rope_rotate(q[b, :, :n], pos, theta)    # [Hq, n, D]
+        k_rot = rope_rotate(k[b, :, :n], pos, theta)    # [Hkv, n, D]
+        v_b = v[b:b + 1, :, :n]
         if block_table is None:
-            kv_cache_append(cache_k[b:b + 1], cache_v[b:b + 1], k_rot[None], v[b:b + 1],
-                            pos[None, :])
+            kv_cache_append(cache_k[b:b + 1], cache_v[b:b + 1], k_rot[None], v_b, pos[None, :])
         else:
-            kv_cache_append(cache_k, cache_v, k_rot[None], v[b:b + 1], pos[None, :],
+            kv_cache_append(cache_k, cache_v, k_rot[None], v_b, pos[None, :],
                             block_table=block_table[b:b + 1], block_size=block_size)
-        kpos = np.arange(P + S)
+        kpos = np.arange(P + n)
         for hq in range(Hq):
             hk = hq // group
-            keys = cache_rows(cache_k, b, hk, P + S, block_table, block_size)
-            vals = cache_rows(cache_v, b, hk, P + S, block_table, block_size)
-            out[b, hq] = causal_attention(q_rot[hq], keys, vals, (pos, kpos), scale)
+            keys = cache_rows(cache_k, b, hk, P + n, block_table, block_size)
+            vals = cache_rows(cache_v, b, hk, P + n, block_table, block_size)
+            out[b, hq, :n] = causal_attention(q_rot[hq], keys, vals, (pos, kpos), scale)
     return out

@@ -638,6 +638,49 @@ def test_chunked_gqa_equals_mha_with_repeated_kv_heads():
     assert np.array_equal(gqa, mha)
 
 
+def test_padded_chunk_batch_equals_each_sequence_alone():
+    """A batch of chunks of lengths n_b padded to S equals each sequence run
+    alone with its n_b tokens; the padding (filled with large values here)
+    changes nothing, padding rows are zero and padding slots stay unwritten."""
+    r = rng(37)
+    B, Hq, Hkv, D, S = 4, 4, 2, 8, 9
+    lens = np.array([0, 3, 16, 7])
+    n = np.array([9, 0, 4, 1])
+    q = r.standard_normal((B, Hq, S, D))
+    k, v = r.standard_normal((B, Hkv, S, D)), r.standard_normal((B, Hkv, S, D))
+    for b in range(B):
+        q[b, :, n[b]:] = 1e6
+        k[b, :, n[b]:] = -1e6
+        v[b, :, n[b]:] = 1e6
+    ck, cv = r.standard_normal((B, Hkv, 32, D)), r.standard_normal((B, Hkv, 32, D))
+    ck2, cv2 = ck.copy(), cv.copy()
+    got = A.attn_prefill_cached(q, k, v, ck, cv, lens, chunk_lens=n)
+    for b in range(B):
+        sl = slice(b, b + 1)
+        if n[b]:
+            alone = A.attn_prefill_cached(q[sl, :, :n[b]], k[sl, :, :n[b]], v[sl, :, :n[b]],
+                                          ck2[sl], cv2[sl], lens[sl])
+            assert np.allclose(got[b, :, :n[b]], alone[0], atol=1e-13)
+        assert np.array_equal(got[b, :, n[b]:], np.zeros_like(got[b, :, n[b]:]))
+    assert np.array_equal(ck, ck2) and np.array_equal(cv, cv2)
+
+
+def test_padded_chunk_pin_catches_ignoring_chunk_lens():
+    """Planted mistake: treating the padding as real tokens.  The padding
+    rows then come out nonzero and the padding is stored in the cache, both
+    of which the pin above rules out."""
+    r = rng(38)
+    B, H, D, S = 2, 2, 8, 5
+    n = np.array([5, 2])
+    q, k, v = (r.standard_normal((B, H, S, D)) for _ in range(3))
+    ck_bad, cv_bad = np.zeros((B, H, 8, D)), np.zeros((B, H, 8, D))
+    ck_good, cv_good = np.zeros((B, H, 8, D)), np.zeros((B, H, 8, D))
+    bad = A.attn_prefill_cached(q, k, v, ck_bad, cv_bad, np.zeros(B, int))
+    good = A.attn_prefill_cached(q, k, v, ck_good, cv_good, np.zeros(B, int), chunk_lens=n)
+    assert np.any(bad[1, :, 2:] != 0) and np.array_equal(good[1, :, 2:], np.zeros((H, 3, D)))
+    assert not np.array_equal(ck_bad[1, :, 2:5], ck_good[1, :, 2:5])
+
+
 def _chunk_mask_without_offset(q, k, v, ck, cv, lens, block_table=None):
     """Planted mistake: the mask compares chunk-local indices, so a chunk
     query sees only the first i+1 cache rows."""
