@@ -71,8 +71,8 @@ def _load() -> ctypes.CDLL:
         "car_attn_prefill_workspace_bytes": (sz, [i32, i32, i32, i32, i32, cache_p]),
         "car_attn_prefill": (i32, [vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, vp, f32, f32,
                                    cache_p, vp, sz, vp]),
-        "car_attn_prefill_cached": (i32, [vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, vp, i32,
-                                          f32, f32, cache_p, vp]),
+        "car_attn_prefill_cached": (i32, [vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, vp, vp,
+                                          i32, f32, f32, cache_p, vp]),
         "car_attn_decode_workspace_bytes": (sz, [i32, i32, i32, i32]),
         "car_attn_decode": (i32, [vp, vp, vp, vp, i32, i32, i32, i32, i32, vp, i32, f32, f32,
                                   cache_p, vp, sz, vp]),
@@ -304,13 +304,16 @@ def attn_prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, positions: t
 def attn_prefill_cached(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
                         seq_lens: torch.Tensor, cache: KVCache, max_seq_len: int,
                         theta: float = 10000.0, scale: Optional[float] = None,
-                        out: Optional[torch.Tensor] = None) -> torch.Tensor:
+                        out: Optional[torch.Tensor] = None,
+                        chunk_lens: Optional[torch.Tensor] = None) -> torch.Tensor:
     """A prompt chunk continuing a cached prefix (see car_attn_prefill_cached).
 
     q [B, Hq, S, D]; k, v [B, Hkv, S, D] (k not rotated); seq_lens int32 [B]
     (tokens already cached = position of the chunk's first token);
-    ``max_seq_len`` is a host bound on seq_lens + S.  Writes the chunk's keys
-    and values into the cache and returns out [B, Hq, S, D].
+    ``chunk_lens`` int32 [B] (optional): sequence b's chunk is its first
+    chunk_lens[b] rows, the rest is padding (zero output rows);
+    ``max_seq_len`` is a host bound on seq_lens + chunk length.  Writes the
+    chunk's keys and values into the cache and returns out [B, Hq, S, D].
     """
     _need(q, "q", dim=4)
     _need(k, "k", dtype=q.dtype, dim=4, device=q.device)
@@ -322,6 +325,10 @@ def attn_prefill_cached(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
     _need(seq_lens, "seq_lens", dtype=torch.int32, dim=1, device=q.device)
     if seq_lens.shape[0] != B:
         raise ValueError("seq_lens must be [B]")
+    if chunk_lens is not None:
+        _need(chunk_lens, "chunk_lens", dtype=torch.int32, dim=1, device=q.device)
+        if chunk_lens.shape[0] != B:
+            raise ValueError("chunk_lens must be [B]")
     if cache.k.dtype != q.dtype or cache.k.device != q.device:
         raise ValueError("cache dtype/device must match q")
     if cache.Hkv != Hkv or cache.D != D:
@@ -336,7 +343,8 @@ def attn_prefill_cached(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
         scale = 1.0 / math.sqrt(D)
     c = cache._c()
     _check(_lib.car_attn_prefill_cached(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _dtype_code(q),
-                                        B, Hq, Hkv, S, D, _ptr(seq_lens), int(max_seq_len),
+                                        B, Hq, Hkv, S, D, _ptr(seq_lens), _ptr(chunk_lens),
+                                        int(max_seq_len),
                                         float(theta), float(scale), ctypes.byref(c), _stream(q)),
            "attn_prefill_cached")
     return out

@@ -169,8 +169,9 @@ car_status car_attn_prefill(const void* q, const void* k, const void* v, void* o
 
 car_status car_attn_prefill_cached(const void* q, const void* k, const void* v, void* out,
                                    car_dtype dtype, int B, int Hq, int Hkv, int S, int D,
-                                   const int32_t* seq_lens, int max_seq_len, float theta,
-                                   float scale, const car_kv_cache* cache, hipStream_t stream) {
+                                   const int32_t* seq_lens, const int32_t* chunk_lens,
+                                   int max_seq_len, float theta, float scale,
+                                   const car_kv_cache* cache, hipStream_t stream) {
   if (!dtype_ok(dtype) || !head_dim_ok(D)) return CAR_ERR_UNSUPPORTED;
   if (cache != nullptr && cache->block_table != nullptr && cache->block_size != 16)
     return CAR_ERR_UNSUPPORTED;
@@ -186,7 +187,9 @@ car_status car_attn_prefill_cached(const void* q, const void* k, const void* v, 
   int64_t cap = 0;
   const car_status cs = check_cache(cache, &c, &cap);
   if (cs != CAR_OK) return cs;
-  if (max_seq_len < S || max_seq_len > cap) return CAR_ERR_INVALID_ARGUMENT;
+  // every sequence's chunk fits: S tokens, or up to S with chunk_lens
+  if (max_seq_len < (chunk_lens == nullptr ? S : 1) || max_seq_len > cap)
+    return CAR_ERR_INVALID_ARGUMENT;
   // launch grids (fp32: B and Hq in grid y, z; bf16: query-tile pairs x B x Hq
   // in x) and 32-bit byte offsets within one head of a contiguous cache
   if (B > 65535 || Hq > 65535 || (int64_t)B * Hq * ((S + 511) / 512) > INT32_MAX ||
@@ -196,10 +199,11 @@ car_status car_attn_prefill_cached(const void* q, const void* k, const void* v, 
   const Dtype dt = dtype == CAR_DTYPE_F32 ? F32 : BF16;
   const RopeFreq fr = make_freq(D, theta);
   const bool paged = cache->block_table != nullptr;
-  hipError_t e = launch_chunk_prep(dt, D, paged, c, k, v, B, Hkv, S, seq_lens, fr, stream);
+  hipError_t e =
+      launch_chunk_prep(dt, D, paged, c, k, v, B, Hkv, S, seq_lens, chunk_lens, fr, stream);
   if (e != hipSuccess) return CAR_ERR_HIP;
-  return from_hip(launch_prefill_cached(dt, D, paged, q, out, B, Hq, Hkv, S, c, seq_lens, fr,
-                                        scale, stream, timing()));
+  return from_hip(launch_prefill_cached(dt, D, paged, q, out, B, Hq, Hkv, S, c, seq_lens,
+                                        chunk_lens, fr, scale, stream, timing()));
 }
 
 size_t car_attn_decode_workspace_bytes(int B, int Hq, int D, int max_seq_len) {

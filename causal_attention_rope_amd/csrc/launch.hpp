@@ -58,7 +58,7 @@ hipError_t launch_prefill_prep(Dtype dt, int D, bool paged, const CacheArgs* cac
 // positions P..P+S-1 and stores the rotated keys and raw values there.
 hipError_t launch_chunk_prep(Dtype dt, int D, bool paged, const CacheArgs& c, const void* k,
                              const void* v, int B, int Hkv, int S, const int32_t* seq_lens,
-                             const RopeFreq& fr, hipStream_t s);
+                             const int32_t* chunk_lens, const RopeFreq& fr, hipStream_t s);
 
 // ---- prefill.hip -----------------------------------------------------------
 hipError_t launch_prefill_attention(Dtype dt, int D, const void* q, const void* k_rot,
@@ -67,10 +67,12 @@ hipError_t launch_prefill_attention(Dtype dt, int D, const void* q, const void* 
                                     hipStream_t s, const TimedLaunch& tl);
 
 // Attention of a chunk over cache rows 0..P+S-1 (after launch_chunk_prep).
+// chunk_lens (nullable): tokens of each sequence's chunk; the rest is padding.
 hipError_t launch_prefill_cached(Dtype dt, int D, bool paged, const void* q, void* out, int B,
                                  int Hq, int Hkv, int S, const CacheArgs& c,
-                                 const int32_t* seq_lens, const RopeFreq& fr, float scale,
-                                 hipStream_t s, const TimedLaunch& tl);
+                                 const int32_t* seq_lens, const int32_t* chunk_lens,
+                                 const RopeFreq& fr, float scale, hipStream_t s,
+                                 const TimedLaunch& tl);
 
 // ---- decode.hip ------------------------------------------------------------
 // Partials: [B, Hq, nsplit, decode_partial_words(D)] fp32 with nsplit =

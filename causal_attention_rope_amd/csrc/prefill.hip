@@ -40,6 +40,14 @@ constexpr int KEYS_PROMPT = 0;  // the prompt's own K' and V, [B, Hkv, S, D]
 constexpr int KEYS_CONTIG = 1;  // a contiguous cache holding the prefix and the chunk
 constexpr int KEYS_PAGED = 2;   // a paged cache holding the prefix and the chunk
 
+// Tokens of sequence b's chunk: S for a prompt or a full chunk, else
+// chunk_lens[b] (a padded batch of chunks of different lengths).
+template <int SRC>
+__device__ __forceinline__ int chunk_len(const int32_t* chunk_lens, int b, int S) {
+  if constexpr (SRC == KEYS_PROMPT) return S;
+  else return chunk_lens == nullptr ? S : min(max(chunk_lens[b], 0), S);
+}
+
 // Tokens cached before the chunk (0 for a prompt): seq_lens[b], kept small
 // enough that the chunk's last key stays inside the cache.
 template <int SRC>
@@ -61,16 +69,18 @@ template <int D, int SRC>
 __global__ __launch_bounds__(F32_ROWS) void prefill_f32_kernel(
     const float* __restrict__ q, const float* __restrict__ kr, const float* __restrict__ v,
     float* __restrict__ out, const int32_t* __restrict__ positions, int Hq, int Hkv, int S,
-    RopeFreq fr, float qk_scale, CacheArgs c, const int32_t* __restrict__ seq_lens) {
+    RopeFreq fr, float qk_scale, CacheArgs c, const int32_t* __restrict__ seq_lens,
+    const int32_t* __restrict__ chunk_lens) {
   __shared__ float4 sk[F32_KT][D / 4];
   __shared__ float4 sv[F32_KT][D / 4];
   const int b = blockIdx.z, hq = blockIdx.y;
   const int hk = hq / (Hq / Hkv);
   const int i0 = blockIdx.x * F32_ROWS;
   const int i = i0 + threadIdx.x;
-  const int ic = min(i, S - 1);
-  const int P = chunk_start<SRC>(c, seq_lens, b, S);  // keys before the chunk
-  const int nkeys = P + S;
+  const int Sb = chunk_len<SRC>(chunk_lens, b, S);   // rows i >= Sb are padding
+  const int ic = min(i, max(Sb - 1, 0));
+  const int P = chunk_start<SRC>(c, seq_lens, b, Sb);  // keys before the chunk
+  const int nkeys = P + Sb;
 
   float qv[D];
   const float* qrow = q + (((int64_t)b * Hq + hq) * S + ic) * D;
@@ -143,11 +153,14 @@ __global__ __launch_bounds__(F32_ROWS) void prefill_f32_kernel(
     m = m_new;
   }
   if (i < S) {
+    const bool pad = i >= Sb;  // padding rows are written as zeros
     const float inv = 1.f / l;
     float* orow = out + (((int64_t)b * Hq + hq) * S + i) * D;
 #pragma unroll
     for (int d = 0; d < D; d += 4) {
-      float f[4] = {acc[d] * inv, acc[d + 1] * inv, acc[d + 2] * inv, acc[d + 3] * inv};
+      float f[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) f[e] = pad ? 0.f : acc[d + e] * inv;
       store16<float>(orow + d, f);
     }
   }
@@ -259,7 +272,8 @@ template <int D, int SRC>
 __global__ __launch_bounds__(Tile<D>::THREADS, 2) void prefill_bf16_kernel(
     const bf16_t* __restrict__ q, const bf16_t* __restrict__ kr, const bf16_t* __restrict__ v,
     bf16_t* __restrict__ out, const int32_t* __restrict__ positions, int Hq, int Hkv, int S,
-    int nqt, RopeFreq fr, float sm_scale_log2, CacheArgs c, const int32_t* __restrict__ seq_lens) {
+    int nqt, RopeFreq fr, float sm_scale_log2, CacheArgs c, const int32_t* __restrict__ seq_lens,
+    const int32_t* __restrict__ chunk_lens) {
   using C = Tile<D>;
   __shared__ __attribute__((aligned(1024))) char smem[2 * C::STAGEB];
 
@@ -294,8 +308,9 @@ __global__ __launch_bounds__(Tile<D>::THREADS, 2) void prefill_bf16_kernel(
   const int l32 = lane & 31, g = lane >> 5;
   // Keys: the prompt itself, or rows 0..P+S-1 of a cache that held P tokens
   // before this chunk; chunk query i sits at key index P+i.
-  const int P = chunk_start<SRC>(c, seq_lens, b, S);
-  const int nkeys = P + S;
+  const int Sb = chunk_len<SRC>(chunk_lens, b, S);  // query rows >= Sb are padding
+  const int P = chunk_start<SRC>(c, seq_lens, b, Sb);
+  const int nkeys = P + Sb;
   const bf16_t* kbase = nullptr;  // the head's key rows (paged: per block, below)
   const bf16_t* vbase = nullptr;
   if constexpr (SRC == KEYS_CONTIG) {
@@ -393,7 +408,18 @@ __global__ __launch_bounds__(Tile<D>::THREADS, 2) void prefill_bf16_kernel(
     const int q0 = qt * C::BM;
     const int qw = q0 + wave * 32;             // first query row of this wave
     const int qrow = qw + l32;                 // this lane's query row
-    const int qrc = min(qrow, S - 1);
+    if (q0 >= Sb) {  // padding rows only (uniform over the workgroup): zeros
+      if (qrow < S) {
+        bf16_t* op = out + ((int64_t)bh * S + qrow) * D;
+  #pragma unroll
+        for (int db = 0; db < C::NDB; ++db)
+  #pragma unroll
+          for (int r4 = 0; r4 < 4; ++r4)
+            *reinterpret_cast<u32x2_t*>(op + db * 32 + 8 * r4 + 4 * g) = u32x2_t{0u, 0u};
+      }
+      continue;
+    }
+    const int qrc = min(qrow, Sb - 1);
 
     // ---- Q fragments (B operand of S^T = K Q^T), rotated, bf16 ----
     bf16x8_t qf[C::QKS];
@@ -420,7 +446,7 @@ __global__ __launch_bounds__(Tile<D>::THREADS, 2) void prefill_bf16_kernel(
     float m_run = -INFINITY, l_run = 0.f;
     f32x16_t sacc[2][C::NKB];  // S^T of the tile being consumed and of the next one
 
-    const int q_end = min(q0 + C::BM, S);  // exclusive
+    const int q_end = min(q0 + C::BM, Sb);  // exclusive
     const int ntiles = (P + q_end + C::BN - 1) / C::BN;
     // tiles 0..wlast hold keys visible to this wave (uniform per wave)
     const int wlast = min(ntiles - 1, (P + qw + 31) / C::BN);
@@ -575,6 +601,7 @@ __global__ __launch_bounds__(Tile<D>::THREADS, 2) void prefill_bf16_kernel(
     // ---- normalise and store: lane holds query qrow, dims db*32+8*(r/4)+4g+r%4 ----
     const float l_tot = l_run + swap_halves(l_run);
     if (qrow < S) {
+      const bool pad = qrow >= Sb;  // padding rows are written as zeros
       const float inv = 1.f / l_tot;
       bf16_t* op = out + ((int64_t)bh * S + qrow) * D;
   #pragma unroll
@@ -584,6 +611,7 @@ __global__ __launch_bounds__(Tile<D>::THREADS, 2) void prefill_bf16_kernel(
           u32x2_t u;
           u[0] = cvt_pk_bf16(oacc[db][4 * r4] * inv, oacc[db][4 * r4 + 1] * inv);
           u[1] = cvt_pk_bf16(oacc[db][4 * r4 + 2] * inv, oacc[db][4 * r4 + 3] * inv);
+          if (pad) u = u32x2_t{0u, 0u};
           *reinterpret_cast<u32x2_t*>(op + db * 32 + 8 * r4 + 4 * g) = u;
         }
     }
@@ -596,6 +624,7 @@ struct KeySource {
   const void* v;
   CacheArgs c;
   const int32_t* seq_lens;
+  const int32_t* chunk_lens;
 };
 
 template <int D, int SRC>
@@ -607,7 +636,7 @@ hipError_t prefill_f32_t(const void* q, const KeySource& ks, void* out, int B, i
                         tl.stop, 0, static_cast<const float*>(q),
                         static_cast<const float*>(ks.k_rot), static_cast<const float*>(ks.v),
                         static_cast<float*>(out), positions, Hq, Hkv, S, fr,
-                        scale * 1.4426950408889634f, ks.c, ks.seq_lens);
+                        scale * 1.4426950408889634f, ks.c, ks.seq_lens, ks.chunk_lens);
   return hipGetLastError();
 }
 
@@ -622,7 +651,7 @@ hipError_t prefill_bf16_t(const void* q, const KeySource& ks, void* out, int B, 
                         st, tl.start, tl.stop, 0, static_cast<const bf16_t*>(q),
                         static_cast<const bf16_t*>(ks.k_rot), static_cast<const bf16_t*>(ks.v),
                         static_cast<bf16_t*>(out), positions, Hq, Hkv, S, nqt, fr,
-                        scale * 1.4426950408889634f, ks.c, ks.seq_lens);
+                        scale * 1.4426950408889634f, ks.c, ks.seq_lens, ks.chunk_lens);
   return hipGetLastError();
 }
 
@@ -646,16 +675,17 @@ hipError_t launch_prefill_attention(Dtype dt, int D, const void* q, const void* 
                                     const void* v, void* out, int B, int Hq, int Hkv, int S,
                                     const int32_t* positions, const RopeFreq& fr, float scale,
                                     hipStream_t s, const TimedLaunch& tl) {
-  const KeySource ks{k_rot, v, CacheArgs{}, nullptr};
+  const KeySource ks{k_rot, v, CacheArgs{}, nullptr, nullptr};
   return prefill_dispatch<KEYS_PROMPT>(dt, D, q, ks, out, B, Hq, Hkv, S, positions, fr, scale, s,
                                        tl);
 }
 
 hipError_t launch_prefill_cached(Dtype dt, int D, bool paged, const void* q, void* out, int B,
                                  int Hq, int Hkv, int S, const CacheArgs& c,
-                                 const int32_t* seq_lens, const RopeFreq& fr, float scale,
-                                 hipStream_t s, const TimedLaunch& tl) {
-  const KeySource ks{nullptr, nullptr, c, seq_lens};
+                                 const int32_t* seq_lens, const int32_t* chunk_lens,
+                                 const RopeFreq& fr, float scale, hipStream_t s,
+                                 const TimedLaunch& tl) {
+  const KeySource ks{nullptr, nullptr, c, seq_lens, chunk_lens};
   return paged ? prefill_dispatch<KEYS_PAGED>(dt, D, q, ks, out, B, Hq, Hkv, S, nullptr, fr,
                                               scale, s, tl)
                : prefill_dispatch<KEYS_CONTIG>(dt, D, q, ks, out, B, Hq, Hkv, S, nullptr, fr,

@@ -106,10 +106,12 @@ __global__ __launch_bounds__(kThreads) void prefill_prep_kernel(
 // A chunk continuing a cached prefix: token s of sequence b sits at position
 // P + s, P = seq_lens[b] (kept so that the chunk fits the cache, as the
 // attention kernel does); its rotated key and raw value go to that index.
+// With chunk_lens, tokens s >= chunk_lens[b] are padding and are not stored.
 template <typename T, int D, bool PAGED>
 __global__ __launch_bounds__(kThreads) void chunk_prep_kernel(
     CacheArgs c, const T* __restrict__ k, const T* __restrict__ v, int Hkv, int S,
-    const int32_t* __restrict__ seq_lens, int64_t nvec, RopeFreq fr) {
+    const int32_t* __restrict__ seq_lens, const int32_t* __restrict__ chunk_lens, int64_t nvec,
+    RopeFreq fr) {
   constexpr int N = Vec16<T>::N;
   constexpr int VPR = D / N;
   const int last = cache_last_slot<PAGED>(c);
@@ -121,7 +123,9 @@ __global__ __launch_bounds__(kThreads) void chunk_prep_kernel(
     const int64_t bh = row / S;
     const int hk = (int)(bh % Hkv);
     const int b = (int)(bh / Hkv);
-    const int P = max(min(max(seq_lens[b], 0), last + 1 - S), 0);
+    const int Sb = chunk_lens == nullptr ? S : min(max(chunk_lens[b], 0), S);
+    if (s >= Sb) continue;  // padding
+    const int P = max(min(max(seq_lens[b], 0), last + 1 - Sb), 0);
     const int pos = min(P + s, last);
     float f[N];
     load16<T>(k + row * D + col, f);
@@ -182,17 +186,17 @@ hipError_t prefill_prep_t(bool paged, const CacheArgs* cache, const void* k, con
 
 template <typename T, int D>
 hipError_t chunk_prep_t(bool paged, const CacheArgs& c, const void* k, const void* v, int B,
-                        int Hkv, int S, const int32_t* seq_lens, const RopeFreq& fr,
-                        hipStream_t st) {
+                        int Hkv, int S, const int32_t* seq_lens, const int32_t* chunk_lens,
+                        const RopeFreq& fr, hipStream_t st) {
   const int64_t nvec = (int64_t)B * Hkv * S * (D / Vec16<T>::N);
   const T* kk = static_cast<const T*>(k);
   const T* vv = static_cast<const T*>(v);
   if (paged)
     hipLaunchKernelGGL((chunk_prep_kernel<T, D, true>), dim3(grid_for(nvec)), dim3(kThreads), 0,
-                       st, c, kk, vv, Hkv, S, seq_lens, nvec, fr);
+                       st, c, kk, vv, Hkv, S, seq_lens, chunk_lens, nvec, fr);
   else
     hipLaunchKernelGGL((chunk_prep_kernel<T, D, false>), dim3(grid_for(nvec)), dim3(kThreads), 0,
-                       st, c, kk, vv, Hkv, S, seq_lens, nvec, fr);
+                       st, c, kk, vv, Hkv, S, seq_lens, chunk_lens, nvec, fr);
   return hipGetLastError();
 }
 
@@ -200,12 +204,14 @@ hipError_t chunk_prep_t(bool paged, const CacheArgs& c, const void* k, const voi
 
 hipError_t launch_chunk_prep(Dtype dt, int D, bool paged, const CacheArgs& c, const void* k,
                              const void* v, int B, int Hkv, int S, const int32_t* seq_lens,
-                             const RopeFreq& fr, hipStream_t s) {
+                             const int32_t* chunk_lens, const RopeFreq& fr, hipStream_t s) {
   if (dt == F32)
-    return D == 64 ? chunk_prep_t<float, 64>(paged, c, k, v, B, Hkv, S, seq_lens, fr, s)
-                   : chunk_prep_t<float, 128>(paged, c, k, v, B, Hkv, S, seq_lens, fr, s);
-  return D == 64 ? chunk_prep_t<bf16_t, 64>(paged, c, k, v, B, Hkv, S, seq_lens, fr, s)
-                 : chunk_prep_t<bf16_t, 128>(paged, c, k, v, B, Hkv, S, seq_lens, fr, s);
+    return D == 64 ? chunk_prep_t<float, 64>(paged, c, k, v, B, Hkv, S, seq_lens, chunk_lens, fr, s)
+                   : chunk_prep_t<float, 128>(paged, c, k, v, B, Hkv, S, seq_lens, chunk_lens, fr,
+                                              s);
+  return D == 64 ? chunk_prep_t<bf16_t, 64>(paged, c, k, v, B, Hkv, S, seq_lens, chunk_lens, fr, s)
+                 : chunk_prep_t<bf16_t, 128>(paged, c, k, v, B, Hkv, S, seq_lens, chunk_lens, fr,
+                                             s);
 }
 
 hipError_t launch_rope_apply(Dtype dt, int D, void* x, int B, int H, int S,

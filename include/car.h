@@ -162,11 +162,16 @@ car_status car_attn_prefill(const void* q, const void* k, const void* v, void* o
  * S = 1 is a decode step; P = 0 is a whole-prompt prefill that fills the cache.
  *   q            [B, Hq, S, D] device;  k, v  [B, Hkv, S, D] device (k not rotated).
  *   out          [B, Hq, S, D] device, written.
- *   seq_lens     int32 [B] device: tokens already cached; seq_lens[b] + S must
- *                not exceed max_seq_len.  (A value that would not fit is
- *                lowered until the chunk fits the cache.)
- *   max_seq_len  host bound on seq_lens[b] + S over the batch; at least S and
- *                at most the cache capacity.
+ *   seq_lens     int32 [B] device: tokens already cached; seq_lens[b] plus the
+ *                chunk's length must not exceed max_seq_len.  (A value that
+ *                would not fit is lowered until the chunk fits the cache.)
+ *   chunk_lens   NULL: every chunk has S tokens.  Otherwise int32 [B] device:
+ *                sequence b's chunk is its first chunk_lens[b] tokens (0..S),
+ *                the rest of its S rows are padding ([Scratch] §3.3 names the
+ *                padding mask): padding tokens are neither stored nor attended
+ *                to, and their output rows are written as zeros.
+ *   max_seq_len  host bound on seq_lens[b] + (chunk length) over the batch; at
+ *                most the cache capacity, and at least S when chunk_lens is NULL.
  *   cache        contiguous or paged; rows 0..P-1 must hold the prefix (as
  *                written by earlier calls), rows P..P+S-1 are written.
  * No workspace: the keys are rotated straight into the cache.  S == 0 or an
@@ -175,8 +180,9 @@ car_status car_attn_prefill(const void* q, const void* k, const void* v, void* o
  */
 car_status car_attn_prefill_cached(const void* q, const void* k, const void* v, void* out,
                                    car_dtype dtype, int B, int Hq, int Hkv, int S, int D,
-                                   const int32_t* seq_lens, int max_seq_len, float theta,
-                                   float scale, const car_kv_cache* cache, hipStream_t stream);
+                                   const int32_t* seq_lens, const int32_t* chunk_lens,
+                                   int max_seq_len, float theta, float scale,
+                                   const car_kv_cache* cache, hipStream_t stream);
 
 /*
  * Bytes of device workspace car_attn_decode needs: per (sequence, query head)

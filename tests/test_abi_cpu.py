@@ -158,12 +158,13 @@ def test_prefill_cached_rejects(car, lib):
     f = lib.car_attn_prefill_cached
     c = _cache(car, max_seq=512)
     args = dict(q=FAKE, k=FAKE, v=FAKE, out=FAKE, dt=BF16, B=2, Hq=8, Hkv=2, S=100, D=128,
-                lens=FAKE, msl=300, theta=1e4, scale=0.088, cache=ctypes.byref(c))
+                lens=FAKE, clens=None, msl=300, theta=1e4, scale=0.088, cache=ctypes.byref(c))
 
     def call(**kw):
         a = dict(args, **kw)
         return f(a["q"], a["k"], a["v"], a["out"], a["dt"], a["B"], a["Hq"], a["Hkv"], a["S"],
-                 a["D"], a["lens"], a["msl"], a["theta"], a["scale"], a["cache"], None)
+                 a["D"], a["lens"], a["clens"], a["msl"], a["theta"], a["scale"], a["cache"],
+                 None)
 
     assert call(D=96) == UNSUPPORTED
     assert call(dt=7) == UNSUPPORTED
@@ -172,6 +173,8 @@ def test_prefill_cached_rejects(car, lib):
     assert call(q=None) == INVALID
     assert call(out=FAKE + 8) == INVALID             # not 16-byte aligned
     assert call(msl=99) == INVALID                   # below the chunk length
+    assert call(msl=0, clens=FAKE) == INVALID        # padded chunks: still at least 1
+    assert call(msl=513, clens=FAKE) == INVALID      # padded chunks: beyond the capacity
     assert call(msl=513) == INVALID                  # beyond the cache capacity
     assert call(cache=None) == INVALID
     assert call(theta=0.0) == INVALID

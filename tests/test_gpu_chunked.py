@@ -153,3 +153,47 @@ def test_paged_gqa_chunk_batch(car):
     case = W.chunk_case("pgqa", 2, 32, 8, 512, 128, torch.bfloat16, [1000, 2500], 560, DEV,
                         paged=True, poison_unused=True, extra_blocks=7)
     run_and_check(car, case, heads=(0, 4))
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16], ids=["f32", "bf16"])
+@pytest.mark.parametrize("paged", [False, True], ids=["contiguous", "paged"])
+def test_padded_chunk_batch(car, dtype, paged):
+    """Chunks of 70, 0, 33, 1 and 64 tokens padded to S = 70, over prefixes
+    of 0, 40, 300, 5 and 129 tokens.  The padding holds 7.0 (never read):
+    outputs against the oracle, padding rows exactly zero, and no cache slot
+    outside [P, P + n) of each sequence changes."""
+    log_case(f"padded chunk batch {dtype} paged={paged}")
+    lens, n, S = [0, 40, 300, 5, 129], [70, 0, 33, 1, 64], 70
+    case = W.chunk_case("pad", 5, 8, 2, S, 128, dtype, lens, 580, DEV, paged=paged,
+                        poison_unused=True, extra_blocks=3)
+    for b, nb in enumerate(n):
+        for t in (case.q, case.k, case.v):
+            t[b, :, nb:] = 7.0
+    cl = torch.tensor(n, dtype=torch.int32, device=DEV)
+    before_k, before_v = case.cache_k.clone(), case.cache_v.clone()
+    q, k, v, ck, cv, table, _, _ = _oracle_inputs(case)
+    cache = car.KVCache(case.cache_k, case.cache_v, case.block_table)
+    out = car.attn_prefill_cached(case.q, case.k, case.v, case.seq_lens, cache,
+                                  max(P + m for P, m in zip(lens, n)), chunk_lens=cl)
+    torch.cuda.synchronize()
+    want = oracle.attn_prefill_cached(q, k, v, ck, cv, np.array(lens), block_table=table,
+                                      chunk_lens=np.array(n))
+    err = max_abs(f64(out), want)
+    for b, nb in enumerate(n):
+        assert torch.equal(bits(out[b, :, nb:].cpu()), torch.zeros_like(bits(out[b, :, nb:].cpu())))
+    # written slots: the chunk tokens only
+    written = torch.zeros(case.cache_k.shape[0], case.cache_k.shape[2], dtype=torch.bool)
+    for b, (P, nb) in enumerate(zip(lens, n)):
+        t = np.arange(P, P + nb)
+        if paged:
+            written[torch.as_tensor(table[b, t // 16]), torch.as_tensor(t % 16)] = True
+        else:
+            written[b, P:P + nb] = True
+    keep = ~written.to(DEV)[:, None, :, None].expand_as(case.cache_k)
+    assert torch.equal(bits(case.cache_k[keep]), bits(before_k[keep])), "K outside the chunks"
+    assert torch.equal(bits(case.cache_v[keep]), bits(before_v[keep])), "V outside the chunks"
+    w = written[:, None, :, None].expand(ck.shape).numpy()
+    err = max(err, max_abs(f64(case.cache_k)[w], ck[w]))
+    assert np.array_equal(f64(case.cache_v)[w], cv[w]), "V of the chunks"
+    log_case(f"padded chunk batch: max-abs error {err:.3e}")
+    assert err <= TOL[dtype]
