@@ -153,7 +153,7 @@ __global__ __launch_bounds__(F32_ROWS) void prefill_f32_kernel(
     m = m_new;
   }
   if (i < S) {
-    const bool pad = i >= Sb;  // padding rows are written as zeros
+    const bool pad = SRC != KEYS_PROMPT && i >= Sb;  // padding rows: zeros
     const float inv = 1.f / l;
     float* orow = out + (((int64_t)b * Hq + hq) * S + i) * D;
 #pragma unroll
@@ -408,7 +408,7 @@ __global__ __launch_bounds__(Tile<D>::THREADS, 2) void prefill_bf16_kernel(
     const int q0 = qt * C::BM;
     const int qw = q0 + wave * 32;             // first query row of this wave
     const int qrow = qw + l32;                 // this lane's query row
-    if (q0 >= Sb) {  // padding rows only (uniform over the workgroup): zeros
+    if (SRC != KEYS_PROMPT && q0 >= Sb) {  // padding rows only (uniform): zeros
       if (qrow < S) {
         bf16_t* op = out + ((int64_t)bh * S + qrow) * D;
   #pragma unroll
@@ -601,7 +601,7 @@ __global__ __launch_bounds__(Tile<D>::THREADS, 2) void prefill_bf16_kernel(
     // ---- normalise and store: lane holds query qrow, dims db*32+8*(r/4)+4g+r%4 ----
     const float l_tot = l_run + swap_halves(l_run);
     if (qrow < S) {
-      const bool pad = qrow >= Sb;  // padding rows are written as zeros
+      const bool pad = SRC != KEYS_PROMPT && qrow >= Sb;  // padding rows: zeros
       const float inv = 1.f / l_tot;
       bf16_t* op = out + ((int64_t)bh * S + qrow) * D;
   #pragma unroll
