@@ -31,6 +31,7 @@ on synthetic data and is fixed only by the text: the RoPE pair layout
 
 from .attention import (  # noqa: F401
     rope_inv_freq,
+    rope_pair_index,
     rope_rotate,
     causal_attention,
     attn_prefill,

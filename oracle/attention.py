@@ -35,8 +35,15 @@ Pins (tests under ``tests/test_oracle_*.py``, none reuses this code):
   batch equals each sequence run alone at its own length, whatever the
   padding holds; padding rows are zero and padding tokens are not stored.
 
+* ``rope_rotate(pairing="half")``: identity at 0, norm preservation and
+  relative position as above; a hand value for D = 4 (pair (x1, x3) at
+  frequency 0.01); and the exact relation half(x) = P^-1 adjacent(P x) for
+  the permutation P that interleaves the two halves, which ties it to the
+  independently pinned adjacent layout.
+
 Convention choices with no pin on synthetic data ("parity unpinned"):
-adjacent pairs (2i, 2i+1) for RoPE, and contiguous GQA groups.
+adjacent pairs (2i, 2i+1) as the default RoPE layout, and contiguous GQA
+groups.
 """
 
 from __future__ import annotations
@@ -45,6 +52,7 @@ import numpy as np
 
 __all__ = [
     "rope_inv_freq",
+    "rope_pair_index",
     "rope_rotate",
     "causal_attention",
     "attn_prefill",
@@ -76,13 +84,31 @@ def rope_inv_freq(D: int, theta: float = 10000.0) -> np.ndarray:
     return np.power(np.float64(theta), -2.0 * i / D)
 
 
-def rope_rotate(x, positions, theta: float = 10000.0) -> np.ndarray:
-    """Rotate each pair (x[2i], x[2i+1]) by the angle m * theta_i.
+def rope_pair_index(D: int, pairing: str = "adjacent"):
+    """Element indices (a_i, b_i) of pair i, i in [0, D/2).
+
+    "adjacent": (2i, 2i+1), the pairs (q0,q1), (q2,q3), ... that [Intuition]
+    §4 writes out.  "half": (i, i + D/2), the split-in-halves layout that
+    checkpoints of the Llama/Qwen families use (the pages name those models,
+    [Guide] §6.1); the same rotations, applied to a permutation of the
+    elements.
+    """
+    i = np.arange(D // 2)
+    if pairing == "adjacent":
+        return 2 * i, 2 * i + 1
+    if pairing == "half":
+        return i, i + D // 2
+    raise ValueError(f"unknown RoPE pairing {pairing!r}")
+
+
+def rope_rotate(x, positions, theta: float = 10000.0, pairing: str = "adjacent") -> np.ndarray:
+    """Rotate each pair (x[a_i], x[b_i]) by the angle m * theta_i.
 
     ``x`` is [..., S, D]; ``positions`` (m) broadcasts against [..., S].  Each
     pair is multiplied by the 2x2 matrix [[cos, -sin], [sin, cos]] of its
     angle, the rotation [Intuition] §4 writes out for the pairs (q0,q1),
-    (q2,q3), ..., with m the token's position index.
+    (q2,q3), ..., with m the token's position index; ``pairing`` chooses
+    which elements form pair i (``rope_pair_index``).
     """
     x = _f64(x)
     D = x.shape[-1]
@@ -91,9 +117,13 @@ def rope_rotate(x, positions, theta: float = 10000.0) -> np.ndarray:
     c, s = np.cos(ang), np.sin(ang)
     R = np.stack([np.stack([c, -s], axis=-1),
                   np.stack([s, c], axis=-1)], axis=-2)  # [..., S, D/2, 2, 2]
-    pairs = x.reshape(x.shape[:-1] + (D // 2, 2))       # [..., S, D/2, 2]
-    out = np.einsum("...ij,...j->...i", R, pairs)
-    return out.reshape(x.shape)
+    ia, ib = rope_pair_index(D, pairing)
+    pairs = np.stack([x[..., ia], x[..., ib]], axis=-1)  # [..., S, D/2, 2]
+    rot = np.einsum("...ij,...j->...i", R, pairs)
+    out = np.empty_like(x)
+    out[..., ia] = rot[..., 0]
+    out[..., ib] = rot[..., 1]
+    return out
 
 
 # --------------------------------------------------------------------------
@@ -122,7 +152,7 @@ def causal_attention(q, k, v, positions, scale: float) -> np.ndarray:
 
 
 def attn_prefill(q, k, v, positions, theta: float = 10000.0,
-                 scale: float | None = None):
+                 scale: float | None = None, pairing: str = "adjacent"):
     """Prefill over a whole prompt: RoPE on Q and K, then causal attention.
 
     q [B, Hq, S, D], k/v [B, Hkv, S, D], positions [B, S].  Query head hq
@@ -143,8 +173,8 @@ def attn_prefill(q, k, v, positions, theta: float = 10000.0,
     if scale is None:
         scale = 1.0 / np.sqrt(D)
     pos_b = positions[:, None, :]
-    q_rot = rope_rotate(q, pos_b, theta)
-    k_rot = rope_rotate(k, pos_b, theta)
+    q_rot = rope_rotate(q, pos_b, theta, pairing)
+    k_rot = rope_rotate(k, pos_b, theta, pairing)
     out = np.empty_like(q_rot)
     for b in range(B):
         for hq in range(Hq):
@@ -203,7 +233,7 @@ def cache_rows(cache, b: int, hk: int, n: int, block_table=None,
 
 def attn_decode(q, k_new, v_new, cache_k, cache_v, seq_lens,
                 theta: float = 10000.0, scale: float | None = None,
-                block_table=None, block_size: int = 16):
+                block_table=None, block_size: int = 16, pairing: str = "adjacent"):
     """One decode step: a single new query token per sequence.
 
     For sequence b with L = seq_lens[b] tokens already cached, the new
@@ -227,8 +257,8 @@ def attn_decode(q, k_new, v_new, cache_k, cache_v, seq_lens,
     out = np.empty((B, Hq, D))
     for b in range(B):
         L = int(seq_lens[b])
-        q_rot = rope_rotate(q[b][:, None, :], np.array([L]), theta)[:, 0, :]
-        k_rot = rope_rotate(k_new[b][:, None, :], np.array([L]), theta)  # [Hkv, 1, D]
+        q_rot = rope_rotate(q[b][:, None, :], np.array([L]), theta, pairing)[:, 0, :]
+        k_rot = rope_rotate(k_new[b][:, None, :], np.array([L]), theta, pairing)  # [Hkv, 1, D]
         v_one = v_new[b][None, :, None, :]                                # [1, Hkv, 1, D]
         if block_table is None:
             kv_cache_append(cache_k[b:b + 1], cache_v[b:b + 1], k_rot[None], v_one,
@@ -248,7 +278,8 @@ def attn_decode(q, k_new, v_new, cache_k, cache_v, seq_lens,
 
 def attn_prefill_cached(q, k, v, cache_k, cache_v, seq_lens,
                         theta: float = 10000.0, scale: float | None = None,
-                        block_table=None, block_size: int = 16, chunk_lens=None):
+                        block_table=None, block_size: int = 16, chunk_lens=None,
+                        pairing: str = "adjacent"):
     """A prompt chunk that continues a cached prefix.
 
     For sequence b with P = seq_lens[b] tokens already cached, the chunk's S
@@ -280,8 +311,8 @@ def attn_prefill_cached(q, k, v, cache_k, cache_v, seq_lens,
         if n == 0:
             continue
         pos = P + np.arange(n)
-        q_rot = rope_rotate(q[b, :, :n], pos, theta)    # [Hq, n, D]
-        k_rot = rope_rotate(k[b, :, :n], pos, theta)    # [Hkv, n, D]
+        q_rot = rope_rotate(q[b, :, :n], pos, theta, pairing)    # [Hq, n, D]
+        k_rot = rope_rotate(k[b, :, :n], pos, theta, pairing)    # [Hkv, n, D]
         v_b = v[b:b + 1, :, :n]
         if block_table is None:
             kv_cache_append(cache_k[b:b + 1], cache_v[b:b + 1], k_rot[None], v_b, pos[None, :])

@@ -109,6 +109,42 @@ def test_rope_inv_freq_values():
     assert np.all(np.diff(f) < 0)
 
 
+# ---- half-split pairing (the Llama/Qwen checkpoint layout) ----
+def _rope_half(x, p, t):
+    return A.rope_rotate(x, p, t, pairing="half")
+
+
+@pytest.mark.parametrize("pin", [check_rope_identity_at_zero, check_rope_norm,
+                                 check_rope_relative], ids=lambda f: f.__name__)
+def test_half_split_rope_pins(pin):
+    assert pin(_rope_half)
+
+
+def test_half_split_rope_hand_value():
+    """D = 4, half split: pair 1 is (x1, x3) at theta_1 = 0.01, so x = (0, 1,
+    0, 0) at m = 1 becomes (0, cos 0.01, 0, sin 0.01); pair 0 = (x0, x2)."""
+    y = _rope_half(np.array([[0.0, 1.0, 0.0, 0.0]]), np.array([1]), 10000.0)[0]
+    assert np.allclose(y, [0.0, math.cos(0.01), 0.0, math.sin(0.01)], atol=1e-15)
+    y = _rope_half(np.array([[1.0, 0.0, 0.0, 0.0]]), np.array([2]), 10000.0)[0]
+    assert np.allclose(y, [math.cos(2.0), 0.0, math.sin(2.0), 0.0], atol=1e-15)
+
+
+def test_half_split_equals_permuted_adjacent():
+    """half(x) = P^-1 adjacent(P x), P taking element i to 2i and i + D/2 to
+    2i + 1: the same rotations on a permutation of the elements."""
+    x = rng(5).standard_normal((3, 7, 128))
+    p = np.array([0, 1, 9, 100, 1000, 4095, 8192])
+    D = 128
+    perm = np.empty(D, int)
+    perm[0::2] = np.arange(D // 2)
+    perm[1::2] = np.arange(D // 2) + D // 2      # adjacent slot j holds half element perm[j]
+    adj = A.rope_rotate(x[..., perm], p, 1e4)
+    back = np.empty_like(adj)
+    back[..., perm] = adj
+    assert np.allclose(_rope_half(x, p, 1e4), back, atol=1e-12)
+    assert not np.allclose(_rope_half(x, p, 1e4), A.rope_rotate(x, p, 1e4), atol=1e-3)
+
+
 # planted mistakes in RoPE, each must trip at least one pin
 def _rope_generic(x, positions, theta, sign=1.0, halfsplit=False, expo=2.0):
     x = np.asarray(x, np.float64)
