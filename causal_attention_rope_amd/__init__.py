@@ -31,6 +31,14 @@ library_path = os.path.join(_HERE, "libcar.so")
 
 F32, BF16 = 0, 1
 _DTYPES = {torch.float32: F32, torch.bfloat16: BF16}
+# RoPE pair layouts (car_rope_pairing): (2i, 2i+1) or (i, i + D/2)
+ROPE_PAIRINGS = {"adjacent": 0, "half": 1}
+
+
+def _pairing(name: str) -> int:
+    if name not in ROPE_PAIRINGS:
+        raise ValueError(f"rope_pairing must be one of {sorted(ROPE_PAIRINGS)}")
+    return ROPE_PAIRINGS[name]
 
 
 class CarError(RuntimeError):
@@ -66,16 +74,16 @@ def _load() -> ctypes.CDLL:
     vp, i32, f32, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
     cache_p = ctypes.POINTER(_CarKVCache)
     sigs = {
-        "car_rope_apply": (i32, [vp, i32, i32, i32, i32, i32, vp, f32, vp]),
+        "car_rope_apply": (i32, [vp, i32, i32, i32, i32, i32, vp, f32, i32, vp]),
         "car_kv_cache_append": (i32, [cache_p, i32, vp, vp, i32, i32, i32, i32, vp, vp]),
         "car_attn_prefill_workspace_bytes": (sz, [i32, i32, i32, i32, i32, cache_p]),
-        "car_attn_prefill": (i32, [vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, vp, f32, f32,
-                                   cache_p, vp, sz, vp]),
+        "car_attn_prefill": (i32, [vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, vp, f32, i32,
+                                   f32, cache_p, vp, sz, vp]),
         "car_attn_prefill_cached": (i32, [vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, vp, vp,
-                                          i32, f32, f32, cache_p, vp]),
+                                          i32, f32, i32, f32, cache_p, vp]),
         "car_attn_decode_workspace_bytes": (sz, [i32, i32, i32, i32]),
-        "car_attn_decode": (i32, [vp, vp, vp, vp, i32, i32, i32, i32, i32, vp, i32, f32, f32,
-                                  cache_p, vp, sz, vp]),
+        "car_attn_decode": (i32, [vp, vp, vp, vp, i32, i32, i32, i32, i32, vp, i32, f32, i32,
+                                  f32, cache_p, vp, sz, vp]),
         "car_status_string": (ctypes.c_char_p, [i32]),
         "car_set_timing_events": (i32, [vp, vp]),
     }
@@ -208,15 +216,17 @@ def set_timing_events(start: Optional[torch.cuda.Event], stop: Optional[torch.cu
                "set_timing_events")
 
 
-def rope_apply(x: torch.Tensor, positions: torch.Tensor, theta: float = 10000.0) -> torch.Tensor:
-    """Rotate x [B, H, S, D] in place by RoPE at positions int32 [B, S]."""
+def rope_apply(x: torch.Tensor, positions: torch.Tensor, theta: float = 10000.0,
+               rope_pairing: str = "adjacent") -> torch.Tensor:
+    """Rotate x [B, H, S, D] in place by RoPE at positions int32 [B, S]
+    (``rope_pairing``: "adjacent" pairs (2i, 2i+1), "half" pairs (i, i + D/2))."""
     _need(x, "x", dim=4)
     B, H, S, D = x.shape
     _need(positions, "positions", dtype=torch.int32, dim=2, device=x.device)
     if tuple(positions.shape) != (B, S):
         raise ValueError("positions must be [B, S]")
     _check(_lib.car_rope_apply(_ptr(x), _dtype_code(x), B, H, S, D, _ptr(positions),
-                               float(theta), _stream(x)), "rope_apply")
+                               float(theta), _pairing(rope_pairing), _stream(x)), "rope_apply")
     return x
 
 
@@ -259,7 +269,8 @@ def _workspace(nbytes: int, device, workspace: Optional[torch.Tensor]) -> torch.
 def attn_prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, positions: torch.Tensor,
                  theta: float = 10000.0, scale: Optional[float] = None,
                  cache: Optional[KVCache] = None, out: Optional[torch.Tensor] = None,
-                 workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+                 workspace: Optional[torch.Tensor] = None,
+                 rope_pairing: str = "adjacent") -> torch.Tensor:
     """Causal attention over a prompt with RoPE on q and k (see car_attn_prefill).
 
     q [B, Hq, S, D]; k, v [B, Hkv, S, D]; positions int32 [B, S], strictly
@@ -295,7 +306,8 @@ def attn_prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, positions: t
     need = int(_lib.car_attn_prefill_workspace_bytes(dt, B, Hkv, S, D, None))
     ws = _workspace(need, q.device, workspace)
     _check(_lib.car_attn_prefill(_ptr(q), _ptr(k), _ptr(v), _ptr(out), dt, B, Hq, Hkv, S, D,
-                                 _ptr(positions), float(theta), float(scale),
+                                 _ptr(positions), float(theta), _pairing(rope_pairing),
+                                 float(scale),
                                  ctypes.byref(c) if c is not None else None, _ptr(ws),
                                  ws.numel() * ws.element_size(), _stream(q)), "attn_prefill")
     return out
@@ -305,7 +317,8 @@ def attn_prefill_cached(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
                         seq_lens: torch.Tensor, cache: KVCache, max_seq_len: int,
                         theta: float = 10000.0, scale: Optional[float] = None,
                         out: Optional[torch.Tensor] = None,
-                        chunk_lens: Optional[torch.Tensor] = None) -> torch.Tensor:
+                        chunk_lens: Optional[torch.Tensor] = None,
+                        rope_pairing: str = "adjacent") -> torch.Tensor:
     """A prompt chunk continuing a cached prefix (see car_attn_prefill_cached).
 
     q [B, Hq, S, D]; k, v [B, Hkv, S, D] (k not rotated); seq_lens int32 [B]
@@ -344,8 +357,8 @@ def attn_prefill_cached(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
     c = cache._c()
     _check(_lib.car_attn_prefill_cached(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _dtype_code(q),
                                         B, Hq, Hkv, S, D, _ptr(seq_lens), _ptr(chunk_lens),
-                                        int(max_seq_len),
-                                        float(theta), float(scale), ctypes.byref(c), _stream(q)),
+                                        int(max_seq_len), float(theta), _pairing(rope_pairing),
+                                        float(scale), ctypes.byref(c), _stream(q)),
            "attn_prefill_cached")
     return out
 
@@ -354,7 +367,8 @@ def attn_decode(q: torch.Tensor, k_new: torch.Tensor, v_new: torch.Tensor,
                 seq_lens: torch.Tensor, cache: KVCache, max_seq_len: int,
                 theta: float = 10000.0, scale: Optional[float] = None,
                 out: Optional[torch.Tensor] = None,
-                workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+                workspace: Optional[torch.Tensor] = None,
+                rope_pairing: str = "adjacent") -> torch.Tensor:
     """One decode step (see car_attn_decode).
 
     q [B, Hq, D]; k_new, v_new [B, Hkv, D] (not rotated); seq_lens int32 [B]
@@ -387,6 +401,6 @@ def attn_decode(q: torch.Tensor, k_new: torch.Tensor, v_new: torch.Tensor,
     c = cache._c()
     _check(_lib.car_attn_decode(_ptr(q), _ptr(k_new), _ptr(v_new), _ptr(out), _dtype_code(q),
                                 B, Hq, Hkv, D, _ptr(seq_lens), int(max_seq_len), float(theta),
-                                float(scale), ctypes.byref(c), _ptr(ws),
+                                _pairing(rope_pairing), float(scale), ctypes.byref(c), _ptr(ws),
                                 ws.numel() * ws.element_size(), _stream(q)), "attn_decode")
     return out

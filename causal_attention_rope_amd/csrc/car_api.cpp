@@ -33,8 +33,11 @@ car_status from_hip(hipError_t e) { return e == hipSuccess ? CAR_OK : CAR_ERR_HI
 
 // theta^(-2i/D) / (2 pi) (revolutions per position) for i < D/2, in double,
 // split into float hi + lo.
-RopeFreq make_freq(int D, float theta) {
+bool pairing_ok(car_rope_pairing p) { return p == CAR_ROPE_ADJACENT || p == CAR_ROPE_HALF; }
+
+RopeFreq make_freq(int D, float theta, car_rope_pairing pairing) {
   RopeFreq f{};
+  f.half = pairing == CAR_ROPE_HALF;
   const double two_pi = 6.283185307179586476925286766559;
   for (int i = 0; i < D / 2; ++i) {
     const double x = pow((double)theta, -2.0 * i / (double)D) / two_pi;
@@ -96,13 +99,14 @@ car_status car_set_timing_events(hipEvent_t start, hipEvent_t stop) {
 }
 
 car_status car_rope_apply(void* x, car_dtype dtype, int B, int H, int S, int D,
-                          const int32_t* positions, float theta, hipStream_t stream) {
-  if (!dtype_ok(dtype) || !head_dim_ok(D)) return CAR_ERR_UNSUPPORTED;
+                          const int32_t* positions, float theta, car_rope_pairing pairing,
+                          hipStream_t stream) {
+  if (!dtype_ok(dtype) || !head_dim_ok(D) || !pairing_ok(pairing)) return CAR_ERR_UNSUPPORTED;
   if (B < 0 || H < 0 || S < 0 || !positive_finite(theta)) return CAR_ERR_INVALID_ARGUMENT;
   if ((int64_t)B * H * S == 0) return CAR_OK;
   if (x == nullptr || positions == nullptr || !aligned16(x)) return CAR_ERR_INVALID_ARGUMENT;
   return from_hip(launch_rope_apply(dtype == CAR_DTYPE_F32 ? F32 : BF16, D, x, B, H, S,
-                                    positions, make_freq(D, theta), stream));
+                                    positions, make_freq(D, theta, pairing), stream));
 }
 
 car_status car_kv_cache_append(const car_kv_cache* cache, car_dtype dtype, const void* k,
@@ -133,10 +137,10 @@ size_t car_attn_prefill_workspace_bytes(car_dtype dtype, int B, int Hkv, int S, 
 
 car_status car_attn_prefill(const void* q, const void* k, const void* v, void* out,
                             car_dtype dtype, int B, int Hq, int Hkv, int S, int D,
-                            const int32_t* positions, float theta, float scale,
-                            const car_kv_cache* cache, void* workspace, size_t workspace_bytes,
-                            hipStream_t stream) {
-  if (!dtype_ok(dtype) || !head_dim_ok(D)) return CAR_ERR_UNSUPPORTED;
+                            const int32_t* positions, float theta, car_rope_pairing pairing,
+                            float scale, const car_kv_cache* cache, void* workspace,
+                            size_t workspace_bytes, hipStream_t stream) {
+  if (!dtype_ok(dtype) || !head_dim_ok(D) || !pairing_ok(pairing)) return CAR_ERR_UNSUPPORTED;
   if (cache != nullptr && cache->block_table != nullptr && cache->block_size != 16)
     return CAR_ERR_UNSUPPORTED;
   if (B < 0 || Hq < 0 || Hkv < 0 || S < 0) return CAR_ERR_INVALID_ARGUMENT;
@@ -158,7 +162,7 @@ car_status car_attn_prefill(const void* q, const void* k, const void* v, void* o
     return CAR_ERR_WORKSPACE;
 
   const Dtype dt = dtype == CAR_DTYPE_F32 ? F32 : BF16;
-  const RopeFreq fr = make_freq(D, theta);
+  const RopeFreq fr = make_freq(D, theta, pairing);
   hipError_t e = launch_prefill_prep(dt, D, cache != nullptr && cache->block_table != nullptr,
                                      cache != nullptr ? &c : nullptr, k, v, workspace, B, Hkv, S,
                                      positions, fr, stream);
@@ -170,9 +174,9 @@ car_status car_attn_prefill(const void* q, const void* k, const void* v, void* o
 car_status car_attn_prefill_cached(const void* q, const void* k, const void* v, void* out,
                                    car_dtype dtype, int B, int Hq, int Hkv, int S, int D,
                                    const int32_t* seq_lens, const int32_t* chunk_lens,
-                                   int max_seq_len, float theta, float scale,
-                                   const car_kv_cache* cache, hipStream_t stream) {
-  if (!dtype_ok(dtype) || !head_dim_ok(D)) return CAR_ERR_UNSUPPORTED;
+                                   int max_seq_len, float theta, car_rope_pairing pairing,
+                                   float scale, const car_kv_cache* cache, hipStream_t stream) {
+  if (!dtype_ok(dtype) || !head_dim_ok(D) || !pairing_ok(pairing)) return CAR_ERR_UNSUPPORTED;
   if (cache != nullptr && cache->block_table != nullptr && cache->block_size != 16)
     return CAR_ERR_UNSUPPORTED;
   if (B < 0 || Hq < 0 || Hkv < 0 || S < 0) return CAR_ERR_INVALID_ARGUMENT;
@@ -197,7 +201,7 @@ car_status car_attn_prefill_cached(const void* q, const void* k, const void* v, 
     return CAR_ERR_UNSUPPORTED;
 
   const Dtype dt = dtype == CAR_DTYPE_F32 ? F32 : BF16;
-  const RopeFreq fr = make_freq(D, theta);
+  const RopeFreq fr = make_freq(D, theta, pairing);
   const bool paged = cache->block_table != nullptr;
   hipError_t e =
       launch_chunk_prep(dt, D, paged, c, k, v, B, Hkv, S, seq_lens, chunk_lens, fr, stream);
@@ -213,10 +217,10 @@ size_t car_attn_decode_workspace_bytes(int B, int Hq, int D, int max_seq_len) {
 
 car_status car_attn_decode(const void* q, const void* k_new, const void* v_new, void* out,
                            car_dtype dtype, int B, int Hq, int Hkv, int D,
-                           const int32_t* seq_lens, int max_seq_len, float theta, float scale,
-                           const car_kv_cache* cache, void* workspace, size_t workspace_bytes,
-                           hipStream_t stream) {
-  if (!dtype_ok(dtype) || !head_dim_ok(D)) return CAR_ERR_UNSUPPORTED;
+                           const int32_t* seq_lens, int max_seq_len, float theta,
+                           car_rope_pairing pairing, float scale, const car_kv_cache* cache,
+                           void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  if (!dtype_ok(dtype) || !head_dim_ok(D) || !pairing_ok(pairing)) return CAR_ERR_UNSUPPORTED;
   if (cache != nullptr && cache->block_table != nullptr && cache->block_size != 16)
     return CAR_ERR_UNSUPPORTED;
   if (B < 0 || Hq < 0 || Hkv < 0 || max_seq_len < 1) return CAR_ERR_INVALID_ARGUMENT;
@@ -243,7 +247,7 @@ car_status car_attn_decode(const void* q, const void* k_new, const void* v_new, 
   return from_hip(launch_decode(dtype == CAR_DTYPE_F32 ? F32 : BF16, D, group,
                                 cache->block_table != nullptr, q, k_new, v_new, out, B, Hq, Hkv,
                                 seq_lens, max_seq_len, c,
-                                static_cast<float*>(workspace), make_freq(D, theta), scale,
+                                static_cast<float*>(workspace), make_freq(D, theta, pairing), scale,
                                 stream, timing()));
 }
 

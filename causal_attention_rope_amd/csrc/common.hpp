@@ -119,6 +119,42 @@ __device__ __forceinline__ void rope_rotate_regs(float (&f)[N], int pos, int p0,
   }
 }
 
+// Half-split layout (pair i = elements i and i + D/2): rotate the chunk
+// f = elements d0..d0+N-1 of a row, given p = the partner elements d0 +- D/2
+// (read from the unrotated row).  Elements of the first half take the first
+// component of their pair's rotation, those of the second half the second.
+template <int N>
+__device__ __forceinline__ void rope_rotate_half_chunk(float (&f)[N], const float (&p)[N], int pos,
+                                                       int d0, int D, const RopeFreq& fr) {
+  const bool first = d0 < D / 2;
+  const int i0 = first ? d0 : d0 - D / 2;
+#pragma unroll
+  for (int j = 0; j < N; ++j) {
+    float c, s;
+    rope_cos_sin(pos, fr.hi[i0 + j], fr.lo[i0 + j], c, s);
+    f[j] = first ? f[j] * c - p[j] * s : p[j] * s + f[j] * c;
+  }
+}
+
+// Element offset of the half-split partner of the chunk starting at d0.
+__device__ __forceinline__ int rope_half_partner(int d0, int D) {
+  return d0 < D / 2 ? d0 + D / 2 : d0 - D / 2;
+}
+
+// Rotate a chunk of a row that is only read: elements d0..d0+N-1 of `row`,
+// already loaded into f, in either pair layout.
+template <typename T, int N>
+__device__ __forceinline__ void rope_rotate_chunk(float (&f)[N], const T* row, int d0, int D,
+                                                  int pos, const RopeFreq& fr) {
+  if (fr.half) {
+    float p[N];
+    load16<T>(row + rope_half_partner(d0, D), p);
+    rope_rotate_half_chunk<N>(f, p, pos, d0, D, fr);
+  } else {
+    rope_rotate_regs<N>(f, pos, d0 / 2, fr);
+  }
+}
+
 // ---------------------------------------------------------------------------
 // Cache addressing: element offset of row (sequence b, head hk, token t).
 // ---------------------------------------------------------------------------

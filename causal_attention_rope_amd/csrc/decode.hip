@@ -153,8 +153,9 @@ __attribute__((amdgpu_waves_per_eu(G <= 4 ? 4 : 2))) void decode_split_kernel(
 #pragma unroll
     for (int ch = 0; ch < C; ++ch) {
       float f[N];
-      load16<T>(q + ((int64_t)b * Hq + hk * G + g) * D + col[ch], f);
-      rope_rotate_regs<N>(f, L, col[ch] / 2, fr);
+      const T* qrow = q + ((int64_t)b * Hq + hk * G + g) * D;
+      load16<T>(qrow + col[ch], f);
+      rope_rotate_chunk<T, N>(f, qrow, col[ch], D, L, fr);
 #pragma unroll
       for (int w = 0; w < 4; ++w) {
         if constexpr (BF)
@@ -178,7 +179,7 @@ __attribute__((amdgpu_waves_per_eu(G <= 4 ? 4 : 2))) void decode_split_kernel(
       const int64_t src = ((int64_t)b * Hkv + hk) * D + col[ch];
       float f[N];
       load16<T>(k_new + src, f);
-      rope_rotate_regs<N>(f, L, col[ch] / 2, fr);
+      rope_rotate_chunk<T, N>(f, k_new + (src - col[ch]), col[ch], D, L, fr);
       T kt[N];
       store16<T>(kt, f);
       kn[ch] = *reinterpret_cast<const u32x4_t*>(kt);

@@ -8,10 +8,12 @@
 namespace car {
 
 // Per-pair RoPE frequency in revolutions per position, theta^(-2i/D) / (2 pi),
-// as an unevaluated float sum hi + lo.
+// as an unevaluated float sum hi + lo, and the pair layout: half == 0 pairs
+// elements (2i, 2i+1), half == 1 pairs (i, i + D/2).
 struct RopeFreq {
   float hi[64];
   float lo[64];
+  int half;
 };
 
 // Device view of one layer's KV cache (see car_kv_cache in car.h).

@@ -88,7 +88,8 @@ __global__ __launch_bounds__(F32_ROWS) void prefill_f32_kernel(
   for (int d = 0; d < D; d += 4) {
     float f[4];
     load16<float>(qrow + d, f);
-    rope_rotate_regs<4>(f, SRC == KEYS_PROMPT ? positions[(int64_t)b * S + ic] : P + ic, d / 2, fr);
+    rope_rotate_chunk<float, 4>(f, qrow, d, D,
+                                SRC == KEYS_PROMPT ? positions[(int64_t)b * S + ic] : P + ic, fr);
 #pragma unroll
     for (int e = 0; e < 4; ++e) qv[d + e] = f[e] * qk_scale;
   }
@@ -431,7 +432,7 @@ __global__ __launch_bounds__(Tile<D>::THREADS, 2) void prefill_bf16_kernel(
         const int d0 = ks * 16 + g * 8;
         float f[8];
         load16<bf16_t>(qp + d0, f);
-        rope_rotate_regs<8>(f, pos, d0 / 2, fr);
+        rope_rotate_chunk<bf16_t, 8>(f, qp, d0, D, pos, fr);
         const u32x4_t u = {cvt_pk_bf16(f[0], f[1]), cvt_pk_bf16(f[2], f[3]),
                            cvt_pk_bf16(f[4], f[5]), cvt_pk_bf16(f[6], f[7])};
         qf[ks] = __builtin_bit_cast(bf16x8_t, u);

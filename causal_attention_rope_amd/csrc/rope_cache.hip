@@ -40,7 +40,20 @@ __global__ __launch_bounds__(kThreads) void rope_apply_kernel(T* __restrict__ x,
     T* p = x + row * D + col;
     float f[N];
     load16<T>(p, f);
-    rope_rotate_regs<N>(f, pos, col / 2, fr);
+    if (fr.half) {
+      // in place: the thread of the first-half chunk rotates both halves
+      if (col >= D / 2) continue;
+      float h[N];
+      load16<T>(p + D / 2, h);
+      float a[N];
+#pragma unroll
+      for (int j = 0; j < N; ++j) a[j] = f[j];
+      rope_rotate_half_chunk<N>(f, h, pos, col, D, fr);
+      rope_rotate_half_chunk<N>(h, a, pos, col + D / 2, D, fr);
+      store16<T>(p + D / 2, h);
+    } else {
+      rope_rotate_regs<N>(f, pos, col / 2, fr);
+    }
     store16<T>(p, f);
   }
 }
@@ -90,7 +103,7 @@ __global__ __launch_bounds__(kThreads) void prefill_prep_kernel(
     const int pos = positions[(int64_t)b * S + s];
     float f[N];
     load16<T>(k + row * D + col, f);
-    rope_rotate_regs<N>(f, pos, col / 2, fr);
+    rope_rotate_chunk<T, N>(f, k + row * D, col, D, pos, fr);
     store16<T>(k_rot + row * D + col, f);
     if constexpr (CACHE) {
       const int hk = (int)(bh % Hkv);
@@ -129,7 +142,7 @@ __global__ __launch_bounds__(kThreads) void chunk_prep_kernel(
     const int pos = min(P + s, last);
     float f[N];
     load16<T>(k + row * D + col, f);
-    rope_rotate_regs<N>(f, pos, col / 2, fr);
+    rope_rotate_chunk<T, N>(f, k + row * D, col, D, pos, fr);
     const int64_t dst = cache_row<PAGED>(c, b, hk, Hkv, pos) * D + col;
     store16<T>(static_cast<T*>(c.k) + dst, f);
     *reinterpret_cast<uint4*>(static_cast<T*>(c.v) + dst) =

@@ -57,13 +57,29 @@ typedef enum car_dtype {
   CAR_DTYPE_BF16 = 1
 } car_dtype;
 
+/*
+ * Which elements RoPE rotates together ([Intuition] §4 writes out the pairs
+ * (q0,q1), (q2,q3), ...; checkpoints of the Llama/Qwen families the pages
+ * name ([Guide] §6.1) pair each element of the first half with its twin in
+ * the second).  Pair i has angle m * theta^(-2i/D) in both layouts.
+ */
+typedef enum car_rope_pairing {
+  CAR_ROPE_ADJACENT = 0,  /* pair i = elements (2i, 2i+1) */
+  CAR_ROPE_HALF = 1       /* pair i = elements (i, i + D/2) */
+} car_rope_pairing;
+/* Every entry point that rotates (car_rope_apply, car_attn_prefill,
+ * car_attn_prefill_cached, car_attn_decode) takes the base theta (10000 on
+ * the pages) and the pairing right after it; keys stored in a cache are
+ * rotated in that layout, so one cache is read with one pairing.  Another
+ * value returns CAR_ERR_UNSUPPORTED. */
+
 typedef enum car_status {
   CAR_OK = 0,
   CAR_ERR_INVALID_ARGUMENT = 1, /* null pointer, negative size, Hq % Hkv != 0,
                                    pointer not 16-byte aligned, bad cache shape */
   CAR_ERR_UNSUPPORTED = 2,      /* well formed but not built: D not in {64, 128},
                                    block_size != 16, Hq/Hkv not in {1, 2, 4, 8},
-                                   unknown dtype */
+                                   unknown dtype or RoPE pairing */
   CAR_ERR_WORKSPACE = 3,        /* workspace missing or smaller than required */
   CAR_ERR_HIP = 4               /* the HIP runtime reported an error at launch */
 } car_status;
@@ -97,7 +113,8 @@ typedef struct car_kv_cache {
  * Every pair of every head and token is rotated by its own angle.
  */
 car_status car_rope_apply(void* x, car_dtype dtype, int B, int H, int S, int D,
-                          const int32_t* positions, float theta, hipStream_t stream);
+                          const int32_t* positions, float theta, car_rope_pairing pairing,
+                          hipStream_t stream);
 
 /*
  * car_kv_cache_append -- store already-rotated keys and raw values in the
@@ -145,7 +162,8 @@ size_t car_attn_prefill_workspace_bytes(car_dtype dtype, int B, int Hkv, int S, 
  */
 car_status car_attn_prefill(const void* q, const void* k, const void* v, void* out,
                             car_dtype dtype, int B, int Hq, int Hkv, int S, int D,
-                            const int32_t* positions, float theta, float scale,
+                            const int32_t* positions, float theta, car_rope_pairing pairing,
+                            float scale,
                             const car_kv_cache* cache, void* workspace,
                             size_t workspace_bytes, hipStream_t stream);
 
@@ -181,7 +199,8 @@ car_status car_attn_prefill(const void* q, const void* k, const void* v, void* o
 car_status car_attn_prefill_cached(const void* q, const void* k, const void* v, void* out,
                                    car_dtype dtype, int B, int Hq, int Hkv, int S, int D,
                                    const int32_t* seq_lens, const int32_t* chunk_lens,
-                                   int max_seq_len, float theta, float scale,
+                                   int max_seq_len, float theta, car_rope_pairing pairing,
+                                   float scale,
                                    const car_kv_cache* cache, hipStream_t stream);
 
 /*
@@ -215,6 +234,7 @@ size_t car_attn_decode_workspace_bytes(int B, int Hq, int D, int max_seq_len);
 car_status car_attn_decode(const void* q, const void* k_new, const void* v_new,
                            void* out, car_dtype dtype, int B, int Hq, int Hkv, int D,
                            const int32_t* seq_lens, int max_seq_len, float theta,
+                           car_rope_pairing pairing,
                            float scale, const car_kv_cache* cache, void* workspace,
                            size_t workspace_bytes, hipStream_t stream);
 

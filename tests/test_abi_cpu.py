@@ -71,14 +71,15 @@ def _cache(car, paged=False, block_size=16, max_seq=64, k=FAKE, v=FAKE):
 
 def test_rope_apply_rejects(lib):
     f = lib.car_rope_apply
-    assert f(FAKE, BF16, 1, 1, 1, 96, FAKE, 1e4, None) == UNSUPPORTED     # D
-    assert f(FAKE, 7, 1, 1, 1, 64, FAKE, 1e4, None) == UNSUPPORTED        # dtype
-    assert f(None, BF16, 1, 1, 1, 64, FAKE, 1e4, None) == INVALID         # null x
-    assert f(FAKE + 8, BF16, 1, 1, 1, 64, FAKE, 1e4, None) == INVALID     # misaligned
-    assert f(FAKE, BF16, -1, 1, 1, 64, FAKE, 1e4, None) == INVALID        # size
-    assert f(FAKE, BF16, 1, 1, 1, 64, FAKE, -1.0, None) == INVALID        # theta
-    assert f(FAKE, BF16, 1, 1, 1, 64, None, 1e4, None) == INVALID         # positions
-    assert f(None, BF16, 0, 4, 4, 64, None, 1e4, None) == OK              # empty: no-op
+    assert f(FAKE, BF16, 1, 1, 1, 96, FAKE, 1e4, 0, None) == UNSUPPORTED     # D
+    assert f(FAKE, 7, 1, 1, 1, 64, FAKE, 1e4, 0, None) == UNSUPPORTED        # dtype
+    assert f(None, BF16, 1, 1, 1, 64, FAKE, 1e4, 0, None) == INVALID         # null x
+    assert f(FAKE + 8, BF16, 1, 1, 1, 64, FAKE, 1e4, 0, None) == INVALID     # misaligned
+    assert f(FAKE, BF16, -1, 1, 1, 64, FAKE, 1e4, 0, None) == INVALID        # size
+    assert f(FAKE, BF16, 1, 1, 1, 64, FAKE, -1.0, 0, None) == INVALID        # theta
+    assert f(FAKE, BF16, 1, 1, 1, 64, None, 1e4, 0, None) == INVALID         # positions
+    assert f(FAKE, BF16, 1, 1, 1, 64, FAKE, 1e4, 2, None) == UNSUPPORTED     # pairing
+    assert f(None, BF16, 0, 4, 4, 64, None, 1e4, 0, None) == OK              # empty: no-op
 
 
 def test_kv_cache_append_rejects(car, lib):
@@ -101,14 +102,16 @@ def test_prefill_rejects(car, lib):
     need = lib.car_attn_prefill_workspace_bytes(BF16, 2, 2, 8, 64, None)
     assert need == 2 * 2 * 8 * 64 * 2
     args = dict(q=FAKE, k=FAKE, v=FAKE, out=FAKE, dt=BF16, B=2, Hq=4, Hkv=2, S=8, D=64,
-                pos=FAKE, theta=1e4, scale=0.125, cache=None, ws=FAKE, wsb=need)
+                pos=FAKE, theta=1e4, pair=0, scale=0.125, cache=None, ws=FAKE, wsb=need)
 
     def call(**kw):
         a = dict(args, **kw)
         return f(a["q"], a["k"], a["v"], a["out"], a["dt"], a["B"], a["Hq"], a["Hkv"], a["S"],
-                 a["D"], a["pos"], a["theta"], a["scale"], a["cache"], a["ws"], a["wsb"], None)
+                 a["D"], a["pos"], a["theta"], a["pair"], a["scale"], a["cache"], a["ws"],
+                 a["wsb"], None)
 
     assert call(D=80) == UNSUPPORTED
+    assert call(pair=5) == UNSUPPORTED               # unknown RoPE pairing
     assert call(Hq=3) == INVALID                     # Hq % Hkv
     assert call(scale=0.0) == INVALID
     assert call(scale=float("nan")) == INVALID
@@ -129,16 +132,18 @@ def test_decode_rejects(car, lib):
     assert need == 2 * 8 * 2 * (128 + 4) * 4        # two 256-token splits
     c = _cache(car, max_seq=512)
     args = dict(q=FAKE, kn=FAKE, vn=FAKE, out=FAKE, dt=BF16, B=2, Hq=8, Hkv=2, D=128,
-                lens=FAKE, msl=300, theta=1e4, scale=0.088, cache=ctypes.byref(c), ws=FAKE,
-                wsb=need - 16)
+                lens=FAKE, msl=300, theta=1e4, pair=1, scale=0.088, cache=ctypes.byref(c),
+                ws=FAKE, wsb=need - 16)
 
     def call(**kw):
         a = dict(args, **kw)
         return f(a["q"], a["kn"], a["vn"], a["out"], a["dt"], a["B"], a["Hq"], a["Hkv"], a["D"],
-                 a["lens"], a["msl"], a["theta"], a["scale"], a["cache"], a["ws"], a["wsb"], None)
+                 a["lens"], a["msl"], a["theta"], a["pair"], a["scale"], a["cache"], a["ws"],
+                 a["wsb"], None)
 
     assert call() == WORKSPACE                       # everything valid but the workspace
     assert call(ws=None) == WORKSPACE
+    assert call(pair=-1) == UNSUPPORTED              # unknown RoPE pairing
     assert call(D=96) == UNSUPPORTED
     assert call(Hq=5) == INVALID                     # Hq % Hkv
     assert call(Hq=6) == UNSUPPORTED                 # group of 3 not built
@@ -158,16 +163,18 @@ def test_prefill_cached_rejects(car, lib):
     f = lib.car_attn_prefill_cached
     c = _cache(car, max_seq=512)
     args = dict(q=FAKE, k=FAKE, v=FAKE, out=FAKE, dt=BF16, B=2, Hq=8, Hkv=2, S=100, D=128,
-                lens=FAKE, clens=None, msl=300, theta=1e4, scale=0.088, cache=ctypes.byref(c))
+                lens=FAKE, clens=None, msl=300, theta=1e4, pair=0, scale=0.088,
+                cache=ctypes.byref(c))
 
     def call(**kw):
         a = dict(args, **kw)
         return f(a["q"], a["k"], a["v"], a["out"], a["dt"], a["B"], a["Hq"], a["Hkv"], a["S"],
-                 a["D"], a["lens"], a["clens"], a["msl"], a["theta"], a["scale"], a["cache"],
-                 None)
+                 a["D"], a["lens"], a["clens"], a["msl"], a["theta"], a["pair"], a["scale"],
+                 a["cache"], None)
 
     assert call(D=96) == UNSUPPORTED
     assert call(dt=7) == UNSUPPORTED
+    assert call(pair=3) == UNSUPPORTED               # unknown RoPE pairing
     assert call(Hq=5) == INVALID                     # Hq % Hkv
     assert call(lens=None) == INVALID
     assert call(q=None) == INVALID
