@@ -142,16 +142,64 @@ __device__ __forceinline__ int rope_half_partner(int d0, int D) {
 }
 
 // Rotate a chunk of a row that is only read: elements d0..d0+N-1 of `row`,
-// already loaded into f, in either pair layout.
-template <typename T, int N>
+// already loaded into f, in either pair layout (HALF: 0 adjacent, 1 half
+// split, -1 taken from fr.half at run time).
+template <typename T, int N, int HALF = -1>
 __device__ __forceinline__ void rope_rotate_chunk(float (&f)[N], const T* row, int d0, int D,
                                                   int pos, const RopeFreq& fr) {
-  if (fr.half) {
+  if (HALF == 1 || (HALF < 0 && fr.half)) {
     float p[N];
     load16<T>(row + rope_half_partner(d0, D), p);
     rope_rotate_half_chunk<N>(f, p, pos, d0, D, fr);
   } else {
     rope_rotate_regs<N>(f, pos, d0 / 2, fr);
+  }
+}
+
+// The cos/sin a lane needs to rotate its chunk (elements d0..d0+N-1) at one
+// position, computed once and applied to any number of rows at that
+// position (the query heads and the new key of a decode step).
+template <int N>
+struct RopeChunk {
+  float c[N], s[N];  // adjacent: N/2 pair angles; half split: one per element
+  int d0;
+};
+
+template <int N, int HALF>  // HALF: 0 adjacent, 1 half split, -1 taken from fr.half
+__device__ __forceinline__ RopeChunk<N> rope_prepare(int pos, int d0, int D, const RopeFreq& fr) {
+  RopeChunk<N> r;
+  r.d0 = d0;
+  if (HALF == 1 || (HALF < 0 && fr.half)) {
+    const int i0 = d0 < D / 2 ? d0 : d0 - D / 2;
+#pragma unroll
+    for (int j = 0; j < N; ++j) rope_cos_sin(pos, fr.hi[i0 + j], fr.lo[i0 + j], r.c[j], r.s[j]);
+  } else {
+#pragma unroll
+    for (int j = 0; j < N / 2; ++j)
+      rope_cos_sin(pos, fr.hi[d0 / 2 + j], fr.lo[d0 / 2 + j], r.c[j], r.s[j]);
+  }
+  return r;
+}
+
+// Rotate the chunk f (elements r.d0.. of `row`, already loaded) with the
+// prepared angles; the half-split layout reads the partner chunk from `row`.
+template <typename T, int N, int HALF>
+__device__ __forceinline__ void rope_apply_prepared(float (&f)[N], const T* row, int D,
+                                                    const RopeChunk<N>& r, const RopeFreq& fr) {
+  if (HALF == 1 || (HALF < 0 && fr.half)) {
+    float p[N];
+    load16<T>(row + rope_half_partner(r.d0, D), p);
+    const bool first = r.d0 < D / 2;
+#pragma unroll
+    for (int j = 0; j < N; ++j)
+      f[j] = first ? f[j] * r.c[j] - p[j] * r.s[j] : p[j] * r.s[j] + f[j] * r.c[j];
+  } else {
+#pragma unroll
+    for (int j = 0; j < N / 2; ++j) {
+      const float x0 = f[2 * j], x1 = f[2 * j + 1];
+      f[2 * j] = x0 * r.c[j] - x1 * r.s[j];
+      f[2 * j + 1] = x0 * r.s[j] + x1 * r.c[j];
+    }
   }
 }
 

@@ -105,7 +105,9 @@ __device__ __forceinline__ float row_score(const uint32_t (&qw)[C][4], const u32
   return group_sum<Gm::LPR>(p);
 }
 
-template <typename T, int D, int G, bool PAGED, int SPLIT>
+// HALF: RoPE pairs (i, i + D/2) instead of (2i, 2i+1), a compile-time choice
+// so that the layout test stays out of the loop's register allocation.
+template <typename T, int D, int G, bool PAGED, int SPLIT, bool HALF>
 __global__ __launch_bounds__(64 * decode_waves<G>())
 __attribute__((amdgpu_waves_per_eu(G <= 4 ? 4 : 2))) void decode_split_kernel(
     const T* __restrict__ q, const T* __restrict__ k_new, const T* __restrict__ v_new,
@@ -147,6 +149,11 @@ __attribute__((amdgpu_waves_per_eu(G <= 4 ? 4 : 2))) void decode_split_kernel(
   // Query heads of this KV head, rotated at position L and pre-scaled so
   // that exp2 of a score difference is the softmax weight; as raw words
   // (packed bf16 pairs, or fp32 bit patterns), 4 per chunk.
+  // The angles depend only on the position L and the lane's columns: one set
+  // serves every query head of the group and the new key.
+  RopeChunk<N> rope[C];
+#pragma unroll
+  for (int ch = 0; ch < C; ++ch) rope[ch] = rope_prepare<N, HALF>(L, col[ch], D, fr);
   uint32_t qw[G][C][4];
 #pragma unroll
   for (int g = 0; g < G; ++g)
@@ -155,7 +162,7 @@ __attribute__((amdgpu_waves_per_eu(G <= 4 ? 4 : 2))) void decode_split_kernel(
       float f[N];
       const T* qrow = q + ((int64_t)b * Hq + hk * G + g) * D;
       load16<T>(qrow + col[ch], f);
-      rope_rotate_chunk<T, N>(f, qrow, col[ch], D, L, fr);
+      rope_apply_prepared<T, N, HALF>(f, qrow, D, rope[ch], fr);
 #pragma unroll
       for (int w = 0; w < 4; ++w) {
         if constexpr (BF)
@@ -179,7 +186,7 @@ __attribute__((amdgpu_waves_per_eu(G <= 4 ? 4 : 2))) void decode_split_kernel(
       const int64_t src = ((int64_t)b * Hkv + hk) * D + col[ch];
       float f[N];
       load16<T>(k_new + src, f);
-      rope_rotate_chunk<T, N>(f, k_new + (src - col[ch]), col[ch], D, L, fr);
+      rope_apply_prepared<T, N, HALF>(f, k_new + (src - col[ch]), D, rope[ch], fr);
       T kt[N];
       store16<T>(kt, f);
       kn[ch] = *reinterpret_cast<const u32x4_t*>(kt);
@@ -488,11 +495,18 @@ hipError_t decode_t(const void* q, const void* k_new, const void* v_new, void* o
   constexpr int SPLIT = split_tokens<G>();
   const int nsplit = (max_seq_len + SPLIT - 1) / SPLIT;  // <= the workspace's split count
   const float qk_scale = scale * 1.4426950408889634f;  // log2(e): softmax in base 2
-  hipExtLaunchKernelGGL((decode_split_kernel<T, D, G, PAGED, SPLIT>), dim3(Hkv * B, nsplit),
-                        dim3(64 * decode_waves<G>()), 0, st, tl.start, tl.stop, 0,
-                        static_cast<const T*>(q), static_cast<const T*>(k_new),
-                        static_cast<const T*>(v_new), seq_lens, c, partials, Hkv, nsplit, fr,
-                        qk_scale);
+  if (fr.half)
+    hipExtLaunchKernelGGL((decode_split_kernel<T, D, G, PAGED, SPLIT, true>),
+                          dim3(Hkv * B, nsplit), dim3(64 * decode_waves<G>()), 0, st, tl.start,
+                          tl.stop, 0, static_cast<const T*>(q), static_cast<const T*>(k_new),
+                          static_cast<const T*>(v_new), seq_lens, c, partials, Hkv, nsplit, fr,
+                          qk_scale);
+  else
+    hipExtLaunchKernelGGL((decode_split_kernel<T, D, G, PAGED, SPLIT, false>),
+                          dim3(Hkv * B, nsplit), dim3(64 * decode_waves<G>()), 0, st, tl.start,
+                          tl.stop, 0, static_cast<const T*>(q), static_cast<const T*>(k_new),
+                          static_cast<const T*>(v_new), seq_lens, c, partials, Hkv, nsplit, fr,
+                          qk_scale);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int last = PAGED ? c.mbps * 16 - 1 : c.max_seq - 1;

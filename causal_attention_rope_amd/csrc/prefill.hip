@@ -65,7 +65,7 @@ __device__ __forceinline__ int chunk_start(const CacheArgs& c, const int32_t* se
 constexpr int F32_ROWS = 64;  // query rows per workgroup (one per thread)
 constexpr int F32_KT = 32;    // keys per LDS tile
 
-template <int D, int SRC>
+template <int D, int SRC, int HALF>
 __global__ __launch_bounds__(F32_ROWS) void prefill_f32_kernel(
     const float* __restrict__ q, const float* __restrict__ kr, const float* __restrict__ v,
     float* __restrict__ out, const int32_t* __restrict__ positions, int Hq, int Hkv, int S,
@@ -88,7 +88,7 @@ __global__ __launch_bounds__(F32_ROWS) void prefill_f32_kernel(
   for (int d = 0; d < D; d += 4) {
     float f[4];
     load16<float>(qrow + d, f);
-    rope_rotate_chunk<float, 4>(f, qrow, d, D,
+    rope_rotate_chunk<float, 4, HALF>(f, qrow, d, D,
                                 SRC == KEYS_PROMPT ? positions[(int64_t)b * S + ic] : P + ic, fr);
 #pragma unroll
     for (int e = 0; e < 4; ++e) qv[d + e] = f[e] * qk_scale;
@@ -269,7 +269,7 @@ __device__ __forceinline__ int logical_chunk(int p, int r) {
   }
 }
 
-template <int D, int SRC>
+template <int D, int SRC, int HALF>
 __global__ __launch_bounds__(Tile<D>::THREADS, 2) void prefill_bf16_kernel(
     const bf16_t* __restrict__ q, const bf16_t* __restrict__ kr, const bf16_t* __restrict__ v,
     bf16_t* __restrict__ out, const int32_t* __restrict__ positions, int Hq, int Hkv, int S,
@@ -432,7 +432,7 @@ __global__ __launch_bounds__(Tile<D>::THREADS, 2) void prefill_bf16_kernel(
         const int d0 = ks * 16 + g * 8;
         float f[8];
         load16<bf16_t>(qp + d0, f);
-        rope_rotate_chunk<bf16_t, 8>(f, qp, d0, D, pos, fr);
+        rope_rotate_chunk<bf16_t, 8, HALF>(f, qp, d0, D, pos, fr);
         const u32x4_t u = {cvt_pk_bf16(f[0], f[1]), cvt_pk_bf16(f[2], f[3]),
                            cvt_pk_bf16(f[4], f[5]), cvt_pk_bf16(f[6], f[7])};
         qf[ks] = __builtin_bit_cast(bf16x8_t, u);
@@ -628,12 +628,12 @@ struct KeySource {
   const int32_t* chunk_lens;
 };
 
-template <int D, int SRC>
+template <int D, int SRC, int HALF>
 hipError_t prefill_f32_t(const void* q, const KeySource& ks, void* out, int B, int Hq, int Hkv,
                          int S, const int32_t* positions, const RopeFreq& fr, float scale,
                          hipStream_t st, const TimedLaunch& tl) {
   const dim3 grid((S + F32_ROWS - 1) / F32_ROWS, Hq, B);
-  hipExtLaunchKernelGGL((prefill_f32_kernel<D, SRC>), grid, dim3(F32_ROWS), 0, st, tl.start,
+  hipExtLaunchKernelGGL((prefill_f32_kernel<D, SRC, HALF>), grid, dim3(F32_ROWS), 0, st, tl.start,
                         tl.stop, 0, static_cast<const float*>(q),
                         static_cast<const float*>(ks.k_rot), static_cast<const float*>(ks.v),
                         static_cast<float*>(out), positions, Hq, Hkv, S, fr,
@@ -641,14 +641,14 @@ hipError_t prefill_f32_t(const void* q, const KeySource& ks, void* out, int B, i
   return hipGetLastError();
 }
 
-template <int D, int SRC>
+template <int D, int SRC, int HALF>
 hipError_t prefill_bf16_t(const void* q, const KeySource& ks, void* out, int B, int Hq, int Hkv,
                           int S, const int32_t* positions, const RopeFreq& fr, float scale,
                           hipStream_t st, const TimedLaunch& tl) {
   using C = Tile<D>;
   const int nqt = (S + C::BM - 1) / C::BM;
   const int npair = SRC == KEYS_PROMPT ? (nqt + 1) / 2 : nqt;  // workgroups per head
-  hipExtLaunchKernelGGL((prefill_bf16_kernel<D, SRC>), dim3(npair * B * Hq), dim3(C::THREADS), 0,
+  hipExtLaunchKernelGGL((prefill_bf16_kernel<D, SRC, HALF>), dim3(npair * B * Hq), dim3(C::THREADS), 0,
                         st, tl.start, tl.stop, 0, static_cast<const bf16_t*>(q),
                         static_cast<const bf16_t*>(ks.k_rot), static_cast<const bf16_t*>(ks.v),
                         static_cast<bf16_t*>(out), positions, Hq, Hkv, S, nqt, fr,
@@ -656,18 +656,33 @@ hipError_t prefill_bf16_t(const void* q, const KeySource& ks, void* out, int B, 
   return hipGetLastError();
 }
 
+template <int SRC, int HALF>
+hipError_t prefill_dispatch_t(Dtype dt, int D, const void* q, const KeySource& ks, void* out,
+                              int B, int Hq, int Hkv, int S, const int32_t* positions,
+                              const RopeFreq& fr, float scale, hipStream_t s,
+                              const TimedLaunch& tl) {
+  if (dt == F32)
+    return D == 64
+               ? prefill_f32_t<64, SRC, HALF>(q, ks, out, B, Hq, Hkv, S, positions, fr, scale, s, tl)
+               : prefill_f32_t<128, SRC, HALF>(q, ks, out, B, Hq, Hkv, S, positions, fr, scale, s,
+                                               tl);
+  return D == 64
+             ? prefill_bf16_t<64, SRC, HALF>(q, ks, out, B, Hq, Hkv, S, positions, fr, scale, s, tl)
+             : prefill_bf16_t<128, SRC, HALF>(q, ks, out, B, Hq, Hkv, S, positions, fr, scale, s,
+                                              tl);
+}
+
+// The RoPE pair layout is a compile-time choice of the kernels, so that the
+// layout test stays out of their register allocation.
 template <int SRC>
 hipError_t prefill_dispatch(Dtype dt, int D, const void* q, const KeySource& ks, void* out,
                             int B, int Hq, int Hkv, int S, const int32_t* positions,
                             const RopeFreq& fr, float scale, hipStream_t s,
                             const TimedLaunch& tl) {
-  if (dt == F32)
-    return D == 64 ? prefill_f32_t<64, SRC>(q, ks, out, B, Hq, Hkv, S, positions, fr, scale, s, tl)
-                   : prefill_f32_t<128, SRC>(q, ks, out, B, Hq, Hkv, S, positions, fr, scale, s,
-                                             tl);
-  return D == 64 ? prefill_bf16_t<64, SRC>(q, ks, out, B, Hq, Hkv, S, positions, fr, scale, s, tl)
-                 : prefill_bf16_t<128, SRC>(q, ks, out, B, Hq, Hkv, S, positions, fr, scale, s,
-                                            tl);
+  return fr.half ? prefill_dispatch_t<SRC, 1>(dt, D, q, ks, out, B, Hq, Hkv, S, positions, fr,
+                                              scale, s, tl)
+                 : prefill_dispatch_t<SRC, 0>(dt, D, q, ks, out, B, Hq, Hkv, S, positions, fr,
+                                              scale, s, tl);
 }
 
 }  // namespace
