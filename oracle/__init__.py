@@ -23,7 +23,7 @@ Pages cited (titles as published):
               (understanding LLM inference engines through Nano-vLLM, part 2)
 
 Pin status of each function (what fixes it other than itself) is listed in
-``oracle/attention.py``.  One convention is *parity unpinned* by any check
+``oracle/attention.py`` and, for the INT8 cache, ``oracle/int8_cache.py``.  One convention is *parity unpinned* by any check
 on synthetic data and is fixed only by the text: the RoPE pair layout
 (adjacent pairs (2i, 2i+1), [Intuition] §4) and the GQA head grouping
 (contiguous groups, hk = hq // (Hq/Hkv)).
@@ -40,4 +40,12 @@ from .attention import (  # noqa: F401
     attn_decode,
     attn_prefill_cached,
     paged_slot,
+)
+from .int8_cache import (  # noqa: F401
+    int8_scale,
+    int8_quantize,
+    int8_dequantize,
+    int8_calibrate,
+    kv_cache_append_int8,
+    attn_decode_int8,
 )
