@@ -191,6 +191,61 @@ def measure_chunked(car, W, dev, stream, new_event, iters: int = 10) -> dict:
     return out
 
 
+def measure_int8_decode(car, W, dev, stream, new_event, iters: int = 20) -> dict:
+    """The two decode workloads with INT8 caches of the same shapes (codes in
+    [-127, 127], per-(KV head, channel) fp32 scales): event times of the
+    decode split kernel and of the whole call, and KV GB/s at one byte per
+    cached element."""
+    import torch
+    out = {}
+    specs = (("contiguous", dict(B=32, Hq=32, Hkv=32, lens=W.contiguous_decode_lens(),
+                                 seed=W.BASE_SEED + 3, paged=False, max_seq=4096)),
+             ("paged_gqa", dict(B=64, Hq=32, Hkv=8, lens=W.paged_decode_lens(),
+                                seed=W.BASE_SEED + 4, paged=True, blocks_per_seq=513)))
+    for name, sp in specs:
+        extra = {k: sp[k] for k in ("max_seq", "blocks_per_seq") if k in sp}
+        case = W.int8_decode_case(f"int8_{name}", sp["B"], sp["Hq"], sp["Hkv"], 128,
+                                  torch.bfloat16, sp["lens"], sp["seed"], dev,
+                                  paged=sp["paged"], **extra)
+        cache = car.KVCache(case.cache_k, case.cache_v, case.block_table,
+                            k_scale=case.k_scale, v_scale=case.v_scale)
+        o = torch.empty_like(case.q)
+        ws = torch.empty(car.decode_workspace_bytes(case.B, case.Hq, 128, case.max_seq_len),
+                         dtype=torch.uint8, device=dev)
+
+        def call():
+            car.attn_decode(case.q, case.k_new, case.v_new, case.seq_lens, cache,
+                            case.max_seq_len, case.theta, case.scale, out=o, workspace=ws)
+        for _ in range(3):
+            call()
+        pairs_k = [(new_event(), new_event()) for _ in range(iters)]
+        pairs_c = [(new_event(), new_event()) for _ in range(iters)]
+        for i in range(iters):
+            car.set_timing_events(*pairs_k[i])
+            pairs_c[i][0].record(stream)
+            call()
+            pairs_c[i][1].record(stream)
+            car.set_timing_events(None, None)
+        torch.cuda.synchronize()
+        if not torch.isfinite(o.float()).all():
+            raise RuntimeError(f"non-finite output in int8 decode ({name})")
+        kms = sum(a.elapsed_time(b) for a, b in pairs_k) / iters
+        cms = sum(a.elapsed_time(b) for a, b in pairs_c) / iters
+        kv = decode_kv_bytes(case.lens_host, case.Hkv, 128, 1)
+        out[f"int8_decode_{name}"] = {
+            "workload": (f"B={case.B},Hq={case.Hq},Hkv={case.Hkv},D=128,bf16 q/k/v,"
+                         + ("paged 16-token blocks" if sp["paged"] else "contiguous 4096")
+                         + ", int8 cache with per-(head, channel) scales"),
+            "kernel_ms": kms, "call_ms": cms,
+            "GBps_kernel": kv / (kms * 1e-3) / 1e9, "GBps_call": kv / (cms * 1e-3) / 1e9,
+            "hbm_frac_kernel": kv / (kms * 1e-3) / 1e9 / PEAK_HBM_GBPS,
+            "tokens_per_s": case.B / (cms * 1e-3),
+            "per_launch": f"{kv} bytes (sum_b L_b * Hkv * D * 2 (K,V) * 1 B)"}
+        del case, cache, o, ws
+        torch.cuda.synchronize()
+    return out
+
+
 def main(argv=None) -> int:
     args = parse_args(argv)
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -289,6 +344,7 @@ def main(argv=None) -> int:
     extras = {}
     if args.only is None and not args.no_extras:
         extras = measure_chunked(car, W, dev, stream, new_event)
+        extras.update(measure_int8_decode(car, W, dev, stream, new_event))
 
     # ---------------- figures ----------------
     kernels = {}

@@ -7,8 +7,9 @@ passes raw device pointers and torch's current HIP stream.  There is no CPU
 fallback: importing fails if the library has not been built.
 
 Entry points (same names as the C ABI without the ``car_`` prefix):
-``rope_apply``, ``kv_cache_append``, ``attn_prefill``, ``attn_decode``,
-plus ``KVCache``, the workspace size queries and ``set_timing_events``.
+``rope_apply``, ``kv_cache_append``, ``kv_int8_calibrate``, ``attn_prefill``,
+``attn_prefill_cached``, ``attn_decode``, plus ``KVCache`` (native or INT8
+elements), the workspace size queries and ``set_timing_events``.
 """
 
 from __future__ import annotations
@@ -22,7 +23,7 @@ import torch
 
 __all__ = [
     "CarError", "KVCache", "rope_apply", "kv_cache_append", "attn_prefill", "attn_decode",
-    "attn_prefill_cached",
+    "attn_prefill_cached", "kv_int8_calibrate",
     "prefill_workspace_bytes", "decode_workspace_bytes", "set_timing_events", "library_path",
 ]
 
@@ -58,7 +59,13 @@ class _CarKVCache(ctypes.Structure):
         ("num_blocks", ctypes.c_int32),
         ("block_size", ctypes.c_int32),
         ("max_blocks_per_seq", ctypes.c_int32),
+        ("format", ctypes.c_int32),
+        ("k_scale", ctypes.c_void_p),
+        ("v_scale", ctypes.c_void_p),
     ]
+
+
+CACHE_NATIVE, CACHE_INT8 = 0, 1
 
 
 def _load() -> ctypes.CDLL:
@@ -76,6 +83,8 @@ def _load() -> ctypes.CDLL:
     sigs = {
         "car_rope_apply": (i32, [vp, i32, i32, i32, i32, i32, vp, f32, i32, vp]),
         "car_kv_cache_append": (i32, [cache_p, i32, vp, vp, i32, i32, i32, i32, vp, vp]),
+        "car_kv_int8_calibrate": (i32, [vp, vp, i32, i32, i32, i32, i32, vp, f32, i32, vp, vp,
+                                        vp]),
         "car_attn_prefill_workspace_bytes": (sz, [i32, i32, i32, i32, i32, cache_p]),
         "car_attn_prefill": (i32, [vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, vp, f32, i32,
                                    f32, cache_p, vp, sz, vp]),
@@ -155,10 +164,15 @@ class KVCache:
     Contiguous: ``k`` and ``v`` are [B, Hkv, max_seq, D].
     Paged: ``k`` and ``v`` are pools [num_blocks, Hkv, 16, D] and
     ``block_table`` is int32 [B, max_blocks_per_seq].
+    Native elements are the calls' dtype (float32 or bfloat16).  INT8: ``k``
+    and ``v`` are torch.int8 codes and ``k_scale``, ``v_scale`` are float32
+    [Hkv, D] (value = code * scale; see ``kv_int8_calibrate``).
     """
 
     def __init__(self, k: torch.Tensor, v: torch.Tensor,
-                 block_table: Optional[torch.Tensor] = None):
+                 block_table: Optional[torch.Tensor] = None,
+                 k_scale: Optional[torch.Tensor] = None,
+                 v_scale: Optional[torch.Tensor] = None):
         _need(k, "cache k", dim=4)
         _need(v, "cache v", dtype=k.dtype, dim=4, device=k.device)
         if k.shape != v.shape:
@@ -169,10 +183,28 @@ class KVCache:
             if k.shape[2] != 16:
                 raise ValueError("paged cache blocks must hold 16 tokens")
         self.Hkv, self.D = k.shape[1], k.shape[3]
+        self.int8 = k.dtype == torch.int8
+        if self.int8:
+            if k_scale is None or v_scale is None:
+                raise ValueError("an int8 cache needs k_scale and v_scale")
+            for s, name in ((k_scale, "k_scale"), (v_scale, "v_scale")):
+                _need(s, name, dtype=torch.float32, dim=2, device=k.device)
+                if tuple(s.shape) != (self.Hkv, self.D):
+                    raise ValueError(f"{name} must be [Hkv, D]")
+        elif k_scale is not None or v_scale is not None:
+            raise ValueError("scales are only used with an int8 cache")
+        elif k.dtype not in _DTYPES:
+            raise ValueError(f"unsupported cache dtype {k.dtype}")
+        self.k_scale, self.v_scale = k_scale, v_scale
 
     @property
     def paged(self) -> bool:
         return self.block_table is not None
+
+    def accepts(self, t: torch.Tensor) -> bool:
+        """Whether a call in t's dtype may use this cache."""
+        return t.device == self.k.device and (
+            t.dtype in _DTYPES if self.int8 else t.dtype == self.k.dtype)
 
     def check_batch(self, B: int) -> None:
         """The cache must hold (or map) at least B sequences."""
@@ -197,6 +229,11 @@ class KVCache:
         else:
             c.block_table = None
             c.max_seq = self.k.shape[2]
+        if self.int8:
+            c.format = CACHE_INT8
+            c.k_scale, c.v_scale = self.k_scale.data_ptr(), self.v_scale.data_ptr()
+        else:
+            c.format = CACHE_NATIVE
         return c
 
 
@@ -232,9 +269,12 @@ def rope_apply(x: torch.Tensor, positions: torch.Tensor, theta: float = 10000.0,
 
 def kv_cache_append(cache: KVCache, k: torch.Tensor, v: torch.Tensor,
                     positions: torch.Tensor) -> None:
-    """Store rotated keys k and values v [B, Hkv, S, D] at cache index == position."""
-    _need(k, "k", dtype=cache.k.dtype, dim=4, device=cache.k.device)
-    _need(v, "v", dtype=cache.k.dtype, dim=4, device=cache.k.device)
+    """Store rotated keys k and values v [B, Hkv, S, D] at cache index == position
+    (as int8 codes in an int8 cache)."""
+    _need(k, "k", dim=4, device=cache.k.device)
+    _need(v, "v", dtype=k.dtype, dim=4, device=cache.k.device)
+    if not cache.accepts(k):
+        raise ValueError("k/v dtype does not match the cache")
     if k.shape != v.shape:
         raise ValueError("k and v must have the same shape")
     B, Hkv, S, D = k.shape
@@ -247,6 +287,29 @@ def kv_cache_append(cache: KVCache, k: torch.Tensor, v: torch.Tensor,
     c = cache._c()
     _check(_lib.car_kv_cache_append(ctypes.byref(c), _dtype_code(k), _ptr(k), _ptr(v), B, Hkv,
                                     S, D, _ptr(positions), _stream(k)), "kv_cache_append")
+
+
+def kv_int8_calibrate(k: torch.Tensor, v: torch.Tensor, positions: torch.Tensor,
+                      theta: float = 10000.0, rope_pairing: str = "adjacent"):
+    """Per-(KV head, channel) INT8 scales of a calibration batch (see
+    car_kv_int8_calibrate): absmax over every (b, s) of the keys rotated at
+    ``positions`` and of the values, divided by 127.  k, v [B, Hkv, S, D]
+    (k not rotated); positions int32 [B, S].  Returns (k_scale, v_scale),
+    float32 [Hkv, D]."""
+    _need(k, "k", dim=4)
+    _need(v, "v", dtype=k.dtype, dim=4, device=k.device)
+    if k.shape != v.shape:
+        raise ValueError("k and v must have the same shape")
+    B, Hkv, S, D = k.shape
+    _need(positions, "positions", dtype=torch.int32, dim=2, device=k.device)
+    if tuple(positions.shape) != (B, S):
+        raise ValueError("positions must be [B, S]")
+    ks = torch.empty((Hkv, D), dtype=torch.float32, device=k.device)
+    vs = torch.empty((Hkv, D), dtype=torch.float32, device=k.device)
+    _check(_lib.car_kv_int8_calibrate(_ptr(k), _ptr(v), _dtype_code(k), B, Hkv, S, D,
+                                      _ptr(positions), float(theta), _pairing(rope_pairing),
+                                      _ptr(ks), _ptr(vs), _stream(k)), "kv_int8_calibrate")
+    return ks, vs
 
 
 def prefill_workspace_bytes(dtype: torch.dtype, B: int, Hkv: int, S: int, D: int) -> int:
@@ -296,7 +359,7 @@ def attn_prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, positions: t
         scale = 1.0 / math.sqrt(D)
     c = None
     if cache is not None:
-        if cache.k.dtype != q.dtype or cache.k.device != q.device:
+        if not cache.accepts(q):
             raise ValueError("cache dtype/device must match q")
         if cache.Hkv != Hkv or cache.D != D:
             raise ValueError("cache heads or head dim do not match k")
@@ -342,7 +405,7 @@ def attn_prefill_cached(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
         _need(chunk_lens, "chunk_lens", dtype=torch.int32, dim=1, device=q.device)
         if chunk_lens.shape[0] != B:
             raise ValueError("chunk_lens must be [B]")
-    if cache.k.dtype != q.dtype or cache.k.device != q.device:
+    if not cache.accepts(q):
         raise ValueError("cache dtype/device must match q")
     if cache.Hkv != Hkv or cache.D != D:
         raise ValueError("cache heads or head dim do not match k")
@@ -386,7 +449,7 @@ def attn_decode(q: torch.Tensor, k_new: torch.Tensor, v_new: torch.Tensor,
     _need(seq_lens, "seq_lens", dtype=torch.int32, dim=1, device=q.device)
     if seq_lens.shape[0] != B:
         raise ValueError("seq_lens must be [B]")
-    if cache.k.dtype != q.dtype or cache.k.device != q.device:
+    if not cache.accepts(q):
         raise ValueError("cache dtype/device must match q")
     if cache.Hkv != Hkv or cache.D != D:
         raise ValueError("cache heads or head dim do not match k_new")

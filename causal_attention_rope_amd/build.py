@@ -24,7 +24,7 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libcar.so")
 
-SOURCES = ["rope_cache.hip", "decode.hip", "prefill.hip", "car_api.cpp"]
+SOURCES = ["rope_cache.hip", "decode.hip", "decode_i8.hip", "prefill.hip", "car_api.cpp"]
 
 ARCH = "gfx950"
 FLAGS = [

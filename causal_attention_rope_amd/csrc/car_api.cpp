@@ -51,10 +51,18 @@ RopeFreq make_freq(int D, float theta, car_rope_pairing pairing) {
 car_status check_cache(const car_kv_cache* c, CacheArgs* out, int64_t* capacity) {
   if (c == nullptr || c->k == nullptr || c->v == nullptr) return CAR_ERR_INVALID_ARGUMENT;
   if (!aligned16(c->k) || !aligned16(c->v)) return CAR_ERR_INVALID_ARGUMENT;
+  if (c->format != CAR_CACHE_NATIVE && c->format != CAR_CACHE_INT8) return CAR_ERR_UNSUPPORTED;
   CacheArgs a{};
   a.k = c->k;
   a.v = c->v;
   a.table = c->block_table;
+  if (c->format == CAR_CACHE_INT8) {
+    if (c->k_scale == nullptr || c->v_scale == nullptr || !aligned16(c->k_scale) ||
+        !aligned16(c->v_scale))
+      return CAR_ERR_INVALID_ARGUMENT;
+    a.k_scale = c->k_scale;
+    a.v_scale = c->v_scale;
+  }
   if (c->block_table != nullptr) {
     if (c->block_size != 16) return CAR_ERR_UNSUPPORTED;
     if (c->num_blocks <= 0 || c->max_blocks_per_seq <= 0) return CAR_ERR_INVALID_ARGUMENT;
@@ -76,6 +84,8 @@ int64_t prefill_ws_bytes(car_dtype dt, int B, int Hkv, int S, int D) {
 }
 
 int decode_nsplit(int max_seq_len) { return (max_seq_len + DECODE_SPLIT - 1) / DECODE_SPLIT; }
+
+bool is_int8(const car_kv_cache* c) { return c != nullptr && c->format == CAR_CACHE_INT8; }
 
 }  // namespace
 
@@ -124,8 +134,27 @@ car_status car_kv_cache_append(const car_kv_cache* cache, car_dtype dtype, const
   const car_status cs = check_cache(cache, &c, &cap);
   if (cs != CAR_OK) return cs;
   return from_hip(launch_kv_append(dtype == CAR_DTYPE_F32 ? F32 : BF16, D,
-                                   cache->block_table != nullptr, c, k, v, B, Hkv, S, positions,
-                                   stream));
+                                   cache->block_table != nullptr, is_int8(cache), c, k, v, B, Hkv,
+                                   S, positions, stream));
+}
+
+car_status car_kv_int8_calibrate(const void* k, const void* v, car_dtype dtype, int B, int Hkv,
+                                 int S, int D, const int32_t* positions, float theta,
+                                 car_rope_pairing pairing, float* k_scale, float* v_scale,
+                                 hipStream_t stream) {
+  if (!dtype_ok(dtype) || !head_dim_ok(D) || !pairing_ok(pairing)) return CAR_ERR_UNSUPPORTED;
+  if (B < 0 || Hkv < 0 || S < 0 || !positive_finite(theta)) return CAR_ERR_INVALID_ARGUMENT;
+  if (Hkv == 0) return CAR_OK;
+  if (k_scale == nullptr || v_scale == nullptr || !aligned16(k_scale) || !aligned16(v_scale))
+    return CAR_ERR_INVALID_ARGUMENT;
+  if ((int64_t)B * S > 0) {
+    if (k == nullptr || v == nullptr || positions == nullptr || !aligned16(k) || !aligned16(v))
+      return CAR_ERR_INVALID_ARGUMENT;
+  }
+  if (Hkv > 65535) return CAR_ERR_UNSUPPORTED;  // one grid row per KV head
+  return from_hip(launch_int8_calibrate(dtype == CAR_DTYPE_F32 ? F32 : BF16, D, k, v, B, Hkv, S,
+                                        positions, make_freq(D, theta, pairing), k_scale,
+                                        v_scale, stream));
 }
 
 size_t car_attn_prefill_workspace_bytes(car_dtype dtype, int B, int Hkv, int S, int D,
@@ -164,8 +193,8 @@ car_status car_attn_prefill(const void* q, const void* k, const void* v, void* o
   const Dtype dt = dtype == CAR_DTYPE_F32 ? F32 : BF16;
   const RopeFreq fr = make_freq(D, theta, pairing);
   hipError_t e = launch_prefill_prep(dt, D, cache != nullptr && cache->block_table != nullptr,
-                                     cache != nullptr ? &c : nullptr, k, v, workspace, B, Hkv, S,
-                                     positions, fr, stream);
+                                     is_int8(cache), cache != nullptr ? &c : nullptr, k, v,
+                                     workspace, B, Hkv, S, positions, fr, stream);
   if (e != hipSuccess) return CAR_ERR_HIP;
   return from_hip(launch_prefill_attention(dt, D, q, workspace, v, out, B, Hq, Hkv, S,
                                            positions, fr, scale, stream, timing()));
@@ -191,6 +220,7 @@ car_status car_attn_prefill_cached(const void* q, const void* k, const void* v, 
   int64_t cap = 0;
   const car_status cs = check_cache(cache, &c, &cap);
   if (cs != CAR_OK) return cs;
+  if (is_int8(cache)) return CAR_ERR_UNSUPPORTED;  // the chunk kernel reads a native cache
   // every sequence's chunk fits: S tokens, or up to S with chunk_lens
   if (max_seq_len < (chunk_lens == nullptr ? S : 1) || max_seq_len > cap)
     return CAR_ERR_INVALID_ARGUMENT;
@@ -244,11 +274,16 @@ car_status car_attn_decode(const void* q, const void* k_new, const void* v_new, 
   const size_t need = car_attn_decode_workspace_bytes(B, Hq, D, max_seq_len);
   if (workspace == nullptr || !aligned16(workspace) || workspace_bytes < need)
     return CAR_ERR_WORKSPACE;
-  return from_hip(launch_decode(dtype == CAR_DTYPE_F32 ? F32 : BF16, D, group,
-                                cache->block_table != nullptr, q, k_new, v_new, out, B, Hq, Hkv,
-                                seq_lens, max_seq_len, c,
-                                static_cast<float*>(workspace), make_freq(D, theta, pairing), scale,
-                                stream, timing()));
+  const Dtype dt = dtype == CAR_DTYPE_F32 ? F32 : BF16;
+  const bool paged = cache->block_table != nullptr;
+  float* part = static_cast<float*>(workspace);
+  const RopeFreq fr = make_freq(D, theta, pairing);
+  if (is_int8(cache))
+    return from_hip(launch_decode_i8(dt, D, group, paged, q, k_new, v_new, out, B, Hq, Hkv,
+                                     seq_lens, max_seq_len, c, part, fr, scale, stream,
+                                     timing()));
+  return from_hip(launch_decode(dt, D, group, paged, q, k_new, v_new, out, B, Hq, Hkv, seq_lens,
+                                max_seq_len, c, part, fr, scale, stream, timing()));
 }
 
 }  // extern "C"

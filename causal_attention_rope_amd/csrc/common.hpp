@@ -204,6 +204,48 @@ __device__ __forceinline__ void rope_apply_prepared(float (&f)[N], const T* row,
 }
 
 // ---------------------------------------------------------------------------
+// INT8 cache codes ([Scratch] "从零手搓AI推理引擎" §2.2 and §5.3: a channel's
+// scale is its absolute maximum over 127; a value is divided by its scale and
+// rounded to store it, and multiplied by it to read it back).
+// ---------------------------------------------------------------------------
+// x / s as one IEEE fp32 division, rounded half away from zero, clamped to the
+// symmetric range [-127, 127]; 0 when s == 0.  Returns the code's byte.
+__device__ __forceinline__ uint32_t int8_code(float x, float s) {
+  if (s == 0.f) return 0u;
+  const float r = fminf(fmaxf(roundf(__fdiv_rn(x, s)), -127.f), 127.f);
+  return (uint32_t)(int32_t)r & 0xffu;
+}
+
+// Codes of f[0..N) with the scales s[0..N) (16-byte aligned), four to a word,
+// element 4w + j in byte j of word w (memory order).
+template <int N>
+__device__ __forceinline__ void int8_codes(const float (&f)[N], const float* s,
+                                           uint32_t (&w)[N / 4]) {
+#pragma unroll
+  for (int i = 0; i < N / 4; ++i) {
+    const float4 sc = *reinterpret_cast<const float4*>(s + 4 * i);
+    w[i] = int8_code(f[4 * i], sc.x) | (int8_code(f[4 * i + 1], sc.y) << 8) |
+           (int8_code(f[4 * i + 2], sc.z) << 16) | (int8_code(f[4 * i + 3], sc.w) << 24);
+  }
+}
+
+// Stores the N codes of f (N = 4, 8 or 16 bytes at p, aligned to N).
+template <int N>
+__device__ __forceinline__ void store_int8(int8_t* p, const float (&f)[N], const float* s) {
+  uint32_t w[N / 4];
+  int8_codes<N>(f, s, w);
+  if constexpr (N == 4) *reinterpret_cast<uint32_t*>(p) = w[0];
+  else if constexpr (N == 8) *reinterpret_cast<uint2*>(p) = make_uint2(w[0], w[1]);
+  else *reinterpret_cast<uint4*>(p) = make_uint4(w[0], w[1], w[2], w[3]);
+}
+
+// Code j (0..3) of a word of four codes as fp32 (a sign-extended byte select
+// folds into one conversion instruction).
+__device__ __forceinline__ float int8_elem(uint32_t w, int j) {
+  return (float)(int8_t)(w >> (8 * j));
+}
+
+// ---------------------------------------------------------------------------
 // Cache addressing: element offset of row (sequence b, head hk, token t).
 // ---------------------------------------------------------------------------
 template <bool PAGED>

@@ -25,7 +25,7 @@
 // the cache, and uses the new row from registers for its own score.
 #include <math.h>
 
-#include "common.hpp"
+#include "decode_common.hpp"
 
 namespace car {
 
@@ -53,7 +53,6 @@ __device__ __forceinline__ uint32_t perm_hi(uint32_t a, uint32_t b) {
 }
 
 constexpr uint32_t kOnePair = 0x3F803F80u;  // (1.0, 1.0) in bf16
-constexpr float kRescaleLog2 = 8.f;          // largest exp2 argument allowed before rescaling
 
 // Per-lane geometry of the decode split kernel.  A lane holds C = 2 chunks
 // of 16 bytes of a cache row, chunks c*LPR + lane%LPR for c < C, so LPR =
@@ -408,74 +407,6 @@ __attribute__((amdgpu_waves_per_eu(G <= 4 ? 4 : 2))) void decode_split_kernel(
     if (d == 0) {
       dst[0] = M;
       dst[1] = l;
-    }
-  }
-}
-
-// One wave per (sequence, query head): merge the partials of the splits that
-// hold tokens 0..L (log-sum-exp rule) and write the normalised output.  Lane s
-// reads split s's maximum and sum; the accumulators are read split by split,
-// 4 splits at a time.
-template <typename T, int D>
-__global__ __launch_bounds__(64) void decode_combine_kernel(const float* __restrict__ part,
-                                                            const int32_t* __restrict__ seq_lens,
-                                                            T* __restrict__ out, int Hq,
-                                                            int nsplit, int split_tokens,
-                                                            int last_slot) {
-  constexpr int PW = decode_partial_words(D);
-  constexpr int E = D / 64;
-  const int bh = blockIdx.x;
-  const int b = bh / Hq;
-  const int lane = threadIdx.x;
-  const int L = min(max(seq_lens[b], 0), last_slot);
-  const int n = min(L / split_tokens + 1, nsplit);
-  const float* p = part + (int64_t)bh * nsplit * PW;
-
-  // max and weighted sum over splits, 64 splits per pass
-  float M = -INFINITY;
-  for (int s = lane; s < n; s += 64) M = fmaxf(M, p[(int64_t)s * PW]);
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) M = fmaxf(M, __shfl_xor(M, o));
-  float l = 0.f;
-  for (int s = lane; s < n; s += 64) l += fast_exp2(p[(int64_t)s * PW] - M) * p[(int64_t)s * PW + 1];
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) l += __shfl_xor(l, o);
-
-  float a[E];
-#pragma unroll
-  for (int e = 0; e < E; ++e) a[e] = 0.f;
-  int s = 0;
-  for (; s + 4 <= n; s += 4) {
-    float w[4], v[4][E];
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const float* ps = p + (int64_t)(s + u) * PW;
-      w[u] = ps[0];
-#pragma unroll
-      for (int e = 0; e < E; ++e) v[u][e] = ps[4 + lane + 64 * e];
-    }
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const float f = fast_exp2(w[u] - M);
-#pragma unroll
-      for (int e = 0; e < E; ++e) a[e] = fmaf(f, v[u][e], a[e]);
-    }
-  }
-  for (; s < n; ++s) {
-    const float* ps = p + (int64_t)s * PW;
-    const float f = fast_exp2(ps[0] - M);
-#pragma unroll
-    for (int e = 0; e < E; ++e) a[e] = fmaf(f, ps[4 + lane + 64 * e], a[e]);
-  }
-  const float inv = 1.f / l;
-#pragma unroll
-  for (int e = 0; e < E; ++e) {
-    const float o = a[e] * inv;
-    if constexpr (sizeof(T) == 4) {
-      out[(int64_t)bh * D + lane + 64 * e] = o;
-    } else {
-      const __bf16 h = (__bf16)o;
-      out[(int64_t)bh * D + lane + 64 * e] = __builtin_bit_cast(uint16_t, h);
     }
   }
 }

@@ -1,0 +1,403 @@
+// Decode attention over an INT8 KV cache.
+//
+// What is computed: the decode step of [Guide] ("手写LLM推理引擎：从黑盒到白盒的底层实现指南")
+// §2.5 and [Scratch] ("从零手搓AI推理引擎") §3.2-§3.3 -- q and k_new rotated at
+// position L, the new key and value appended at cache index L, attention over
+// indices 0..L -- with a cache whose rows are int8 codes and whose value is
+// code * scale, one fp32 scale per (KV head, channel) ([Intuition]
+// ("手写LLM推理引擎：重建对Tokenizer、KV Cache与RoPE的底层直觉") §2: the cache
+// compressed from 16-bit floats to INT8; [Scratch] §2.2 and §5.3: per-channel
+// absmax/127 scales, divide and round to store, multiply back to read).  The
+// new key and value are quantized when appended and read in that form, like
+// every other cached token.
+//
+// How it maps to MI355X.  The step streams every cached row once, now at one
+// byte per element, so it stays bound by HBM bandwidth at half the bytes of a
+// bf16 cache.  Because the scales are per channel they factor out of both
+// contractions: q . (code_k * s_k) = (q * s_k) . code_k, folded into the query
+// once per workgroup, and sum_j p_j (code_v * s_v) = s_v * sum_j p_j code_v,
+// applied to the partial result once.  The inner loop is then one
+// int8 -> fp32 conversion per element (a sign-extended byte select folds into
+// the conversion instruction) and one fp32 FMA per element and query head;
+// no dequantized copy of a row is ever formed.  Lanes hold E = 16 codes of a
+// row (one 16-byte load; 8 codes with 8 query heads per KV head, to bound the
+// registers of G query rows and accumulators), so LPR = D/E lanes cover a row
+// and a load instruction moves 64/LPR rows.  The work split (splits of the
+// sequence per workgroup, grid order, the online softmax with a lazy rescale,
+// merging across rows, waves and workgroups) is that of the decode over a
+// native cache.
+#include <math.h>
+
+#include "decode_common.hpp"
+
+namespace car {
+
+namespace {
+
+template <int G>
+constexpr int i8_waves() { return G > 1 ? 8 : 4; }
+
+template <int D, int G, int SPLIT>
+struct I8Geom {
+  static constexpr int WAVES = i8_waves<G>();
+  static constexpr int TPW = SPLIT / WAVES;  // tokens per wave
+  static constexpr int E = G >= 8 ? 8 : 16;  // codes per lane per row (bytes per load)
+  static constexpr int LPR = D / E;          // lanes per cache row
+  static constexpr int NG = 64 / LPR;        // rows per load instruction
+  static constexpr int STEPS = TPW / NG;
+  static constexpr int R = STEPS < 2 ? STEPS : 2;  // row steps per round
+  static constexpr int ROUNDS = STEPS / R;
+  static constexpr int W = E / 4;  // 32-bit words per lane per row
+  static_assert(SPLIT % DECODE_SPLIT == 0 && TPW % 64 == 0, "whole 16-token blocks per wave");
+  static_assert(LPR == 4 || LPR == 8 || LPR == 16 || LPR == 32, "lanes per row");
+  static_assert(NG <= 16 && 16 % NG == 0, "a row step stays inside one 16-token block");
+  static_assert(R % 2 == 0 && ROUNDS * R == STEPS, "rounds must tile the wave's tokens");
+  static_assert(ROUNDS == 1 || ROUNDS % 2 == 0, "rounds are consumed in pairs");
+};
+
+template <int W> struct ChunkOf;
+template <> struct ChunkOf<2> { typedef uint32_t type __attribute__((ext_vector_type(2))); };
+template <> struct ChunkOf<4> { typedef uint32_t type __attribute__((ext_vector_type(4))); };
+
+// Tokens per workgroup, as for the native cache: 256 with one query head per
+// KV head, 1024 with several.
+template <int G>
+constexpr int i8_split_tokens() { return G == 1 ? DECODE_SPLIT : 4 * DECODE_SPLIT; }
+
+template <typename T, int D, int G, bool PAGED, int SPLIT, bool HALF>
+__global__ __launch_bounds__(64 * i8_waves<G>())
+__attribute__((amdgpu_waves_per_eu(G == 1 ? 4 : 2))) void decode_i8_split_kernel(
+    const T* __restrict__ q, const T* __restrict__ k_new, const T* __restrict__ v_new,
+    const int32_t* __restrict__ seq_lens, CacheArgs c, float* __restrict__ part, int Hkv,
+    int nsplit, RopeFreq fr, float qk_scale) {
+  using Gm = I8Geom<D, G, SPLIT>;
+  using Chunk = typename ChunkOf<Gm::W>::type;
+  constexpr int E = Gm::E, W = Gm::W, LPR = Gm::LPR, NG = Gm::NG, R = Gm::R,
+                ROUNDS = Gm::ROUNDS, TPW = Gm::TPW;
+  constexpr int NT = Vec16<T>::N;  // input elements per 16-byte load
+  constexpr int SUB = E / NT;      // input loads per lane chunk
+  constexpr int PW = decode_partial_words(D);
+  constexpr int kWaves = Gm::WAVES, kThreads = 64 * kWaves;
+  __shared__ float sm_acc[kWaves][G][D];
+  __shared__ float sm_ml[kWaves][G][2];
+
+  // Grid order as for the native cache: (sequence, KV head) fastest, splits
+  // aligned to the last row so that the short last splits run last.
+  const int hk = blockIdx.x % Hkv, b = blockIdx.x / Hkv;
+  const int Hq = Hkv * G;
+  const int L = min(max(seq_lens[b], 0), cache_last_slot<PAGED>(c));
+  const int nsb = min(L / SPLIT + 1, nsplit);
+  const int split = (int)blockIdx.y - (nsplit - nsb);
+  if (split < 0) return;  // uniform over the workgroup
+  const int t0 = split * SPLIT;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int grp = lane / LPR;             // row of the step
+  const int col = (lane % LPR) * E;       // first channel of the lane's codes
+  const int tw = t0 + wave * TPW;         // first token of this wave
+  const float* ks = c.k_scale + (int64_t)hk * D + col;
+
+  // Query heads rotated at L, times the softmax scale (base 2) and the key
+  // scale of each channel.  One set of angles serves all heads and k_new.
+  RopeChunk<NT> rope[SUB];
+#pragma unroll
+  for (int j = 0; j < SUB; ++j) rope[j] = rope_prepare<NT, HALF>(L, col + j * NT, D, fr);
+  float kscale[E];
+#pragma unroll
+  for (int e = 0; e < E; e += 4) {
+    const float4 s4 = *reinterpret_cast<const float4*>(ks + e);
+    kscale[e] = s4.x; kscale[e + 1] = s4.y; kscale[e + 2] = s4.z; kscale[e + 3] = s4.w;
+  }
+  float qf[G][E];
+#pragma unroll
+  for (int g = 0; g < G; ++g) {
+    const T* qrow = q + ((int64_t)b * Hq + hk * G + g) * D;
+#pragma unroll
+    for (int j = 0; j < SUB; ++j) {
+      float f[NT];
+      load16<T>(qrow + col + j * NT, f);
+      rope_apply_prepared<T, NT, HALF>(f, qrow, D, rope[j], fr);
+#pragma unroll
+      for (int e = 0; e < NT; ++e) qf[g][j * NT + e] = f[e] * qk_scale * kscale[j * NT + e];
+    }
+  }
+
+  // The new token (index L): codes of the rotated key and of the value,
+  // stored by the split that holds L and used from registers for token L.
+  int8_t* const Kc = static_cast<int8_t*>(c.k);
+  int8_t* const Vc = static_cast<int8_t*>(c.v);
+  Chunk kn, vn;
+#pragma unroll
+  for (int w = 0; w < W; ++w) kn[w] = vn[w] = 0u;
+  if (L < t0 + SPLIT) {
+    const int64_t src = ((int64_t)b * Hkv + hk) * D;
+    const float* vs = c.v_scale + (int64_t)hk * D + col;
+#pragma unroll
+    for (int j = 0; j < SUB; ++j) {
+      float f[NT], g[NT];
+      load16<T>(k_new + src + col + j * NT, f);
+      rope_apply_prepared<T, NT, HALF>(f, k_new + src, D, rope[j], fr);
+      load16<T>(v_new + src + col + j * NT, g);
+      uint32_t kw[NT / 4], vw[NT / 4];
+      int8_codes<NT>(f, ks + j * NT, kw);
+      int8_codes<NT>(g, vs + j * NT, vw);
+#pragma unroll
+      for (int w = 0; w < NT / 4; ++w) {
+        kn[j * NT / 4 + w] = kw[w];
+        vn[j * NT / 4 + w] = vw[w];
+      }
+    }
+    if (wave == 0 && grp == 0) {
+      const int64_t dst = cache_row<PAGED>(c, b, hk, Hkv, L) * D + col;
+      *reinterpret_cast<Chunk*>(Kc + dst) = kn;
+      *reinterpret_cast<Chunk*>(Vc + dst) = vn;
+    }
+  }
+
+  float m_run[G], l_run[G], acc[G][E];
+#pragma unroll
+  for (int g = 0; g < G; ++g) {
+    m_run[g] = -INFINITY;
+    l_run[g] = 0.f;
+#pragma unroll
+    for (int e = 0; e < E; ++e) acc[g][e] = 0.f;
+  }
+
+  if (tw <= L) {  // uniform per wave: this wave holds at least one token
+    constexpr int NBLK = TPW / 16;
+    static_assert(NBLK <= 64, "one block id per lane");
+    int myblk = 0;
+    if constexpr (PAGED) {
+      const int32_t* trow = c.table + (int64_t)b * c.mbps;
+      if (lane < NBLK)
+        myblk = min(max(trow[min((tw >> 4) + lane, L >> 4)], 0), c.num_blocks - 1);
+    }
+
+    Chunk kb[2][R], vb[2][R];
+    // Loads of round r into register buffer BUF.  Rows at or past L are only
+    // ever replaced (consume), so they just stay inside the cache: paged
+    // block ids are clamped to the sequence's last block, contiguous rows to L.
+    const int64_t cbase = PAGED ? 0 : ((int64_t)b * Hkv + hk) * c.max_seq + tw;
+    auto issue = [&](int r, auto BUF) {
+      constexpr int buf = decltype(BUF)::value;
+#pragma unroll
+      for (int st = 0; st < R; ++st) {
+        const int x = r * R + st;
+        int64_t row0;
+        int lrow = grp;
+        if constexpr (PAGED) {
+          const int blk = __builtin_amdgcn_readlane(myblk, (x * NG) >> 4);  // uniform index
+          row0 = (((int64_t)blk * Hkv + hk) << 4) + ((x * NG) & 15);
+        } else {
+          row0 = cbase + x * NG;
+          lrow = min(grp, L - tw - x * NG);
+        }
+        const int64_t off = row0 * D + lrow * D + col;
+        // streamed once: non-temporal loads keep the rows out of the caches
+        kb[buf][st] = __builtin_nontemporal_load(reinterpret_cast<const Chunk*>(Kc + off));
+        vb[buf][st] = __builtin_nontemporal_load(reinterpret_cast<const Chunk*>(Vc + off));
+      }
+    };
+
+    auto consume = [&](int r, auto BUF) {
+      constexpr int buf = decltype(BUF)::value;
+      const bool full = tw + (r + 1) * R * NG - 1 < L;
+      if (!full) {
+        // the round reaches index L: token L from registers, later rows zeroed
+#pragma unroll
+        for (int st = 0; st < R; ++st) {
+          const int t = tw + (r * R + st) * NG + grp;
+#pragma unroll
+          for (int w = 0; w < W; ++w) {
+            kb[buf][st][w] = t < L ? kb[buf][st][w] : kn[w];
+            vb[buf][st][w] = t < L ? vb[buf][st][w] : (t == L ? vn[w] : 0u);
+          }
+        }
+      }
+      float sc[R][G];
+#pragma unroll
+      for (int st = 0; st < R; ++st) {
+        const int t = tw + (r * R + st) * NG + grp;
+        float kf[E];
+#pragma unroll
+        for (int e = 0; e < E; ++e) kf[e] = int8_elem(kb[buf][st][e >> 2], e & 3);
+#pragma unroll
+        for (int g = 0; g < G; ++g) {
+          float p0 = 0.f, p1 = 0.f;  // two chains for latency
+#pragma unroll
+          for (int e = 0; e < E; e += 2) {
+            p0 = fmaf(qf[g][e], kf[e], p0);
+            p1 = fmaf(qf[g][e + 1], kf[e + 1], p1);
+          }
+          const float sv = group_sum<LPR>(p0 + p1);
+          sc[st][g] = (full || t <= L) ? sv : -INFINITY;
+        }
+      }
+      // Lazy rescale, as for the native cache: the reference maximum of a
+      // head moves only when a score exceeds it by more than kRescaleLog2.
+#pragma unroll
+      for (int g = 0; g < G; ++g) {
+        float mx = sc[0][g];
+#pragma unroll
+        for (int st = 1; st < R; ++st) mx = fmaxf(mx, sc[st][g]);
+        if (__builtin_amdgcn_ballot_w64(mx - m_run[g] > kRescaleLog2) != 0) {  // uniform
+          const float m_new = fmaxf(m_run[g], class_max<LPR>(mx));
+          const float alpha = fast_exp2(m_run[g] - m_new);
+          m_run[g] = m_new;
+          l_run[g] *= alpha;
+#pragma unroll
+          for (int e = 0; e < E; ++e) acc[g][e] *= alpha;
+        }
+      }
+#pragma unroll
+      for (int st = 0; st < R; ++st) {
+        float vf[E];
+#pragma unroll
+        for (int e = 0; e < E; ++e) vf[e] = int8_elem(vb[buf][st][e >> 2], e & 3);
+#pragma unroll
+        for (int g = 0; g < G; ++g) {
+          const float p = fast_exp2(sc[st][g] - m_run[g]);
+          l_run[g] += p;
+#pragma unroll
+          for (int e = 0; e < E; ++e) acc[g][e] = fmaf(p, vf[e], acc[g][e]);
+        }
+      }
+    };
+
+    using B0 = std::integral_constant<int, 0>;
+    using B1 = std::integral_constant<int, 1>;
+    issue(0, B0{});
+    if constexpr (ROUNDS == 1) {
+      consume(0, B0{});
+    } else {
+#pragma unroll 1
+      for (int r = 0; r < ROUNDS; r += 2) {
+        issue(r + 1, B1{});
+        consume(r, B0{});
+        if (r + 2 < ROUNDS) issue(r + 2, B0{});
+        consume(r + 1, B1{});
+      }
+    }
+  }
+
+  // Merge the rows of the wave (lanes that share the same channels).
+#pragma unroll
+  for (int g = 0; g < G; ++g) {
+    l_run[g] = class_sum<LPR>(l_run[g]);
+#pragma unroll
+    for (int e = 0; e < E; ++e) acc[g][e] = class_sum<LPR>(acc[g][e]);
+  }
+  if (grp == 0) {
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+#pragma unroll
+      for (int e = 0; e < E; ++e) sm_acc[wave][g][col + e] = acc[g][e];
+      if (lane == 0) {
+        sm_ml[wave][g][0] = m_run[g];
+        sm_ml[wave][g][1] = l_run[g];
+      }
+    }
+  }
+  __syncthreads();
+
+  // Merge the waves; the value scale of each channel is applied here, once.
+  const float* vsc = c.v_scale + (int64_t)hk * D;
+  for (int i = threadIdx.x; i < G * D; i += kThreads) {
+    const int g = i / D, d = i % D;
+    float M = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) M = fmaxf(M, sm_ml[w][g][0]);
+    float a = 0.f, l = 0.f;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) {
+      const float mw = sm_ml[w][g][0];
+      const float f = mw == -INFINITY ? 0.f : fast_exp2(mw - M);
+      a = fmaf(f, sm_acc[w][g][d], a);
+      l = fmaf(f, sm_ml[w][g][1], l);
+    }
+    float* dst = part + (((int64_t)b * Hq + hk * G + g) * nsplit + split) * PW;
+    dst[4 + d] = a * vsc[d];
+    if (d == 0) {
+      dst[0] = M;
+      dst[1] = l;
+    }
+  }
+}
+
+template <typename T, int D, int G, bool PAGED>
+hipError_t decode_i8_t(const void* q, const void* k_new, const void* v_new, void* out, int B,
+                       int Hkv, const int32_t* seq_lens, int max_seq_len, const CacheArgs& c,
+                       float* partials, const RopeFreq& fr, float scale, hipStream_t st,
+                       const TimedLaunch& tl) {
+  constexpr int SPLIT = i8_split_tokens<G>();
+  const int nsplit = (max_seq_len + SPLIT - 1) / SPLIT;  // <= the workspace's split count
+  const float qk_scale = scale * 1.4426950408889634f;  // log2(e): softmax in base 2
+  const dim3 grid(Hkv * B, nsplit), block(64 * i8_waves<G>());
+  const T* qq = static_cast<const T*>(q);
+  const T* kk = static_cast<const T*>(k_new);
+  const T* vv = static_cast<const T*>(v_new);
+  if (fr.half)
+    hipExtLaunchKernelGGL((decode_i8_split_kernel<T, D, G, PAGED, SPLIT, true>), grid, block,
+                          0, st, tl.start, tl.stop, 0, qq, kk, vv, seq_lens, c, partials, Hkv,
+                          nsplit, fr, qk_scale);
+  else
+    hipExtLaunchKernelGGL((decode_i8_split_kernel<T, D, G, PAGED, SPLIT, false>), grid, block,
+                          0, st, tl.start, tl.stop, 0, qq, kk, vv, seq_lens, c, partials, Hkv,
+                          nsplit, fr, qk_scale);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int last = PAGED ? c.mbps * 16 - 1 : c.max_seq - 1;
+  hipLaunchKernelGGL((decode_combine_kernel<T, D>), dim3(B * Hkv * G), dim3(64), 0, st,
+                     partials, seq_lens, static_cast<T*>(out), Hkv * G, nsplit, SPLIT, last);
+  return hipGetLastError();
+}
+
+template <typename T, int D, int G>
+hipError_t decode_i8_paged(bool paged, const void* q, const void* kn, const void* vn, void* out,
+                           int B, int Hkv, const int32_t* sl, int max_seq_len,
+                           const CacheArgs& c, float* part, const RopeFreq& fr, float scale,
+                           hipStream_t st, const TimedLaunch& tl) {
+  return paged ? decode_i8_t<T, D, G, true>(q, kn, vn, out, B, Hkv, sl, max_seq_len, c, part,
+                                            fr, scale, st, tl)
+               : decode_i8_t<T, D, G, false>(q, kn, vn, out, B, Hkv, sl, max_seq_len, c, part,
+                                             fr, scale, st, tl);
+}
+
+template <typename T, int D>
+hipError_t decode_i8_group(int group, bool paged, const void* q, const void* kn, const void* vn,
+                           void* out, int B, int Hkv, const int32_t* sl, int max_seq_len,
+                           const CacheArgs& c, float* part, const RopeFreq& fr, float scale,
+                           hipStream_t st, const TimedLaunch& tl) {
+  switch (group) {
+    case 1: return decode_i8_paged<T, D, 1>(paged, q, kn, vn, out, B, Hkv, sl, max_seq_len, c, part, fr, scale, st, tl);
+    case 2: return decode_i8_paged<T, D, 2>(paged, q, kn, vn, out, B, Hkv, sl, max_seq_len, c, part, fr, scale, st, tl);
+    case 4: return decode_i8_paged<T, D, 4>(paged, q, kn, vn, out, B, Hkv, sl, max_seq_len, c, part, fr, scale, st, tl);
+    case 8: return decode_i8_paged<T, D, 8>(paged, q, kn, vn, out, B, Hkv, sl, max_seq_len, c, part, fr, scale, st, tl);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_decode_i8(Dtype dt, int D, int group, bool paged, const void* q,
+                            const void* k_new, const void* v_new, void* out, int B, int Hq,
+                            int Hkv, const int32_t* seq_lens, int max_seq_len,
+                            const CacheArgs& c, float* partials, const RopeFreq& fr,
+                            float scale, hipStream_t s, const TimedLaunch& tl) {
+  (void)Hq;
+  if (dt == F32)
+    return D == 64 ? decode_i8_group<float, 64>(group, paged, q, k_new, v_new, out, B, Hkv,
+                                                seq_lens, max_seq_len, c, partials, fr, scale, s,
+                                                tl)
+                   : decode_i8_group<float, 128>(group, paged, q, k_new, v_new, out, B, Hkv,
+                                                 seq_lens, max_seq_len, c, partials, fr, scale,
+                                                 s, tl);
+  return D == 64 ? decode_i8_group<bf16_t, 64>(group, paged, q, k_new, v_new, out, B, Hkv,
+                                               seq_lens, max_seq_len, c, partials, fr, scale, s,
+                                               tl)
+                 : decode_i8_group<bf16_t, 128>(group, paged, q, k_new, v_new, out, B, Hkv,
+                                                seq_lens, max_seq_len, c, partials, fr, scale, s,
+                                                tl);
+}
+
+}  // namespace car

@@ -24,6 +24,8 @@ struct CacheArgs {
   int max_seq;           // contiguous: slots per sequence
   int num_blocks;        // paged: pool size in blocks
   int mbps;              // paged: row length of the block table
+  const float* k_scale;  // INT8 cache: fp32 [Hkv, D]; value = code * scale
+  const float* v_scale;
 };
 
 enum Dtype { F32 = 0, BF16 = 1 };
@@ -45,16 +47,23 @@ __host__ __device__ constexpr int decode_partial_words(int D) { return D + 4; }
 hipError_t launch_rope_apply(Dtype dt, int D, void* x, int B, int H, int S,
                              const int32_t* positions, const RopeFreq& fr, hipStream_t s);
 
-hipError_t launch_kv_append(Dtype dt, int D, bool paged, const CacheArgs& c, const void* k,
-                            const void* v, int B, int Hkv, int S, const int32_t* positions,
-                            hipStream_t s);
+// i8: the cache holds int8 codes (quantized with c.k_scale / c.v_scale).
+hipError_t launch_kv_append(Dtype dt, int D, bool paged, bool i8, const CacheArgs& c,
+                            const void* k, const void* v, int B, int Hkv, int S,
+                            const int32_t* positions, hipStream_t s);
 
 // Rotates k into k_rot (dense [B,Hkv,S,D]) and, if cache != nullptr, also
-// stores the rotated keys and raw values into the cache.
-hipError_t launch_prefill_prep(Dtype dt, int D, bool paged, const CacheArgs* cache,
+// stores the rotated keys and raw values into the cache (as int8 codes if i8).
+hipError_t launch_prefill_prep(Dtype dt, int D, bool paged, bool i8, const CacheArgs* cache,
                                const void* k, const void* v, void* k_rot, int B, int Hkv,
                                int S, const int32_t* positions, const RopeFreq& fr,
                                hipStream_t s);
+
+// Per-(KV head, channel) absmax / 127 of the rotated keys and of the values
+// of a calibration batch, into k_scale / v_scale (fp32 [Hkv, D]).
+hipError_t launch_int8_calibrate(Dtype dt, int D, const void* k, const void* v, int B, int Hkv,
+                                 int S, const int32_t* positions, const RopeFreq& fr,
+                                 float* k_scale, float* v_scale, hipStream_t s);
 
 // A chunk continuing a cached prefix (P = seq_lens[b] tokens): rotates k at
 // positions P..P+S-1 and stores the rotated keys and raw values there.
@@ -84,5 +93,13 @@ hipError_t launch_decode(Dtype dt, int D, int group, bool paged, const void* q,
                          int Hkv, const int32_t* seq_lens, int max_seq_len, const CacheArgs& c,
                          float* partials, const RopeFreq& fr, float scale, hipStream_t s,
                          const TimedLaunch& tl);
+
+// ---- decode_i8.hip ---------------------------------------------------------
+// launch_decode over an INT8 cache (same partials workspace).
+hipError_t launch_decode_i8(Dtype dt, int D, int group, bool paged, const void* q,
+                            const void* k_new, const void* v_new, void* out, int B, int Hq,
+                            int Hkv, const int32_t* seq_lens, int max_seq_len,
+                            const CacheArgs& c, float* partials, const RopeFreq& fr,
+                            float scale, hipStream_t s, const TimedLaunch& tl);
 
 }  // namespace car

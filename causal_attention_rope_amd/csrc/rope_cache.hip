@@ -9,7 +9,9 @@
 // store follows [Scratch] ("从零手搓AI推理引擎") §3.2: a token is written at the
 // cache index equal to its position; paged caches resolve the index through
 // the block table as in [NanoVLLM] ("以 Nano-vLLM 为例，深入理解 LLM 推理引擎（Part 2）")
-// §05, 5.3.
+// §05, 5.3.  An INT8 cache ([Intuition] §2: a cache compressed from 16-bit
+// floats to INT8) stores codes with per-(KV head, channel) scales ([Scratch]
+// §2.2, §5.3); its scales come from absmax_kernel over a calibration batch.
 #include "common.hpp"
 
 namespace car {
@@ -58,7 +60,7 @@ __global__ __launch_bounds__(kThreads) void rope_apply_kernel(T* __restrict__ x,
   }
 }
 
-template <typename T, int D, bool PAGED>
+template <typename T, int D, bool PAGED, bool I8>
 __global__ __launch_bounds__(kThreads) void kv_append_kernel(CacheArgs c,
                                                              const T* __restrict__ k,
                                                              const T* __restrict__ v, int Hkv,
@@ -78,16 +80,24 @@ __global__ __launch_bounds__(kThreads) void kv_append_kernel(CacheArgs c,
     const int b = (int)(bh / Hkv);
     const int pos = min(max(positions[(int64_t)b * S + s], 0), last);
     const int64_t dst = cache_row<PAGED>(c, b, hk, Hkv, pos) * D + col;
-    *reinterpret_cast<uint4*>(static_cast<T*>(c.k) + dst) =
-        *reinterpret_cast<const uint4*>(k + row * D + col);
-    *reinterpret_cast<uint4*>(static_cast<T*>(c.v) + dst) =
-        *reinterpret_cast<const uint4*>(v + row * D + col);
+    if constexpr (I8) {
+      float kf[N], vf[N];
+      load16<T>(k + row * D + col, kf);
+      load16<T>(v + row * D + col, vf);
+      store_int8<N>(static_cast<int8_t*>(c.k) + dst, kf, c.k_scale + hk * D + col);
+      store_int8<N>(static_cast<int8_t*>(c.v) + dst, vf, c.v_scale + hk * D + col);
+    } else {
+      *reinterpret_cast<uint4*>(static_cast<T*>(c.k) + dst) =
+          *reinterpret_cast<const uint4*>(k + row * D + col);
+      *reinterpret_cast<uint4*>(static_cast<T*>(c.v) + dst) =
+          *reinterpret_cast<const uint4*>(v + row * D + col);
+    }
   }
 }
 
 // Rotate the prompt's keys once (dense copy for the attention kernel) and,
 // with a cache, store rotated keys and raw values at their positions.
-template <typename T, int D, bool PAGED, bool CACHE>
+template <typename T, int D, bool PAGED, bool CACHE, bool I8>
 __global__ __launch_bounds__(kThreads) void prefill_prep_kernel(
     CacheArgs c, const T* __restrict__ k, const T* __restrict__ v, T* __restrict__ k_rot,
     int Hkv, int S, const int32_t* __restrict__ positions, int64_t nvec, RopeFreq fr) {
@@ -109,9 +119,17 @@ __global__ __launch_bounds__(kThreads) void prefill_prep_kernel(
       const int hk = (int)(bh % Hkv);
       const int slot = min(max(pos, 0), cache_last_slot<PAGED>(c));
       const int64_t dst = cache_row<PAGED>(c, b, hk, Hkv, slot) * D + col;
-      store16<T>(static_cast<T*>(c.k) + dst, f);
-      *reinterpret_cast<uint4*>(static_cast<T*>(c.v) + dst) =
-          *reinterpret_cast<const uint4*>(v + row * D + col);
+      if constexpr (I8) {
+        // the fp32 rotated key is quantized (not its rounded copy in k_rot)
+        float vf[N];
+        load16<T>(v + row * D + col, vf);
+        store_int8<N>(static_cast<int8_t*>(c.k) + dst, f, c.k_scale + hk * D + col);
+        store_int8<N>(static_cast<int8_t*>(c.v) + dst, vf, c.v_scale + hk * D + col);
+      } else {
+        store16<T>(static_cast<T*>(c.k) + dst, f);
+        *reinterpret_cast<uint4*>(static_cast<T*>(c.v) + dst) =
+            *reinterpret_cast<const uint4*>(v + row * D + col);
+      }
     }
   }
 }
@@ -150,6 +168,100 @@ __global__ __launch_bounds__(kThreads) void chunk_prep_kernel(
   }
 }
 
+// Calibration of an INT8 cache ([Scratch] §2.2): per (KV head, channel), the
+// absolute maximum over a batch of rotated keys and of values.  Workgroup
+// (hk, y) scans a contiguous range of the B*S tokens of KV head hk, VPR lanes
+// per row; the row groups are merged through LDS and each workgroup leaves
+// one atomic maximum per channel on the fp32 bit patterns (ordered like the
+// values, all being >= 0).  The arrays are zeroed before and divided by 127
+// after (scale_finish_kernel).
+template <typename T, int D>
+__global__ __launch_bounds__(kThreads) void absmax_kernel(const T* __restrict__ k,
+                                                          const T* __restrict__ v, int Hkv,
+                                                          int S,
+                                                          const int32_t* __restrict__ positions,
+                                                          int64_t rows, int64_t rows_per_block,
+                                                          RopeFreq fr, uint32_t* __restrict__ kmax,
+                                                          uint32_t* __restrict__ vmax) {
+  constexpr int N = Vec16<T>::N;
+  constexpr int VPR = D / N;          // lanes per row
+  constexpr int RPI = kThreads / VPR;  // rows per pass of the workgroup
+  __shared__ float red[2][RPI][D];
+  const int hk = blockIdx.x;
+  const int col = (int)(threadIdx.x % VPR) * N;
+  const int rg = (int)(threadIdx.x / VPR);
+  float km[N], vm[N];
+#pragma unroll
+  for (int j = 0; j < N; ++j) km[j] = vm[j] = 0.f;
+  const int64_t r0 = (int64_t)blockIdx.y * rows_per_block;
+  const int64_t r1 = min(rows, r0 + rows_per_block);
+  for (int64_t r = r0 + rg; r < r1; r += RPI) {
+    const int b = (int)(r / S), s = (int)(r % S);
+    const int64_t row = ((int64_t)b * Hkv + hk) * S + s;
+    float f[N], g[N];
+    load16<T>(k + row * D + col, f);
+    rope_rotate_chunk<T, N>(f, k + row * D, col, D, positions[(int64_t)b * S + s], fr);
+    load16<T>(v + row * D + col, g);
+#pragma unroll
+    for (int j = 0; j < N; ++j) {
+      km[j] = fmaxf(km[j], fabsf(f[j]));
+      vm[j] = fmaxf(vm[j], fabsf(g[j]));
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < N; ++j) {
+    red[0][rg][col + j] = km[j];
+    red[1][rg][col + j] = vm[j];
+  }
+  __syncthreads();
+  for (int i = threadIdx.x; i < 2 * D; i += kThreads) {
+    const int t = i / D, d = i % D;
+    float m = 0.f;
+#pragma unroll
+    for (int g = 0; g < RPI; ++g) m = fmaxf(m, red[t][g][d]);
+    atomicMax((t ? vmax : kmax) + (int64_t)hk * D + d, __float_as_uint(m));
+  }
+}
+
+__global__ __launch_bounds__(kThreads) void scale_zero_kernel(uint32_t* __restrict__ a,
+                                                              uint32_t* __restrict__ b, int n) {
+  const int i = blockIdx.x * kThreads + threadIdx.x;
+  if (i < n) a[i] = b[i] = 0u;
+}
+
+// absmax bits -> absmax / 127 (one IEEE fp32 division)
+__global__ __launch_bounds__(kThreads) void scale_finish_kernel(float* __restrict__ a,
+                                                                float* __restrict__ b, int n) {
+  const int i = blockIdx.x * kThreads + threadIdx.x;
+  if (i < n) {
+    a[i] = __fdiv_rn(a[i], 127.f);
+    b[i] = __fdiv_rn(b[i], 127.f);
+  }
+}
+
+template <typename T, int D>
+hipError_t int8_calibrate_t(const void* k, const void* v, int B, int Hkv, int S,
+                            const int32_t* positions, const RopeFreq& fr, float* ks, float* vs,
+                            hipStream_t st) {
+  const int n = Hkv * D;
+  const int gn = (n + kThreads - 1) / kThreads;
+  hipLaunchKernelGGL(scale_zero_kernel, dim3(gn), dim3(kThreads), 0, st,
+                     reinterpret_cast<uint32_t*>(ks), reinterpret_cast<uint32_t*>(vs), n);
+  const int64_t rows = (int64_t)B * S;
+  if (rows > 0) {
+    const int64_t want = (rows + 255) / 256;  // >= 1
+    const int64_t by = want < 1024 ? want : 1024;
+    const int64_t rpb = (rows + by - 1) / by;
+    const int gy = (int)((rows + rpb - 1) / rpb);
+    hipLaunchKernelGGL((absmax_kernel<T, D>), dim3(Hkv, gy), dim3(kThreads), 0, st,
+                       static_cast<const T*>(k), static_cast<const T*>(v), Hkv, S, positions,
+                       rows, rpb, fr, reinterpret_cast<uint32_t*>(ks),
+                       reinterpret_cast<uint32_t*>(vs));
+  }
+  hipLaunchKernelGGL(scale_finish_kernel, dim3(gn), dim3(kThreads), 0, st, ks, vs, n);
+  return hipGetLastError();
+}
+
 template <typename T, int D>
 hipError_t rope_apply_t(void* x, int B, int H, int S, const int32_t* positions,
                         const RopeFreq& fr, hipStream_t st) {
@@ -159,22 +271,22 @@ hipError_t rope_apply_t(void* x, int B, int H, int S, const int32_t* positions,
   return hipGetLastError();
 }
 
-template <typename T, int D>
+template <typename T, int D, bool I8>
 hipError_t kv_append_t(bool paged, const CacheArgs& c, const void* k, const void* v, int B,
                        int Hkv, int S, const int32_t* positions, hipStream_t st) {
   const int64_t nvec = (int64_t)B * Hkv * S * (D / Vec16<T>::N);
   const T* kk = static_cast<const T*>(k);
   const T* vv = static_cast<const T*>(v);
   if (paged)
-    hipLaunchKernelGGL((kv_append_kernel<T, D, true>), dim3(grid_for(nvec)), dim3(kThreads), 0,
-                       st, c, kk, vv, Hkv, S, positions, nvec);
-  else
-    hipLaunchKernelGGL((kv_append_kernel<T, D, false>), dim3(grid_for(nvec)), dim3(kThreads),
+    hipLaunchKernelGGL((kv_append_kernel<T, D, true, I8>), dim3(grid_for(nvec)), dim3(kThreads),
                        0, st, c, kk, vv, Hkv, S, positions, nvec);
+  else
+    hipLaunchKernelGGL((kv_append_kernel<T, D, false, I8>), dim3(grid_for(nvec)),
+                       dim3(kThreads), 0, st, c, kk, vv, Hkv, S, positions, nvec);
   return hipGetLastError();
 }
 
-template <typename T, int D>
+template <typename T, int D, bool I8>
 hipError_t prefill_prep_t(bool paged, const CacheArgs* cache, const void* k, const void* v,
                           void* k_rot, int B, int Hkv, int S, const int32_t* positions,
                           const RopeFreq& fr, hipStream_t st) {
@@ -185,14 +297,14 @@ hipError_t prefill_prep_t(bool paged, const CacheArgs* cache, const void* k, con
   const dim3 grid(grid_for(nvec)), block(kThreads);
   if (cache == nullptr) {
     CacheArgs none{};
-    hipLaunchKernelGGL((prefill_prep_kernel<T, D, false, false>), grid, block, 0, st, none, kk,
-                       vv, kr, Hkv, S, positions, nvec, fr);
+    hipLaunchKernelGGL((prefill_prep_kernel<T, D, false, false, false>), grid, block, 0, st,
+                       none, kk, vv, kr, Hkv, S, positions, nvec, fr);
   } else if (paged) {
-    hipLaunchKernelGGL((prefill_prep_kernel<T, D, true, true>), grid, block, 0, st, *cache, kk,
-                       vv, kr, Hkv, S, positions, nvec, fr);
-  } else {
-    hipLaunchKernelGGL((prefill_prep_kernel<T, D, false, true>), grid, block, 0, st, *cache,
+    hipLaunchKernelGGL((prefill_prep_kernel<T, D, true, true, I8>), grid, block, 0, st, *cache,
                        kk, vv, kr, Hkv, S, positions, nvec, fr);
+  } else {
+    hipLaunchKernelGGL((prefill_prep_kernel<T, D, false, true, I8>), grid, block, 0, st,
+                       *cache, kk, vv, kr, Hkv, S, positions, nvec, fr);
   }
   return hipGetLastError();
 }
@@ -236,29 +348,48 @@ hipError_t launch_rope_apply(Dtype dt, int D, void* x, int B, int H, int S,
                  : rope_apply_t<bf16_t, 128>(x, B, H, S, positions, fr, s);
 }
 
-hipError_t launch_kv_append(Dtype dt, int D, bool paged, const CacheArgs& c, const void* k,
-                            const void* v, int B, int Hkv, int S, const int32_t* positions,
-                            hipStream_t s) {
+hipError_t launch_kv_append(Dtype dt, int D, bool paged, bool i8, const CacheArgs& c,
+                            const void* k, const void* v, int B, int Hkv, int S,
+                            const int32_t* positions, hipStream_t s) {
+  if (i8) {
+    if (dt == F32)
+      return D == 64 ? kv_append_t<float, 64, true>(paged, c, k, v, B, Hkv, S, positions, s)
+                     : kv_append_t<float, 128, true>(paged, c, k, v, B, Hkv, S, positions, s);
+    return D == 64 ? kv_append_t<bf16_t, 64, true>(paged, c, k, v, B, Hkv, S, positions, s)
+                   : kv_append_t<bf16_t, 128, true>(paged, c, k, v, B, Hkv, S, positions, s);
+  }
   if (dt == F32)
-    return D == 64 ? kv_append_t<float, 64>(paged, c, k, v, B, Hkv, S, positions, s)
-                   : kv_append_t<float, 128>(paged, c, k, v, B, Hkv, S, positions, s);
-  return D == 64 ? kv_append_t<bf16_t, 64>(paged, c, k, v, B, Hkv, S, positions, s)
-                 : kv_append_t<bf16_t, 128>(paged, c, k, v, B, Hkv, S, positions, s);
+    return D == 64 ? kv_append_t<float, 64, false>(paged, c, k, v, B, Hkv, S, positions, s)
+                   : kv_append_t<float, 128, false>(paged, c, k, v, B, Hkv, S, positions, s);
+  return D == 64 ? kv_append_t<bf16_t, 64, false>(paged, c, k, v, B, Hkv, S, positions, s)
+                 : kv_append_t<bf16_t, 128, false>(paged, c, k, v, B, Hkv, S, positions, s);
 }
 
-hipError_t launch_prefill_prep(Dtype dt, int D, bool paged, const CacheArgs* cache,
+hipError_t launch_prefill_prep(Dtype dt, int D, bool paged, bool i8, const CacheArgs* cache,
                                const void* k, const void* v, void* k_rot, int B, int Hkv,
                                int S, const int32_t* positions, const RopeFreq& fr,
                                hipStream_t s) {
+#define CAR_PREP(T, DD, I)                                                                    \
+  prefill_prep_t<T, DD, I>(paged, cache, k, v, k_rot, B, Hkv, S, positions, fr, s)
+  if (i8 && cache != nullptr) {
+    if (dt == F32) return D == 64 ? CAR_PREP(float, 64, true) : CAR_PREP(float, 128, true);
+    return D == 64 ? CAR_PREP(bf16_t, 64, true) : CAR_PREP(bf16_t, 128, true);
+  }
+  if (dt == F32) return D == 64 ? CAR_PREP(float, 64, false) : CAR_PREP(float, 128, false);
+  return D == 64 ? CAR_PREP(bf16_t, 64, false) : CAR_PREP(bf16_t, 128, false);
+#undef CAR_PREP
+}
+
+hipError_t launch_int8_calibrate(Dtype dt, int D, const void* k, const void* v, int B, int Hkv,
+                                 int S, const int32_t* positions, const RopeFreq& fr,
+                                 float* k_scale, float* v_scale, hipStream_t s) {
   if (dt == F32)
-    return D == 64
-               ? prefill_prep_t<float, 64>(paged, cache, k, v, k_rot, B, Hkv, S, positions, fr, s)
-               : prefill_prep_t<float, 128>(paged, cache, k, v, k_rot, B, Hkv, S, positions, fr,
-                                            s);
-  return D == 64
-             ? prefill_prep_t<bf16_t, 64>(paged, cache, k, v, k_rot, B, Hkv, S, positions, fr, s)
-             : prefill_prep_t<bf16_t, 128>(paged, cache, k, v, k_rot, B, Hkv, S, positions, fr,
-                                           s);
+    return D == 64 ? int8_calibrate_t<float, 64>(k, v, B, Hkv, S, positions, fr, k_scale, v_scale, s)
+                   : int8_calibrate_t<float, 128>(k, v, B, Hkv, S, positions, fr, k_scale,
+                                                  v_scale, s);
+  return D == 64 ? int8_calibrate_t<bf16_t, 64>(k, v, B, Hkv, S, positions, fr, k_scale, v_scale, s)
+                 : int8_calibrate_t<bf16_t, 128>(k, v, B, Hkv, S, positions, fr, k_scale,
+                                                 v_scale, s);
 }
 
 }  // namespace car

@@ -18,8 +18,9 @@
  *     positions   int32 [B, S]        (decode uses seq_lens instead)
  *   Query head hq reads KV head hq / (Hq / Hkv) (contiguous GQA groups).
  * Element type.  CAR_DTYPE_F32 or CAR_DTYPE_BF16 for every float tensor of
- *   one call, caches included.  Arithmetic is fp32 (MFMA accumulation in
- *   fp32 for bf16); outputs are rounded to the element type, nearest-even.
+ *   one call, caches included unless a cache is INT8 (car_cache_format).
+ *   Arithmetic is fp32 (MFMA accumulation in fp32 for bf16); outputs are
+ *   rounded to the element type, nearest-even.
  * Head dimension.  D must be 64 or 128; otherwise CAR_ERR_UNSUPPORTED.
  * RoPE ([Intuition] §4).  Each adjacent pair (x[2i], x[2i+1]) is rotated by
  *   the angle m * theta^(-2i/D), m the token's position:
@@ -73,13 +74,35 @@ typedef enum car_rope_pairing {
  * rotated in that layout, so one cache is read with one pairing.  Another
  * value returns CAR_ERR_UNSUPPORTED. */
 
+/*
+ * Element format of a KV cache.  [Intuition] §2 counts precision
+ * compression of the cache, from 16-bit floats to INT8, among what a cache
+ * has to support; [Scratch] §2.2 takes a channel's absolute maximum over 127
+ * as its INT8 scale, computed once before inference and kept with the data,
+ * and §5.3 divides by the scale and rounds to store, multiplying back to read.
+ *   CAR_CACHE_NATIVE  elements of the call's dtype.
+ *   CAR_CACHE_INT8    int8 codes, one fp32 scale per (KV head, channel):
+ *     a value x of channel d, KV head hk is stored as
+ *       code = clamp(round(x / s), -127, 127),  s = scale[hk][d],
+ *     with x / s one IEEE fp32 division, ties rounded away from zero, and
+ *     code 0 where s == 0; the cached value is code * s.  Keys are quantized
+ *     from their fp32 rotated values.  car_kv_int8_calibrate computes the
+ *     scales.  car_kv_cache_append, car_attn_prefill (its cache store) and
+ *     car_attn_decode accept an INT8 cache; car_attn_prefill_cached returns
+ *     CAR_ERR_UNSUPPORTED for one.
+ */
+typedef enum car_cache_format {
+  CAR_CACHE_NATIVE = 0,
+  CAR_CACHE_INT8 = 1
+} car_cache_format;
+
 typedef enum car_status {
   CAR_OK = 0,
   CAR_ERR_INVALID_ARGUMENT = 1, /* null pointer, negative size, Hq % Hkv != 0,
                                    pointer not 16-byte aligned, bad cache shape */
   CAR_ERR_UNSUPPORTED = 2,      /* well formed but not built: D not in {64, 128},
                                    block_size != 16, Hq/Hkv not in {1, 2, 4, 8},
-                                   unknown dtype or RoPE pairing */
+                                   unknown dtype, RoPE pairing or cache format */
   CAR_ERR_WORKSPACE = 3,        /* workspace missing or smaller than required */
   CAR_ERR_HIP = 4               /* the HIP runtime reported an error at launch */
 } car_status;
@@ -95,6 +118,9 @@ typedef enum car_status {
  *     block_size must be 16.
  * The caller keeps the table entries of every block a call touches in
  * [0, num_blocks) and distinct across sequences.
+ * Element format (see car_cache_format): the call's dtype, or int8 codes in
+ * the same shapes with fp32 scales k_scale, v_scale [Hkv, D] (device,
+ * 16-byte aligned, read only).
  */
 typedef struct car_kv_cache {
   void* k;
@@ -104,6 +130,9 @@ typedef struct car_kv_cache {
   int32_t num_blocks;         /* paged only */
   int32_t block_size;         /* paged only; must be 16 */
   int32_t max_blocks_per_seq; /* paged only: row length of block_table */
+  int32_t format;             /* car_cache_format; 0 (zero-initialised) is native */
+  const float* k_scale;       /* CAR_CACHE_INT8 only */
+  const float* v_scale;       /* CAR_CACHE_INT8 only */
 } car_kv_cache;
 
 /*
@@ -124,11 +153,28 @@ car_status car_rope_apply(void* x, car_dtype dtype, int B, int H, int S, int D,
  *   positions  int32 [B, S] device: cache index of each token; every index
  *              must lie below the cache capacity (max_seq, or
  *              max_blocks_per_seq * 16 when paged).
- *   cache      host pointer to the cache description; its k, v are written.
+ *   cache      host pointer to the cache description; its k, v are written
+ *              (as int8 codes for an INT8 cache).
  */
 car_status car_kv_cache_append(const car_kv_cache* cache, car_dtype dtype,
                                const void* k, const void* v, int B, int Hkv, int S,
                                int D, const int32_t* positions, hipStream_t stream);
+
+/*
+ * car_kv_int8_calibrate -- the per-(KV head, channel) scales of an INT8 cache
+ * from a calibration batch ([Scratch] §2.2: a channel's absolute maximum
+ * divided by 127, computed once, before inference).  The keys are rotated at
+ * their positions first, in fp32, because the cache holds rotated keys.
+ *   k, v       [B, Hkv, S, D] device (k not rotated);  positions  int32 [B, S] device.
+ *   k_scale, v_scale  fp32 [Hkv, D] device, 16-byte aligned, written:
+ *              max over every (b, s) of |rotated key| (|value|) of the
+ *              channel, divided by 127 (one fp32 division).
+ * B * S == 0 writes zeros.  Inputs must be finite.
+ */
+car_status car_kv_int8_calibrate(const void* k, const void* v, car_dtype dtype, int B, int Hkv,
+                                 int S, int D, const int32_t* positions, float theta,
+                                 car_rope_pairing pairing, float* k_scale, float* v_scale,
+                                 hipStream_t stream);
 
 /*
  * Bytes of device workspace car_attn_prefill needs for these sizes: room for
@@ -155,7 +201,9 @@ size_t car_attn_prefill_workspace_bytes(car_dtype dtype, int B, int Hkv, int S, 
  *              pages ([Intuition] §4).
  *   cache      NULL: nothing is stored.  Otherwise every rotated key and raw
  *              value is also stored at index positions[b][s], as by
- *              car_kv_cache_append.
+ *              car_kv_cache_append.  With an INT8 cache only the stored
+ *              copy is quantized: the prompt attends to its own keys and
+ *              values at full precision.
  *   workspace  device scratch of at least car_attn_prefill_workspace_bytes();
  *              its contents on entry are ignored and on exit unspecified.
  * S == 0 is a no-op returning CAR_OK.
@@ -190,7 +238,8 @@ car_status car_attn_prefill(const void* q, const void* k, const void* v, void* o
  *                to, and their output rows are written as zeros.
  *   max_seq_len  host bound on seq_lens[b] + (chunk length) over the batch; at
  *                most the cache capacity, and at least S when chunk_lens is NULL.
- *   cache        contiguous or paged; rows 0..P-1 must hold the prefix (as
+ *   cache        contiguous or paged, native format (an INT8 cache returns
+ *                CAR_ERR_UNSUPPORTED); rows 0..P-1 must hold the prefix (as
  *                written by earlier calls), rows P..P+S-1 are written.
  * No workspace: the keys are rotated straight into the cache.  S == 0 or an
  * empty batch is a no-op returning CAR_OK.  Sizes one launch cannot cover
@@ -225,6 +274,9 @@ size_t car_attn_decode_workspace_bytes(int B, int Hq, int D, int max_seq_len);
  *   max_seq_len host bound on seq_lens[b] + 1 over the batch; it sizes the
  *               launch (tokens beyond it are not read).
  *   cache       contiguous or paged, written at index L for every sequence.
+ *               With an INT8 cache the new key and value are stored as codes
+ *               and token L is attended to in that quantized form, like
+ *               every cached token.
  *   workspace   device scratch of at least car_attn_decode_workspace_bytes();
  *               contents on entry ignored, on exit unspecified.
  * Calls that share a workspace must be ordered on one stream.

@@ -57,9 +57,11 @@ def test_status_strings(lib):
     assert "unknown" in lib.car_status_string(99).decode()
 
 
-def _cache(car, paged=False, block_size=16, max_seq=64, k=FAKE, v=FAKE):
+def _cache(car, paged=False, block_size=16, max_seq=64, k=FAKE, v=FAKE, fmt=0, ks=None,
+           vs=None):
     c = car._CarKVCache()
     c.k, c.v = k, v
+    c.format, c.k_scale, c.v_scale = fmt, ks, vs
     if paged:
         c.block_table = FAKE
         c.num_blocks, c.block_size, c.max_blocks_per_seq = 8, block_size, 4
@@ -190,6 +192,44 @@ def test_prefill_cached_rejects(car, lib):
     assert call(cache=ctypes.byref(bad)) == UNSUPPORTED
     assert call(B=0, q=None) == OK                   # empty batch: no-op
     assert call(S=0, q=None) == OK                   # empty chunk: no-op
+
+
+def test_int8_cache_rejects(car, lib):
+    """An INT8 cache needs both scale arrays, 16-byte aligned; an unknown
+    format is unsupported; the chunked prefill does not read INT8 caches."""
+    app = lib.car_kv_cache_append
+    for c, want in ((_cache(car, fmt=1), INVALID),                          # no scales
+                    (_cache(car, fmt=1, ks=FAKE), INVALID),                 # no v_scale
+                    (_cache(car, fmt=1, ks=FAKE, vs=FAKE + 4), INVALID),    # misaligned
+                    (_cache(car, fmt=2, ks=FAKE, vs=FAKE), UNSUPPORTED)):   # unknown format
+        assert app(ctypes.byref(c), BF16, FAKE, FAKE, 1, 1, 1, 64, FAKE, None) == want
+    good = _cache(car, max_seq=512, fmt=1, ks=FAKE, vs=FAKE)
+    chunk = lib.car_attn_prefill_cached(FAKE, FAKE, FAKE, FAKE, BF16, 2, 8, 2, 100, 128, FAKE,
+                                        None, 300, 1e4, 0, 0.088, ctypes.byref(good), None)
+    assert chunk == UNSUPPORTED
+    noscale = _cache(car, max_seq=512, fmt=1)
+    dec = lib.car_attn_decode(FAKE, FAKE, FAKE, FAKE, BF16, 2, 8, 2, 128, FAKE, 300, 1e4, 0,
+                              0.088, ctypes.byref(noscale), FAKE, 1 << 20, None)
+    assert dec == INVALID
+    # the same INT8 cache with scales passes every check up to the workspace
+    dec = lib.car_attn_decode(FAKE, FAKE, FAKE, FAKE, BF16, 2, 8, 2, 128, FAKE, 300, 1e4, 0,
+                              0.088, ctypes.byref(good), None, 0, None)
+    assert dec == WORKSPACE
+
+
+def test_int8_calibrate_rejects(lib):
+    f = lib.car_kv_int8_calibrate
+    assert f(FAKE, FAKE, BF16, 1, 2, 8, 96, FAKE, 1e4, 0, FAKE, FAKE, None) == UNSUPPORTED
+    assert f(FAKE, FAKE, 7, 1, 2, 8, 64, FAKE, 1e4, 0, FAKE, FAKE, None) == UNSUPPORTED
+    assert f(FAKE, FAKE, BF16, 1, 2, 8, 64, FAKE, 1e4, 4, FAKE, FAKE, None) == UNSUPPORTED
+    assert f(FAKE, FAKE, BF16, -1, 2, 8, 64, FAKE, 1e4, 0, FAKE, FAKE, None) == INVALID
+    assert f(FAKE, FAKE, BF16, 1, 2, 8, 64, FAKE, 0.0, 0, FAKE, FAKE, None) == INVALID
+    assert f(FAKE, FAKE, BF16, 1, 2, 8, 64, FAKE, 1e4, 0, None, FAKE, None) == INVALID
+    assert f(FAKE, FAKE, BF16, 1, 2, 8, 64, FAKE, 1e4, 0, FAKE, FAKE + 8, None) == INVALID
+    assert f(None, FAKE, BF16, 1, 2, 8, 64, FAKE, 1e4, 0, FAKE, FAKE, None) == INVALID
+    assert f(FAKE, FAKE, BF16, 1, 2, 8, 64, None, 1e4, 0, FAKE, FAKE, None) == INVALID
+    assert f(FAKE + 2, FAKE, BF16, 1, 2, 8, 64, FAKE, 1e4, 0, FAKE, FAKE, None) == INVALID
+    assert f(None, None, BF16, 1, 0, 8, 64, None, 1e4, 0, None, None, None) == OK   # no heads
 
 
 def test_workspace_sizes(lib):

@@ -27,6 +27,11 @@ The five named workloads:
 5. ``paged_decode``: B=64, Hq=32, Hkv=8, D=128, bf16, 16-token blocks,
    lengths uniform in [512, 8192], pool of 64*513 blocks, block table taken
    from a seeded random permutation of the pool.
+
+INT8 caches (``int8_decode_case``) have the same shapes with int8 codes drawn
+uniformly from [-127, 127] and fp32 per-(KV head, channel) scales drawn
+uniformly from [0.01, 0.03], so that cached values spread over about the
+range of N(0, 1) data.
 """
 
 from __future__ import annotations
@@ -99,6 +104,8 @@ class DecodeCase:
     max_seq: int = 0                   # contiguous capacity (0 for paged)
     theta: float = 10000.0
     lens_host: List[int] = field(default_factory=list)
+    k_scale: Optional[torch.Tensor] = None   # INT8 cache: fp32 [Hkv, D]
+    v_scale: Optional[torch.Tensor] = None
 
     @property
     def scale(self) -> float:
@@ -172,6 +179,49 @@ def decode_case(name, B, Hq, Hkv, D, dtype, lens, seed, device, paged: bool,
     bt = torch.from_numpy(table).to(device)
     return DecodeCase(name, B, Hq, Hkv, D, dtype, q, k_new, v_new, seq_lens, ck, cv,
                       bt.contiguous(), 0, lens_host=lens)
+
+
+def randcodes(shape, device, seed: int, stream: int) -> torch.Tensor:
+    """int8 codes drawn uniformly from [-127, 127]."""
+    return torch.randint(-127, 128, tuple(shape), generator=_gen(device, seed, stream),
+                         device=device, dtype=torch.int32).to(torch.int8)
+
+
+def randscales(shape, device, seed: int, stream: int) -> torch.Tensor:
+    """fp32 scales drawn uniformly from [0.01, 0.03]."""
+    u = torch.rand(tuple(shape), generator=_gen(device, seed, stream), device=device,
+                   dtype=torch.float32)
+    return 0.01 + 0.02 * u
+
+
+def int8_decode_case(name, B, Hq, Hkv, D, dtype, lens, seed, device, paged: bool,
+                     max_seq: Optional[int] = None, extra_blocks: int = 0,
+                     blocks_per_seq: Optional[int] = None) -> DecodeCase:
+    """A decode step over an INT8 cache: the layout of ``decode_case`` with
+    int8 codes in every slot and per-(KV head, channel) scales."""
+    lens = [int(x) for x in lens]
+    rng = host_rng(seed)
+    q = randn((B, Hq, D), dtype, device, seed, 3)
+    k_new = randn((B, Hkv, D), dtype, device, seed, 4)
+    v_new = randn((B, Hkv, D), dtype, device, seed, 5)
+    seq_lens = torch.tensor(lens, dtype=torch.int32, device=device)
+    ks = randscales((Hkv, D), device, seed, 8)
+    vs = randscales((Hkv, D), device, seed, 9)
+    if not paged:
+        cap = max_seq if max_seq is not None else max(lens) + 1
+        ck = randcodes((B, Hkv, cap, D), device, seed, 6)
+        cv = randcodes((B, Hkv, cap, D), device, seed, 7)
+        return DecodeCase(name, B, Hq, Hkv, D, dtype, q, k_new, v_new, seq_lens, ck, cv, None,
+                          cap, lens_host=lens, k_scale=ks, v_scale=vs)
+    mbps = blocks_per_seq or (max(lens) + 1 + BLOCK_SIZE - 1) // BLOCK_SIZE
+    nblocks = B * mbps + extra_blocks
+    perm = rng.permutation(nblocks)
+    table = perm[: B * mbps].reshape(B, mbps).astype(np.int32)
+    ck = randcodes((nblocks, Hkv, BLOCK_SIZE, D), device, seed, 6)
+    cv = randcodes((nblocks, Hkv, BLOCK_SIZE, D), device, seed, 7)
+    bt = torch.from_numpy(table).to(device)
+    return DecodeCase(name, B, Hq, Hkv, D, dtype, q, k_new, v_new, seq_lens, ck, cv,
+                      bt.contiguous(), 0, lens_host=lens, k_scale=ks, v_scale=vs)
 
 
 @dataclass
