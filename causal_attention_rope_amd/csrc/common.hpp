@@ -299,6 +299,17 @@ __device__ __forceinline__ float group_sum(float x) {
   return x;
 }
 
+// Maximum over aligned groups of LANES consecutive lanes (LANES in 1..32).
+template <int LANES>
+__device__ __forceinline__ float group_max(float x) {
+  if constexpr (LANES >= 2) x = fmaxf(x, dpp_mov<DPP_QUAD_XOR1>(x));
+  if constexpr (LANES >= 4) x = fmaxf(x, dpp_mov<DPP_QUAD_XOR2>(x));
+  if constexpr (LANES >= 8) x = fmaxf(x, dpp_mov<DPP_ROW_HALF_MIRROR>(x));
+  if constexpr (LANES >= 16) x = fmaxf(x, dpp_mov<DPP_ROW_MIRROR>(x));
+  if constexpr (LANES >= 32) x = fmaxf(x, __shfl_xor(x, 16));
+  return x;
+}
+
 // All-reduce over the lanes that share lane % STRIDE, STRIDE in {4, 8, 16, 32},
 // without LDS traffic: rotations by 4 and 8 inside each row of 16 lanes (DPP
 // row_ror), then the swaps of 16-lane rows and of 32-lane halves
