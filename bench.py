@@ -76,7 +76,8 @@ def parse_args(argv=None):
 
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
-KERNEL_SOURCES = ["rope_cache.hip", "decode.hip", "prefill.hip", "common.hpp", "launch.hpp"]
+KERNEL_SOURCES = ["rope_cache.hip", "decode.hip", "decode_i8.hip", "prefill.hip", "common.hpp",
+                  "decode_common.hpp", "launch.hpp"]
 COPY_BYTES = 1 << 30
 
 
@@ -380,6 +381,9 @@ def main(argv=None) -> int:
     for name, k in kernels.items():
         t = traffic.get(name)
         k["traffic"] = None if t is None else t["fetch_bytes"] + t["write_bytes"]
+    for name, e in extras.items():
+        t = traffic.get(name)
+        e["traffic"] = None if t is None else t["fetch_bytes"] + t["write_bytes"]
 
     dominant = max(kernels, key=lambda k: kernels[k]["avg_us"])
     roofline = {k: v for k, v in kernels[dominant].items() if k in
