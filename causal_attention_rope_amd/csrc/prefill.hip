@@ -216,9 +216,9 @@ __device__ __forceinline__ float swap_halves(float x) {
   return __builtin_bit_cast(float, (__lane_id() < 32) ? r[1] : r[0]);
 }
 
-template <int D>
+template <int D, int W>
 struct Tile {
-  static constexpr int WAVES = 8;
+  static constexpr int WAVES = W;
   static constexpr int THREADS = 64 * WAVES;
   static constexpr int BM = 32 * WAVES;           // query rows per workgroup
   static constexpr int BN = D == 128 ? 64 : 128;  // keys per tile
@@ -269,13 +269,22 @@ __device__ __forceinline__ int logical_chunk(int p, int r) {
   }
 }
 
+// Waves per workgroup (32 query rows each).  A whole prompt balances pairs of
+// query tiles over 8 waves; a chunk after a cached prefix has one tile per
+// workgroup, and with 4 waves (128 query rows) a 1024-token chunk of 32 heads
+// fills 256 workgroups instead of 128 (measured: 104 -> 80 us).  The paged
+// chunk keeps 8 waves: each wave's tile loads there take their block ids
+// from the table, and 4 waves would double those per wave (148 -> 174 us).
+template <int SRC>
+constexpr int tile_waves() { return SRC == KEYS_CONTIG ? 4 : 8; }
+
 template <int D, int SRC, int HALF>
-__global__ __launch_bounds__(Tile<D>::THREADS, 2) void prefill_bf16_kernel(
+__global__ __launch_bounds__((Tile<D, tile_waves<SRC>()>::THREADS), 2) void prefill_bf16_kernel(
     const bf16_t* __restrict__ q, const bf16_t* __restrict__ kr, const bf16_t* __restrict__ v,
     bf16_t* __restrict__ out, const int32_t* __restrict__ positions, int Hq, int Hkv, int S,
     int nqt, RopeFreq fr, float sm_scale_log2, CacheArgs c, const int32_t* __restrict__ seq_lens,
     const int32_t* __restrict__ chunk_lens) {
-  using C = Tile<D>;
+  using C = Tile<D, tile_waves<SRC>()>;
   __shared__ __attribute__((aligned(1024))) char smem[2 * C::STAGEB];
 
   // ---- work assignment: balanced query-tile pairs, heads pinned to XCDs ----
@@ -645,7 +654,7 @@ template <int D, int SRC, int HALF>
 hipError_t prefill_bf16_t(const void* q, const KeySource& ks, void* out, int B, int Hq, int Hkv,
                           int S, const int32_t* positions, const RopeFreq& fr, float scale,
                           hipStream_t st, const TimedLaunch& tl) {
-  using C = Tile<D>;
+  using C = Tile<D, tile_waves<SRC>()>;
   const int nqt = (S + C::BM - 1) / C::BM;
   const int npair = SRC == KEYS_PROMPT ? (nqt + 1) / 2 : nqt;  // workgroups per head
   hipExtLaunchKernelGGL((prefill_bf16_kernel<D, SRC, HALF>), dim3(npair * B * Hq), dim3(C::THREADS), 0,
