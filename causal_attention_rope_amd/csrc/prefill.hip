@@ -272,11 +272,10 @@ __device__ __forceinline__ int logical_chunk(int p, int r) {
 // Waves per workgroup (32 query rows each).  A whole prompt balances pairs of
 // query tiles over 8 waves; a chunk after a cached prefix has one tile per
 // workgroup, and with 4 waves (128 query rows) a 1024-token chunk of 32 heads
-// fills 256 workgroups instead of 128 (measured: 104 -> 80 us).  The paged
-// chunk keeps 8 waves: each wave's tile loads there take their block ids
-// from the table, and 4 waves would double those per wave (148 -> 174 us).
+// fills 256 workgroups instead of 128 (measured on a 3072-token prefix:
+// contiguous 104 -> 80 us; paged 120 -> 101 us).
 template <int SRC>
-constexpr int tile_waves() { return SRC == KEYS_CONTIG ? 4 : 8; }
+constexpr int tile_waves() { return SRC == KEYS_PROMPT ? 8 : 4; }
 
 template <int D, int SRC, int HALF>
 __global__ __launch_bounds__((Tile<D, tile_waves<SRC>()>::THREADS), 2) void prefill_bf16_kernel(
@@ -341,8 +340,12 @@ __global__ __launch_bounds__((Tile<D, tile_waves<SRC>()>::THREADS), 2) void pref
   // K and V have two buffers each: K holds tiles t+1 and t+2 while V holds t
   // and t+1 (the QK^T of tile t+1 is issued before the softmax of tile t).
   // In a paged cache each load's RPI rows lie in one 16-token block (tiles
-  // and loads are aligned to RPI, which divides 16), so a load takes its
-  // block from the table as a scalar and addresses that block alone.
+  // and loads are aligned to RPI, which divides 16), so a load addresses that
+  // block alone.  The block ids of a tile are read from the table one
+  // pipeline step before its first load, into lanes (lane j: the tile's j-th
+  // block), so the load takes its id with a v_readlane instead of waiting on
+  // a scalar table read; the wait for that vector read is the per-step wait
+  // for the tile loads.
   const uint32_t head_bytes = (uint32_t)nkeys * C::ROWB;
   const __amdgpu_buffer_rsrc_t krs = make_rsrc(kbase, head_bytes);
   const __amdgpu_buffer_rsrc_t vrs = make_rsrc(vbase, head_bytes);
@@ -353,7 +356,16 @@ __global__ __launch_bounds__((Tile<D, tile_waves<SRC>()>::THREADS), 2) void pref
     dma_off[i] = row * C::ROWB + (logical_chunk<C::CPR>(lane % C::CPR, row) << 4);
   }
   const int32_t* const trow = SRC == KEYS_PAGED ? c.table + (int64_t)b * c.mbps : nullptr;
-  auto issue = [&](__amdgpu_buffer_rsrc_t rs, const void* pool, int j0, char* dst) {
+  // lane j's block id of the tile starting at key j0 (clamped to the keys and the pool)
+  auto block_ids = [&](int j0) -> int {
+    if constexpr (SRC == KEYS_PAGED) {
+      const int jb = min(j0 + 16 * (lane % (C::BN / 16)), nkeys - 1);
+      return min(max(trow[jb >> 4], 0), c.num_blocks - 1);
+    } else {
+      return 0;
+    }
+  };
+  auto issue = [&](__amdgpu_buffer_rsrc_t rs, const void* pool, int j0, char* dst, int ids) {
     if constexpr (SRC == KEYS_PAGED) {
       static_assert(16 % C::RPI == 0 && C::BN % 16 == 0, "a load stays inside one block");
 #pragma unroll
@@ -361,13 +373,14 @@ __global__ __launch_bounds__((Tile<D, tile_waves<SRC>()>::THREADS), 2) void pref
         const int r0 = (wave * C::IPW + i) * C::RPI;  // first tile row of this load
         const int row = r0 + lane / C::CPR;
         const int j = min(j0 + row, nkeys - 1);        // rows past the end: the last key
-        const int jb = min(j0 + r0, nkeys - 1);        // uniform: the load's block
-        const int blk = min(max(trow[jb >> 4], 0), c.num_blocks - 1);
+        // the load's block (uniform); rows past the end keep the last key's block
+        const int blk = __builtin_amdgcn_readlane(ids, min(r0, nkeys - 1 - j0) >> 4);
         const bf16_t* bp = static_cast<const bf16_t*>(pool) + (((int64_t)blk * Hkv + hk) << 4) * D;
         const uint32_t off = (j & 15) * C::ROWB + (logical_chunk<C::CPR>(lane % C::CPR, row) << 4);
         dma16(make_rsrc(bp, 16 * C::ROWB), off, 0, dst + (wave * C::IPW + i) * 1024);
       }
     } else if (j0 + C::BN <= nkeys) {  // uniform
+      (void)ids;
 #pragma unroll
       for (int i = 0; i < C::IPW; ++i)
         dma16(rs, dma_off[i], (uint32_t)j0 * C::ROWB, dst + (wave * C::IPW + i) * 1024);
@@ -585,20 +598,35 @@ __global__ __launch_bounds__((Tile<D, tile_waves<SRC>()>::THREADS), 2) void pref
     // One pipeline step for tile t (S^T of tile t already issued into
     // sacc[SC]): make K(t+1) and V(t) visible, start the loads of K(t+2) and
     // V(t+1), issue QK^T of tile t+1 into sacc[SN], then softmax and P V of t.
+    // Paged: block ids of tiles t+1 (V loads of step t), t+2 (K loads) and
+    // t+3 (read during step t for the next step).
+    int ids_v = 0, ids_k = 0;
     auto step = [&](int t, auto SC, auto SN) {
       __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's loads landed
       __syncthreads();                     // everyone's loads landed; old buffers free
-      if (t + 2 < ntiles) issue(krs, c.k, (t + 2) * C::BN, kbuf + (t & 1) * C::TILEB);
-      if (t + 1 < ntiles) issue(vrs, c.v, (t + 1) * C::BN, vbuf + ((t + 1) & 1) * C::TILEB);
+      if (t + 2 < ntiles) issue(krs, c.k, (t + 2) * C::BN, kbuf + (t & 1) * C::TILEB, ids_k);
+      if (t + 1 < ntiles)
+        issue(vrs, c.v, (t + 1) * C::BN, vbuf + ((t + 1) & 1) * C::TILEB, ids_v);
+      if constexpr (SRC == KEYS_PAGED) {
+        ids_v = ids_k;
+        if (t + 3 < ntiles) ids_k = block_ids((t + 3) * C::BN);
+      }
       if (t + 1 <= wlast) qk((t + 1) & 1, SN);
       if (t <= wlast) softmax_pv(t, SC);
     };
 
     using S0 = std::integral_constant<int, 0>;
     using S1 = std::integral_constant<int, 1>;
-    issue(krs, c.k, 0, kbuf);
-    issue(vrs, c.v, 0, vbuf);
-    if (ntiles > 1) issue(krs, c.k, C::BN, kbuf + C::TILEB);
+    {
+      const int ids0 = block_ids(0);
+      issue(krs, c.k, 0, kbuf, ids0);
+      issue(vrs, c.v, 0, vbuf, ids0);
+      if (ntiles > 1) {
+        ids_v = block_ids(C::BN);
+        issue(krs, c.k, C::BN, kbuf + C::TILEB, ids_v);
+      }
+      if (ntiles > 2) ids_k = block_ids(2 * C::BN);
+    }
     __builtin_amdgcn_s_waitcnt(0x0F70);
     __syncthreads();
     // K(0) is visible; K(1) and V(0) may still be in flight (waited for in step 0)
