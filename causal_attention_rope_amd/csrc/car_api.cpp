@@ -192,12 +192,17 @@ car_status car_attn_prefill(const void* q, const void* k, const void* v, void* o
 
   const Dtype dt = dtype == CAR_DTYPE_F32 ? F32 : BF16;
   const RopeFreq fr = make_freq(D, theta, pairing);
-  hipError_t e = launch_prefill_prep(dt, D, cache != nullptr && cache->block_table != nullptr,
-                                     is_int8(cache), cache != nullptr ? &c : nullptr, k, v,
-                                     workspace, B, Hkv, S, positions, fr, stream);
+  const bool paged = cache != nullptr && cache->block_table != nullptr;
+  // bf16 into a contiguous native cache: prompts at consecutive slots keep
+  // their rotated keys in the cache only, and the attention reads them there
+  const bool keys_in_cache = cache != nullptr && !paged && !is_int8(cache) && dt == BF16;
+  hipError_t e = launch_prefill_prep(dt, D, paged, is_int8(cache),
+                                     cache != nullptr ? &c : nullptr, k, v, workspace, B, Hkv,
+                                     S, positions, fr, keys_in_cache, stream);
   if (e != hipSuccess) return CAR_ERR_HIP;
   return from_hip(launch_prefill_attention(dt, D, q, workspace, v, out, B, Hq, Hkv, S,
-                                           positions, fr, scale, stream, timing()));
+                                           positions, fr, scale, keys_in_cache ? &c : nullptr,
+                                           stream, timing()));
 }
 
 car_status car_attn_prefill_cached(const void* q, const void* k, const void* v, void* out,

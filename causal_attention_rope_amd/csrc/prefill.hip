@@ -328,6 +328,9 @@ __global__ __launch_bounds__((Tile<D, tile_waves<SRC>()>::THREADS), 2) void pref
   } else if constexpr (SRC == KEYS_PROMPT) {
     kbase = kr + ((int64_t)b * Hkv + hk) * S * D;
     vbase = v + ((int64_t)b * Hkv + hk) * S * D;
+    int p0;  // keys the K pass left in the cache only (at consecutive slots p0..)
+    if (c.k != nullptr && prompt_rows_in_cache(positions, b, S, c.max_seq, &p0))
+      kbase = static_cast<const bf16_t*>(c.k) + (((int64_t)b * Hkv + hk) * c.max_seq + p0) * D;
   }
 
   // ---- direct buffer -> LDS loads of K and V tiles ----
@@ -727,8 +730,11 @@ hipError_t prefill_dispatch(Dtype dt, int D, const void* q, const KeySource& ks,
 hipError_t launch_prefill_attention(Dtype dt, int D, const void* q, const void* k_rot,
                                     const void* v, void* out, int B, int Hq, int Hkv, int S,
                                     const int32_t* positions, const RopeFreq& fr, float scale,
-                                    hipStream_t s, const TimedLaunch& tl) {
-  const KeySource ks{k_rot, v, CacheArgs{}, nullptr, nullptr};
+                                    const CacheArgs* kcache, hipStream_t s,
+                                    const TimedLaunch& tl) {
+  // the fp32 kernel always reads k_rot (its K pass never skips it)
+  const KeySource ks{k_rot, v, kcache != nullptr && dt == BF16 ? *kcache : CacheArgs{}, nullptr,
+                     nullptr};
   return prefill_dispatch<KEYS_PROMPT>(dt, D, q, ks, out, B, Hq, Hkv, S, positions, fr, scale, s,
                                        tl);
 }

@@ -97,7 +97,10 @@ __global__ __launch_bounds__(kThreads) void kv_append_kernel(CacheArgs c,
 
 // Rotate the prompt's keys once (dense copy for the attention kernel) and,
 // with a cache, store rotated keys and raw values at their positions.
-template <typename T, int D, bool PAGED, bool CACHE, bool I8>
+// KEYS_IN_CACHE (contiguous native cache): a prompt whose positions are
+// consecutive slots of the cache gets no dense copy; the attention kernel
+// reads its rotated keys from the cache rows instead.
+template <typename T, int D, bool PAGED, bool CACHE, bool I8, bool KEYS_IN_CACHE = false>
 __global__ __launch_bounds__(kThreads) void prefill_prep_kernel(
     CacheArgs c, const T* __restrict__ k, const T* __restrict__ v, T* __restrict__ k_rot,
     int Hkv, int S, const int32_t* __restrict__ positions, int64_t nvec, RopeFreq fr) {
@@ -114,7 +117,9 @@ __global__ __launch_bounds__(kThreads) void prefill_prep_kernel(
     float f[N];
     load16<T>(k + row * D + col, f);
     rope_rotate_chunk<T, N>(f, k + row * D, col, D, pos, fr);
-    store16<T>(k_rot + row * D + col, f);
+    int p0;
+    if (!KEYS_IN_CACHE || !prompt_rows_in_cache(positions, b, S, c.max_seq, &p0))
+      store16<T>(k_rot + row * D + col, f);
     if constexpr (CACHE) {
       const int hk = (int)(bh % Hkv);
       const int slot = min(max(pos, 0), cache_last_slot<PAGED>(c));
@@ -289,7 +294,7 @@ hipError_t kv_append_t(bool paged, const CacheArgs& c, const void* k, const void
 template <typename T, int D, bool I8>
 hipError_t prefill_prep_t(bool paged, const CacheArgs* cache, const void* k, const void* v,
                           void* k_rot, int B, int Hkv, int S, const int32_t* positions,
-                          const RopeFreq& fr, hipStream_t st) {
+                          const RopeFreq& fr, bool keys_in_cache, hipStream_t st) {
   const int64_t nvec = (int64_t)B * Hkv * S * (D / Vec16<T>::N);
   const T* kk = static_cast<const T*>(k);
   const T* vv = static_cast<const T*>(v);
@@ -302,6 +307,9 @@ hipError_t prefill_prep_t(bool paged, const CacheArgs* cache, const void* k, con
   } else if (paged) {
     hipLaunchKernelGGL((prefill_prep_kernel<T, D, true, true, I8>), grid, block, 0, st, *cache,
                        kk, vv, kr, Hkv, S, positions, nvec, fr);
+  } else if (!I8 && keys_in_cache) {
+    hipLaunchKernelGGL((prefill_prep_kernel<T, D, false, true, false, true>), grid, block, 0, st,
+                       *cache, kk, vv, kr, Hkv, S, positions, nvec, fr);
   } else {
     hipLaunchKernelGGL((prefill_prep_kernel<T, D, false, true, I8>), grid, block, 0, st,
                        *cache, kk, vv, kr, Hkv, S, positions, nvec, fr);
@@ -368,9 +376,9 @@ hipError_t launch_kv_append(Dtype dt, int D, bool paged, bool i8, const CacheArg
 hipError_t launch_prefill_prep(Dtype dt, int D, bool paged, bool i8, const CacheArgs* cache,
                                const void* k, const void* v, void* k_rot, int B, int Hkv,
                                int S, const int32_t* positions, const RopeFreq& fr,
-                               hipStream_t s) {
+                               bool keys_in_cache, hipStream_t s) {
 #define CAR_PREP(T, DD, I)                                                                    \
-  prefill_prep_t<T, DD, I>(paged, cache, k, v, k_rot, B, Hkv, S, positions, fr, s)
+  prefill_prep_t<T, DD, I>(paged, cache, k, v, k_rot, B, Hkv, S, positions, fr, keys_in_cache, s)
   if (i8 && cache != nullptr) {
     if (dt == F32) return D == 64 ? CAR_PREP(float, 64, true) : CAR_PREP(float, 128, true);
     return D == 64 ? CAR_PREP(bf16_t, 64, true) : CAR_PREP(bf16_t, 128, true);

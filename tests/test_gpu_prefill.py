@@ -75,6 +75,11 @@ def check_prefill(car, case, paged=False, cap=None, heads=None):
                     gv = cache.v[blk, hk, off]
                 worst = max(worst, max_abs(gk, k_rot[0, j]))
                 assert torch.equal(bits(gv.cpu()), bits(case.v[b, hk].cpu())), "cached V"
+    if cache is not None and heads is None:
+        # nothing but the prompt's rows was written (the cache starts as NaN)
+        for name, t in (("K", cache.k), ("V", cache.v)):
+            rows = (~torch.isnan(t.float()).all(dim=-1)).sum().item()
+            assert rows == case.B * case.Hkv * case.S, f"cache {name}: {rows} rows written"
     log_case(f"{case.name}: max-abs error {worst:.3e} (tol {tol})")
     assert worst <= tol
     return out, cache
@@ -103,6 +108,24 @@ def test_prefill_writes_cache_at_offset_positions(car, dtype, paged):
     log_case(f"prefill into cache {dtype} paged={paged}")
     case = W.prefill_case("offset", 2, 4, 2, 150, 64, dtype, 55, DEV, pos_offset=9)
     check_prefill(car, case, paged=paged, cap=200)
+
+
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("paged", [False, True], ids=["contiguous", "paged"])
+def test_prefill_cache_at_gapped_positions(car, D, paged):
+    """Strictly increasing positions with gaps (cache index = position, so
+    the stored rows are scattered) beside consecutive ones in one batch:
+    sequence 0 at slots 17..316 (its rotated keys are read back from the
+    cache), sequences 1 and 2 with different gaps (read from the dense
+    copy); GQA, two query tiles with a ragged tail."""
+    log_case(f"prefill bf16 into cache at gapped positions D={D} paged={paged}")
+    S, cap = 300, 1000
+    case = W.prefill_case("gapped", 3, 8, 2, S, D, torch.bfloat16, 91 + D, DEV)
+    rng = np.random.default_rng(D)
+    pos = np.stack([np.arange(S) + 17] +
+                   [np.sort(rng.choice(cap, S, replace=False)) for _ in range(2)])
+    case.positions = torch.from_numpy(pos.astype(np.int32)).to(DEV)
+    check_prefill(car, case, paged=paged, cap=cap)
 
 
 def test_prefill_many_tiles_bf16(car):
