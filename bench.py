@@ -247,6 +247,95 @@ def measure_int8_decode(car, W, dev, stream, new_event, iters: int = 20) -> dict
     return out
 
 
+def measure_small_prefills(car, W, dev, stream, new_event, iters: int = 20) -> dict:
+    """The two small workloads.  GPT-2-shaped prefill (B=4, H=12, D=64,
+    S=512, bf16, no cache): TFLOP/s against the bf16 peak and, since at 128
+    flop per byte it sits below the ridge, its bytes (q, k, v read, out
+    written) against the HBM peak.  The fp32 tiny case (B=1, H=4, D=64:
+    a 128-token prefill into a 144-slot cache, then 16 decode steps at
+    positions 128..143) as one sequence of 17 calls: its total time, the
+    prefill's TFLOP/s and the decode steps' tokens/s.  Both are launch-bound
+    sizes; the kernel time is the attention kernel's, the call time the
+    whole entry point's."""
+    import torch
+    out = {}
+    c2 = W.gpt2_prefill(dev)
+    o2 = torch.empty_like(c2.q)
+    ws2 = torch.empty(car.prefill_workspace_bytes(torch.bfloat16, c2.B, c2.Hkv, c2.S, c2.D),
+                      dtype=torch.uint8, device=dev)
+
+    def call2():
+        car.attn_prefill(c2.q, c2.k, c2.v, c2.positions, c2.theta, c2.scale, out=o2,
+                         workspace=ws2)
+    for _ in range(3):
+        call2()
+    pairs_k = [(new_event(), new_event()) for _ in range(iters)]
+    pairs_c = [(new_event(), new_event()) for _ in range(iters)]
+    for i in range(iters):
+        car.set_timing_events(*pairs_k[i])
+        pairs_c[i][0].record(stream)
+        call2()
+        pairs_c[i][1].record(stream)
+        car.set_timing_events(None, None)
+    torch.cuda.synchronize()
+    if not torch.isfinite(o2.float()).all():
+        raise RuntimeError("non-finite output in the GPT-2-shaped prefill")
+    kms = sorted(a.elapsed_time(b) for a, b in pairs_k)[iters // 2]
+    cms = sorted(a.elapsed_time(b) for a, b in pairs_c)[iters // 2]
+    fl = prefill_flops(c2.B, c2.Hq, c2.S, c2.D)
+    io = 4 * c2.B * c2.Hq * c2.S * c2.D * 2
+    out["gpt2_prefill"] = {
+        "workload": "B=4,H=12,D=64,S=512,bf16, no cache",
+        "kernel_ms": kms, "call_ms": cms,
+        "TFLOPs_kernel": fl / (kms * 1e-3) / 1e12, "TFLOPs_call": fl / (cms * 1e-3) / 1e12,
+        "mfma_frac_kernel": fl / (kms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
+        "hbm_frac_kernel": io / (kms * 1e-3) / 1e9 / PEAK_HBM_GBPS,
+        "per_launch": f"{fl} flops (2*B*H*D*S*(S+1)); {io} bytes (q, k, v, out)"}
+    del c2, o2, ws2
+
+    pre, steps = W.tiny(dev)
+    cache = car.KVCache(torch.zeros((1, 4, 144, 64), dtype=torch.float32, device=dev),
+                        torch.zeros((1, 4, 144, 64), dtype=torch.float32, device=dev))
+    o1 = torch.empty_like(pre.q)
+    ws1 = torch.empty(car.prefill_workspace_bytes(torch.float32, 1, 4, 128, 64),
+                      dtype=torch.uint8, device=dev)
+    od = torch.empty_like(steps[0][0])
+    wsd = torch.empty(car.decode_workspace_bytes(1, 4, 64, 144), dtype=torch.uint8, device=dev)
+    lens = [torch.tensor([128 + t], dtype=torch.int32, device=dev) for t in range(16)]
+
+    def seq1(ev=None):
+        if ev is not None:
+            ev[0].record(stream)
+        car.attn_prefill(pre.q, pre.k, pre.v, pre.positions, pre.theta, pre.scale,
+                         cache=cache, out=o1, workspace=ws1)
+        if ev is not None:
+            ev[1].record(stream)
+        for t, (q, kn, vn) in enumerate(steps):
+            car.attn_decode(q, kn, vn, lens[t], cache, 144, pre.theta, pre.scale, out=od,
+                            workspace=wsd)
+        if ev is not None:
+            ev[2].record(stream)
+    for _ in range(3):
+        seq1()
+    evs = [tuple(new_event() for _ in range(3)) for _ in range(iters)]
+    for i in range(iters):
+        seq1(evs[i])
+    torch.cuda.synchronize()
+    if not (torch.isfinite(o1).all() and torch.isfinite(od).all()):
+        raise RuntimeError("non-finite output in the fp32 tiny workload")
+    pms = sorted(a.elapsed_time(b) for a, b, _ in evs)[iters // 2]
+    dms = sorted(b.elapsed_time(c) for _, b, c in evs)[iters // 2]
+    fl1 = prefill_flops(1, 4, 128, 64)
+    out["tiny_prefill_decode_fp32"] = {
+        "workload": "B=1,H=4,D=64,fp32: prefill S=128 into a 144-slot cache, then 16 decode "
+                    "steps at positions 128..143",
+        "total_ms": pms + dms, "prefill_call_ms": pms, "decode_16_steps_ms": dms,
+        "prefill_TFLOPs_call": fl1 / (pms * 1e-3) / 1e12,
+        "decode_tokens_per_s": 16 / (dms * 1e-3),
+        "per_launch": f"prefill {fl1} flops (2*B*H*D*S*(S+1)); each step reads L*4*64*2*4 B"}
+    return out
+
+
 def main(argv=None) -> int:
     args = parse_args(argv)
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -346,6 +435,7 @@ def main(argv=None) -> int:
     if args.only is None and not args.no_extras:
         extras = measure_chunked(car, W, dev, stream, new_event)
         extras.update(measure_int8_decode(car, W, dev, stream, new_event))
+        extras.update(measure_small_prefills(car, W, dev, stream, new_event))
 
     # ---------------- figures ----------------
     kernels = {}

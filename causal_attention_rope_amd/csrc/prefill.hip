@@ -269,21 +269,24 @@ __device__ __forceinline__ int logical_chunk(int p, int r) {
   }
 }
 
-// Waves per workgroup (32 query rows each).  A whole prompt balances pairs of
-// query tiles over 8 waves; a chunk after a cached prefix has one tile per
-// workgroup, and with 4 waves (128 query rows) a 1024-token chunk of 32 heads
-// fills 256 workgroups instead of 128 (measured on a 3072-token prefix:
-// contiguous 104 -> 80 us; paged 120 -> 101 us).
-template <int SRC>
-constexpr int tile_waves() { return SRC == KEYS_PROMPT ? 8 : 4; }
+// Waves per workgroup (32 query rows each), W.  A whole prompt balances
+// pairs of query tiles over 8 waves (PAIRED).  A chunk after a cached prefix
+// has one tile per workgroup, and with 4 waves (128 query rows) a 1024-token
+// chunk of 32 heads fills 256 workgroups instead of 128 (measured on a
+// 3072-token prefix: contiguous 104 -> 80 us; paged 120 -> 101 us).  A short
+// prompt whose pairs would leave most compute units idle takes the same
+// 4-wave single-tile form (at B=4, H=12, S=512: 192 workgroups, not 48).
+template <int SRC, int W>
+constexpr bool paired() { return SRC == KEYS_PROMPT && W == 8; }
 
-template <int D, int SRC, int HALF>
-__global__ __launch_bounds__((Tile<D, tile_waves<SRC>()>::THREADS), 2) void prefill_bf16_kernel(
+template <int D, int SRC, int HALF, int W>
+__global__ __launch_bounds__((Tile<D, W>::THREADS), 2) void prefill_bf16_kernel(
     const bf16_t* __restrict__ q, const bf16_t* __restrict__ kr, const bf16_t* __restrict__ v,
     bf16_t* __restrict__ out, const int32_t* __restrict__ positions, int Hq, int Hkv, int S,
     int nqt, RopeFreq fr, float sm_scale_log2, CacheArgs c, const int32_t* __restrict__ seq_lens,
     const int32_t* __restrict__ chunk_lens) {
-  using C = Tile<D, tile_waves<SRC>()>;
+  using C = Tile<D, W>;
+  constexpr bool PAIRED = paired<SRC, W>();
   __shared__ __attribute__((aligned(1024))) char smem[2 * C::STAGEB];
 
   // ---- work assignment: balanced query-tile pairs, heads pinned to XCDs ----
@@ -295,7 +298,7 @@ __global__ __launch_bounds__((Tile<D, tile_waves<SRC>()>::THREADS), 2) void pref
   // [x*hpx, (x+1)*hpx), so query heads of one KV group share its L2.
   // With a cached prefix every query tile costs about the same (the prefix
   // dominates), so a workgroup then takes a single tile: twice the workgroups.
-  const int npair = SRC == KEYS_PROMPT ? (nqt + 1) >> 1 : nqt;
+  const int npair = PAIRED ? (nqt + 1) >> 1 : nqt;
   const int nbh = gridDim.x / npair;
   const int bid = blockIdx.x;
   int bh, pr;
@@ -426,9 +429,9 @@ __global__ __launch_bounds__((Tile<D, tile_waves<SRC>()>::THREADS), 2) void pref
   // ---- the pair's two query tiles, longest first ----
 #pragma nounroll
   for (int pass = 0; pass < 2; ++pass) {
-    const int qt = SRC != KEYS_PROMPT ? pr : (pass == 0 ? nqt - 1 - pr : pr);
+    const int qt = !PAIRED ? pr : (pass == 0 ? nqt - 1 - pr : pr);
     if (pass == 1) {
-      if (SRC != KEYS_PROMPT || qt == nqt - 1 - pr) break;  // one tile, or no partner
+      if (!PAIRED || qt == nqt - 1 - pr) break;  // one tile, or no partner
       __syncthreads();                // every wave is done with the LDS tiles
     }
     const int q0 = qt * C::BM;
@@ -681,19 +684,36 @@ hipError_t prefill_f32_t(const void* q, const KeySource& ks, void* out, int B, i
   return hipGetLastError();
 }
 
-template <int D, int SRC, int HALF>
-hipError_t prefill_bf16_t(const void* q, const KeySource& ks, void* out, int B, int Hq, int Hkv,
+template <int D, int SRC, int HALF, int W>
+hipError_t prefill_bf16_w(const void* q, const KeySource& ks, void* out, int B, int Hq, int Hkv,
                           int S, const int32_t* positions, const RopeFreq& fr, float scale,
                           hipStream_t st, const TimedLaunch& tl) {
-  using C = Tile<D, tile_waves<SRC>()>;
+  using C = Tile<D, W>;
   const int nqt = (S + C::BM - 1) / C::BM;
-  const int npair = SRC == KEYS_PROMPT ? (nqt + 1) / 2 : nqt;  // workgroups per head
-  hipExtLaunchKernelGGL((prefill_bf16_kernel<D, SRC, HALF>), dim3(npair * B * Hq), dim3(C::THREADS), 0,
+  const int npair = paired<SRC, W>() ? (nqt + 1) / 2 : nqt;  // workgroups per head
+  hipExtLaunchKernelGGL((prefill_bf16_kernel<D, SRC, HALF, W>), dim3(npair * B * Hq), dim3(C::THREADS), 0,
                         st, tl.start, tl.stop, 0, static_cast<const bf16_t*>(q),
                         static_cast<const bf16_t*>(ks.k_rot), static_cast<const bf16_t*>(ks.v),
                         static_cast<bf16_t*>(out), positions, Hq, Hkv, S, nqt, fr,
                         scale * 1.4426950408889634f, ks.c, ks.seq_lens, ks.chunk_lens);
   return hipGetLastError();
+}
+
+// MI355X compute units: a whole prompt whose 8-wave query-tile pairs number
+// fewer than this runs as 4-wave single tiles instead.
+constexpr int kComputeUnits = 256;
+
+template <int D, int SRC, int HALF>
+hipError_t prefill_bf16_t(const void* q, const KeySource& ks, void* out, int B, int Hq, int Hkv,
+                          int S, const int32_t* positions, const RopeFreq& fr, float scale,
+                          hipStream_t st, const TimedLaunch& tl) {
+  if constexpr (SRC == KEYS_PROMPT) {
+    const int64_t pairs = (int64_t)((S + Tile<D, 8>::BM - 1) / Tile<D, 8>::BM + 1) / 2 * B * Hq;
+    if (pairs >= kComputeUnits)
+      return prefill_bf16_w<D, SRC, HALF, 8>(q, ks, out, B, Hq, Hkv, S, positions, fr, scale, st,
+                                             tl);
+  }
+  return prefill_bf16_w<D, SRC, HALF, 4>(q, ks, out, B, Hq, Hkv, S, positions, fr, scale, st, tl);
 }
 
 template <int SRC, int HALF>

@@ -129,12 +129,24 @@ def test_prefill_cache_at_gapped_positions(car, D, paged):
 
 
 def test_prefill_many_tiles_bf16(car):
-    """Many KV tiles and an odd number of 256-row query tiles (5): two
+    """Many KV tiles and an odd number of 256-row query tiles (5) with enough
+    heads (90, so 270 query-tile pairs) for the 8-wave paired form: two
     workgroups per head take a long and a short tile, the middle tile runs
-    alone."""
-    log_case("prefill bf16 many tiles, odd query-tile count")
-    case = W.prefill_case("long", 1, 64, 64, 1100, 128, torch.bfloat16, 77, DEV)
-    check_prefill(car, case, heads=[0, 31, 63])
+    alone; 90 heads are not a multiple of the 8 XCDs, and pairs of query
+    heads share a KV head."""
+    log_case("prefill bf16 many tiles, odd query-tile count, 8-wave pairs")
+    case = W.prefill_case("long", 1, 90, 45, 1100, 128, torch.bfloat16, 77, DEV)
+    check_prefill(car, case, heads=[0, 45, 89])
+
+
+@pytest.mark.parametrize("D", [64, 128])
+def test_prefill_short_prompt_single_tiles(car, D):
+    """A prompt whose 8-wave pairs would fill few compute units (B=3, H=8,
+    S=700: 48 pairs) runs as 4-wave single query tiles: 6 tiles per head
+    with a ragged last one."""
+    log_case(f"prefill bf16 short prompt, 4-wave single tiles D={D}")
+    case = W.prefill_case("short", 3, 8, 4, 700, D, torch.bfloat16, 13 + D, DEV)
+    check_prefill(car, case)
 
 
 @pytest.mark.parametrize("D", [64, 128])
