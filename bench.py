@@ -148,6 +148,25 @@ def cpu_baseline(pf, c4, heads: int):
     }
 
 
+def timed_calls(car, call, stream, new_event, iters: int):
+    """Event pairs around `iters` whole calls, then around the main kernel
+    of `iters` further calls (the library records those; kept out of the
+    call iterations so that they add nothing to the call times)."""
+    import torch
+    pairs_c = [(new_event(), new_event()) for _ in range(iters)]
+    pairs_k = [(new_event(), new_event()) for _ in range(iters)]
+    for a, b in pairs_c:
+        a.record(stream)
+        call()
+        b.record(stream)
+    for a, b in pairs_k:
+        car.set_timing_events(a, b)
+        call()
+        car.set_timing_events(None, None)
+    torch.cuda.synchronize()
+    return pairs_k, pairs_c
+
+
 def measure_chunked(car, W, dev, stream, new_event, iters: int = 10) -> dict:
     """A 1024-token chunk continuing a 3072-token cached prefix, 32 query
     heads, D = 128, bf16: contiguous cache [1, 32, 4096, 128], and a paged
@@ -167,15 +186,7 @@ def measure_chunked(car, W, dev, stream, new_event, iters: int = 10) -> dict:
                                     case.theta, case.scale, out=o)
         for _ in range(2):
             call()
-        pairs_k = [(new_event(), new_event()) for _ in range(iters)]
-        pairs_c = [(new_event(), new_event()) for _ in range(iters)]
-        for i in range(iters):
-            car.set_timing_events(*pairs_k[i])
-            pairs_c[i][0].record(stream)
-            call()
-            pairs_c[i][1].record(stream)
-            car.set_timing_events(None, None)
-        torch.cuda.synchronize()
+        pairs_k, pairs_c = timed_calls(car, call, stream, new_event, iters)
         if not torch.isfinite(o.float()).all():
             raise RuntimeError(f"non-finite output in chunked prefill ({name})")
         kms = sum(a.elapsed_time(b) for a, b in pairs_k) / iters
@@ -219,15 +230,7 @@ def measure_int8_decode(car, W, dev, stream, new_event, iters: int = 20) -> dict
                             case.max_seq_len, case.theta, case.scale, out=o, workspace=ws)
         for _ in range(3):
             call()
-        pairs_k = [(new_event(), new_event()) for _ in range(iters)]
-        pairs_c = [(new_event(), new_event()) for _ in range(iters)]
-        for i in range(iters):
-            car.set_timing_events(*pairs_k[i])
-            pairs_c[i][0].record(stream)
-            call()
-            pairs_c[i][1].record(stream)
-            car.set_timing_events(None, None)
-        torch.cuda.synchronize()
+        pairs_k, pairs_c = timed_calls(car, call, stream, new_event, iters)
         if not torch.isfinite(o.float()).all():
             raise RuntimeError(f"non-finite output in int8 decode ({name})")
         kms = sum(a.elapsed_time(b) for a, b in pairs_k) / iters
@@ -269,15 +272,7 @@ def measure_small_prefills(car, W, dev, stream, new_event, iters: int = 20) -> d
                          workspace=ws2)
     for _ in range(3):
         call2()
-    pairs_k = [(new_event(), new_event()) for _ in range(iters)]
-    pairs_c = [(new_event(), new_event()) for _ in range(iters)]
-    for i in range(iters):
-        car.set_timing_events(*pairs_k[i])
-        pairs_c[i][0].record(stream)
-        call2()
-        pairs_c[i][1].record(stream)
-        car.set_timing_events(None, None)
-    torch.cuda.synchronize()
+    pairs_k, pairs_c = timed_calls(car, call2, stream, new_event, iters)
     if not torch.isfinite(o2.float()).all():
         raise RuntimeError("non-finite output in the GPT-2-shaped prefill")
     kms = sorted(a.elapsed_time(b) for a, b in pairs_k)[iters // 2]
@@ -380,10 +375,15 @@ def main(argv=None) -> int:
     ev = {s: {"call": [(new_event(), new_event()) for _ in range(n_ev)],
               "kernel": [(new_event(), new_event()) for _ in range(n_ev)]} for s in stages}
 
-    def run_stage(s, i=None):
+    def run_stage(s, i=None, kernel_events=False):
+        # call events bracket the whole entry point; with kernel_events the
+        # library brackets its main kernel instead (separate iterations, so
+        # that the inner events add nothing to the call times)
         if i is not None:
-            car.set_timing_events(*ev[s]["kernel"][i])
-            ev[s]["call"][i][0].record(stream)
+            if kernel_events:
+                car.set_timing_events(*ev[s]["kernel"][i])
+            else:
+                ev[s]["call"][i][0].record(stream)
         if s == "prefill":
             car.attn_prefill(pf.q, pf.k, pf.v, pf.positions, pf.theta, pf.scale,
                              cache=pf_cache, out=pf_out, workspace=pf_ws)
@@ -394,8 +394,10 @@ def main(argv=None) -> int:
             car.attn_decode(c5.q, c5.k_new, c5.v_new, c5.seq_lens, c5_cache, c5.max_seq_len,
                             c5.theta, c5.scale, out=c5_out, workspace=c5_ws)
         if i is not None:
-            ev[s]["call"][i][1].record(stream)
-            car.set_timing_events(None, None)
+            if kernel_events:
+                car.set_timing_events(None, None)
+            else:
+                ev[s]["call"][i][1].record(stream)
 
     if args.copy_calibration:
         src = torch.empty(COPY_BYTES, dtype=torch.uint8, device=dev)
@@ -416,6 +418,11 @@ def main(argv=None) -> int:
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms_per_step = wall / args.steps * 1e3
+    # the same steps again, untimed as a whole, for the per-kernel event times
+    for i in range(args.steps):
+        for s in stages:
+            run_stage(s, i, kernel_events=True)
+    torch.cuda.synchronize()
 
     def avg_ms(pairs):
         return sum(a.elapsed_time(b) for a, b in pairs) / len(pairs)

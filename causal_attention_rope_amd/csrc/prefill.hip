@@ -285,9 +285,17 @@ __global__ __launch_bounds__((Tile<D, W>::THREADS), 2) void prefill_bf16_kernel(
     bf16_t* __restrict__ out, const int32_t* __restrict__ positions, int Hq, int Hkv, int S,
     int nqt, RopeFreq fr, float sm_scale_log2, CacheArgs c, const int32_t* __restrict__ seq_lens,
     const int32_t* __restrict__ chunk_lens) {
-  using C = Tile<D, W>;
   constexpr bool PAIRED = paired<SRC, W>();
-  __shared__ __attribute__((aligned(1024))) char smem[2 * C::STAGEB];
+  // Chunk modes with 8 waves split the key range: waves 0..3 take the first
+  // half of the query tile's key tiles and waves 4..7 the second, each group
+  // with its own double-buffered K and V tiles; their partial results merge
+  // through LDS at the end.  (A chunk's query tiles all cost about the same,
+  // so 128-row tiles already give enough workgroups; the second wave per
+  // SIMD hides each other's latency as in the prompt kernel.)
+  constexpr bool KSPLIT = SRC != KEYS_PROMPT && W == 8;
+  constexpr int NGRP = KSPLIT ? 2 : 1;
+  using C = Tile<D, W / NGRP>;  // tile geometry of one group: BM query rows, its loads
+  __shared__ __attribute__((aligned(1024))) char smem[NGRP * 2 * C::STAGEB];
 
   // ---- work assignment: balanced query-tile pairs, heads pinned to XCDs ----
   // Query tile i needs i+1 key-tile rows of the causal triangle, so a
@@ -317,6 +325,8 @@ __global__ __launch_bounds__((Tile<D, W>::THREADS), 2) void prefill_bf16_kernel(
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform per wave
+  const int grp = KSPLIT ? wave / C::WAVES : 0;  // key-range group
+  const int wq = wave - grp * C::WAVES;           // wave within its group
   const int l32 = lane & 31, g = lane >> 5;
   // Keys: the prompt itself, or rows 0..P+S-1 of a cache that held P tokens
   // before this chunk; chunk query i sits at key index P+i.
@@ -358,7 +368,7 @@ __global__ __launch_bounds__((Tile<D, W>::THREADS), 2) void prefill_bf16_kernel(
   uint32_t dma_off[C::IPW];
 #pragma unroll
   for (int i = 0; i < C::IPW; ++i) {
-    const int row = (wave * C::IPW + i) * C::RPI + lane / C::CPR;
+    const int row = (wq * C::IPW + i) * C::RPI + lane / C::CPR;
     dma_off[i] = row * C::ROWB + (logical_chunk<C::CPR>(lane % C::CPR, row) << 4);
   }
   const int32_t* const trow = SRC == KEYS_PAGED ? c.table + (int64_t)b * c.mbps : nullptr;
@@ -376,32 +386,32 @@ __global__ __launch_bounds__((Tile<D, W>::THREADS), 2) void prefill_bf16_kernel(
       static_assert(16 % C::RPI == 0 && C::BN % 16 == 0, "a load stays inside one block");
 #pragma unroll
       for (int i = 0; i < C::IPW; ++i) {
-        const int r0 = (wave * C::IPW + i) * C::RPI;  // first tile row of this load
+        const int r0 = (wq * C::IPW + i) * C::RPI;  // first tile row of this load
         const int row = r0 + lane / C::CPR;
         const int j = min(j0 + row, nkeys - 1);        // rows past the end: the last key
         // the load's block (uniform); rows past the end keep the last key's block
         const int blk = __builtin_amdgcn_readlane(ids, min(r0, nkeys - 1 - j0) >> 4);
         const bf16_t* bp = static_cast<const bf16_t*>(pool) + (((int64_t)blk * Hkv + hk) << 4) * D;
         const uint32_t off = (j & 15) * C::ROWB + (logical_chunk<C::CPR>(lane % C::CPR, row) << 4);
-        dma16(make_rsrc(bp, 16 * C::ROWB), off, 0, dst + (wave * C::IPW + i) * 1024);
+        dma16(make_rsrc(bp, 16 * C::ROWB), off, 0, dst + (wq * C::IPW + i) * 1024);
       }
     } else if (j0 + C::BN <= nkeys) {  // uniform
       (void)ids;
 #pragma unroll
       for (int i = 0; i < C::IPW; ++i)
-        dma16(rs, dma_off[i], (uint32_t)j0 * C::ROWB, dst + (wave * C::IPW + i) * 1024);
+        dma16(rs, dma_off[i], (uint32_t)j0 * C::ROWB, dst + (wq * C::IPW + i) * 1024);
     } else {
 #pragma unroll
       for (int i = 0; i < C::IPW; ++i) {
-        const int row = (wave * C::IPW + i) * C::RPI + lane / C::CPR;
+        const int row = (wq * C::IPW + i) * C::RPI + lane / C::CPR;
         const uint32_t off = min(j0 + row, nkeys - 1) * C::ROWB +
                              (logical_chunk<C::CPR>(lane % C::CPR, row) << 4);
-        dma16(rs, off, 0, dst + (wave * C::IPW + i) * 1024);
+        dma16(rs, off, 0, dst + (wq * C::IPW + i) * 1024);
       }
     }
   };
-  char* const kbuf = smem;                    // [2][TILEB]
-  char* const vbuf = smem + 2 * C::TILEB;     // [2][TILEB]
+  char* const kbuf = smem + grp * 2 * C::STAGEB;  // [2][TILEB] of this group
+  char* const vbuf = kbuf + 2 * C::TILEB;         // [2][TILEB]
 
   // ---- per-lane LDS read offsets (bytes within a tile) ----
   // K operand (S^T = K Q^T, A = K rows): row kb*32 + l32, chunk 2*kk + g.
@@ -435,10 +445,10 @@ __global__ __launch_bounds__((Tile<D, W>::THREADS), 2) void prefill_bf16_kernel(
       __syncthreads();                // every wave is done with the LDS tiles
     }
     const int q0 = qt * C::BM;
-    const int qw = q0 + wave * 32;             // first query row of this wave
+    const int qw = q0 + wq * 32;               // first query row of this wave
     const int qrow = qw + l32;                 // this lane's query row
     if (SRC != KEYS_PROMPT && q0 >= Sb) {  // padding rows only (uniform): zeros
-      if (qrow < S) {
+      if (grp == 0 && qrow < S) {
         bf16_t* op = out + ((int64_t)bh * S + qrow) * D;
   #pragma unroll
         for (int db = 0; db < C::NDB; ++db)
@@ -479,6 +489,12 @@ __global__ __launch_bounds__((Tile<D, W>::THREADS), 2) void prefill_bf16_kernel(
     const int ntiles = (P + q_end + C::BN - 1) / C::BN;
     // tiles 0..wlast hold keys visible to this wave (uniform per wave)
     const int wlast = min(ntiles - 1, (P + qw + 31) / C::BN);
+    // this wave's group walks tiles tbeg .. tbeg+tcnt-1; the lambdas below
+    // take the local index t - tbeg, which also picks the LDS buffers
+    const int nt0 = KSPLIT ? (ntiles + 1) >> 1 : ntiles;  // steps of the launch
+    const int tbeg = grp == 0 ? 0 : nt0;
+    const int tcnt = grp == 0 ? nt0 : ntiles - nt0;
+    const int ulast = min(wlast - tbeg, tcnt - 1);  // local index of the last visible tile
 
     // S^T = K Q^T for the tile in K buffer kb_i: lane holds keys
     // kb*32 + 8*(r/4) + 4*g + r%4 of query qrow.  The two 32-key blocks are
@@ -517,7 +533,7 @@ __global__ __launch_bounds__((Tile<D, W>::THREADS), 2) void prefill_bf16_kernel(
     // most tiles.
     auto softmax_pv = [&](int t, auto SI) {
       constexpr int si = decltype(SI)::value;
-      const int j0 = t * C::BN;
+      const int j0 = (tbeg + t) * C::BN;
       if (j0 + C::BN - 1 > P + qw) {  // causal mask where the tile passes this wave's first row
   #pragma unroll
         for (int kb = 0; kb < C::NKB; ++kb)
@@ -536,7 +552,11 @@ __global__ __launch_bounds__((Tile<D, W>::THREADS), 2) void prefill_bf16_kernel(
       const bool grow = (mt - m_run) * sm_scale_log2 > kRescaleLog2;
       if (__builtin_amdgcn_ballot_w64(grow) != 0) {  // wave-uniform branch
         const float m_new = fmaxf(m_run, mt);
-        const float alpha = fast_exp2((m_run - m_new) * sm_scale_log2);
+        // (a row of key group 1 with no visible key so far keeps m = -inf and
+        // alpha = 1 instead of exp2(-inf + inf))
+        const float alpha = KSPLIT && m_new == -INFINITY
+                                ? 1.f
+                                : fast_exp2((m_run - m_new) * sm_scale_log2);
         m_run = m_new;
         l_run *= alpha;
   #pragma unroll
@@ -544,7 +564,8 @@ __global__ __launch_bounds__((Tile<D, W>::THREADS), 2) void prefill_bf16_kernel(
   #pragma unroll
           for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
       }
-      const float mc = m_run * sm_scale_log2;
+      // Such a row's P must be 0, not exp2(-inf + inf).
+      const float mc = KSPLIT && m_run == -INFINITY ? INFINITY : m_run * sm_scale_log2;
 
       // P (bf16) in the B-operand layout of O^T = V^T P^T; l sums the rounded P
       bf16x8_t pf[C::PKS];
@@ -606,40 +627,73 @@ __global__ __launch_bounds__((Tile<D, W>::THREADS), 2) void prefill_bf16_kernel(
     // V(t+1), issue QK^T of tile t+1 into sacc[SN], then softmax and P V of t.
     // Paged: block ids of tiles t+1 (V loads of step t), t+2 (K loads) and
     // t+3 (read during step t for the next step).
+    // (t is the group's local tile index throughout.)
     int ids_v = 0, ids_k = 0;
     auto step = [&](int t, auto SC, auto SN) {
       __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's loads landed
       __syncthreads();                     // everyone's loads landed; old buffers free
-      if (t + 2 < ntiles) issue(krs, c.k, (t + 2) * C::BN, kbuf + (t & 1) * C::TILEB, ids_k);
-      if (t + 1 < ntiles)
-        issue(vrs, c.v, (t + 1) * C::BN, vbuf + ((t + 1) & 1) * C::TILEB, ids_v);
+      if (t + 2 < tcnt)
+        issue(krs, c.k, (tbeg + t + 2) * C::BN, kbuf + (t & 1) * C::TILEB, ids_k);
+      if (t + 1 < tcnt)
+        issue(vrs, c.v, (tbeg + t + 1) * C::BN, vbuf + ((t + 1) & 1) * C::TILEB, ids_v);
       if constexpr (SRC == KEYS_PAGED) {
         ids_v = ids_k;
-        if (t + 3 < ntiles) ids_k = block_ids((t + 3) * C::BN);
+        if (t + 3 < tcnt) ids_k = block_ids((tbeg + t + 3) * C::BN);
       }
-      if (t + 1 <= wlast) qk((t + 1) & 1, SN);
-      if (t <= wlast) softmax_pv(t, SC);
+      if (t + 1 <= ulast) qk((t + 1) & 1, SN);
+      if (t <= ulast) softmax_pv(t, SC);
     };
 
     using S0 = std::integral_constant<int, 0>;
     using S1 = std::integral_constant<int, 1>;
-    {
-      const int ids0 = block_ids(0);
-      issue(krs, c.k, 0, kbuf, ids0);
-      issue(vrs, c.v, 0, vbuf, ids0);
-      if (ntiles > 1) {
-        ids_v = block_ids(C::BN);
-        issue(krs, c.k, C::BN, kbuf + C::TILEB, ids_v);
+    if (tcnt > 0) {
+      const int ids0 = block_ids(tbeg * C::BN);
+      issue(krs, c.k, tbeg * C::BN, kbuf, ids0);
+      issue(vrs, c.v, tbeg * C::BN, vbuf, ids0);
+      if (tcnt > 1) {
+        ids_v = block_ids((tbeg + 1) * C::BN);
+        issue(krs, c.k, (tbeg + 1) * C::BN, kbuf + C::TILEB, ids_v);
       }
-      if (ntiles > 2) ids_k = block_ids(2 * C::BN);
+      if (tcnt > 2) ids_k = block_ids((tbeg + 2) * C::BN);
     }
     __builtin_amdgcn_s_waitcnt(0x0F70);
     __syncthreads();
     // K(0) is visible; K(1) and V(0) may still be in flight (waited for in step 0)
-    qk(0, S0{});
-    for (int t = 0; t < ntiles; t += 2) {
+    if (ulast >= 0) qk(0, S0{});
+    for (int t = 0; t < nt0; t += 2) {
       step(t, S0{}, S1{});
-      if (t + 1 < ntiles) step(t + 1, S1{}, S0{});
+      if (t + 1 < nt0) step(t + 1, S1{}, S0{});
+    }
+
+    if constexpr (KSPLIT) {
+      // Group 1 hands its running maximum, sum and O to the wave of group 0
+      // with the same query rows, lane by lane through LDS (the tile buffers
+      // are free once every wave has passed the barrier); that wave merges
+      // them by the online-softmax rule and stores the rows.  A wave of
+      // group 1 that saw no visible key has m = -inf and contributes zero.
+      constexpr int NV = C::NDB * 16 + 2;  // floats per lane
+      float* const xo = reinterpret_cast<float*>(smem) + wq * NV * 64;
+      __syncthreads();
+      if (grp == 1) {
+  #pragma unroll
+        for (int db = 0; db < C::NDB; ++db)
+  #pragma unroll
+          for (int r = 0; r < 16; ++r) xo[(db * 16 + r) * 64 + lane] = oacc[db][r];
+        xo[(NV - 2) * 64 + lane] = m_run;
+        xo[(NV - 1) * 64 + lane] = l_run;
+      }
+      __syncthreads();
+      if (grp == 1) continue;  // (no later barrier: group 0 only merges and stores)
+      const float m1 = xo[(NV - 2) * 64 + lane];
+      const float m = fmaxf(m_run, m1);  // m_run is finite: key 0 is visible to every row
+      const float a0 = fast_exp2((m_run - m) * sm_scale_log2);
+      const float a1 = fast_exp2((m1 - m) * sm_scale_log2);
+      l_run = l_run * a0 + xo[(NV - 1) * 64 + lane] * a1;
+  #pragma unroll
+      for (int db = 0; db < C::NDB; ++db)
+  #pragma unroll
+        for (int r = 0; r < 16; ++r)
+          oacc[db][r] = oacc[db][r] * a0 + xo[(db * 16 + r) * 64 + lane] * a1;
     }
 
     // ---- normalise and store: lane holds query qrow, dims db*32+8*(r/4)+4g+r%4 ----
@@ -688,10 +742,11 @@ template <int D, int SRC, int HALF, int W>
 hipError_t prefill_bf16_w(const void* q, const KeySource& ks, void* out, int B, int Hq, int Hkv,
                           int S, const int32_t* positions, const RopeFreq& fr, float scale,
                           hipStream_t st, const TimedLaunch& tl) {
-  using C = Tile<D, W>;
+  constexpr bool ksplit = SRC != KEYS_PROMPT && W == 8;  // two key-range groups
+  using C = Tile<D, ksplit ? W / 2 : W>;                 // BM query rows per workgroup
   const int nqt = (S + C::BM - 1) / C::BM;
   const int npair = paired<SRC, W>() ? (nqt + 1) / 2 : nqt;  // workgroups per head
-  hipExtLaunchKernelGGL((prefill_bf16_kernel<D, SRC, HALF, W>), dim3(npair * B * Hq), dim3(C::THREADS), 0,
+  hipExtLaunchKernelGGL((prefill_bf16_kernel<D, SRC, HALF, W>), dim3(npair * B * Hq), dim3(64 * W), 0,
                         st, tl.start, tl.stop, 0, static_cast<const bf16_t*>(q),
                         static_cast<const bf16_t*>(ks.k_rot), static_cast<const bf16_t*>(ks.v),
                         static_cast<bf16_t*>(out), positions, Hq, Hkv, S, nqt, fr,
@@ -712,8 +767,12 @@ hipError_t prefill_bf16_t(const void* q, const KeySource& ks, void* out, int B, 
     if (pairs >= kComputeUnits)
       return prefill_bf16_w<D, SRC, HALF, 8>(q, ks, out, B, Hq, Hkv, S, positions, fr, scale, st,
                                              tl);
+    return prefill_bf16_w<D, SRC, HALF, 4>(q, ks, out, B, Hq, Hkv, S, positions, fr, scale, st,
+                                           tl);
+  } else {  // chunks: 128-row query tiles, the key range split over two 4-wave groups
+    return prefill_bf16_w<D, SRC, HALF, 8>(q, ks, out, B, Hq, Hkv, S, positions, fr, scale, st,
+                                           tl);
   }
-  return prefill_bf16_w<D, SRC, HALF, 4>(q, ks, out, B, Hq, Hkv, S, positions, fr, scale, st, tl);
 }
 
 template <int SRC, int HALF>
