@@ -269,32 +269,31 @@ __device__ __forceinline__ int logical_chunk(int p, int r) {
   }
 }
 
-// Waves per workgroup (32 query rows each), W.  A whole prompt balances
-// pairs of query tiles over 8 waves (PAIRED).  A chunk after a cached prefix
-// has one tile per workgroup, and with 4 waves (128 query rows) a 1024-token
-// chunk of 32 heads fills 256 workgroups instead of 128 (measured on a
-// 3072-token prefix: contiguous 104 -> 80 us; paged 120 -> 101 us).  A short
-// prompt whose pairs would leave most compute units idle takes the same
-// 4-wave single-tile form (at B=4, H=12, S=512: 192 workgroups, not 48).
-template <int SRC, int W>
-constexpr bool paired() { return SRC == KEYS_PROMPT && W == 8; }
+// Workgroup forms, 8 waves (two per SIMD) either way:
+//  * FORM_PAIR: 256 query rows (32 per wave) over the whole key range, and a
+//    workgroup takes a long and a short query tile of a whole prompt;
+//  * FORM_SPLIT: 128 query rows, one tile per workgroup, its key range split
+//    over two groups of 4 waves (see KSPLIT below).  Chunks after a cached
+//    prefix, whose tiles all cost about the same, and short prompts whose
+//    pairs would leave most compute units idle take it: a 1024-token chunk
+//    of 32 heads gets 256 workgroups, and B=4, H=12, S=512 gets 192, not 48.
+constexpr int FORM_PAIR = 0;
+constexpr int FORM_SPLIT = 1;
 
-template <int D, int SRC, int HALF, int W>
-__global__ __launch_bounds__((Tile<D, W>::THREADS), 2) void prefill_bf16_kernel(
+template <int D, int SRC, int HALF, int FORM>
+__global__ __launch_bounds__((Tile<D, 8>::THREADS), 2) void prefill_bf16_kernel(
     const bf16_t* __restrict__ q, const bf16_t* __restrict__ kr, const bf16_t* __restrict__ v,
     bf16_t* __restrict__ out, const int32_t* __restrict__ positions, int Hq, int Hkv, int S,
     int nqt, RopeFreq fr, float sm_scale_log2, CacheArgs c, const int32_t* __restrict__ seq_lens,
     const int32_t* __restrict__ chunk_lens) {
-  constexpr bool PAIRED = paired<SRC, W>();
-  // Chunk modes with 8 waves split the key range: waves 0..3 take the first
-  // half of the query tile's key tiles and waves 4..7 the second, each group
-  // with its own double-buffered K and V tiles; their partial results merge
-  // through LDS at the end.  (A chunk's query tiles all cost about the same,
-  // so 128-row tiles already give enough workgroups; the second wave per
-  // SIMD hides each other's latency as in the prompt kernel.)
-  constexpr bool KSPLIT = SRC != KEYS_PROMPT && W == 8;
+  constexpr bool PAIRED = FORM == FORM_PAIR;
+  // FORM_SPLIT: waves 0..3 take the first half of the query tile's key tiles
+  // and waves 4..7 the second, each group with its own double-buffered K and
+  // V tiles; their partial results merge through LDS at the end.  The second
+  // wave per SIMD hides the other's latency as in the paired form.
+  constexpr bool KSPLIT = FORM == FORM_SPLIT;
   constexpr int NGRP = KSPLIT ? 2 : 1;
-  using C = Tile<D, W / NGRP>;  // tile geometry of one group: BM query rows, its loads
+  using C = Tile<D, 8 / NGRP>;  // tile geometry of one group: BM query rows, its loads
   __shared__ __attribute__((aligned(1024))) char smem[NGRP * 2 * C::STAGEB];
 
   // ---- work assignment: balanced query-tile pairs, heads pinned to XCDs ----
@@ -738,15 +737,14 @@ hipError_t prefill_f32_t(const void* q, const KeySource& ks, void* out, int B, i
   return hipGetLastError();
 }
 
-template <int D, int SRC, int HALF, int W>
+template <int D, int SRC, int HALF, int FORM>
 hipError_t prefill_bf16_w(const void* q, const KeySource& ks, void* out, int B, int Hq, int Hkv,
                           int S, const int32_t* positions, const RopeFreq& fr, float scale,
                           hipStream_t st, const TimedLaunch& tl) {
-  constexpr bool ksplit = SRC != KEYS_PROMPT && W == 8;  // two key-range groups
-  using C = Tile<D, ksplit ? W / 2 : W>;                 // BM query rows per workgroup
+  using C = Tile<D, FORM == FORM_SPLIT ? 4 : 8>;  // BM query rows per workgroup
   const int nqt = (S + C::BM - 1) / C::BM;
-  const int npair = paired<SRC, W>() ? (nqt + 1) / 2 : nqt;  // workgroups per head
-  hipExtLaunchKernelGGL((prefill_bf16_kernel<D, SRC, HALF, W>), dim3(npair * B * Hq), dim3(64 * W), 0,
+  const int npair = FORM == FORM_PAIR ? (nqt + 1) / 2 : nqt;  // workgroups per head
+  hipExtLaunchKernelGGL((prefill_bf16_kernel<D, SRC, HALF, FORM>), dim3(npair * B * Hq), dim3(512), 0,
                         st, tl.start, tl.stop, 0, static_cast<const bf16_t*>(q),
                         static_cast<const bf16_t*>(ks.k_rot), static_cast<const bf16_t*>(ks.v),
                         static_cast<bf16_t*>(out), positions, Hq, Hkv, S, nqt, fr,
@@ -754,8 +752,8 @@ hipError_t prefill_bf16_w(const void* q, const KeySource& ks, void* out, int B, 
   return hipGetLastError();
 }
 
-// MI355X compute units: a whole prompt whose 8-wave query-tile pairs number
-// fewer than this runs as 4-wave single tiles instead.
+// MI355X compute units: a whole prompt whose query-tile pairs number fewer
+// than this runs in the split form instead.
 constexpr int kComputeUnits = 256;
 
 template <int D, int SRC, int HALF>
@@ -765,14 +763,11 @@ hipError_t prefill_bf16_t(const void* q, const KeySource& ks, void* out, int B, 
   if constexpr (SRC == KEYS_PROMPT) {
     const int64_t pairs = (int64_t)((S + Tile<D, 8>::BM - 1) / Tile<D, 8>::BM + 1) / 2 * B * Hq;
     if (pairs >= kComputeUnits)
-      return prefill_bf16_w<D, SRC, HALF, 8>(q, ks, out, B, Hq, Hkv, S, positions, fr, scale, st,
-                                             tl);
-    return prefill_bf16_w<D, SRC, HALF, 4>(q, ks, out, B, Hq, Hkv, S, positions, fr, scale, st,
-                                           tl);
-  } else {  // chunks: 128-row query tiles, the key range split over two 4-wave groups
-    return prefill_bf16_w<D, SRC, HALF, 8>(q, ks, out, B, Hq, Hkv, S, positions, fr, scale, st,
-                                           tl);
+      return prefill_bf16_w<D, SRC, HALF, FORM_PAIR>(q, ks, out, B, Hq, Hkv, S, positions, fr,
+                                                     scale, st, tl);
   }
+  return prefill_bf16_w<D, SRC, HALF, FORM_SPLIT>(q, ks, out, B, Hq, Hkv, S, positions, fr, scale,
+                                                  st, tl);
 }
 
 template <int SRC, int HALF>

@@ -140,11 +140,12 @@ def test_prefill_many_tiles_bf16(car):
 
 
 @pytest.mark.parametrize("D", [64, 128])
-def test_prefill_short_prompt_single_tiles(car, D):
-    """A prompt whose 8-wave pairs would fill few compute units (B=3, H=8,
-    S=700: 48 pairs) runs as 4-wave single query tiles: 6 tiles per head
-    with a ragged last one."""
-    log_case(f"prefill bf16 short prompt, 4-wave single tiles D={D}")
+def test_prefill_short_prompt_split_form(car, D):
+    """A prompt whose query-tile pairs would fill few compute units (B=3,
+    H=8, S=700: 48 pairs) runs in the split form: one 128-row query tile per
+    workgroup (6 per head, the last ragged), its key range split over two
+    wave groups, rows of the second group that see none of its keys."""
+    log_case(f"prefill bf16 short prompt, split form D={D}")
     case = W.prefill_case("short", 3, 8, 4, 700, D, torch.bfloat16, 13 + D, DEV)
     check_prefill(car, case)
 
