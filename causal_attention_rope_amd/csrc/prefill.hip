@@ -177,6 +177,7 @@ typedef short s16x4_t __attribute__((ext_vector_type(4)));
 
 constexpr uint32_t kOnePair = 0x3F803F80u;  // (1.0, 1.0) in bf16
 constexpr float kRescaleLog2 = 8.f;          // largest exp2 argument allowed before rescaling
+constexpr float kFastMax = 16777216.f;       // 2^24: largest per-lane tile sum of P kept as is
 
 __device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
   return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a),
@@ -542,45 +543,62 @@ __global__ __launch_bounds__((Tile<D, 8>::THREADS), 2) void prefill_bf16_kernel(
             if (key > P + qrow) sacc[si][kb][r] = -INFINITY;
           }
       }
-      float mt = -INFINITY;
-  #pragma unroll
-      for (int kb = 0; kb < C::NKB; ++kb)
-  #pragma unroll
-        for (int r = 0; r < 16; ++r) mt = fmaxf(mt, sacc[si][kb][r]);
-      mt = fmaxf(mt, swap_halves(mt));
-      const bool grow = (mt - m_run) * sm_scale_log2 > kRescaleLog2;
-      if (__builtin_amdgcn_ballot_w64(grow) != 0) {  // wave-uniform branch
-        const float m_new = fmaxf(m_run, mt);
-        // (a row of key group 1 with no visible key so far keeps m = -inf and
-        // alpha = 1 instead of exp2(-inf + inf))
-        const float alpha = KSPLIT && m_new == -INFINITY
-                                ? 1.f
-                                : fast_exp2((m_run - m_new) * sm_scale_log2);
-        m_run = m_new;
-        l_run *= alpha;
-  #pragma unroll
-        for (int db = 0; db < C::NDB; ++db)
-  #pragma unroll
-          for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
-      }
-      // Such a row's P must be 0, not exp2(-inf + inf).
-      const float mc = KSPLIT && m_run == -INFINITY ? INFINITY : m_run * sm_scale_log2;
-
-      // P (bf16) in the B-operand layout of O^T = V^T P^T; l sums the rounded P
+      // P (bf16) in the B-operand layout of O^T = V^T P^T against the
+      // reference mc; lt sums the rounded P of this lane's keys
       bf16x8_t pf[C::PKS];
+      float lt;
+      auto make_p = [&](float mc) {
+        lt = 0.f;
   #pragma unroll
-      for (int kk = 0; kk < C::PKS; ++kk) {
-        uint32_t pw[4];
+        for (int kk = 0; kk < C::PKS; ++kk) {
+          uint32_t pw[4];
   #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const float p0 = fast_exp2(fmaf(sacc[si][kk >> 1][8 * (kk & 1) + 2 * i], sm_scale_log2, -mc));
-          const float p1 = fast_exp2(fmaf(sacc[si][kk >> 1][8 * (kk & 1) + 2 * i + 1], sm_scale_log2, -mc));
-          pw[i] = cvt_pk_bf16(p0, p1);
-          l_run = dot2_bf16(pw[i], kOnePair, l_run);
+          for (int i = 0; i < 4; ++i) {
+            const float p0 = fast_exp2(fmaf(sacc[si][kk >> 1][8 * (kk & 1) + 2 * i], sm_scale_log2, -mc));
+            const float p1 = fast_exp2(fmaf(sacc[si][kk >> 1][8 * (kk & 1) + 2 * i + 1], sm_scale_log2, -mc));
+            pw[i] = cvt_pk_bf16(p0, p1);
+            lt = dot2_bf16(pw[i], kOnePair, lt);
+          }
+          const u32x4_t u = {pw[0], pw[1], pw[2], pw[3]};
+          pf[kk] = __builtin_bit_cast(bf16x8_t, u);
         }
-        const u32x4_t u = {pw[0], pw[1], pw[2], pw[3]};
-        pf[kk] = __builtin_bit_cast(bf16x8_t, u);
+      };
+      // Fast path: P against the current reference m_run, kept unless some
+      // lane's sum of it exceeds 2^kFastLog2 or is not finite (a score far
+      // above m_run).  P up to that size is as exact in bf16 and as safe in
+      // the fp32 sums as P up to 1, so the row maximum is only computed for
+      // a wave's first tile and when the check fails.
+      bool redo = __builtin_amdgcn_ballot_w64(m_run == -INFINITY) != 0;  // first tile
+      if (!redo) {
+        make_p(m_run * sm_scale_log2);
+        redo = __builtin_amdgcn_ballot_w64(!(lt <= kFastMax)) != 0;  // also NaN, inf
       }
+      if (redo) {  // wave-uniform
+        float mt = -INFINITY;
+  #pragma unroll
+        for (int kb = 0; kb < C::NKB; ++kb)
+  #pragma unroll
+          for (int r = 0; r < 16; ++r) mt = fmaxf(mt, sacc[si][kb][r]);
+        mt = fmaxf(mt, swap_halves(mt));
+        const bool grow = (mt - m_run) * sm_scale_log2 > kRescaleLog2;
+        if (__builtin_amdgcn_ballot_w64(grow) != 0) {  // wave-uniform branch
+          const float m_new = fmaxf(m_run, mt);
+          // (a row of key group 1 with no visible key so far keeps m = -inf and
+          // alpha = 1 instead of exp2(-inf + inf))
+          const float alpha = KSPLIT && m_new == -INFINITY
+                                  ? 1.f
+                                  : fast_exp2((m_run - m_new) * sm_scale_log2);
+          m_run = m_new;
+          l_run *= alpha;
+  #pragma unroll
+          for (int db = 0; db < C::NDB; ++db)
+  #pragma unroll
+            for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
+        }
+        // Such a row's P must be 0, not exp2(-inf + inf).
+        make_p(KSPLIT && m_run == -INFINITY ? INFINITY : m_run * sm_scale_log2);
+      }
+      l_run += lt;
 
       // O^T += V^T P^T: operand i is k-step i / NDB (16 keys) of head-dim
       // block i % NDB, from two transposing reads.  At D = 128 the operands

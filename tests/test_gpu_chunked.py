@@ -105,6 +105,34 @@ def test_one_token_chunk(car, dtype):
     run_and_check(car, case)
 
 
+@pytest.mark.parametrize("paged", [False, True], ids=["contiguous", "paged"])
+def test_chunk_scores_jump_after_first_keys(car, paged):
+    """The first 128 cached keys score over 140 below (in log2 units) the
+    later cached keys and the chunk's own, with zero values (queries 12 and
+    those keys -12 in the last 8 dims, every other key 0 there): the key
+    group that starts with them must raise its running maximum and rescale
+    at the next tile, where exponentials against the old maximum would
+    overflow fp32."""
+    log_case(f"chunk bf16 score jump paged={paged}")
+    case = W.chunk_case("jump", 2, 4, 2, 100, 128, torch.bfloat16, [200, 333], 590, DEV,
+                        paged=paged)
+    case.q[..., -8:] = 12.0
+    case.k[..., -8:] = 0.0
+    if paged:
+        table = case.block_table.cpu().numpy()
+        for b in range(case.B):
+            lo = torch.as_tensor(table[b, :8], device=DEV, dtype=torch.long)  # tokens 0..127
+            hi = torch.as_tensor(table[b, 8:], device=DEV, dtype=torch.long)
+            case.cache_k[lo, :, :, -8:] = -12.0
+            case.cache_v[lo] = 0.0
+            case.cache_k[hi, :, :, -8:] = 0.0
+    else:
+        case.cache_k[:, :, :128, -8:] = -12.0
+        case.cache_k[:, :, 128:, -8:] = 0.0
+        case.cache_v[:, :, :128] = 0.0
+    run_and_check(car, case)
+
+
 def test_prompt_in_two_chunks_matches_whole_prompt_oracle(car):
     """Chunk [0, 300) then chunk [300, 600) of one prompt over one cache:
     both chunks' outputs against the whole-prompt oracle rows."""

@@ -128,6 +128,35 @@ def test_prefill_cache_at_gapped_positions(car, D, paged):
     check_prefill(car, case, paged=paged, cap=cap)
 
 
+def low_first_keys(q, k, v, n_low):
+    """Make keys 0..n_low-1 score about 1152/sqrt(D) below the others (over
+    140 in log2 units at D <= 128) against every query while the other keys
+    score O(1): queries hold 12 in their last 8 dims, the first keys -12
+    there and the others 0 (RoPE turns those dims by under 0.1 rad over
+    these positions), and the first keys' values are 0.  Exponentials of the
+    later keys against the first keys' maximum would overflow fp32, yet
+    every output is well conditioned: rows that see only the first keys
+    average zeros exactly."""
+    q[..., -8:] = 12.0
+    k[:, :, :n_low, -8:] = -12.0
+    k[:, :, n_low:, -8:] = 0.0
+    v[:, :, :n_low] = 0.0
+
+
+@pytest.mark.parametrize("form,D", [("split", 64), ("split", 128), ("paired", 128)])
+def test_prefill_scores_jump_after_first_keys(car, form, D):
+    """The first 128 keys score far below the rest (see low_first_keys), so
+    the online softmax must raise its running maximum and rescale when the
+    later tiles arrive; P against the low reference would overflow.  The
+    paired form needs enough heads (256, 3 checked)."""
+    log_case(f"prefill bf16 score jump form={form} D={D}")
+    H = 256 if form == "paired" else 4
+    case = W.prefill_case("jump", 1, H, H, 600, D, torch.bfloat16, 71 + D, DEV)
+    low_first_keys(case.q, case.k, case.v, 128)
+    out, _ = check_prefill(car, case, heads=[0, 101, 255] if form == "paired" else None)
+    assert torch.equal(out[:, :, :128], torch.zeros_like(out[:, :, :128]))
+
+
 def test_prefill_many_tiles_bf16(car):
     """Many KV tiles and an odd number of 256-row query tiles (5) with enough
     heads (90, so 270 query-tile pairs) for the 8-wave paired form: two
