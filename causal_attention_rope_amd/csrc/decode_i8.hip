@@ -438,6 +438,323 @@ __attribute__((amdgpu_waves_per_eu(G == 1 ? 4 : 2))) void decode_i8_split_kernel
   }
 }
 
+// ---------------------------------------- several heads: the matrix cores ---
+// With G = Hq/Hkv query heads (2..8) per KV head and bf16 inputs, both
+// contractions of a 16-token block run on the matrix cores, so the ALU does
+// only the byte-to-fp16 conversion (one v_perm per two codes) and the
+// softmax of the block:
+//   scores S^T[t][n] = sum_d (1152 + K[t][d]) Q[n][d]  v_mfma_f32_16x16x32_f16
+//   values O[n][d]  += sum_t P[n][t] (1152 + V[t][d])   v_mfma_f32_16x16x16_f16
+// (the fp16 forms of the codes as in the packed-dot path; the constant 1152
+// shifts every score of a head equally and adds 1152 * l to O, removed once).
+// A wave streams 16-token blocks (one paged block, 2 KB per tensor at
+// D = 128).  Lane l holds row r = l % 16 of the block and, at D = 128, the
+// 32 codes of dims 16*(l/16) + [0, 16) and 64 + 16*(l/16) + [0, 16) (two
+// 16-byte loads, each instruction reading 64 contiguous bytes of every row),
+// which is the A operand of the score MFMAs with the contraction index
+// permuted the same way in Q.  The score accumulator then holds S^T[token
+// 4*(l/16) + i][head l % 16], which is exactly the A operand (P, heads x
+// tokens) of the value MFMAs.  Their B operand (tokens x dims) needs the
+// value codes transposed: each wave writes its block's rows to LDS and reads
+// back, for dims 8c .. 8c+7 (c = l % 16), the four tokens 4*(l/16) + e; MFMA
+// j then takes dim 8c + j of each.  Lanes with l % 16 >= G carry zero
+// queries and their results are ignored.
+typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+
+template <int D>
+struct I8MfmaGeom {
+  static constexpr int WAVES = 8;
+  static constexpr int SPLIT = 4 * DECODE_SPLIT;  // tokens per workgroup (as i8_split_tokens)
+  static constexpr int TPW = SPLIT / WAVES;       // tokens per wave
+  static constexpr int NBLK = TPW / 16;           // 16-token blocks per wave
+  static constexpr int KS = D / 32;               // score MFMAs (32 dims each)
+  static constexpr int NL = D / 64;               // 16-byte loads per lane per row
+  static constexpr int NJ = D / 16;               // value MFMAs (16 dims each)
+  static constexpr int LROW = D + 16;             // LDS row stride of a value block (bytes)
+  static_assert(NBLK <= 64, "one block id per lane");
+};
+
+// Dim of element e (0..7) of score k-step s for a lane of group g4 = l / 16.
+template <int D>
+__device__ __forceinline__ int i8m_dim(int s, int g4, int e) {
+  return 64 * (s >> 1) + 16 * g4 + 8 * (s & 1) + e;
+}
+
+// Eight codes (two words) as the fp16 values 1152 + c.
+__device__ __forceinline__ f16x8_t codes8_f16(uint32_t w0, uint32_t w1) {
+  const uint32_t x0 = w0 ^ 0x80808080u, x1 = w1 ^ 0x80808080u;
+  const u32x4_t u = {codes_f16_lo(x0), codes_f16_hi(x0), codes_f16_lo(x1), codes_f16_hi(x1)};
+  return __builtin_bit_cast(f16x8_t, u);
+}
+
+template <int D, int G, bool PAGED, bool HALF>
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4))) void
+decode_i8_mfma_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k_new,
+                      const bf16_t* __restrict__ v_new, const int32_t* __restrict__ seq_lens,
+                      CacheArgs c, float* __restrict__ part, int Hkv, int nsplit, RopeFreq fr,
+                      float qk_scale) {
+  using Gm = I8MfmaGeom<D>;
+  constexpr int WAVES = Gm::WAVES, SPLIT = Gm::SPLIT, TPW = Gm::TPW, NBLK = Gm::NBLK;
+  constexpr int KS = Gm::KS, NL = Gm::NL, NJ = Gm::NJ, LROW = Gm::LROW;
+  constexpr int PW = decode_partial_words(D);
+  __shared__ __attribute__((aligned(16))) uint8_t sv[WAVES][16 * LROW];
+  __shared__ __attribute__((aligned(16))) uint8_t snew[2][D];  // the new token's K and V codes
+  __shared__ float sm_acc[WAVES][G][D];
+  __shared__ float sm_ml[WAVES][G][2];
+
+  // grid order, splits and the new token as in decode_i8_split_kernel
+  const int hk = blockIdx.x % Hkv, b = blockIdx.x / Hkv;
+  const int Hq = Hkv * G;
+  const int L = min(max(seq_lens[b], 0), cache_last_slot<PAGED>(c));
+  const int nsb = min(L / SPLIT + 1, nsplit);
+  const int split = (int)blockIdx.y - (nsplit - nsb);
+  if (split < 0) return;  // uniform over the workgroup
+  const int t0 = split * SPLIT;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int r16 = lane & 15, g4 = lane >> 4;
+  const int tw = t0 + wave * TPW;  // first token of this wave
+  const float* ksc = c.k_scale + (int64_t)hk * D;
+  const float* vsc = c.v_scale + (int64_t)hk * D;
+
+  // Q^T as the B operand: lane (g4, n = r16) holds, for k-step s, head n's
+  // rotated query at dims i8m_dim(s, g4, 0..7) times qk_scale and the key
+  // scale of each dim, divided by 2^ex (the power of two that brings the
+  // head's largest element into [0.5, 1)); zero for n >= G.
+  f16x8_t qb[KS];
+  float qs;
+  {
+    float f[KS][8];
+    if (r16 < G) {
+      const bf16_t* qrow = q + ((int64_t)b * Hq + hk * G + r16) * D;
+#pragma unroll
+      for (int s = 0; s < KS; ++s) {
+        const int col = i8m_dim<D>(s, g4, 0);
+        load16<bf16_t>(qrow + col, f[s]);
+        rope_rotate_chunk<bf16_t, 8, HALF>(f[s], qrow, col, D, L, fr);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) f[s][e] *= qk_scale * ksc[col + e];
+      }
+    } else {
+#pragma unroll
+      for (int s = 0; s < KS; ++s)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) f[s][e] = 0.f;
+    }
+    float mx = 0.f;
+#pragma unroll
+    for (int s = 0; s < KS; ++s)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) mx = fmaxf(mx, fabsf(f[s][e]));
+    int ex = 0;
+    (void)frexpf(class_max<16>(mx), &ex);
+    const float inv = ldexpf(1.f, -ex);
+    qs = ldexpf(1.f, ex);
+#pragma unroll
+    for (int s = 0; s < KS; ++s)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) qb[s][e] = (_Float16)(f[s][e] * inv);
+  }
+
+  // The new token (index L): the codes of its rotated key and of its value,
+  // computed by the lanes of wave 0 that hold row 0 (each its dims), stored
+  // into the cache and into LDS, from where the lanes of row L take them in
+  // place of the cached row.
+  int8_t* const Kc = static_cast<int8_t*>(c.k);
+  int8_t* const Vc = static_cast<int8_t*>(c.v);
+  const bool has_new = L < t0 + SPLIT;  // uniform
+  if (has_new && wave == 0 && r16 == 0) {
+    const int64_t src = ((int64_t)b * Hkv + hk) * D;
+    const int64_t dst = cache_row<PAGED>(c, b, hk, Hkv, L) * D;
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+      const int col = i8m_dim<D>(s, g4, 0);
+      float f[8], g[8];
+      load16<bf16_t>(k_new + src + col, f);
+      rope_rotate_chunk<bf16_t, 8, HALF>(f, k_new + src, col, D, L, fr);
+      load16<bf16_t>(v_new + src + col, g);
+      uint32_t kw[2], vw[2];
+      int8_codes<8>(f, ksc + col, kw);
+      int8_codes<8>(g, vsc + col, vw);
+      *reinterpret_cast<u32x2_t*>(Kc + dst + col) = u32x2_t{kw[0], kw[1]};
+      *reinterpret_cast<u32x2_t*>(Vc + dst + col) = u32x2_t{vw[0], vw[1]};
+      *reinterpret_cast<u32x2_t*>(&snew[0][col]) = u32x2_t{kw[0], kw[1]};
+      *reinterpret_cast<u32x2_t*>(&snew[1][col]) = u32x2_t{vw[0], vw[1]};
+    }
+  }
+  if (has_new) __syncthreads();  // uniform over the workgroup
+
+  f32x4_t o[NJ];  // O[head 4*g4 + i][dim 8*r16 + j] (D = 128; 4*r16 + j at D = 64)
+#pragma unroll
+  for (int j = 0; j < NJ; ++j) o[j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  float m_run = -INFINITY;  // head r16's reference maximum (log2 units)
+  float l_run = 0.f;        // its sum over this lane's tokens
+
+  if (tw <= L) {  // uniform per wave: this wave holds at least one token
+    int myblk = 0;  // lane j: physical block of the wave's j-th block
+    if constexpr (PAGED) {
+      const int32_t* trow = c.table + (int64_t)b * c.mbps;
+      if (lane < NBLK)
+        myblk = min(max(trow[min((tw >> 4) + lane, L >> 4)], 0), c.num_blocks - 1);
+    }
+    const int64_t cbase = PAGED ? 0 : ((int64_t)b * Hkv + hk) * c.max_seq;
+    const int nb = min(NBLK, ((L - tw) >> 4) + 1);  // blocks holding tokens <= L
+    // row r16 of block bi: NL 16-byte loads of K and of V (streamed once)
+    auto load_blk = [&](int bi, u32x4_t (&kb)[NL], u32x4_t (&vb)[NL]) {
+      int64_t row;
+      if constexpr (PAGED) {
+        const int blk = __builtin_amdgcn_readlane(myblk, bi);  // uniform index
+        row = (((int64_t)blk * Hkv + hk) << 4) + r16;
+      } else {
+        row = cbase + min(tw + 16 * bi + r16, L);  // rows past L stay inside the cache
+      }
+#pragma unroll
+      for (int h = 0; h < NL; ++h) {
+        const int64_t off = row * D + 64 * h + 16 * g4;
+        kb[h] = *reinterpret_cast<const u32x4_t*>(Kc + off);
+        vb[h] = *reinterpret_cast<const u32x4_t*>(Vc + off);
+      }
+    };
+    uint8_t* const svw = sv[wave];
+    auto consume = [&](int bi, u32x4_t (&kb)[NL], u32x4_t (&vb)[NL]) {
+      const int tb = tw + 16 * bi;  // first token of the block
+      if (tb + 15 >= L) {  // the block reaches index L (uniform): token L from LDS
+        if (tb + r16 == L) {
+#pragma unroll
+          for (int h = 0; h < NL; ++h) {
+            kb[h] = *reinterpret_cast<const u32x4_t*>(&snew[0][64 * h + 16 * g4]);
+            vb[h] = *reinterpret_cast<const u32x4_t*>(&snew[1][64 * h + 16 * g4]);
+          }
+        }
+      }
+      // scores: S^T[token 4*g4 + i][head r16], log2 units
+      f32x4_t sacc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int s = 0; s < KS; ++s) {
+        const u32x4_t& w = kb[s >> 1];
+        const f16x8_t a = codes8_f16(w[2 * (s & 1)], w[2 * (s & 1) + 1]);
+        sacc = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, qb[s], sacc, 0, 0, 0);
+      }
+      // the block's rows into LDS (row-major, one row per r16) for the
+      // transposed read of the value operand
+#pragma unroll
+      for (int h = 0; h < NL; ++h)
+        *reinterpret_cast<u32x4_t*>(svw + r16 * LROW + 64 * h + 16 * g4) = vb[h];
+      float sc[4];
+      float mx = -INFINITY;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int t = tb + 4 * g4 + i;
+        sc[i] = t <= L ? sacc[i] * qs : -INFINITY;
+        mx = fmaxf(mx, sc[i]);
+      }
+      mx = class_max<16>(mx);  // the block's maximum of head r16
+      // lazy rescale: the reference moves only when a score exceeds it by
+      // more than kRescaleLog2; O's rows are heads 4*g4 + i, so each lane
+      // takes the factors of those heads from the lanes that own them
+      if (__builtin_amdgcn_ballot_w64(mx - m_run > kRescaleLog2) != 0) {  // uniform
+        const float m_new = fmaxf(m_run, mx);  // finite: token tb <= L is visible
+        const float alpha = fast_exp2(m_run - m_new);
+        m_run = m_new;
+        l_run *= alpha;
+        float ah[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int a0 = __builtin_amdgcn_readlane(__builtin_bit_cast(int, alpha), i);
+          const int a1 = __builtin_amdgcn_readlane(__builtin_bit_cast(int, alpha), 4 + i);
+          ah[i] = __builtin_bit_cast(float, g4 == 0 ? a0 : a1);
+        }
+#pragma unroll
+        for (int j = 0; j < NJ; ++j)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) o[j][i] *= ah[i];
+      }
+      // P (fp16) as the A operand of the value MFMAs; l sums the rounded P
+      const uint32_t p01 = pack_f16x2(fast_exp2(sc[0] - m_run), fast_exp2(sc[1] - m_run));
+      const uint32_t p23 = pack_f16x2(fast_exp2(sc[2] - m_run), fast_exp2(sc[3] - m_run));
+      l_run = dot2_f16(p01, kOnePairF16, l_run);
+      l_run = dot2_f16(p23, kOnePairF16, l_run);
+      const f16x4_t pa = __builtin_bit_cast(f16x4_t, u32x2_t{p01, p23});
+      // values: lane (g4, c = r16) reads dims NJ*c .. NJ*c + NJ-1 of tokens
+      // 4*g4 + e; MFMA j takes dim NJ*c + j of each
+      uint32_t vw[4][NJ / 4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const uint8_t* src = svw + (4 * g4 + e) * LROW + NJ * r16;
+        if constexpr (NJ == 8) {
+          const u32x2_t x = *reinterpret_cast<const u32x2_t*>(src);
+          vw[e][0] = x[0];
+          vw[e][1] = x[1];
+        } else {
+          vw[e][0] = *reinterpret_cast<const uint32_t*>(src);
+        }
+      }
+      static_for<0, NJ>([&](auto J) {
+        constexpr int j = decltype(J)::value;
+        const uint32_t lo = codes_f16_rows<j % 4>(vw[0][j / 4], vw[1][j / 4]);
+        const uint32_t hi = codes_f16_rows<j % 4>(vw[2][j / 4], vw[3][j / 4]);
+        const f16x4_t vbm = __builtin_bit_cast(f16x4_t, u32x2_t{lo, hi});
+        o[j] = __builtin_amdgcn_mfma_f32_16x16x16f16(pa, vbm, o[j], 0, 0, 0);
+      });
+    };
+
+    // double-buffered blocks: block bi+1's loads are in flight while block
+    // bi is consumed
+    u32x4_t kb0[NL], vb0[NL], kb1[NL], vb1[NL];
+    load_blk(0, kb0, vb0);
+#pragma unroll 1
+    for (int bi = 0; bi < nb; bi += 2) {
+      if (bi + 1 < nb) load_blk(bi + 1, kb1, vb1);
+      consume(bi, kb0, vb0);
+      if (bi + 1 < nb) {
+        if (bi + 2 < nb) load_blk(bi + 2, kb0, vb0);
+        consume(bi + 1, kb1, vb1);
+      }
+    }
+  }
+
+  // Merge the four lanes of each head column, then the waves (as the packed
+  // path), removing the code bias 1152 * l and applying the value scales.
+  l_run = class_sum<16>(l_run);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int hd = 4 * g4 + i;
+    if (hd < G) {
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) sm_acc[wave][hd][NJ * r16 + j] = o[j][i];
+    }
+  }
+  if (g4 == 0 && r16 < G) {
+    sm_ml[wave][r16][0] = m_run;
+    sm_ml[wave][r16][1] = l_run;
+  }
+  __syncthreads();
+  for (int i = threadIdx.x; i < G * D; i += 64 * WAVES) {
+    const int g = i / D, d = i % D;
+    float M = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < WAVES; ++w) M = fmaxf(M, sm_ml[w][g][0]);
+    float a = 0.f, l = 0.f;
+#pragma unroll
+    for (int w = 0; w < WAVES; ++w) {
+      const float mw = sm_ml[w][g][0];
+      const float f = mw == -INFINITY ? 0.f : fast_exp2(mw - M);
+      a = fmaf(f, sm_acc[w][g][d], a);
+      l = fmaf(f, sm_ml[w][g][1], l);
+    }
+    float* dst = part + (((int64_t)b * Hq + hk * G + g) * nsplit + split) * PW;
+    dst[4 + d] = (a - kCodeBias * l) * vsc[d];
+    if (d == 0) {
+      dst[0] = M;
+      dst[1] = l;
+    }
+  }
+}
+
 template <typename T, int D, int G, bool PAGED>
 hipError_t decode_i8_t(const void* q, const void* k_new, const void* v_new, void* out, int B,
                        int Hkv, const int32_t* seq_lens, int max_seq_len, const CacheArgs& c,
@@ -450,7 +767,17 @@ hipError_t decode_i8_t(const void* q, const void* k_new, const void* v_new, void
   const T* qq = static_cast<const T*>(q);
   const T* kk = static_cast<const T*>(k_new);
   const T* vv = static_cast<const T*>(v_new);
-  if (fr.half)
+  if constexpr (sizeof(T) == 2 && G > 1) {  // bf16, several heads: the matrix-core kernel
+    static_assert(SPLIT == I8MfmaGeom<D>::SPLIT, "both kernels split the sequence alike");
+    if (fr.half)
+      hipExtLaunchKernelGGL((decode_i8_mfma_kernel<D, G, PAGED, true>), grid, dim3(512), 0, st,
+                            tl.start, tl.stop, 0, qq, kk, vv, seq_lens, c, partials, Hkv, nsplit,
+                            fr, qk_scale);
+    else
+      hipExtLaunchKernelGGL((decode_i8_mfma_kernel<D, G, PAGED, false>), grid, dim3(512), 0, st,
+                            tl.start, tl.stop, 0, qq, kk, vv, seq_lens, c, partials, Hkv, nsplit,
+                            fr, qk_scale);
+  } else if (fr.half)
     hipExtLaunchKernelGGL((decode_i8_split_kernel<T, D, G, PAGED, SPLIT, true>), grid, block,
                           0, st, tl.start, tl.stop, 0, qq, kk, vv, seq_lens, c, partials, Hkv,
                           nsplit, fr, qk_scale);

@@ -328,6 +328,32 @@ def test_decode_int8_gqa(car, dtype, group, paged):
     run_and_check(car, case)
 
 
+@pytest.mark.parametrize("group", [4, 8])
+@pytest.mark.parametrize("paged", [False, True], ids=["contiguous", "paged"])
+def test_decode_int8_gqa_scores_jump(car, group, paged):
+    """Cached keys from index J = L // 3 on score far above the earlier ones
+    (queries 3 in their last 8 dims, those keys' codes +127 there and the
+    earlier keys' -127: over 20 in log2 units at these scales), so the
+    running maximum of the waves and splits that cross J moves by far more
+    than the lazy-rescale threshold in a later block, and O and l must be
+    rescaled together."""
+    lens = [700, 1500, 2900]
+    Hkv = 2
+    case = make_case(f"i8 gqa{group} jump paged={paged}", len(lens), Hkv * group, Hkv, 128,
+                     torch.bfloat16, lens, 75 + group, paged, extra_blocks=2 if paged else 0)
+    case.q[..., -8:] = 3.0
+    for b, L in enumerate(lens):
+        t = torch.arange(L, device=DEV)
+        code = torch.where(t < L // 3, -127, 127).to(torch.int8)[:, None, None]
+        if paged:
+            blk = case.block_table[b].to(torch.long)[t // 16]
+            case.cache_k[blk, :, t % 16, -8:] = code.expand(L, Hkv, 8)
+        else:
+            case.cache_k[b, :, :L, -8:] = code.expand(L, 1, 8).transpose(0, 1)
+    log_case(case.name)
+    run_and_check(car, case)
+
+
 @pytest.mark.parametrize("pairing", ["half"])
 def test_decode_int8_half_split(car, pairing):
     """The half-split RoPE layout through the int8 decode (bf16, GQA 4)."""
