@@ -703,17 +703,25 @@ decode_i8_mfma_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k
     };
 
     // double-buffered blocks: block bi+1's loads are in flight while block
-    // bi is consumed
+    // bi is consumed.  The steady-state loop issues its loads unconditionally
+    // (so that each wait covers only the older block); the last one or two
+    // blocks are consumed after it.
     u32x4_t kb0[NL], vb0[NL], kb1[NL], vb1[NL];
     load_blk(0, kb0, vb0);
+    int bi = 0;
 #pragma unroll 1
-    for (int bi = 0; bi < nb; bi += 2) {
-      if (bi + 1 < nb) load_blk(bi + 1, kb1, vb1);
+    for (; bi + 2 < nb; bi += 2) {
+      load_blk(bi + 1, kb1, vb1);
       consume(bi, kb0, vb0);
-      if (bi + 1 < nb) {
-        if (bi + 2 < nb) load_blk(bi + 2, kb0, vb0);
-        consume(bi + 1, kb1, vb1);
-      }
+      load_blk(bi + 2, kb0, vb0);
+      consume(bi + 1, kb1, vb1);
+    }
+    if (bi + 1 < nb) {
+      load_blk(bi + 1, kb1, vb1);
+      consume(bi, kb0, vb0);
+      consume(bi + 1, kb1, vb1);
+    } else {
+      consume(bi, kb0, vb0);
     }
   }
 
