@@ -379,17 +379,22 @@ __attribute__((amdgpu_waves_per_eu(G == 1 ? 4 : 2))) void decode_i8_split_kernel
 
     using B0 = std::integral_constant<int, 0>;
     using B1 = std::integral_constant<int, 1>;
+    // The steady-state loop issues its loads unconditionally, so that each
+    // wait covers only the round being consumed; the last two rounds follow.
     issue(0, B0{});
     if constexpr (ROUNDS == 1) {
       consume(0, B0{});
     } else {
 #pragma unroll 1
-      for (int r = 0; r < ROUNDS; r += 2) {
+      for (int r = 0; r < ROUNDS - 2; r += 2) {
         issue(r + 1, B1{});
         consume(r, B0{});
-        if (r + 2 < ROUNDS) issue(r + 2, B0{});
+        issue(r + 2, B0{});
         consume(r + 1, B1{});
       }
+      issue(ROUNDS - 1, B1{});
+      consume(ROUNDS - 2, B0{});
+      consume(ROUNDS - 1, B1{});
     }
   }
 
