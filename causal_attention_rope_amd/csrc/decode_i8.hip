@@ -22,21 +22,21 @@
 // no dequantized copy of a row is ever formed.
 //
 // With several query heads per KV head (GQA) and bf16 inputs that FMA work
-// grows G-fold per byte and would bound the kernel, so the contractions run
-// as packed fp16 dot products (v_dot2_f32_f16, two multiply-adds per
-// instruction, fp32 accumulation) instead.  A code c becomes the fp16 value
-// 1152 + c with one byte permute per pair: the byte c XOR 0x80 = c + 128 is
-// placed under the exponent byte 0x64 (fp16 1024 + m for an 8-bit m), which
-// is exact.  The constant 1152 adds the same amount to every score of a head
-// (1152 times the sum of its query), which the softmax ignores; in P V it
-// adds 1152 * l, removed once at the end.  Each head's query is scaled by a
-// power of two so that its largest element lies in [0.5, 1) before rounding
-// to fp16 (11 significant bits, against bf16's 8 in the native path), and the
-// score is scaled back exactly.
+// grows G-fold per byte and would bound the kernel, so that case runs in
+// decode_i8_mfma_kernel (below) with both contractions on the matrix cores.
+// There a code c becomes the fp16 value 1152 + c with one byte permute per
+// pair: the byte c XOR 0x80 = c + 128 is placed under the exponent byte 0x64
+// (fp16 1024 + m for an 8-bit m), which is exact.  The constant 1152 adds the
+// same amount to every score of a head (1152 times the sum of its query),
+// which the softmax ignores; in P V it adds 1152 * l, removed once at the
+// end.  Each head's query is scaled by a power of two so that its largest
+// element lies in [0.5, 1) before rounding to fp16 (11 significant bits,
+// against bf16's 8 in the native path), and the score is scaled back exactly.
 //
-// Lanes hold E = 16 codes of a row (one 16-byte load), or 8 with several
-// query heads (registers for G query rows and accumulators), so LPR = D/E
-// lanes cover a row and a load instruction moves 64/LPR rows.  The work split
+// In decode_i8_split_kernel (one query head per KV head, or fp32 inputs)
+// lanes hold E = 16 codes of a row (one 16-byte load), or 8 with eight query
+// heads (registers for G query rows and accumulators), so LPR = D/E lanes
+// cover a row and a load instruction moves 64/LPR rows.  The work split
 // (splits of the sequence per workgroup, grid order, the online softmax with
 // a lazy rescale, merging across rows, waves and workgroups) is that of the
 // decode over a native cache.
@@ -51,11 +51,11 @@ namespace {
 template <int G>
 constexpr int i8_waves() { return G > 1 ? 8 : 4; }
 
-template <int D, int G, int SPLIT, bool F16>
+template <int D, int G, int SPLIT>
 struct I8Geom {
   static constexpr int WAVES = i8_waves<G>();
   static constexpr int TPW = SPLIT / WAVES;  // tokens per wave
-  static constexpr int E = (G >= 8 || (G > 1 && F16)) ? 8 : 16;  // codes per lane per row
+  static constexpr int E = G >= 8 ? 8 : 16;  // codes per lane per row
   static constexpr int LPR = D / E;          // lanes per cache row
   static constexpr int NG = 64 / LPR;        // rows per load instruction
   static constexpr int STEPS = TPW / NG;
@@ -118,9 +118,7 @@ __attribute__((amdgpu_waves_per_eu(G == 1 ? 4 : 2))) void decode_i8_split_kernel
     const T* __restrict__ q, const T* __restrict__ k_new, const T* __restrict__ v_new,
     const int32_t* __restrict__ seq_lens, CacheArgs c, float* __restrict__ part, int Hkv,
     int nsplit, RopeFreq fr, float qk_scale) {
-  // packed fp16 contractions for bf16 inputs with several query heads
-  constexpr bool F16 = sizeof(T) == 2 && G > 1;
-  using Gm = I8Geom<D, G, SPLIT, F16>;
+  using Gm = I8Geom<D, G, SPLIT>;
   using Chunk = typename ChunkOf<Gm::W>::type;
   constexpr int E = Gm::E, W = Gm::W, LPR = Gm::LPR, NG = Gm::NG, R = Gm::R,
                 ROUNDS = Gm::ROUNDS, TPW = Gm::TPW;
@@ -171,25 +169,6 @@ __attribute__((amdgpu_waves_per_eu(G == 1 ? 4 : 2))) void decode_i8_split_kernel
       for (int e = 0; e < NT; ++e) qf[g][j * NT + e] = f[e] * qk_scale * kscale[j * NT + e];
     }
   }
-  // fp16 queries: head g as qh[g] * qs[g], qs[g] a power of two
-  uint32_t qh[G][E / 2];
-  float qs[G];
-  if constexpr (F16) {
-#pragma unroll
-    for (int g = 0; g < G; ++g) {
-      float mx = 0.f;
-#pragma unroll
-      for (int e = 0; e < E; ++e) mx = fmaxf(mx, fabsf(qf[g][e]));
-      int ex = 0;
-      (void)frexpf(group_max<LPR>(mx), &ex);  // max = m * 2^ex, m in [0.5, 1)
-      const float inv = ldexpf(1.f, -ex);
-      qs[g] = ldexpf(1.f, ex);
-#pragma unroll
-      for (int w = 0; w < E / 2; ++w)
-        qh[g][w] = pack_f16x2(qf[g][2 * w] * inv, qf[g][2 * w + 1] * inv);
-    }
-  }
-
   // The new token (index L): codes of the rotated key and of the value,
   // stored by the split that holds L and used from registers for token L.
   int8_t* const Kc = static_cast<int8_t*>(c.k);
@@ -286,40 +265,19 @@ __attribute__((amdgpu_waves_per_eu(G == 1 ? 4 : 2))) void decode_i8_split_kernel
 #pragma unroll
       for (int st = 0; st < R; ++st) {
         const int t = tw + (r * R + st) * NG + grp;
-        if constexpr (F16) {
-          uint32_t kp[E / 2];
+        float kf[E];
 #pragma unroll
-          for (int w = 0; w < W; ++w) {
-            const uint32_t x = kb[buf][st][w] ^ 0x80808080u;
-            kp[2 * w] = codes_f16_lo(x);
-            kp[2 * w + 1] = codes_f16_hi(x);
+        for (int e = 0; e < E; ++e) kf[e] = int8_elem(kb[buf][st][e >> 2], e & 3);
+#pragma unroll
+        for (int g = 0; g < G; ++g) {
+          float p0 = 0.f, p1 = 0.f;  // two chains for latency
+#pragma unroll
+          for (int e = 0; e < E; e += 2) {
+            p0 = fmaf(qf[g][e], kf[e], p0);
+            p1 = fmaf(qf[g][e + 1], kf[e + 1], p1);
           }
-#pragma unroll
-          for (int g = 0; g < G; ++g) {
-            float p0 = 0.f, p1 = 0.f;  // two chains for latency
-#pragma unroll
-            for (int i = 0; i < E / 2; i += 2) {
-              p0 = dot2_f16(qh[g][i], kp[i], p0);
-              p1 = dot2_f16(qh[g][i + 1], kp[i + 1], p1);
-            }
-            const float sv = group_sum<LPR>(p0 + p1) * qs[g];
-            sc[st][g] = (full || t <= L) ? sv : -INFINITY;
-          }
-        } else {
-          float kf[E];
-#pragma unroll
-          for (int e = 0; e < E; ++e) kf[e] = int8_elem(kb[buf][st][e >> 2], e & 3);
-#pragma unroll
-          for (int g = 0; g < G; ++g) {
-            float p0 = 0.f, p1 = 0.f;  // two chains for latency
-#pragma unroll
-            for (int e = 0; e < E; e += 2) {
-              p0 = fmaf(qf[g][e], kf[e], p0);
-              p1 = fmaf(qf[g][e + 1], kf[e + 1], p1);
-            }
-            const float sv = group_sum<LPR>(p0 + p1);
-            sc[st][g] = (full || t <= L) ? sv : -INFINITY;
-          }
+          const float sv = group_sum<LPR>(p0 + p1);
+          sc[st][g] = (full || t <= L) ? sv : -INFINITY;
         }
       }
       // Lazy rescale, as for the native cache: the reference maximum of a
@@ -338,41 +296,17 @@ __attribute__((amdgpu_waves_per_eu(G == 1 ? 4 : 2))) void decode_i8_split_kernel
           for (int e = 0; e < E; ++e) acc[g][e] *= alpha;
         }
       }
-      if constexpr (F16) {
-        // P V over a pair of rows: (p_a, p_b) . (1152 + a_e, 1152 + b_e)
 #pragma unroll
-        for (int st = 0; st < R; st += 2) {
-          uint32_t vp[E];
+      for (int st = 0; st < R; ++st) {
+        float vf[E];
 #pragma unroll
-          for (int w = 0; w < W; ++w) {
-            const uint32_t a = vb[buf][st][w], bb = vb[buf][st + 1][w];
-            vp[4 * w] = codes_f16_rows<0>(a, bb);
-            vp[4 * w + 1] = codes_f16_rows<1>(a, bb);
-            vp[4 * w + 2] = codes_f16_rows<2>(a, bb);
-            vp[4 * w + 3] = codes_f16_rows<3>(a, bb);
-          }
+        for (int e = 0; e < E; ++e) vf[e] = int8_elem(vb[buf][st][e >> 2], e & 3);
 #pragma unroll
-          for (int g = 0; g < G; ++g) {
-            const uint32_t pp = pack_f16x2(fast_exp2(sc[st][g] - m_run[g]),
-                                           fast_exp2(sc[st + 1][g] - m_run[g]));
-            l_run[g] = dot2_f16(pp, kOnePairF16, l_run[g]);
+        for (int g = 0; g < G; ++g) {
+          const float p = fast_exp2(sc[st][g] - m_run[g]);
+          l_run[g] += p;
 #pragma unroll
-            for (int e = 0; e < E; ++e) acc[g][e] = dot2_f16(pp, vp[e], acc[g][e]);
-          }
-        }
-      } else {
-#pragma unroll
-        for (int st = 0; st < R; ++st) {
-          float vf[E];
-#pragma unroll
-          for (int e = 0; e < E; ++e) vf[e] = int8_elem(vb[buf][st][e >> 2], e & 3);
-#pragma unroll
-          for (int g = 0; g < G; ++g) {
-            const float p = fast_exp2(sc[st][g] - m_run[g]);
-            l_run[g] += p;
-#pragma unroll
-            for (int e = 0; e < E; ++e) acc[g][e] = fmaf(p, vf[e], acc[g][e]);
-          }
+          for (int e = 0; e < E; ++e) acc[g][e] = fmaf(p, vf[e], acc[g][e]);
         }
       }
     };
@@ -435,7 +369,7 @@ __attribute__((amdgpu_waves_per_eu(G == 1 ? 4 : 2))) void decode_i8_split_kernel
       l = fmaf(f, sm_ml[w][g][1], l);
     }
     float* dst = part + (((int64_t)b * Hq + hk * G + g) * nsplit + split) * PW;
-    dst[4 + d] = (F16 ? a - kCodeBias * l : a) * vsc[d];
+    dst[4 + d] = a * vsc[d];
     if (d == 0) {
       dst[0] = M;
       dst[1] = l;
