@@ -440,6 +440,7 @@ decode_i8_mfma_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k
   constexpr int WAVES = Gm::WAVES, SPLIT = Gm::SPLIT, TPW = Gm::TPW, NBLK = Gm::NBLK;
   constexpr int KS = Gm::KS, NL = Gm::NL, NJ = Gm::NJ, LROW = Gm::LROW;
   constexpr int PW = decode_partial_words(D);
+  __shared__ __attribute__((aligned(16))) uint8_t sk[WAVES][16 * LROW];
   __shared__ __attribute__((aligned(16))) uint8_t sv[WAVES][16 * LROW];
   __shared__ __attribute__((aligned(16))) uint8_t snew[2][D];  // the new token's K and V codes
   __shared__ float sm_acc[WAVES][G][D];
@@ -542,47 +543,60 @@ decode_i8_mfma_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k
     }
     const int64_t cbase = PAGED ? 0 : ((int64_t)b * Hkv + hk) * c.max_seq;
     const int nb = min(NBLK, ((L - tw) >> 4) + 1);  // blocks holding tokens <= L
-    // row r16 of block bi: NL 16-byte loads of K and of V (streamed once)
+    // Block bi's 16 rows of K and of V (streamed once), each load instruction
+    // reading whole rows: load h of a lane covers row RPI*h + lrow, bytes
+    // 16*lchunk .. 16*lchunk + 15.
+    constexpr int CPR = D / 16, RPI = 64 / CPR;  // 16-byte chunks per row, rows per load
+    const int lrow = lane / CPR, lchunk = lane % CPR;
     auto load_blk = [&](int bi, u32x4_t (&kb)[NL], u32x4_t (&vb)[NL]) {
-      int64_t row;
+      int64_t row0 = 0;
       if constexpr (PAGED) {
         const int blk = __builtin_amdgcn_readlane(myblk, bi);  // uniform index
-        row = (((int64_t)blk * Hkv + hk) << 4) + r16;
-      } else {
-        row = cbase + min(tw + 16 * bi + r16, L);  // rows past L stay inside the cache
+        row0 = ((int64_t)blk * Hkv + hk) << 4;
       }
 #pragma unroll
       for (int h = 0; h < NL; ++h) {
-        const int64_t off = row * D + 64 * h + 16 * g4;
+        const int r = RPI * h + lrow;
+        // contiguous: rows past L stay inside the cache
+        const int64_t row = PAGED ? row0 + r : cbase + min(tw + 16 * bi + r, L);
+        const int64_t off = row * D + 16 * lchunk;
         kb[h] = *reinterpret_cast<const u32x4_t*>(Kc + off);
         vb[h] = *reinterpret_cast<const u32x4_t*>(Vc + off);
       }
     };
+    uint8_t* const skw = sk[wave];
     uint8_t* const svw = sv[wave];
     auto consume = [&](int bi, u32x4_t (&kb)[NL], u32x4_t (&vb)[NL]) {
       const int tb = tw + 16 * bi;  // first token of the block
       if (tb + 15 >= L) {  // the block reaches index L (uniform): token L from LDS
-        if (tb + r16 == L) {
 #pragma unroll
-          for (int h = 0; h < NL; ++h) {
-            kb[h] = *reinterpret_cast<const u32x4_t*>(&snew[0][64 * h + 16 * g4]);
-            vb[h] = *reinterpret_cast<const u32x4_t*>(&snew[1][64 * h + 16 * g4]);
+        for (int h = 0; h < NL; ++h) {
+          if (tb + RPI * h + lrow == L) {
+            kb[h] = *reinterpret_cast<const u32x4_t*>(&snew[0][16 * lchunk]);
+            vb[h] = *reinterpret_cast<const u32x4_t*>(&snew[1][16 * lchunk]);
           }
         }
       }
-      // scores: S^T[token 4*g4 + i][head r16], log2 units
+      // the block's rows into LDS (row-major) for the reads of both operands
+#pragma unroll
+      for (int h = 0; h < NL; ++h) {
+        const int o16 = (RPI * h + lrow) * LROW + 16 * lchunk;
+        *reinterpret_cast<u32x4_t*>(skw + o16) = kb[h];
+        *reinterpret_cast<u32x4_t*>(svw + o16) = vb[h];
+      }
+      // scores: S^T[token 4*g4 + i][head r16], log2 units; lane (r16, g4)
+      // reads key row r16's bytes 64*h + 16*g4 .. + 15
+      u32x4_t kr[NL];
+#pragma unroll
+      for (int h = 0; h < NL; ++h)
+        kr[h] = *reinterpret_cast<const u32x4_t*>(skw + r16 * LROW + 64 * h + 16 * g4);
       f32x4_t sacc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int s = 0; s < KS; ++s) {
-        const u32x4_t& w = kb[s >> 1];
+        const u32x4_t& w = kr[s >> 1];
         const f16x8_t a = codes8_f16(w[2 * (s & 1)], w[2 * (s & 1) + 1]);
         sacc = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, qb[s], sacc, 0, 0, 0);
       }
-      // the block's rows into LDS (row-major, one row per r16) for the
-      // transposed read of the value operand
-#pragma unroll
-      for (int h = 0; h < NL; ++h)
-        *reinterpret_cast<u32x4_t*>(svw + r16 * LROW + 64 * h + 16 * g4) = vb[h];
       float sc[4];
       float mx = -INFINITY;
 #pragma unroll
