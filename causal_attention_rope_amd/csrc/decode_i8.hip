@@ -51,7 +51,13 @@ namespace {
 template <int G>
 constexpr int i8_waves() { return G > 1 ? 8 : 4; }
 
-template <int D, int G, int SPLIT>
+// Row steps per round: four (8 KB of K and V in flight per wave at D = 128)
+// for bf16 with one query head and adjacent-pair RoPE, where the registers
+// allow it; two otherwise (four would spill there).
+template <typename T, int G, bool HALF>
+constexpr int i8_round_steps() { return sizeof(T) == 2 && G == 1 && !HALF ? 4 : 2; }
+
+template <int D, int G, int SPLIT, int RMAX>
 struct I8Geom {
   static constexpr int WAVES = i8_waves<G>();
   static constexpr int TPW = SPLIT / WAVES;  // tokens per wave
@@ -59,7 +65,7 @@ struct I8Geom {
   static constexpr int LPR = D / E;          // lanes per cache row
   static constexpr int NG = 64 / LPR;        // rows per load instruction
   static constexpr int STEPS = TPW / NG;
-  static constexpr int R = STEPS < 2 ? STEPS : 2;  // row steps per round
+  static constexpr int R = STEPS < RMAX ? STEPS : RMAX;  // row steps per round
   static constexpr int ROUNDS = STEPS / R;
   static constexpr int W = E / 4;  // 32-bit words per lane per row
   static_assert(SPLIT % DECODE_SPLIT == 0 && TPW % 64 == 0, "whole 16-token blocks per wave");
@@ -118,7 +124,7 @@ __attribute__((amdgpu_waves_per_eu(G == 1 ? 4 : 2))) void decode_i8_split_kernel
     const T* __restrict__ q, const T* __restrict__ k_new, const T* __restrict__ v_new,
     const int32_t* __restrict__ seq_lens, CacheArgs c, float* __restrict__ part, int Hkv,
     int nsplit, RopeFreq fr, float qk_scale) {
-  using Gm = I8Geom<D, G, SPLIT>;
+  using Gm = I8Geom<D, G, SPLIT, i8_round_steps<T, G, HALF>()>;
   using Chunk = typename ChunkOf<Gm::W>::type;
   constexpr int E = Gm::E, W = Gm::W, LPR = Gm::LPR, NG = Gm::NG, R = Gm::R,
                 ROUNDS = Gm::ROUNDS, TPW = Gm::TPW;
