@@ -566,8 +566,9 @@ decode_i8_mfma_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k
         // contiguous: rows past L stay inside the cache
         const int64_t row = PAGED ? row0 + r : cbase + min(tw + 16 * bi + r, L);
         const int64_t off = row * D + 16 * lchunk;
-        kb[h] = *reinterpret_cast<const u32x4_t*>(Kc + off);
-        vb[h] = *reinterpret_cast<const u32x4_t*>(Vc + off);
+        // streamed once: non-temporal loads keep the rows out of the caches
+        kb[h] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(Kc + off));
+        vb[h] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(Vc + off));
       }
     };
     uint8_t* const skw = sk[wave];
