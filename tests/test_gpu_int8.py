@@ -328,6 +328,22 @@ def test_decode_int8_gqa(car, dtype, group, paged):
     run_and_check(car, case)
 
 
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("group", [2, 4])
+@pytest.mark.parametrize("paged", [False, True], ids=["contiguous", "paged"])
+def test_decode_int8_gqa_new_token_every_row(car, D, group, paged):
+    """bf16 with several query heads: L = 145 j puts the new token at row
+    L % 16 = j of its 16-token block for j = 0..15, in different waves and
+    splits, so each lane position of the block's loads is the one whose
+    cached row is replaced by the token computed in the kernel."""
+    lens = [145 * j for j in range(16)]
+    Hkv = 2
+    case = make_case(f"i8 gqa{group} every row D={D} paged={paged}", len(lens), Hkv * group, Hkv,
+                     D, torch.bfloat16, lens, 91 + group, paged, extra_blocks=2 if paged else 0)
+    log_case(case.name)
+    run_and_check(car, case)
+
+
 @pytest.mark.parametrize("group", [4, 8])
 @pytest.mark.parametrize("paged", [False, True], ids=["contiguous", "paged"])
 def test_decode_int8_gqa_scores_jump(car, group, paged):
