@@ -150,8 +150,9 @@ def cpu_baseline(pf, c4, heads: int):
 
 def timed_calls(car, call, stream, new_event, iters: int):
     """Event pairs around `iters` whole calls, then around the main kernel
-    of `iters` further calls (the library records those; kept out of the
-    call iterations so that they add nothing to the call times)."""
+    of `iters` further calls (`call(timing)` hands the pair to the library,
+    which records it around that kernel; kept out of the call iterations so
+    that they add nothing to the call times)."""
     import torch
     pairs_c = [(new_event(), new_event()) for _ in range(iters)]
     pairs_k = [(new_event(), new_event()) for _ in range(iters)]
@@ -159,10 +160,8 @@ def timed_calls(car, call, stream, new_event, iters: int):
         a.record(stream)
         call()
         b.record(stream)
-    for a, b in pairs_k:
-        car.set_timing_events(a, b)
-        call()
-        car.set_timing_events(None, None)
+    for pair in pairs_k:
+        call(pair)
     torch.cuda.synchronize()
     return pairs_k, pairs_c
 
@@ -181,9 +180,9 @@ def measure_chunked(car, W, dev, stream, new_event, iters: int = 10) -> dict:
         cache = car.KVCache(case.cache_k, case.cache_v, case.block_table)
         o = torch.empty_like(case.q)
 
-        def call():
+        def call(timing=None):
             car.attn_prefill_cached(case.q, case.k, case.v, case.seq_lens, cache, P + S,
-                                    case.theta, case.scale, out=o)
+                                    case.theta, case.scale, out=o, timing=timing)
         for _ in range(2):
             call()
         pairs_k, pairs_c = timed_calls(car, call, stream, new_event, iters)
@@ -225,9 +224,10 @@ def measure_int8_decode(car, W, dev, stream, new_event, iters: int = 20) -> dict
         ws = torch.empty(car.decode_workspace_bytes(case.B, case.Hq, 128, case.max_seq_len),
                          dtype=torch.uint8, device=dev)
 
-        def call():
+        def call(timing=None):
             car.attn_decode(case.q, case.k_new, case.v_new, case.seq_lens, cache,
-                            case.max_seq_len, case.theta, case.scale, out=o, workspace=ws)
+                            case.max_seq_len, case.theta, case.scale, out=o, workspace=ws,
+                            timing=timing)
         for _ in range(3):
             call()
         pairs_k, pairs_c = timed_calls(car, call, stream, new_event, iters)
@@ -267,9 +267,9 @@ def measure_small_prefills(car, W, dev, stream, new_event, iters: int = 20) -> d
     ws2 = torch.empty(car.prefill_workspace_bytes(torch.bfloat16, c2.B, c2.Hkv, c2.S, c2.D),
                       dtype=torch.uint8, device=dev)
 
-    def call2():
+    def call2(timing=None):
         car.attn_prefill(c2.q, c2.k, c2.v, c2.positions, c2.theta, c2.scale, out=o2,
-                         workspace=ws2)
+                         workspace=ws2, timing=timing)
     for _ in range(3):
         call2()
     pairs_k, pairs_c = timed_calls(car, call2, stream, new_event, iters)
@@ -379,25 +379,20 @@ def main(argv=None) -> int:
         # call events bracket the whole entry point; with kernel_events the
         # library brackets its main kernel instead (separate iterations, so
         # that the inner events add nothing to the call times)
-        if i is not None:
-            if kernel_events:
-                car.set_timing_events(*ev[s]["kernel"][i])
-            else:
-                ev[s]["call"][i][0].record(stream)
+        timing = ev[s]["kernel"][i] if (i is not None and kernel_events) else None
+        if i is not None and not kernel_events:
+            ev[s]["call"][i][0].record(stream)
         if s == "prefill":
             car.attn_prefill(pf.q, pf.k, pf.v, pf.positions, pf.theta, pf.scale,
-                             cache=pf_cache, out=pf_out, workspace=pf_ws)
+                             cache=pf_cache, out=pf_out, workspace=pf_ws, timing=timing)
         elif s == "contiguous":
             car.attn_decode(c4.q, c4.k_new, c4.v_new, c4.seq_lens, c4_cache, c4.max_seq_len,
-                            c4.theta, c4.scale, out=c4_out, workspace=c4_ws)
+                            c4.theta, c4.scale, out=c4_out, workspace=c4_ws, timing=timing)
         else:
             car.attn_decode(c5.q, c5.k_new, c5.v_new, c5.seq_lens, c5_cache, c5.max_seq_len,
-                            c5.theta, c5.scale, out=c5_out, workspace=c5_ws)
-        if i is not None:
-            if kernel_events:
-                car.set_timing_events(None, None)
-            else:
-                ev[s]["call"][i][1].record(stream)
+                            c5.theta, c5.scale, out=c5_out, workspace=c5_ws, timing=timing)
+        if i is not None and not kernel_events:
+            ev[s]["call"][i][1].record(stream)
 
     if args.copy_calibration:
         src = torch.empty(COPY_BYTES, dtype=torch.uint8, device=dev)

@@ -9,7 +9,9 @@ fallback: importing fails if the library has not been built.
 Entry points (same names as the C ABI without the ``car_`` prefix):
 ``rope_apply``, ``kv_cache_append``, ``kv_int8_calibrate``, ``attn_prefill``,
 ``attn_prefill_cached``, ``attn_decode``, plus ``KVCache`` (native or INT8
-elements), the workspace size queries and ``set_timing_events``.
+elements) and the workspace size queries.  The three attention calls take an
+optional ``timing=(start, stop)`` pair of torch.cuda.Event, recorded around
+their attention kernel (the ``_timed`` entry points of the C ABI).
 """
 
 from __future__ import annotations
@@ -24,7 +26,7 @@ import torch
 __all__ = [
     "CarError", "KVCache", "rope_apply", "kv_cache_append", "attn_prefill", "attn_decode",
     "attn_prefill_cached", "kv_int8_calibrate",
-    "prefill_workspace_bytes", "decode_workspace_bytes", "set_timing_events", "library_path",
+    "prefill_workspace_bytes", "decode_workspace_bytes", "library_path",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -80,21 +82,26 @@ def _load() -> ctypes.CDLL:
                           "`python causal_attention_rope_amd/build.py`") from e
     vp, i32, f32, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
     cache_p = ctypes.POINTER(_CarKVCache)
+    prefill = [vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, vp, f32, i32, f32, cache_p, vp, sz,
+               vp]
+    cached = [vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, vp, vp, i32, f32, i32, f32, cache_p,
+              vp]
+    decode = [vp, vp, vp, vp, i32, i32, i32, i32, i32, vp, i32, f32, i32, f32, cache_p, vp, sz,
+              vp]
     sigs = {
         "car_rope_apply": (i32, [vp, i32, i32, i32, i32, i32, vp, f32, i32, vp]),
         "car_kv_cache_append": (i32, [cache_p, i32, vp, vp, i32, i32, i32, i32, vp, vp]),
         "car_kv_int8_calibrate": (i32, [vp, vp, i32, i32, i32, i32, i32, vp, f32, i32, vp, vp,
                                         vp]),
         "car_attn_prefill_workspace_bytes": (sz, [i32, i32, i32, i32, i32, cache_p]),
-        "car_attn_prefill": (i32, [vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, vp, f32, i32,
-                                   f32, cache_p, vp, sz, vp]),
-        "car_attn_prefill_cached": (i32, [vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, vp, vp,
-                                          i32, f32, i32, f32, cache_p, vp]),
+        "car_attn_prefill": (i32, prefill),
+        "car_attn_prefill_timed": (i32, prefill + [vp, vp]),
+        "car_attn_prefill_cached": (i32, cached),
+        "car_attn_prefill_cached_timed": (i32, cached + [vp, vp]),
         "car_attn_decode_workspace_bytes": (sz, [i32, i32, i32, i32]),
-        "car_attn_decode": (i32, [vp, vp, vp, vp, i32, i32, i32, i32, i32, vp, i32, f32, i32,
-                                  f32, cache_p, vp, sz, vp]),
+        "car_attn_decode": (i32, decode),
+        "car_attn_decode_timed": (i32, decode + [vp, vp]),
         "car_status_string": (ctypes.c_char_p, [i32]),
-        "car_set_timing_events": (i32, [vp, vp]),
     }
     for name, (res, args) in sigs.items():
         fn = getattr(lib, name)
@@ -241,16 +248,12 @@ class KVCache:
 # entry points
 # --------------------------------------------------------------------------
 
-def set_timing_events(start: Optional[torch.cuda.Event], stop: Optional[torch.cuda.Event]):
-    """Record ``start``/``stop`` around the main attention kernel of the
-    following attn_prefill / attn_decode calls (None, None switches off).
-    The events must already exist (recorded once)."""
-    if start is None or stop is None:
-        _check(_lib.car_set_timing_events(None, None), "set_timing_events")
-    else:
-        _check(_lib.car_set_timing_events(ctypes.c_void_p(start.cuda_event),
-                                          ctypes.c_void_p(stop.cuda_event)),
-               "set_timing_events")
+def _events(timing):
+    """Raw hipEvent_t handles of a (start, stop) pair of torch.cuda.Event."""
+    if timing is None:
+        return None
+    start, stop = timing
+    return [ctypes.c_void_p(start.cuda_event), ctypes.c_void_p(stop.cuda_event)]
 
 
 def rope_apply(x: torch.Tensor, positions: torch.Tensor, theta: float = 10000.0,
@@ -333,7 +336,7 @@ def attn_prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, positions: t
                  theta: float = 10000.0, scale: Optional[float] = None,
                  cache: Optional[KVCache] = None, out: Optional[torch.Tensor] = None,
                  workspace: Optional[torch.Tensor] = None,
-                 rope_pairing: str = "adjacent") -> torch.Tensor:
+                 rope_pairing: str = "adjacent", timing=None) -> torch.Tensor:
     """Causal attention over a prompt with RoPE on q and k (see car_attn_prefill).
 
     q [B, Hq, S, D]; k, v [B, Hkv, S, D]; positions int32 [B, S], strictly
@@ -368,11 +371,15 @@ def attn_prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, positions: t
     dt = _dtype_code(q)
     need = int(_lib.car_attn_prefill_workspace_bytes(dt, B, Hkv, S, D, None))
     ws = _workspace(need, q.device, workspace)
-    _check(_lib.car_attn_prefill(_ptr(q), _ptr(k), _ptr(v), _ptr(out), dt, B, Hq, Hkv, S, D,
-                                 _ptr(positions), float(theta), _pairing(rope_pairing),
-                                 float(scale),
-                                 ctypes.byref(c) if c is not None else None, _ptr(ws),
-                                 ws.numel() * ws.element_size(), _stream(q)), "attn_prefill")
+    args = [_ptr(q), _ptr(k), _ptr(v), _ptr(out), dt, B, Hq, Hkv, S, D, _ptr(positions),
+            float(theta), _pairing(rope_pairing), float(scale),
+            ctypes.byref(c) if c is not None else None, _ptr(ws),
+            ws.numel() * ws.element_size(), _stream(q)]
+    ev = _events(timing)
+    if ev is None:
+        _check(_lib.car_attn_prefill(*args), "attn_prefill")
+    else:
+        _check(_lib.car_attn_prefill_timed(*args, *ev), "attn_prefill")
     return out
 
 
@@ -381,7 +388,7 @@ def attn_prefill_cached(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
                         theta: float = 10000.0, scale: Optional[float] = None,
                         out: Optional[torch.Tensor] = None,
                         chunk_lens: Optional[torch.Tensor] = None,
-                        rope_pairing: str = "adjacent") -> torch.Tensor:
+                        rope_pairing: str = "adjacent", timing=None) -> torch.Tensor:
     """A prompt chunk continuing a cached prefix (see car_attn_prefill_cached).
 
     q [B, Hq, S, D]; k, v [B, Hkv, S, D] (k not rotated); seq_lens int32 [B]
@@ -418,11 +425,14 @@ def attn_prefill_cached(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
     if scale is None:
         scale = 1.0 / math.sqrt(D)
     c = cache._c()
-    _check(_lib.car_attn_prefill_cached(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _dtype_code(q),
-                                        B, Hq, Hkv, S, D, _ptr(seq_lens), _ptr(chunk_lens),
-                                        int(max_seq_len), float(theta), _pairing(rope_pairing),
-                                        float(scale), ctypes.byref(c), _stream(q)),
-           "attn_prefill_cached")
+    args = [_ptr(q), _ptr(k), _ptr(v), _ptr(out), _dtype_code(q), B, Hq, Hkv, S, D,
+            _ptr(seq_lens), _ptr(chunk_lens), int(max_seq_len), float(theta),
+            _pairing(rope_pairing), float(scale), ctypes.byref(c), _stream(q)]
+    ev = _events(timing)
+    if ev is None:
+        _check(_lib.car_attn_prefill_cached(*args), "attn_prefill_cached")
+    else:
+        _check(_lib.car_attn_prefill_cached_timed(*args, *ev), "attn_prefill_cached")
     return out
 
 
@@ -431,7 +441,7 @@ def attn_decode(q: torch.Tensor, k_new: torch.Tensor, v_new: torch.Tensor,
                 theta: float = 10000.0, scale: Optional[float] = None,
                 out: Optional[torch.Tensor] = None,
                 workspace: Optional[torch.Tensor] = None,
-                rope_pairing: str = "adjacent") -> torch.Tensor:
+                rope_pairing: str = "adjacent", timing=None) -> torch.Tensor:
     """One decode step (see car_attn_decode).
 
     q [B, Hq, D]; k_new, v_new [B, Hkv, D] (not rotated); seq_lens int32 [B]
@@ -462,8 +472,12 @@ def attn_decode(q: torch.Tensor, k_new: torch.Tensor, v_new: torch.Tensor,
     need = int(_lib.car_attn_decode_workspace_bytes(B, Hq, D, int(max_seq_len)))
     ws = _workspace(need, q.device, workspace)
     c = cache._c()
-    _check(_lib.car_attn_decode(_ptr(q), _ptr(k_new), _ptr(v_new), _ptr(out), _dtype_code(q),
-                                B, Hq, Hkv, D, _ptr(seq_lens), int(max_seq_len), float(theta),
-                                _pairing(rope_pairing), float(scale), ctypes.byref(c), _ptr(ws),
-                                ws.numel() * ws.element_size(), _stream(q)), "attn_decode")
+    args = [_ptr(q), _ptr(k_new), _ptr(v_new), _ptr(out), _dtype_code(q), B, Hq, Hkv, D,
+            _ptr(seq_lens), int(max_seq_len), float(theta), _pairing(rope_pairing),
+            float(scale), ctypes.byref(c), _ptr(ws), ws.numel() * ws.element_size(), _stream(q)]
+    ev = _events(timing)
+    if ev is None:
+        _check(_lib.car_attn_decode(*args), "attn_decode")
+    else:
+        _check(_lib.car_attn_decode_timed(*args, *ev), "attn_decode")
     return out

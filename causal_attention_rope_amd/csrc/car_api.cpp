@@ -1,11 +1,9 @@
 // C-ABI entry points (include/car.h): argument validation, RoPE frequency
 // table, workspace sizing and dispatch to the HIP kernels.  Every check runs
 // before any launch; a failed check returns its status with nothing
-// enqueued.
+// enqueued.  The library keeps no state between calls.
 #include <math.h>
 #include <stdint.h>
-
-#include <atomic>
 
 #include "car.h"
 #include "launch.hpp"
@@ -14,13 +12,10 @@ using namespace car;
 
 namespace {
 
-std::atomic<hipEvent_t> g_ev_start{nullptr};
-std::atomic<hipEvent_t> g_ev_stop{nullptr};
-
-TimedLaunch timing() {
-  TimedLaunch t{g_ev_start.load(), g_ev_stop.load()};
-  if (t.start == nullptr || t.stop == nullptr) t.start = t.stop = nullptr;
-  return t;
+// Events recorded around the main kernel (both or neither).
+TimedLaunch timed(hipEvent_t start, hipEvent_t stop) {
+  if (start == nullptr || stop == nullptr) return TimedLaunch{nullptr, nullptr};
+  return TimedLaunch{start, stop};
 }
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
@@ -102,12 +97,6 @@ const char* car_status_string(car_status s) {
   return "unknown car_status";
 }
 
-car_status car_set_timing_events(hipEvent_t start, hipEvent_t stop) {
-  g_ev_start.store(start);
-  g_ev_stop.store(stop);
-  return CAR_OK;
-}
-
 car_status car_rope_apply(void* x, car_dtype dtype, int B, int H, int S, int D,
                           const int32_t* positions, float theta, car_rope_pairing pairing,
                           hipStream_t stream) {
@@ -164,11 +153,13 @@ size_t car_attn_prefill_workspace_bytes(car_dtype dtype, int B, int Hkv, int S, 
   return (size_t)prefill_ws_bytes(dtype, B, Hkv, S, D);
 }
 
-car_status car_attn_prefill(const void* q, const void* k, const void* v, void* out,
-                            car_dtype dtype, int B, int Hq, int Hkv, int S, int D,
-                            const int32_t* positions, float theta, car_rope_pairing pairing,
-                            float scale, const car_kv_cache* cache, void* workspace,
-                            size_t workspace_bytes, hipStream_t stream) {
+car_status car_attn_prefill_timed(const void* q, const void* k, const void* v, void* out,
+                                  car_dtype dtype, int B, int Hq, int Hkv, int S, int D,
+                                  const int32_t* positions, float theta,
+                                  car_rope_pairing pairing, float scale,
+                                  const car_kv_cache* cache, void* workspace,
+                                  size_t workspace_bytes, hipStream_t stream,
+                                  hipEvent_t kernel_start, hipEvent_t kernel_stop) {
   if (!dtype_ok(dtype) || !head_dim_ok(D) || !pairing_ok(pairing)) return CAR_ERR_UNSUPPORTED;
   if (cache != nullptr && cache->block_table != nullptr && cache->block_size != 16)
     return CAR_ERR_UNSUPPORTED;
@@ -202,14 +193,26 @@ car_status car_attn_prefill(const void* q, const void* k, const void* v, void* o
   if (e != hipSuccess) return CAR_ERR_HIP;
   return from_hip(launch_prefill_attention(dt, D, q, workspace, v, out, B, Hq, Hkv, S,
                                            positions, fr, scale, keys_in_cache ? &c : nullptr,
-                                           stream, timing()));
+                                           stream, timed(kernel_start, kernel_stop)));
 }
 
-car_status car_attn_prefill_cached(const void* q, const void* k, const void* v, void* out,
-                                   car_dtype dtype, int B, int Hq, int Hkv, int S, int D,
-                                   const int32_t* seq_lens, const int32_t* chunk_lens,
-                                   int max_seq_len, float theta, car_rope_pairing pairing,
-                                   float scale, const car_kv_cache* cache, hipStream_t stream) {
+car_status car_attn_prefill(const void* q, const void* k, const void* v, void* out,
+                            car_dtype dtype, int B, int Hq, int Hkv, int S, int D,
+                            const int32_t* positions, float theta, car_rope_pairing pairing,
+                            float scale, const car_kv_cache* cache, void* workspace,
+                            size_t workspace_bytes, hipStream_t stream) {
+  return car_attn_prefill_timed(q, k, v, out, dtype, B, Hq, Hkv, S, D, positions, theta,
+                                pairing, scale, cache, workspace, workspace_bytes, stream,
+                                nullptr, nullptr);
+}
+
+car_status car_attn_prefill_cached_timed(const void* q, const void* k, const void* v,
+                                         void* out, car_dtype dtype, int B, int Hq, int Hkv,
+                                         int S, int D, const int32_t* seq_lens,
+                                         const int32_t* chunk_lens, int max_seq_len,
+                                         float theta, car_rope_pairing pairing, float scale,
+                                         const car_kv_cache* cache, hipStream_t stream,
+                                         hipEvent_t kernel_start, hipEvent_t kernel_stop) {
   if (!dtype_ok(dtype) || !head_dim_ok(D) || !pairing_ok(pairing)) return CAR_ERR_UNSUPPORTED;
   if (cache != nullptr && cache->block_table != nullptr && cache->block_size != 16)
     return CAR_ERR_UNSUPPORTED;
@@ -242,7 +245,18 @@ car_status car_attn_prefill_cached(const void* q, const void* k, const void* v, 
       launch_chunk_prep(dt, D, paged, c, k, v, B, Hkv, S, seq_lens, chunk_lens, fr, stream);
   if (e != hipSuccess) return CAR_ERR_HIP;
   return from_hip(launch_prefill_cached(dt, D, paged, q, out, B, Hq, Hkv, S, c, seq_lens,
-                                        chunk_lens, fr, scale, stream, timing()));
+                                        chunk_lens, fr, scale, stream,
+                                        timed(kernel_start, kernel_stop)));
+}
+
+car_status car_attn_prefill_cached(const void* q, const void* k, const void* v, void* out,
+                                   car_dtype dtype, int B, int Hq, int Hkv, int S, int D,
+                                   const int32_t* seq_lens, const int32_t* chunk_lens,
+                                   int max_seq_len, float theta, car_rope_pairing pairing,
+                                   float scale, const car_kv_cache* cache, hipStream_t stream) {
+  return car_attn_prefill_cached_timed(q, k, v, out, dtype, B, Hq, Hkv, S, D, seq_lens,
+                                       chunk_lens, max_seq_len, theta, pairing, scale, cache,
+                                       stream, nullptr, nullptr);
 }
 
 size_t car_attn_decode_workspace_bytes(int B, int Hq, int D, int max_seq_len) {
@@ -250,11 +264,13 @@ size_t car_attn_decode_workspace_bytes(int B, int Hq, int D, int max_seq_len) {
   return (size_t)B * Hq * decode_nsplit(max_seq_len) * decode_partial_words(D) * sizeof(float);
 }
 
-car_status car_attn_decode(const void* q, const void* k_new, const void* v_new, void* out,
-                           car_dtype dtype, int B, int Hq, int Hkv, int D,
-                           const int32_t* seq_lens, int max_seq_len, float theta,
-                           car_rope_pairing pairing, float scale, const car_kv_cache* cache,
-                           void* workspace, size_t workspace_bytes, hipStream_t stream) {
+car_status car_attn_decode_timed(const void* q, const void* k_new, const void* v_new,
+                                 void* out, car_dtype dtype, int B, int Hq, int Hkv, int D,
+                                 const int32_t* seq_lens, int max_seq_len, float theta,
+                                 car_rope_pairing pairing, float scale,
+                                 const car_kv_cache* cache, void* workspace,
+                                 size_t workspace_bytes, hipStream_t stream,
+                                 hipEvent_t kernel_start, hipEvent_t kernel_stop) {
   if (!dtype_ok(dtype) || !head_dim_ok(D) || !pairing_ok(pairing)) return CAR_ERR_UNSUPPORTED;
   if (cache != nullptr && cache->block_table != nullptr && cache->block_size != 16)
     return CAR_ERR_UNSUPPORTED;
@@ -283,12 +299,22 @@ car_status car_attn_decode(const void* q, const void* k_new, const void* v_new, 
   const bool paged = cache->block_table != nullptr;
   float* part = static_cast<float*>(workspace);
   const RopeFreq fr = make_freq(D, theta, pairing);
+  const TimedLaunch tl = timed(kernel_start, kernel_stop);
   if (is_int8(cache))
     return from_hip(launch_decode_i8(dt, D, group, paged, q, k_new, v_new, out, B, Hq, Hkv,
-                                     seq_lens, max_seq_len, c, part, fr, scale, stream,
-                                     timing()));
+                                     seq_lens, max_seq_len, c, part, fr, scale, stream, tl));
   return from_hip(launch_decode(dt, D, group, paged, q, k_new, v_new, out, B, Hq, Hkv, seq_lens,
-                                max_seq_len, c, part, fr, scale, stream, timing()));
+                                max_seq_len, c, part, fr, scale, stream, tl));
+}
+
+car_status car_attn_decode(const void* q, const void* k_new, const void* v_new, void* out,
+                           car_dtype dtype, int B, int Hq, int Hkv, int D,
+                           const int32_t* seq_lens, int max_seq_len, float theta,
+                           car_rope_pairing pairing, float scale, const car_kv_cache* cache,
+                           void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  return car_attn_decode_timed(q, k_new, v_new, out, dtype, B, Hq, Hkv, D, seq_lens,
+                               max_seq_len, theta, pairing, scale, cache, workspace,
+                               workspace_bytes, stream, nullptr, nullptr);
 }
 
 }  // extern "C"

@@ -54,30 +54,26 @@ __device__ __forceinline__ uint32_t perm_hi(uint32_t a, uint32_t b) {
 
 constexpr uint32_t kOnePair = 0x3F803F80u;  // (1.0, 1.0) in bf16
 
-// Per-lane geometry of the decode split kernel.  A lane holds C = 2 chunks
-// of 16 bytes of a cache row, chunks c*LPR + lane%LPR for c < C, so LPR =
-// D*sizeof(T)/32 lanes cover a row and each load instruction (one chunk per
-// lane) moves 64/LPR rows, each as a contiguous half row.  Two chunks per lane
-// halve the lanes per row against one chunk: a score needs one fewer
-// reduction step and every per-row step (exp, pack, max) runs on half as many
-// lanes.  A round is R row steps (two register buffers of R steps are live).
-#ifndef CAR_DECODE_RMAX
-#define CAR_DECODE_RMAX 2
-#endif
-#ifndef CAR_DECODE_C
-#define CAR_DECODE_C 1
-#endif
+// Per-lane geometry of the decode split kernel.  A lane holds C chunks of
+// 16 bytes of a cache row, chunks c*LPR + lane%LPR for c < C, so LPR =
+// D*sizeof(T)/(16*C) lanes cover a row and each load instruction (one chunk
+// per lane) moves 64/LPR rows.  C = 1 (measured faster than 2: it needs
+// fewer registers per row step, so more rows are in flight).  A round is R
+// row steps (two register buffers of R steps are live); R = 2 (more steps
+// per round spilled or measured no faster).
+constexpr int kDecodeChunks = 1;
+constexpr int kDecodeRoundMax = 2;
 template <typename T, int D, int G, int SPLIT = DECODE_SPLIT>
 struct DecodeGeom {
   static constexpr int WAVES = decode_waves<G>();
   static constexpr int TPW = SPLIT / WAVES;    // tokens per wave
   static constexpr int N = Vec16<T>::N;        // elements per 16-byte chunk
-  static constexpr int C = CAR_DECODE_C;       // chunks per lane per row
+  static constexpr int C = kDecodeChunks;      // chunks per lane per row
   static constexpr int LPR = D / N / C;        // lanes per cache row
   static constexpr int NG = 64 / LPR;          // rows per load instruction
   static constexpr int STEPS = TPW / NG;
   static_assert(SPLIT % DECODE_SPLIT == 0 && TPW % 64 == 0, "whole 16-token blocks per wave");
-  static constexpr int R_MAX = CAR_DECODE_RMAX;
+  static constexpr int R_MAX = kDecodeRoundMax;
   static constexpr int R = STEPS < R_MAX ? STEPS : R_MAX;  // steps per round
   static constexpr int ROUNDS = STEPS / R;
   static_assert(LPR == 4 || LPR == 8 || LPR == 16 || LPR == 32, "lanes per row");
@@ -131,7 +127,11 @@ __attribute__((amdgpu_waves_per_eu(G <= 4 ? 4 : 2))) void decode_split_kernel(
   // exit at once.
   const int hk = blockIdx.x % Hkv, b = blockIdx.x / Hkv;
   const int Hq = Hkv * G;
-  const int L = min(max(seq_lens[b], 0), cache_last_slot<PAGED>(c));
+  // A length outside the cache is clamped for the reads (the output is then
+  // unspecified) and the new token is not stored.
+  const int L_in = seq_lens[b];
+  const int L = min(max(L_in, 0), cache_last_slot<PAGED>(c));
+  const bool store_new = L_in == L;
   const int nsb = min(L / SPLIT + 1, nsplit);  // splits that hold tokens 0..L
   const int split = (int)blockIdx.y - (nsplit - nsb);
   if (split < 0) return;  // uniform over the workgroup
@@ -190,7 +190,7 @@ __attribute__((amdgpu_waves_per_eu(G <= 4 ? 4 : 2))) void decode_split_kernel(
       store16<T>(kt, f);
       kn[ch] = *reinterpret_cast<const u32x4_t*>(kt);
       vn[ch] = *reinterpret_cast<const u32x4_t*>(v_new + src);
-      if (wave == 0 && grp == 0) {
+      if (wave == 0 && grp == 0 && store_new) {
         const int64_t dst = cache_row<PAGED>(c, b, hk, Hkv, L) * D + col[ch];
         *reinterpret_cast<u32x4_t*>(Kc + dst) = kn[ch];
         *reinterpret_cast<u32x4_t*>(Vc + dst) = vn[ch];

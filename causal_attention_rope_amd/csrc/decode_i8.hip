@@ -139,7 +139,9 @@ __attribute__((amdgpu_waves_per_eu(G == 1 ? 4 : 2))) void decode_i8_split_kernel
   // aligned to the last row so that the short last splits run last.
   const int hk = blockIdx.x % Hkv, b = blockIdx.x / Hkv;
   const int Hq = Hkv * G;
-  const int L = min(max(seq_lens[b], 0), cache_last_slot<PAGED>(c));
+  const int L_in = seq_lens[b];  // outside the cache: clamped reads, no store
+  const int L = min(max(L_in, 0), cache_last_slot<PAGED>(c));
+  const bool store_new = L_in == L;
   const int nsb = min(L / SPLIT + 1, nsplit);
   const int split = (int)blockIdx.y - (nsplit - nsb);
   if (split < 0) return;  // uniform over the workgroup
@@ -200,7 +202,7 @@ __attribute__((amdgpu_waves_per_eu(G == 1 ? 4 : 2))) void decode_i8_split_kernel
         vn[j * NT / 4 + w] = vw[w];
       }
     }
-    if (wave == 0 && grp == 0) {
+    if (wave == 0 && grp == 0 && store_new) {
       const int64_t dst = cache_row<PAGED>(c, b, hk, Hkv, L) * D + col;
       *reinterpret_cast<Chunk*>(Kc + dst) = kn;
       *reinterpret_cast<Chunk*>(Vc + dst) = vn;
@@ -455,7 +457,9 @@ decode_i8_mfma_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k
   // grid order, splits and the new token as in decode_i8_split_kernel
   const int hk = blockIdx.x % Hkv, b = blockIdx.x / Hkv;
   const int Hq = Hkv * G;
-  const int L = min(max(seq_lens[b], 0), cache_last_slot<PAGED>(c));
+  const int L_in = seq_lens[b];  // outside the cache: clamped reads, no store
+  const int L = min(max(L_in, 0), cache_last_slot<PAGED>(c));
+  const bool store_new = L_in == L;
   const int nsb = min(L / SPLIT + 1, nsplit);
   const int split = (int)blockIdx.y - (nsplit - nsb);
   if (split < 0) return;  // uniform over the workgroup
@@ -526,8 +530,10 @@ decode_i8_mfma_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k
       uint32_t kw[2], vw[2];
       int8_codes<8>(f, ksc + col, kw);
       int8_codes<8>(g, vsc + col, vw);
-      *reinterpret_cast<u32x2_t*>(Kc + dst + col) = u32x2_t{kw[0], kw[1]};
-      *reinterpret_cast<u32x2_t*>(Vc + dst + col) = u32x2_t{vw[0], vw[1]};
+      if (store_new) {
+        *reinterpret_cast<u32x2_t*>(Kc + dst + col) = u32x2_t{kw[0], kw[1]};
+        *reinterpret_cast<u32x2_t*>(Vc + dst + col) = u32x2_t{vw[0], vw[1]};
+      }
       *reinterpret_cast<u32x2_t*>(&snew[0][col]) = u32x2_t{kw[0], kw[1]};
       *reinterpret_cast<u32x2_t*>(&snew[1][col]) = u32x2_t{vw[0], vw[1]};
     }

@@ -30,7 +30,8 @@ struct CacheArgs {
 
 enum Dtype { F32 = 0, BF16 = 1 };
 
-// Launch-time timing events (benchmark hook); both null when unused.
+// Events recorded on the launch stream just before and just after the main
+// kernel of a call (both null when the caller times nothing).
 struct TimedLaunch {
   hipEvent_t start;
   hipEvent_t stop;

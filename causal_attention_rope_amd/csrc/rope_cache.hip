@@ -25,13 +25,16 @@ inline int grid_for(int64_t nvec) {
   return (int)(blocks < 16384 ? (blocks > 0 ? blocks : 1) : 16384);
 }
 
-template <typename T, int D>
+// HALF: pairs (i, i + D/2): a thread takes one 16-byte chunk of the first
+// half of a row and its partner chunk in the second half (nvec counts those
+// chunk pairs); otherwise one chunk of adjacent pairs (nvec counts chunks).
+template <typename T, int D, bool HALF>
 __global__ __launch_bounds__(kThreads) void rope_apply_kernel(T* __restrict__ x,
                                                               const int32_t* __restrict__ positions,
                                                               int H, int S, int64_t nvec,
                                                               RopeFreq fr) {
   constexpr int N = Vec16<T>::N;
-  constexpr int VPR = D / N;  // vectors per row
+  constexpr int VPR = HALF ? D / N / 2 : D / N;  // work items per row
   for (int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x; i < nvec;
        i += (int64_t)gridDim.x * kThreads) {
     const int64_t row = i / VPR;
@@ -42,12 +45,9 @@ __global__ __launch_bounds__(kThreads) void rope_apply_kernel(T* __restrict__ x,
     T* p = x + row * D + col;
     float f[N];
     load16<T>(p, f);
-    if (fr.half) {
-      // in place: the thread of the first-half chunk rotates both halves
-      if (col >= D / 2) continue;
-      float h[N];
+    if constexpr (HALF) {
+      float h[N], a[N];
       load16<T>(p + D / 2, h);
-      float a[N];
 #pragma unroll
       for (int j = 0; j < N; ++j) a[j] = f[j];
       rope_rotate_half_chunk<N>(f, h, pos, col, D, fr);
@@ -78,7 +78,8 @@ __global__ __launch_bounds__(kThreads) void kv_append_kernel(CacheArgs c,
     const int64_t bh = row / S;
     const int hk = (int)(bh % Hkv);
     const int b = (int)(bh / Hkv);
-    const int pos = min(max(positions[(int64_t)b * S + s], 0), last);
+    const int pos = positions[(int64_t)b * S + s];
+    if (pos < 0 || pos > last) continue;  // outside the cache: not stored
     const int64_t dst = cache_row<PAGED>(c, b, hk, Hkv, pos) * D + col;
     if constexpr (I8) {
       float kf[N], vf[N];
@@ -120,10 +121,9 @@ __global__ __launch_bounds__(kThreads) void prefill_prep_kernel(
     int p0;
     if (!KEYS_IN_CACHE || !prompt_rows_in_cache(positions, b, S, c.max_seq, &p0))
       store16<T>(k_rot + row * D + col, f);
-    if constexpr (CACHE) {
+    if (CACHE && pos >= 0 && pos <= cache_last_slot<PAGED>(c)) {  // else not stored
       const int hk = (int)(bh % Hkv);
-      const int slot = min(max(pos, 0), cache_last_slot<PAGED>(c));
-      const int64_t dst = cache_row<PAGED>(c, b, hk, Hkv, slot) * D + col;
+      const int64_t dst = cache_row<PAGED>(c, b, hk, Hkv, pos) * D + col;
       if constexpr (I8) {
         // the fp32 rotated key is quantized (not its rounded copy in k_rot)
         float vf[N];
@@ -140,8 +140,9 @@ __global__ __launch_bounds__(kThreads) void prefill_prep_kernel(
 }
 
 // A chunk continuing a cached prefix: token s of sequence b sits at position
-// P + s, P = seq_lens[b] (kept so that the chunk fits the cache, as the
-// attention kernel does); its rotated key and raw value go to that index.
+// P + s, P = seq_lens[b]; its rotated key and raw value go to that index.  A
+// chunk that does not fit the cache is not stored (the attention kernel then
+// reads clamped rows and its output is unspecified).
 // With chunk_lens, tokens s >= chunk_lens[b] are padding and are not stored.
 template <typename T, int D, bool PAGED>
 __global__ __launch_bounds__(kThreads) void chunk_prep_kernel(
@@ -161,8 +162,9 @@ __global__ __launch_bounds__(kThreads) void chunk_prep_kernel(
     const int b = (int)(bh / Hkv);
     const int Sb = chunk_lens == nullptr ? S : min(max(chunk_lens[b], 0), S);
     if (s >= Sb) continue;  // padding
-    const int P = max(min(max(seq_lens[b], 0), last + 1 - Sb), 0);
-    const int pos = min(P + s, last);
+    const int P = seq_lens[b];
+    if (P < 0 || P + Sb > last + 1) continue;  // the chunk does not fit: not stored
+    const int pos = P + s;
     float f[N];
     load16<T>(k + row * D + col, f);
     rope_rotate_chunk<T, N>(f, k + row * D, col, D, pos, fr);
@@ -270,9 +272,16 @@ hipError_t int8_calibrate_t(const void* k, const void* v, int B, int Hkv, int S,
 template <typename T, int D>
 hipError_t rope_apply_t(void* x, int B, int H, int S, const int32_t* positions,
                         const RopeFreq& fr, hipStream_t st) {
-  const int64_t nvec = (int64_t)B * H * S * (D / Vec16<T>::N);
-  hipLaunchKernelGGL((rope_apply_kernel<T, D>), dim3(grid_for(nvec)), dim3(kThreads), 0, st,
-                     static_cast<T*>(x), positions, H, S, nvec, fr);
+  const int64_t rows = (int64_t)B * H * S;
+  if (fr.half) {
+    const int64_t nvec = rows * (D / Vec16<T>::N / 2);
+    hipLaunchKernelGGL((rope_apply_kernel<T, D, true>), dim3(grid_for(nvec)), dim3(kThreads), 0,
+                       st, static_cast<T*>(x), positions, H, S, nvec, fr);
+  } else {
+    const int64_t nvec = rows * (D / Vec16<T>::N);
+    hipLaunchKernelGGL((rope_apply_kernel<T, D, false>), dim3(grid_for(nvec)), dim3(kThreads), 0,
+                       st, static_cast<T*>(x), positions, H, S, nvec, fr);
+  }
   return hipGetLastError();
 }
 

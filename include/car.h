@@ -30,7 +30,7 @@
  *   ([Scratch] §3.2); positions are 0-based.
  * Ownership.  The caller owns every buffer.  The library never allocates,
  *   frees or keeps a pointer after a call returns, and holds no state
- *   except the benchmark event pair of car_set_timing_events().
+ *   between calls.
  * Asynchrony.  Each call only enqueues kernels on `stream` (0 = the null
  *   stream) and returns; results are ready when the stream reaches them.
  * Errors.  Everything the host can check (null pointers, sizes, D, Hq/Hkv,
@@ -38,9 +38,11 @@
  *   checked before any launch, and a failed check returns its status with
  *   nothing enqueued.  Nothing throws or aborts across the ABI.  Values in
  *   device memory (positions, seq_lens, block_table) cannot be checked by
- *   the host: the kernels clamp indices so that memory outside the given
- *   buffers is never touched, but results for out-of-range values are
- *   unspecified.
+ *   the host: the kernels clamp the indices they read, so that memory
+ *   outside the given buffers is never touched, and store nothing at a cache
+ *   index outside the cache (a position or seq_lens[b] outside [0, capacity),
+ *   a chunk that does not fit), so that no other token's cached row is
+ *   overwritten.  Outputs for such values are unspecified.
  */
 #ifndef CAR_H_
 #define CAR_H_
@@ -290,18 +292,38 @@ car_status car_attn_decode(const void* q, const void* k_new, const void* v_new,
                            float scale, const car_kv_cache* cache, void* workspace,
                            size_t workspace_bytes, hipStream_t stream);
 
+/*
+ * Timed variants: the same calls, with `kernel_start` recorded on `stream`
+ * immediately before the call's attention kernel and `kernel_stop`
+ * immediately after it, so that hipEventElapsedTime(kernel_start,
+ * kernel_stop) is that one kernel's duration (a prefill's key-rotation
+ * pass and any other kernel of the call fall outside).  Both events NULL:
+ * exactly the untimed call.  Only one of the two NULL: nothing is recorded.
+ */
+car_status car_attn_prefill_timed(const void* q, const void* k, const void* v, void* out,
+                                  car_dtype dtype, int B, int Hq, int Hkv, int S, int D,
+                                  const int32_t* positions, float theta,
+                                  car_rope_pairing pairing, float scale,
+                                  const car_kv_cache* cache, void* workspace,
+                                  size_t workspace_bytes, hipStream_t stream,
+                                  hipEvent_t kernel_start, hipEvent_t kernel_stop);
+car_status car_attn_prefill_cached_timed(const void* q, const void* k, const void* v,
+                                         void* out, car_dtype dtype, int B, int Hq, int Hkv,
+                                         int S, int D, const int32_t* seq_lens,
+                                         const int32_t* chunk_lens, int max_seq_len,
+                                         float theta, car_rope_pairing pairing, float scale,
+                                         const car_kv_cache* cache, hipStream_t stream,
+                                         hipEvent_t kernel_start, hipEvent_t kernel_stop);
+car_status car_attn_decode_timed(const void* q, const void* k_new, const void* v_new,
+                                 void* out, car_dtype dtype, int B, int Hq, int Hkv, int D,
+                                 const int32_t* seq_lens, int max_seq_len, float theta,
+                                 car_rope_pairing pairing, float scale,
+                                 const car_kv_cache* cache, void* workspace,
+                                 size_t workspace_bytes, hipStream_t stream,
+                                 hipEvent_t kernel_start, hipEvent_t kernel_stop);
+
 /* Human-readable name of a status code (static storage). */
 const char* car_status_string(car_status status);
-
-/*
- * Benchmark hook.  When both events are non-NULL, the main attention kernel
- * of each following car_attn_prefill / car_attn_decode call is launched with
- * `start` recorded immediately before it and `stop` immediately after it on
- * the call's stream, so that hipEventElapsedTime(start, stop) is that
- * kernel's duration.  Pass NULL, NULL to switch it off.  Process-wide; not
- * meant for concurrent use from several threads.
- */
-car_status car_set_timing_events(hipEvent_t start, hipEvent_t stop);
 
 #ifdef __cplusplus
 }

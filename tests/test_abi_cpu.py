@@ -235,9 +235,28 @@ def test_int8_calibrate_rejects(lib):
 def test_workspace_sizes(lib):
     assert lib.car_attn_decode_workspace_bytes(32, 32, 128, 4096) == 32 * 32 * 16 * 132 * 4
     assert lib.car_attn_decode_workspace_bytes(64, 32, 128, 8193) == 64 * 32 * 33 * 132 * 4
+    assert lib.car_attn_decode_workspace_bytes(3, 5, 64, 300) == 3 * 5 * 2 * 68 * 4
     assert lib.car_attn_decode_workspace_bytes(1, 1, 96, 10) == 0
     assert lib.car_attn_prefill_workspace_bytes(F32, 1, 4, 128, 64, None) == 4 * 128 * 64 * 4
     assert lib.car_attn_prefill_workspace_bytes(BF16, 1, 4, 128, 72, None) == 0
+
+
+def test_timed_variants_check_like_the_plain_calls(car, lib):
+    """The _timed entry points run the same host checks (events unused)."""
+    c = _cache(car, max_seq=512)
+    need = lib.car_attn_decode_workspace_bytes(2, 8, 128, 300)
+    common = (FAKE, FAKE, FAKE, FAKE, BF16, 2, 8, 2, 128, FAKE, 300, 1e4, 1, 0.088,
+              ctypes.byref(c), FAKE)
+    assert lib.car_attn_decode_timed(*common, need - 16, None, None, None) == WORKSPACE
+    assert lib.car_attn_decode_timed(*common, need - 16, None, FAKE, FAKE) == WORKSPACE
+    pre = (FAKE, FAKE, FAKE, FAKE, BF16, 1, 4, 4, 8, 96, FAKE, 1e4, 0, 0.1, None, FAKE, 1 << 20,
+           None)
+    assert lib.car_attn_prefill_timed(*pre, None, None) == UNSUPPORTED
+    assert lib.car_attn_prefill(*pre) == UNSUPPORTED
+    cached = (FAKE, FAKE, FAKE, FAKE, BF16, 1, 4, 3, 8, 128, FAKE, None, 64, 1e4, 0, 0.1,
+              ctypes.byref(c), None)
+    assert lib.car_attn_prefill_cached_timed(*cached, None, None) == INVALID   # Hq % Hkv
+    assert lib.car_attn_prefill_cached(*cached) == INVALID
 
 
 def test_binding_refuses_cpu_tensors(car):
