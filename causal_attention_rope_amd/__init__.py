@@ -26,6 +26,7 @@ import torch
 __all__ = [
     "CarError", "KVCache", "rope_apply", "kv_cache_append", "attn_prefill", "attn_decode",
     "attn_prefill_cached", "kv_int8_calibrate",
+    "attn_decode_noalloc", "DECODE_NOALLOC_MAX_BYTES",
     "prefill_workspace_bytes", "decode_workspace_bytes", "library_path",
 ]
 
@@ -68,6 +69,8 @@ class _CarKVCache(ctypes.Structure):
 
 
 CACHE_NATIVE, CACHE_INT8 = 0, 1
+# CAR_DECODE_NOALLOC_MAX_BYTES: size of the per-GPU partials array of attn_decode_noalloc
+DECODE_NOALLOC_MAX_BYTES = 48 << 20
 
 
 def _load() -> ctypes.CDLL:
@@ -101,6 +104,7 @@ def _load() -> ctypes.CDLL:
         "car_attn_decode_workspace_bytes": (sz, [i32, i32, i32, i32]),
         "car_attn_decode": (i32, decode),
         "car_attn_decode_timed": (i32, decode + [vp, vp]),
+        "car_attn_decode_noalloc": (i32, decode[:15] + [vp]),
         "car_status_string": (ctypes.c_char_p, [i32]),
     }
     for name, (res, args) in sigs.items():
@@ -436,19 +440,8 @@ def attn_prefill_cached(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
     return out
 
 
-def attn_decode(q: torch.Tensor, k_new: torch.Tensor, v_new: torch.Tensor,
-                seq_lens: torch.Tensor, cache: KVCache, max_seq_len: int,
-                theta: float = 10000.0, scale: Optional[float] = None,
-                out: Optional[torch.Tensor] = None,
-                workspace: Optional[torch.Tensor] = None,
-                rope_pairing: str = "adjacent", timing=None) -> torch.Tensor:
-    """One decode step (see car_attn_decode).
-
-    q [B, Hq, D]; k_new, v_new [B, Hkv, D] (not rotated); seq_lens int32 [B]
-    (tokens already cached = position of the new token); ``max_seq_len`` is a
-    host bound on seq_lens + 1.  Writes the new key/value into the cache and
-    returns out [B, Hq, D].
-    """
+def _decode_checks(q, k_new, v_new, seq_lens, cache, out):
+    """Shape/dtype/device checks shared by the decode calls; returns (B, Hq, Hkv, D)."""
     _need(q, "q", dim=3)
     _need(k_new, "k_new", dtype=q.dtype, dim=3, device=q.device)
     _need(v_new, "v_new", dtype=q.dtype, dim=3, device=q.device)
@@ -464,9 +457,28 @@ def attn_decode(q: torch.Tensor, k_new: torch.Tensor, v_new: torch.Tensor,
     if cache.Hkv != Hkv or cache.D != D:
         raise ValueError("cache heads or head dim do not match k_new")
     cache.check_batch(B)
+    _need(out, "out", dtype=q.dtype, dim=3, device=q.device)
+    if out.shape != q.shape:
+        raise ValueError("out must have q's shape")
+    return B, Hq, Hkv, D
+
+
+def attn_decode(q: torch.Tensor, k_new: torch.Tensor, v_new: torch.Tensor,
+                seq_lens: torch.Tensor, cache: KVCache, max_seq_len: int,
+                theta: float = 10000.0, scale: Optional[float] = None,
+                out: Optional[torch.Tensor] = None,
+                workspace: Optional[torch.Tensor] = None,
+                rope_pairing: str = "adjacent", timing=None) -> torch.Tensor:
+    """One decode step (see car_attn_decode).
+
+    q [B, Hq, D]; k_new, v_new [B, Hkv, D] (not rotated); seq_lens int32 [B]
+    (tokens already cached = position of the new token); ``max_seq_len`` is a
+    host bound on seq_lens + 1.  Writes the new key/value into the cache and
+    returns out [B, Hq, D].
+    """
     if out is None:
         out = torch.empty_like(q)
-    _need(out, "out", dtype=q.dtype, dim=3, device=q.device)
+    B, Hq, Hkv, D = _decode_checks(q, k_new, v_new, seq_lens, cache, out)
     if scale is None:
         scale = 1.0 / math.sqrt(D)
     need = int(_lib.car_attn_decode_workspace_bytes(B, Hq, D, int(max_seq_len)))
@@ -480,4 +492,25 @@ def attn_decode(q: torch.Tensor, k_new: torch.Tensor, v_new: torch.Tensor,
         _check(_lib.car_attn_decode(*args), "attn_decode")
     else:
         _check(_lib.car_attn_decode_timed(*args, *ev), "attn_decode")
+    return out
+
+
+def attn_decode_noalloc(q: torch.Tensor, k_new: torch.Tensor, v_new: torch.Tensor,
+                        seq_lens: torch.Tensor, cache: KVCache, max_seq_len: int,
+                        out: torch.Tensor, theta: float = 10000.0,
+                        scale: Optional[float] = None,
+                        rope_pairing: str = "adjacent") -> torch.Tensor:
+    """attn_decode without a workspace (see car_attn_decode_noalloc): the
+    library keeps the split partials in a fixed device array of
+    ``DECODE_NOALLOC_MAX_BYTES`` per GPU, so nothing is allocated; ``out``
+    must be given.  Calls that overlap on one GPU race on that array."""
+    B, Hq, Hkv, D = _decode_checks(q, k_new, v_new, seq_lens, cache, out)
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    c = cache._c()
+    _check(_lib.car_attn_decode_noalloc(_ptr(q), _ptr(k_new), _ptr(v_new), _ptr(out),
+                                        _dtype_code(q), B, Hq, Hkv, D, _ptr(seq_lens),
+                                        int(max_seq_len), float(theta), _pairing(rope_pairing),
+                                        float(scale), ctypes.byref(c), _stream(q)),
+           "attn_decode_noalloc")
     return out

@@ -24,7 +24,8 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libcar.so")
 
-SOURCES = ["rope_cache.hip", "decode.hip", "decode_i8.hip", "prefill.hip", "car_api.cpp"]
+SOURCES = ["rope_cache.hip", "decode.hip", "decode_i8.hip", "prefill.hip", "car_api.cpp",
+           "decode_noalloc.hip"]
 
 ARCH = "gfx950"
 FLAGS = [

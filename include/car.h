@@ -322,6 +322,31 @@ car_status car_attn_decode_timed(const void* q, const void* k_new, const void* v
                                  size_t workspace_bytes, hipStream_t stream,
                                  hipEvent_t kernel_start, hipEvent_t kernel_stop);
 
+/*
+ * car_attn_decode_noalloc -- car_attn_decode for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc).  Same arguments and results as car_attn_decode
+ * without the workspace: the split partials live in a file-scope device array
+ * of CAR_DECODE_NOALLOC_MAX_BYTES that every GPU the library runs on holds
+ * until the process ends.  The call allocates and frees nothing.
+ *   Limit: sizes with car_attn_decode_workspace_bytes(B, Hq, D, max_seq_len)
+ *   above CAR_DECODE_NOALLOC_MAX_BYTES return CAR_ERR_WORKSPACE before any
+ *   work is queued (48 MiB holds, e.g., 64 sequences of 32 query heads,
+ *   D = 128, up to 11776 tokens).
+ *   Device: the stream's (the current device for the null stream).  The first
+ *   call on a device looks up the array's address there (hipGetSymbolAddress)
+ *   and keeps it.
+ *   Concurrency: every call on one GPU shares that GPU's array, so calls that
+ *   overlap on a GPU (different streams or threads, unordered) race and must
+ *   not be issued; calls ordered on one stream are safe.
+ */
+#define CAR_DECODE_NOALLOC_MAX_BYTES ((size_t)48 << 20)
+car_status car_attn_decode_noalloc(const void* q, const void* k_new, const void* v_new,
+                                   void* out, car_dtype dtype, int B, int Hq, int Hkv, int D,
+                                   const int32_t* seq_lens, int max_seq_len, float theta,
+                                   car_rope_pairing pairing, float scale,
+                                   const car_kv_cache* cache, hipStream_t stream);
+
 /* Human-readable name of a status code (static storage). */
 const char* car_status_string(car_status status);
 

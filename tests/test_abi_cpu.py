@@ -259,6 +259,21 @@ def test_timed_variants_check_like_the_plain_calls(car, lib):
     assert lib.car_attn_prefill_cached(*cached) == INVALID
 
 
+def test_noalloc_decode_limit(car, lib):
+    """The no-allocation decode refuses sizes whose partials exceed its
+    array before any HIP call (so this runs without a GPU), and the
+    binding's constant is the header's."""
+    text = open(HEADER, encoding="utf-8").read()
+    m = re.search(r"#define CAR_DECODE_NOALLOC_MAX_BYTES \(\(size_t\)(\d+) << (\d+)\)", text)
+    assert m and int(m.group(1)) << int(m.group(2)) == car.DECODE_NOALLOC_MAX_BYTES
+    limit = car.DECODE_NOALLOC_MAX_BYTES
+    assert lib.car_attn_decode_workspace_bytes(64, 32, 128, 46 * 256) <= limit
+    assert lib.car_attn_decode_workspace_bytes(64, 32, 128, 46 * 256 + 1) > limit
+    f = lib.car_attn_decode_noalloc
+    assert f(FAKE, FAKE, FAKE, FAKE, BF16, 64, 32, 8, 128, FAKE, 46 * 256 + 1, 1e4, 0, 0.088,
+             None, None) == WORKSPACE
+
+
 def test_binding_refuses_cpu_tensors(car):
     import torch
     x = torch.zeros(1, 1, 4, 64)
