@@ -177,6 +177,12 @@ car_status car_attn_prefill_timed(const void* q, const void* k, const void* v, v
     const car_status cs = check_cache(cache, &c, &cap);
     if (cs != CAR_OK) return cs;
   }
+  // launch grids (fp32: Hq and B in grid y and z; bf16: query tiles x B x Hq
+  // in x, at least 64 rows per tile) and 32-bit byte offsets within one
+  // head's keys (the prompt's, or a contiguous cache's)
+  if (B > 65535 || Hq > 65535 || (int64_t)B * Hq * ((S + 63) / 64) > INT32_MAX ||
+      (S > cap ? (int64_t)S : cap) * D * 4 > (int64_t)UINT32_MAX)
+    return CAR_ERR_UNSUPPORTED;
   const int64_t need = prefill_ws_bytes(dtype, B, Hkv, S, D);
   if (workspace == nullptr || !aligned16(workspace) || (int64_t)workspace_bytes < need)
     return CAR_ERR_WORKSPACE;
@@ -280,8 +286,9 @@ car_status car_attn_decode_timed(const void* q, const void* k_new, const void* v
   if ((int64_t)B * Hq == 0) return CAR_OK;
   const int group = Hq / Hkv;
   if (group != 1 && group != 2 && group != 4 && group != 8) return CAR_ERR_UNSUPPORTED;
-  // launch grid: B * Hkv workgroups in x, one row per 256-token split in y
-  if ((int64_t)B * Hkv > INT32_MAX || decode_nsplit(max_seq_len) > 65535) return CAR_ERR_UNSUPPORTED;
+  // launch grids: B * Hkv workgroups in x and one row per 256-token split in
+  // y for the splits, B * Hq workgroups for the merge
+  if ((int64_t)B * Hq > INT32_MAX || decode_nsplit(max_seq_len) > 65535) return CAR_ERR_UNSUPPORTED;
   if (q == nullptr || k_new == nullptr || v_new == nullptr || out == nullptr ||
       seq_lens == nullptr)
     return CAR_ERR_INVALID_ARGUMENT;

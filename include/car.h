@@ -208,7 +208,10 @@ size_t car_attn_prefill_workspace_bytes(car_dtype dtype, int B, int Hkv, int S, 
  *              values at full precision.
  *   workspace  device scratch of at least car_attn_prefill_workspace_bytes();
  *              its contents on entry are ignored and on exit unspecified.
- * S == 0 is a no-op returning CAR_OK.
+ * S == 0 is a no-op returning CAR_OK.  Sizes one launch cannot cover (B or
+ * Hq above 65535, B * Hq * ceil(S / 64) above 2^31 - 1, or S, or a cache's
+ * capacity, times D * 4 bytes above 2^32 - 1) return CAR_ERR_UNSUPPORTED
+ * before any work is queued.
  */
 car_status car_attn_prefill(const void* q, const void* k, const void* v, void* out,
                             car_dtype dtype, int B, int Hq, int Hkv, int S, int D,
@@ -282,7 +285,7 @@ size_t car_attn_decode_workspace_bytes(int B, int Hq, int D, int max_seq_len);
  *   workspace   device scratch of at least car_attn_decode_workspace_bytes();
  *               contents on entry ignored, on exit unspecified.
  * Calls that share a workspace must be ordered on one stream.
- * Sizes one launch cannot cover (B * Hkv above 2^31 - 1, or max_seq_len above
+ * Sizes one launch cannot cover (B * Hq above 2^31 - 1, or max_seq_len above
  * 65535 * 256 tokens) return CAR_ERR_UNSUPPORTED before any work is queued.
  */
 car_status car_attn_decode(const void* q, const void* k_new, const void* v_new,

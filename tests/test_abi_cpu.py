@@ -241,6 +241,34 @@ def test_workspace_sizes(lib):
     assert lib.car_attn_prefill_workspace_bytes(BF16, 1, 4, 128, 72, None) == 0
 
 
+def test_prefill_launch_limits_fail_before_any_launch(car, lib):
+    """Sizes beyond one launch's grid or 32-bit offsets are refused with
+    CAR_ERR_UNSUPPORTED by the host checks, before the K pass is queued
+    (without the checks these calls would reach a launch, which fails here
+    with CAR_ERR_HIP since there is no GPU)."""
+    f = lib.car_attn_prefill
+    ws = 1 << 40  # the workspace check passes; nothing is dereferenced
+
+    def call(dt, B, Hq, Hkv, S, D, cache=None):
+        return f(FAKE, FAKE, FAKE, FAKE, dt, B, Hq, Hkv, S, D, FAKE, 1e4, 0, 0.1, cache, FAKE,
+                 ws, None)
+
+    assert call(F32, 65536, 1, 1, 4, 64) == UNSUPPORTED      # fp32 grid z
+    assert call(F32, 1, 65536, 1, 4, 64) == UNSUPPORTED      # fp32 grid y
+    assert call(BF16, 65535, 65535, 1, 64, 64) == UNSUPPORTED  # bf16 grid x
+    assert call(BF16, 1, 1, 1, 1 << 23, 128) == UNSUPPORTED  # 32-bit key offsets
+    big = _cache(car, max_seq=1 << 23)
+    assert call(BF16, 1, 1, 1, 64, 128, ctypes.byref(big)) == UNSUPPORTED  # cache offsets
+
+
+def test_decode_merge_grid_bound(car, lib):
+    """The merge launches B * Hq workgroups: B * Hq above 2^31 - 1 is refused
+    even when B * Hkv fits."""
+    c = _cache(car, max_seq=64)
+    assert lib.car_attn_decode(FAKE, FAKE, FAKE, FAKE, BF16, 1 << 28, 8, 1, 128, FAKE, 16, 1e4,
+                               0, 0.1, ctypes.byref(c), FAKE, 1 << 60, None) == UNSUPPORTED
+
+
 def test_timed_variants_check_like_the_plain_calls(car, lib):
     """The _timed entry points run the same host checks (events unused)."""
     c = _cache(car, max_seq=512)
