@@ -19,6 +19,11 @@ which gives the roofline fractions.  The fp64 oracle, timed on the host
 cores on a bounded sample of the same workloads, is reported as a baseline.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--only NAME] [--no-cpu-baseline]
+                    [--stat-iters N]
+
+Every stage and extra is also timed over N (default 100) further iterations
+for its median, p10 and p90; the decode kernels once more after 512 MiB of
+writes before each iteration (cold Infinity Cache).
 """
 
 from __future__ import annotations
@@ -28,6 +33,12 @@ import json
 import os
 import sys
 import time
+
+# The oracle's BLAS threads: every host core this process may run on, unless
+# the environment already fixes the count (set before numpy is imported).
+HOST_THREADS = len(os.sched_getaffinity(0))
+for _var in ("OMP_NUM_THREADS", "OPENBLAS_NUM_THREADS", "MKL_NUM_THREADS"):
+    os.environ.setdefault(_var, str(HOST_THREADS))
 
 METRIC = "prefill TFLOP/s (% MFMA peak); decode KV GB/s (% HBM peak) + tokens/s"
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
@@ -70,6 +81,10 @@ def parse_args(argv=None):
                    help="prefill heads in the oracle's timed sample")
     p.add_argument("--no-extras", action="store_true",
                    help="skip the chunked-prefill measurements outside the timed step")
+    p.add_argument("--stat-iters", type=int, default=100,
+                   help="timed iterations per stage for the median / p10 / p90 figures")
+    p.add_argument("--cpu-heads-1t", type=int, default=2,
+                   help="prefill heads in the oracle's single-thread sample")
     p.add_argument("--copy-calibration", action="store_true",
                    help="first run one plain 1 GiB device copy (HBM counter calibration)")
     return p.parse_args(argv)
@@ -79,6 +94,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 KERNEL_SOURCES = ["rope_cache.hip", "decode.hip", "decode_i8.hip", "prefill.hip", "common.hpp",
                   "decode_common.hpp", "launch.hpp"]
 COPY_BYTES = 1 << 30
+FLUSH_BYTES = 512 << 20
 
 
 def kernel_source_sha() -> str:
@@ -105,8 +121,27 @@ def measured_traffic():
     return t.get("kernels", {})
 
 
-def cpu_baseline(pf, c4, heads: int):
-    """Time the fp64 oracle on the host on a bounded sample of the workloads."""
+def blas_info() -> dict:
+    """numpy's BLAS build and the thread pools threadpoolctl sees."""
+    import numpy as np
+    import threadpoolctl
+    info = {"numpy": np.__version__}
+    try:
+        cfg = np.show_config(mode="dicts")
+        blas = cfg.get("Build Dependencies", {}).get("blas", {})
+        info["blas"] = {k: blas.get(k) for k in ("name", "version", "openblas configuration")
+                        if blas.get(k) is not None}
+    except Exception as e:  # older numpy: no dict mode
+        info["blas"] = f"unavailable ({e.__class__.__name__})"
+    info["pools"] = [{k: d.get(k) for k in ("internal_api", "version", "num_threads",
+                                            "threading_layer")}
+                     for d in threadpoolctl.threadpool_info()]
+    return info
+
+
+def cpu_baseline(pf, c4, heads: int, heads_1t: int):
+    """Time the fp64 oracle on the host on a bounded sample of the workloads,
+    with every BLAS thread and again with one thread."""
     import numpy as np
     import threadpoolctl
     import oracle
@@ -121,6 +156,11 @@ def cpu_baseline(pf, c4, heads: int):
     oracle.attn_prefill(q, k, v, pos, pf.theta, pf.scale)
     t_pf = time.perf_counter() - t0
     flops = prefill_flops(1, heads, S, D)
+    with threadpoolctl.threadpool_limits(1):
+        t0 = time.perf_counter()
+        oracle.attn_prefill(q[:, :heads_1t], k[:, :heads_1t], v[:, :heads_1t], pos, pf.theta,
+                            pf.scale)
+        t_1t = time.perf_counter() - t0
     # decode sample: the first 8 sequences of the contiguous workload
     bsel = list(range(8))
     lens = np.array([c4.lens_host[b] for b in bsel])
@@ -141,11 +181,29 @@ def cpu_baseline(pf, c4, heads: int):
         "kind": "oracle",
         "sample": (f"fp64 oracle prefill of {heads} of the 32 heads of the S=4096 prompt "
                    f"({t_pf:.1f} s); decode of 8 of the 32 contiguous-cache sequences "
-                   f"({t_dec:.2f} s)"),
+                   f"({t_dec:.2f} s); single-thread prefill of {heads_1t} heads "
+                   f"({t_1t:.1f} s)"),
         "decode_GBps": dbytes / t_dec / 1e9,
         "decode_tokens_per_s": len(bsel) / t_dec,
-        "host_cores_visible": len(os.sched_getaffinity(0)),
+        "single_thread_TFLOPs": prefill_flops(1, heads_1t, S, D) / t_1t / 1e12,
+        "host_cores_visible": HOST_THREADS,
+        "blas": blas_info(),
     }
+
+
+def pct(xs, q: float) -> float:
+    """q-quantile (0..1) of xs by linear interpolation."""
+    xs = sorted(xs)
+    if not xs:
+        return float("nan")
+    f = q * (len(xs) - 1)
+    i = int(f)
+    j = min(i + 1, len(xs) - 1)
+    return xs[i] + (xs[j] - xs[i]) * (f - i)
+
+
+def spread(ms) -> dict:
+    return {"median": pct(ms, 0.5), "p10": pct(ms, 0.1), "p90": pct(ms, 0.9), "n": len(ms)}
 
 
 def timed_calls(car, call, stream, new_event, iters: int):
@@ -166,7 +224,7 @@ def timed_calls(car, call, stream, new_event, iters: int):
     return pairs_k, pairs_c
 
 
-def measure_chunked(car, W, dev, stream, new_event, iters: int = 10) -> dict:
+def measure_chunked(car, W, dev, stream, new_event, iters: int = 100) -> dict:
     """A 1024-token chunk continuing a 3072-token cached prefix, 32 query
     heads, D = 128, bf16: contiguous cache [1, 32, 4096, 128], and a paged
     cache with 8 KV heads behind a random block table.  Event times of the
@@ -195,6 +253,8 @@ def measure_chunked(car, W, dev, stream, new_event, iters: int = 10) -> dict:
             "workload": f"B=1,Hq=32,Hkv={hkv},D=128,cached={P},chunk={S},bf16,"
                         + ("paged 16-token blocks" if paged else "contiguous cache 4096"),
             "kernel_ms": kms, "call_ms": cms,
+            "kernel_spread_ms": spread([a.elapsed_time(b) for a, b in pairs_k]),
+            "call_spread_ms": spread([a.elapsed_time(b) for a, b in pairs_c]),
             "TFLOPs_kernel": fl / (kms * 1e-3) / 1e12, "TFLOPs_call": fl / (cms * 1e-3) / 1e12,
             "mfma_frac_kernel": fl / (kms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
             "per_launch": f"{fl} flops (4*B*H*D*(S*P + S(S+1)/2))"}
@@ -202,7 +262,7 @@ def measure_chunked(car, W, dev, stream, new_event, iters: int = 10) -> dict:
     return out
 
 
-def measure_int8_decode(car, W, dev, stream, new_event, iters: int = 20) -> dict:
+def measure_int8_decode(car, W, dev, stream, new_event, iters: int = 100) -> dict:
     """The two decode workloads with INT8 caches of the same shapes (codes in
     [-127, 127], per-(KV head, channel) fp32 scales): event times of the
     decode split kernel and of the whole call, and KV GB/s at one byte per
@@ -241,6 +301,8 @@ def measure_int8_decode(car, W, dev, stream, new_event, iters: int = 20) -> dict
                          + ("paged 16-token blocks" if sp["paged"] else "contiguous 4096")
                          + ", int8 cache with per-(head, channel) scales"),
             "kernel_ms": kms, "call_ms": cms,
+            "kernel_spread_ms": spread([a.elapsed_time(b) for a, b in pairs_k]),
+            "call_spread_ms": spread([a.elapsed_time(b) for a, b in pairs_c]),
             "GBps_kernel": kv / (kms * 1e-3) / 1e9, "GBps_call": kv / (cms * 1e-3) / 1e9,
             "hbm_frac_kernel": kv / (kms * 1e-3) / 1e9 / PEAK_HBM_GBPS,
             "tokens_per_s": case.B / (cms * 1e-3),
@@ -250,7 +312,7 @@ def measure_int8_decode(car, W, dev, stream, new_event, iters: int = 20) -> dict
     return out
 
 
-def measure_small_prefills(car, W, dev, stream, new_event, iters: int = 20) -> dict:
+def measure_small_prefills(car, W, dev, stream, new_event, iters: int = 100) -> dict:
     """The two small workloads.  GPT-2-shaped prefill (B=4, H=12, D=64,
     S=512, bf16, no cache): TFLOP/s against the bf16 peak and, since at 128
     flop per byte it sits below the ridge, its bytes (q, k, v read, out
@@ -275,13 +337,14 @@ def measure_small_prefills(car, W, dev, stream, new_event, iters: int = 20) -> d
     pairs_k, pairs_c = timed_calls(car, call2, stream, new_event, iters)
     if not torch.isfinite(o2.float()).all():
         raise RuntimeError("non-finite output in the GPT-2-shaped prefill")
-    kms = sorted(a.elapsed_time(b) for a, b in pairs_k)[iters // 2]
-    cms = sorted(a.elapsed_time(b) for a, b in pairs_c)[iters // 2]
+    ksp = spread([a.elapsed_time(b) for a, b in pairs_k])
+    csp = spread([a.elapsed_time(b) for a, b in pairs_c])
+    kms, cms = ksp["median"], csp["median"]
     fl = prefill_flops(c2.B, c2.Hq, c2.S, c2.D)
     io = 4 * c2.B * c2.Hq * c2.S * c2.D * 2
     out["gpt2_prefill"] = {
         "workload": "B=4,H=12,D=64,S=512,bf16, no cache",
-        "kernel_ms": kms, "call_ms": cms,
+        "kernel_ms": kms, "call_ms": cms, "kernel_spread_ms": ksp, "call_spread_ms": csp,
         "TFLOPs_kernel": fl / (kms * 1e-3) / 1e12, "TFLOPs_call": fl / (cms * 1e-3) / 1e12,
         "mfma_frac_kernel": fl / (kms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
         "hbm_frac_kernel": io / (kms * 1e-3) / 1e9 / PEAK_HBM_GBPS,
@@ -318,16 +381,58 @@ def measure_small_prefills(car, W, dev, stream, new_event, iters: int = 20) -> d
     torch.cuda.synchronize()
     if not (torch.isfinite(o1).all() and torch.isfinite(od).all()):
         raise RuntimeError("non-finite output in the fp32 tiny workload")
-    pms = sorted(a.elapsed_time(b) for a, b, _ in evs)[iters // 2]
-    dms = sorted(b.elapsed_time(c) for _, b, c in evs)[iters // 2]
+    psp = spread([a.elapsed_time(b) for a, b, _ in evs])
+    dsp = spread([b.elapsed_time(c) for _, b, c in evs])
+    pms, dms = psp["median"], dsp["median"]
     fl1 = prefill_flops(1, 4, 128, 64)
     out["tiny_prefill_decode_fp32"] = {
         "workload": "B=1,H=4,D=64,fp32: prefill S=128 into a 144-slot cache, then 16 decode "
                     "steps at positions 128..143",
         "total_ms": pms + dms, "prefill_call_ms": pms, "decode_16_steps_ms": dms,
+        "prefill_call_spread_ms": psp, "decode_16_steps_spread_ms": dsp,
         "prefill_TFLOPs_call": fl1 / (pms * 1e-3) / 1e12,
         "decode_tokens_per_s": 16 / (dms * 1e-3),
         "per_launch": f"prefill {fl1} flops (2*B*H*D*S*(S+1)); each step reads L*4*64*2*4 B"}
+    return out
+
+
+def measure_rope_append(car, pf, dev, stream, new_event, iters: int) -> dict:
+    """The standalone rope_apply (in place on the prompt's keys) and
+    kv_cache_append (rotated keys and values into a cache of the prompt's
+    shape) at the Qwen-shaped prompt (B=1, H=32, S=4096, D=128, bf16): event
+    times of each call (one kernel each) and GB/s of the bytes each must move
+    against the HBM peak."""
+    import torch
+    x = pf.k.clone()
+    ck = torch.empty_like(pf.k)
+    cv = torch.empty_like(pf.v)
+    cache = car.KVCache(ck, cv)
+    elems = x.numel()
+    pos_bytes = pf.positions.numel() * 4
+    specs = (
+        ("rope_apply", lambda: car.rope_apply(x, pf.positions, pf.theta),
+         2 * elems * 2 + pos_bytes, "K read and written in place"),
+        ("kv_cache_append", lambda: car.kv_cache_append(cache, x, pf.v, pf.positions),
+         4 * elems * 2 + pos_bytes, "K and V read, K and V rows written"))
+    out = {}
+    for name, fn, nbytes, what in specs:
+        for _ in range(3):
+            fn()
+        pairs = [(new_event(), new_event()) for _ in range(iters)]
+        for a, b in pairs:
+            a.record(stream)
+            fn()
+            b.record(stream)
+        torch.cuda.synchronize()
+        sp = spread([a.elapsed_time(b) for a, b in pairs])
+        gbps = nbytes / (sp["median"] * 1e-3) / 1e9
+        out[f"{name}_qwen"] = {
+            "workload": "B=1,H=32,S=4096,D=128,bf16" + (", contiguous cache 4096"
+                                                        if name != "rope_apply" else ""),
+            "call_spread_ms": sp, "GBps_median": gbps, "hbm_frac_median": gbps / PEAK_HBM_GBPS,
+            "per_launch": f"{nbytes} bytes ({what}, plus int32 positions)"}
+    if not torch.isfinite(x.float()).all():
+        raise RuntimeError("non-finite keys after rope_apply")
     return out
 
 
@@ -375,13 +480,7 @@ def main(argv=None) -> int:
     ev = {s: {"call": [(new_event(), new_event()) for _ in range(n_ev)],
               "kernel": [(new_event(), new_event()) for _ in range(n_ev)]} for s in stages}
 
-    def run_stage(s, i=None, kernel_events=False):
-        # call events bracket the whole entry point; with kernel_events the
-        # library brackets its main kernel instead (separate iterations, so
-        # that the inner events add nothing to the call times)
-        timing = ev[s]["kernel"][i] if (i is not None and kernel_events) else None
-        if i is not None and not kernel_events:
-            ev[s]["call"][i][0].record(stream)
+    def stage_call(s, timing=None):
         if s == "prefill":
             car.attn_prefill(pf.q, pf.k, pf.v, pf.positions, pf.theta, pf.scale,
                              cache=pf_cache, out=pf_out, workspace=pf_ws, timing=timing)
@@ -391,6 +490,15 @@ def main(argv=None) -> int:
         else:
             car.attn_decode(c5.q, c5.k_new, c5.v_new, c5.seq_lens, c5_cache, c5.max_seq_len,
                             c5.theta, c5.scale, out=c5_out, workspace=c5_ws, timing=timing)
+
+    def run_stage(s, i=None, kernel_events=False):
+        # call events bracket the whole entry point; with kernel_events the
+        # library brackets its main kernel instead (separate iterations, so
+        # that the inner events add nothing to the call times)
+        timing = ev[s]["kernel"][i] if (i is not None and kernel_events) else None
+        if i is not None and not kernel_events:
+            ev[s]["call"][i][0].record(stream)
+        stage_call(s, timing)
         if i is not None and not kernel_events:
             ev[s]["call"][i][1].record(stream)
 
@@ -426,6 +534,32 @@ def main(argv=None) -> int:
     for s in stages:
         res[s] = {"call_ms": avg_ms(ev[s]["call"]), "kernel_ms": avg_ms(ev[s]["kernel"])}
 
+    # ---------------- spreads: median / p10 / p90 over stat_iters iterations ----------------
+    # call times back to back; kernel times alone; for the decode steps also
+    # the kernel after 512 MiB of writes (more than the 256 MiB Infinity
+    # Cache), outside the timed region, so that no KV byte is served from it
+    flush = torch.empty(FLUSH_BYTES, dtype=torch.uint8, device=dev)
+    n_stat = max(args.stat_iters, 1)
+    for s in stages:
+        calls = [(new_event(), new_event()) for _ in range(n_stat)]
+        kerns = [(new_event(), new_event()) for _ in range(n_stat)]
+        cold = [(new_event(), new_event()) for _ in range(n_stat)] if s != "prefill" else []
+        for a, b in calls:
+            a.record(stream)
+            stage_call(s)
+            b.record(stream)
+        for pair in kerns:
+            stage_call(s, pair)
+        for i, pair in enumerate(cold):
+            flush.fill_(i & 0xFF)
+            stage_call(s, pair)
+        torch.cuda.synchronize()
+        res[s]["call_spread_ms"] = spread([a.elapsed_time(b) for a, b in calls])
+        res[s]["kernel_spread_ms"] = spread([a.elapsed_time(b) for a, b in kerns])
+        if cold:
+            res[s]["kernel_cold_spread_ms"] = spread([a.elapsed_time(b) for a, b in cold])
+    del flush
+
     outs = {"prefill": pf_out, "contiguous": c4_out, "paged": c5_out}
     for s in stages:
         if not torch.isfinite(outs[s].float()).all():
@@ -435,9 +569,10 @@ def main(argv=None) -> int:
     # ---------------- chunked prefill (outside the timed step) ----------------
     extras = {}
     if args.only is None and not args.no_extras:
-        extras = measure_chunked(car, W, dev, stream, new_event)
-        extras.update(measure_int8_decode(car, W, dev, stream, new_event))
-        extras.update(measure_small_prefills(car, W, dev, stream, new_event))
+        extras = measure_chunked(car, W, dev, stream, new_event, n_stat)
+        extras.update(measure_int8_decode(car, W, dev, stream, new_event, n_stat))
+        extras.update(measure_small_prefills(car, W, dev, stream, new_event, n_stat))
+        extras.update(measure_rope_append(car, pf, dev, stream, new_event, n_stat))
 
     # ---------------- figures ----------------
     kernels = {}
@@ -447,6 +582,8 @@ def main(argv=None) -> int:
         r = res["prefill"]
         r["TFLOPs_call"] = pf_flops / (r["call_ms"] * 1e-3) / 1e12
         r["TFLOPs_kernel"] = pf_flops / (r["kernel_ms"] * 1e-3) / 1e12
+        r["TFLOPs_kernel_median"] = pf_flops / (r["kernel_spread_ms"]["median"] * 1e-3) / 1e12
+        r["TFLOPs_call_median"] = pf_flops / (r["call_spread_ms"]["median"] * 1e-3) / 1e12
         kernels["prefill_attention"] = {
             "bound": "mfma", "achieved": r["TFLOPs_kernel"], "peak": PEAK_BF16_TFLOPS,
             "unit": "TFLOP/s", "frac": r["TFLOPs_kernel"] / PEAK_BF16_TFLOPS,
@@ -463,6 +600,10 @@ def main(argv=None) -> int:
         r["hbm_frac_call"] = r["GBps_call"] / PEAK_HBM_GBPS
         r["kv_bytes"] = kv
         r["io_bytes"] = decode_io_bytes(c.B, c.Hq, c.Hkv, c.D, 2)
+        r["GBps_kernel_median"] = kv / (r["kernel_spread_ms"]["median"] * 1e-3) / 1e9
+        if "kernel_cold_spread_ms" in r:
+            r["GBps_kernel_cold_median"] = (kv / (r["kernel_cold_spread_ms"]["median"] * 1e-3)
+                                            / 1e9)
         kernels[f"decode_{s}_split"] = {
             "bound": "hbm", "achieved": r["GBps_kernel"], "peak": PEAK_HBM_GBPS,
             "unit": "GB/s", "frac": r["GBps_kernel"] / PEAK_HBM_GBPS, "traffic": None,
@@ -520,7 +661,7 @@ def main(argv=None) -> int:
     if extras:
         line["extras"] = extras
     if not args.no_cpu_baseline and args.only is None:
-        line["cpu_baseline"] = cpu_baseline(pf, c4, args.cpu_heads)
+        line["cpu_baseline"] = cpu_baseline(pf, c4, args.cpu_heads, args.cpu_heads_1t)
     else:
         line["cpu_baseline"] = None
     print(json.dumps(line), flush=True)

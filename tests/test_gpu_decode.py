@@ -2,7 +2,8 @@
 index L, attention over indices 0..L) for contiguous and paged caches, GQA
 groups, lengths around the 256- and 1024-token split boundaries, L = 0, NaN canaries in
 every slot that must not be read; workload 1's 16 decode steps after its
-prefill; workloads 4 and 5 at full size on sampled sequences."""
+prefill; workloads 4 and 5 at full size on every sequence, and workload 4's
+shape with a sequence at the cache's last slot."""
 
 import numpy as np
 import pytest
@@ -154,23 +155,60 @@ def test_tiny_workload_prefill_then_16_decode_steps(car):
     assert worst <= 1e-4
 
 
+def check_every_sequence(car, case):
+    """One GPU decode step over the whole case, then the oracle sequence by
+    sequence (bounded host memory).  The inputs of sequence b are gathered
+    after the step, so its slot L holds the GPU's appended row; the oracle
+    writes its own row there before attending, and the GPU's row is compared
+    with it."""
+    cache = car.KVCache(case.cache_k, case.cache_v, case.block_table)
+    out = car.attn_decode(case.q, case.k_new, case.v_new, case.seq_lens, cache,
+                          case.max_seq_len, theta=case.theta, scale=case.scale)
+    torch.cuda.synchronize()
+    assert torch.isfinite(out.float()).all()
+    worst = 0.0
+    for b in range(case.B):
+        q, kn, vn, ck, cv, lens, table = decode_inputs_for(case, [b])
+        want = oracle.attn_decode(q, kn, vn, ck, cv, lens, case.theta, case.scale,
+                                  block_table=table)
+        worst = max(worst, max_abs(f64(out[b:b + 1]), want))
+        L = int(lens[0])
+        if case.paged:
+            blk = int(case.block_table[b, L // 16])
+            gk, gv = case.cache_k[blk, :, L % 16], case.cache_v[blk, :, L % 16]
+            wk = ck[table[0, L // 16], :, L % 16]
+        else:
+            gk, gv = case.cache_k[b, :, L], case.cache_v[b, :, L]
+            wk = ck[0, :, L]
+        worst = max(worst, max_abs(f64(gk), wk))
+        assert torch.equal(bits(gv.cpu()), bits(case.v_new[b].cpu())), f"appended V, b={b}"
+    tol = TOL[case.dtype]
+    log_case(f"{case.name}: every sequence, max-abs error {worst:.3e} (tol {tol})")
+    assert worst <= tol
+
+
 def test_contiguous_decode_workload(car):
     """Workload 4 at full size (B=32, H=32, D=128, cache [32,32,4096,128]) in
-    the launch configuration the benchmark times; the oracle checks 6
-    sequences, including the shortest and the longest."""
-    case = W.contiguous_decode(DEV)
-    lens = case.lens_host
-    bsel = sorted({int(np.argmin(lens)), int(np.argmax(lens)), 0, 7, 19, 31})
-    run_and_check(car, case, bsel)
+    the launch configuration the benchmark times; every sequence against the
+    oracle."""
+    check_every_sequence(car, W.contiguous_decode(DEV))
+
+
+def test_contiguous_decode_last_slot(car):
+    """Workload 4's shape with sequence 5 at L = 4095: the new token goes to
+    the cache's last slot and the query attends over all 4096 slots."""
+    lens = list(W.contiguous_decode_lens())
+    lens[5] = 4095
+    case = W.decode_case("contiguous_last_slot", 32, 32, 32, 128, torch.bfloat16, lens,
+                         W.BASE_SEED + 40, DEV, paged=False, max_seq=4096)
+    assert case.max_seq_len == 4096
+    run_and_check(car, case, [0, 5, 31])
 
 
 def test_paged_decode_workload(car):
     """Workload 5 at full size (B=64, Hq=32, Hkv=8, 16-token blocks, lengths
-    in [512, 8192]); the oracle checks 6 sequences."""
-    case = W.paged_decode(DEV)
-    lens = case.lens_host
-    bsel = sorted({int(np.argmin(lens)), int(np.argmax(lens)), 1, 22, 40, 63})
-    run_and_check(car, case, bsel)
+    in [512, 8192]); every sequence against the oracle."""
+    check_every_sequence(car, W.paged_decode(DEV))
 
 
 def test_paged_decode_workload_poisoned(car):

@@ -1,7 +1,7 @@
 """GPU parity: attn_prefill against the oracle's full-matrix masked attention
 with explicit RoPE rotations, element by element, at sizes spanning several
 tiles with ragged tails, plus the cache it writes; the two full-size prefill
-workloads on sampled heads."""
+workloads on every head."""
 
 import numpy as np
 import pytest
@@ -206,7 +206,9 @@ def test_gpt2_workload_prefill(car):
     check_prefill(car, W.gpt2_prefill(DEV))
 
 
-def test_qwen_workload_prefill_sampled_heads(car):
+def test_qwen_workload_prefill_every_head(car):
     """Workload 3 at full size (B=1, H=32, D=128, S=4096, cache 4096), in the
-    launch configuration the benchmark times; the oracle checks 3 heads."""
-    check_prefill(car, W.qwen_prefill(DEV), cap=4096, heads=[0, 17, 31])
+    launch configuration the benchmark times: every head against the oracle
+    (one head at a time), every cached row checked, and no other row of the
+    NaN-filled cache written."""
+    check_prefill(car, W.qwen_prefill(DEV), cap=4096)
