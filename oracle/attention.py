@@ -34,6 +34,10 @@ Pins (tests under ``tests/test_oracle_*.py``, none reuses this code):
   equals MHA with each KV head repeated.  With ``chunk_lens``: a padded
   batch equals each sequence run alone at its own length, whatever the
   padding holds; padding rows are zero and padding tokens are not stored.
+* ``attn_prefill(seq_lens=...)``: a padded batch of prompts equals each
+  prompt run alone at its own length, whatever the padding (even NaN)
+  holds; padding rows of the output and of k_rot are zero; a length-1
+  prompt gives O = v of its token.
 
 * ``rope_rotate(pairing="half")``: identity at 0, norm preservation and
   relative position as above; a hand value for D = 4 (pair (x1, x3) at
@@ -152,7 +156,7 @@ def causal_attention(q, k, v, positions, scale: float) -> np.ndarray:
 
 
 def attn_prefill(q, k, v, positions, theta: float = 10000.0,
-                 scale: float | None = None, pairing: str = "adjacent"):
+                 scale: float | None = None, pairing: str = "adjacent", seq_lens=None):
     """Prefill over a whole prompt: RoPE on Q and K, then causal attention.
 
     q [B, Hq, S, D], k/v [B, Hkv, S, D], positions [B, S].  Query head hq
@@ -160,6 +164,12 @@ def attn_prefill(q, k, v, positions, theta: float = 10000.0,
     pages only name GQA).  The scale defaults to 1/sqrt(D), applied to the
     scores before the softmax ([Intuition] §4: 1/sqrt(d_k) with d_k the head
     dimension; [Scratch] §3.1).
+
+    With ``seq_lens`` (a batch of prompts of different lengths padded to S;
+    [Scratch] §3.3 names the padding mask) prompt b has only its first
+    seq_lens[b] rows: padding keys are masked for every query besides the
+    causal mask, padding rows of the output are zero, and padding rows of
+    k_rot are zero (they are never stored).
 
     Returns (out [B, Hq, S, D], k_rot [B, Hkv, S, D]); V is not rotated.
     """
@@ -172,15 +182,19 @@ def attn_prefill(q, k, v, positions, theta: float = 10000.0,
     group = Hq // Hkv
     if scale is None:
         scale = 1.0 / np.sqrt(D)
-    pos_b = positions[:, None, :]
-    q_rot = rope_rotate(q, pos_b, theta, pairing)
-    k_rot = rope_rotate(k, pos_b, theta, pairing)
-    out = np.empty_like(q_rot)
+    out = np.zeros_like(q)
+    k_rot = np.zeros_like(k)
     for b in range(B):
+        n = S if seq_lens is None else min(max(int(seq_lens[b]), 0), S)
+        if n == 0:
+            continue
+        pos = positions[b, :n]
+        q_rot = rope_rotate(q[b, :, :n], pos[None, :], theta, pairing)
+        k_rot[b, :, :n] = rope_rotate(k[b, :, :n], pos[None, :], theta, pairing)
         for hq in range(Hq):
             hk = hq // group
-            out[b, hq] = causal_attention(q_rot[b, hq], k_rot[b, hk], v[b, hk],
-                                          (positions[b], positions[b]), scale)
+            out[b, hq, :n] = causal_attention(q_rot[hq], k_rot[b, hk, :n], v[b, hk, :n],
+                                              (pos, pos), scale)
     return out, k_rot
 
 

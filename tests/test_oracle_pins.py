@@ -789,3 +789,59 @@ def test_kv_bytes_formula_printed_on_pages():
     assert abs(one - val) <= tol
     val, tol = g["kv_bytes_ten_requests"]
     assert abs(10 * one - val) <= tol
+
+
+def test_padded_prompt_batch_equals_each_prompt_alone():
+    """A batch of prompts of lengths n_b padded to S equals each prompt run
+    alone at its own length; the padding (NaN in q, k, v and a negative
+    position here) changes nothing; padding rows of the output and of k_rot
+    are zero.  GQA with two query heads per KV head."""
+    r = rng(39)
+    B, Hq, Hkv, D, S = 4, 4, 2, 8, 9
+    n = np.array([9, 0, 4, 1])
+    q = r.standard_normal((B, Hq, S, D))
+    k, v = r.standard_normal((B, Hkv, S, D)), r.standard_normal((B, Hkv, S, D))
+    pos = np.tile(np.arange(S) * 3 + 2, (B, 1))
+    for b in range(B):
+        q[b, :, n[b]:] = np.nan
+        k[b, :, n[b]:] = np.nan
+        v[b, :, n[b]:] = np.nan
+        pos[b, n[b]:] = -5
+    got, got_k = A.attn_prefill(q, k, v, pos, seq_lens=n)
+    assert np.all(np.isfinite(got)) and np.all(np.isfinite(got_k))
+    for b in range(B):
+        sl = slice(b, b + 1)
+        if n[b]:
+            alone, alone_k = A.attn_prefill(q[sl, :, :n[b]], k[sl, :, :n[b]], v[sl, :, :n[b]],
+                                            pos[sl, :n[b]])
+            assert np.allclose(got[b, :, :n[b]], alone[0], atol=1e-13)
+            assert np.allclose(got_k[b, :, :n[b]], alone_k[0], atol=1e-13)
+        assert np.array_equal(got[b, :, n[b]:], np.zeros_like(got[b, :, n[b]:]))
+        assert np.array_equal(got_k[b, :, n[b]:], np.zeros_like(got_k[b, :, n[b]:]))
+
+
+def test_one_token_prompt_gives_its_value():
+    """A prompt of one token (padded to 5 rows) sees only itself: O = v."""
+    r = rng(40)
+    q, k, v = (r.standard_normal((1, 2, 5, 8)) for _ in range(3))
+    out, _ = A.attn_prefill(q, k, v, np.arange(5)[None], seq_lens=np.array([1]))
+    assert np.allclose(out[0, :, 0], v[0, :, 0], atol=1e-15)
+    assert not np.any(out[0, :, 1:])
+
+
+def test_padded_prompt_pin_catches_plausible_mistakes():
+    """Planted mistakes the pins above rule out: ignoring the lengths (the
+    padding rows come out nonzero), and a length short by one (the last
+    prompt token's row is zero instead of its attention output)."""
+    r = rng(41)
+    B, H, D, S = 2, 2, 8, 6
+    n = np.array([6, 3])
+    q, k, v = (r.standard_normal((B, H, S, D)) for _ in range(3))
+    pos = np.tile(np.arange(S), (B, 1))
+    good, _ = A.attn_prefill(q, k, v, pos, seq_lens=n)
+    ignored, _ = A.attn_prefill(q, k, v, pos)
+    short, _ = A.attn_prefill(q, k, v, pos, seq_lens=n - 1)
+    assert np.any(ignored[1, :, 3:] != 0) and not np.any(good[1, :, 3:])
+    alone, _ = A.attn_prefill(q[1:, :, :3], k[1:, :, :3], v[1:, :, :3], pos[1:, :3])
+    assert np.allclose(good[1, :, :3], alone[0], atol=1e-13)
+    assert not np.allclose(short[1, :, :3], alone[0], atol=1e-6)
