@@ -396,6 +396,44 @@ def measure_small_prefills(car, W, dev, stream, new_event, iters: int = 100) -> 
     return out
 
 
+def measure_varlen_prefill(car, W, dev, stream, new_event, iters: int = 100) -> dict:
+    """A padded batch of whole prompts (B=8, H=32, D=128, bf16, lengths
+    U{128..2048} padded to S=2048, positions from 0, a contiguous cache
+    [8, 32, 2048, 128]): event times of the attention kernel and of the whole
+    call (K pass with the cache store, then attention), TFLOP/s of the
+    prompts' own causal work against the bf16 peak."""
+    import torch
+    case, lens = W.varlen_prefill(dev)
+    seq_lens = torch.tensor(lens, dtype=torch.int32, device=dev)
+    cache = car.KVCache(torch.zeros((8, 32, 2048, 128), dtype=torch.bfloat16, device=dev),
+                        torch.zeros((8, 32, 2048, 128), dtype=torch.bfloat16, device=dev))
+    o = torch.empty_like(case.q)
+    ws = torch.empty(car.prefill_workspace_bytes(torch.bfloat16, 8, 32, 2048, 128),
+                     dtype=torch.uint8, device=dev)
+
+    def call(timing=None):
+        car.attn_prefill(case.q, case.k, case.v, case.positions, case.theta, case.scale,
+                         cache=cache, out=o, workspace=ws, timing=timing, seq_lens=seq_lens)
+    for _ in range(3):
+        call()
+    pairs_k, pairs_c = timed_calls(car, call, stream, new_event, iters)
+    if not torch.isfinite(o.float()).all():
+        raise RuntimeError("non-finite output in the padded prompt batch")
+    ksp = spread([a.elapsed_time(b) for a, b in pairs_k])
+    csp = spread([a.elapsed_time(b) for a, b in pairs_c])
+    fl = sum(prefill_flops(1, 32, n, 128) for n in lens)
+    return {"varlen_prefill": {
+        "workload": f"B=8,H=32,D=128,bf16, prompts of {lens} tokens padded to 2048, "
+                    "contiguous cache [8,32,2048,128]",
+        "kernel_ms": sum(a.elapsed_time(b) for a, b in pairs_k) / iters,
+        "call_ms": sum(a.elapsed_time(b) for a, b in pairs_c) / iters,
+        "kernel_spread_ms": ksp, "call_spread_ms": csp,
+        "TFLOPs_kernel_median": fl / (ksp["median"] * 1e-3) / 1e12,
+        "TFLOPs_call_median": fl / (csp["median"] * 1e-3) / 1e12,
+        "mfma_frac_kernel_median": fl / (ksp["median"] * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
+        "per_launch": f"{fl} flops (sum_b 2*H*D*n_b*(n_b+1) over the prompts' own tokens)"}}
+
+
 def measure_rope_append(car, pf, dev, stream, new_event, iters: int) -> dict:
     """The standalone rope_apply (in place on the prompt's keys) and
     kv_cache_append (rotated keys and values into a cache of the prompt's
@@ -572,6 +610,7 @@ def main(argv=None) -> int:
         extras = measure_chunked(car, W, dev, stream, new_event, n_stat)
         extras.update(measure_int8_decode(car, W, dev, stream, new_event, n_stat))
         extras.update(measure_small_prefills(car, W, dev, stream, new_event, n_stat))
+        extras.update(measure_varlen_prefill(car, W, dev, stream, new_event, n_stat))
         extras.update(measure_rope_append(car, pf, dev, stream, new_event, n_stat))
 
     # ---------------- figures ----------------

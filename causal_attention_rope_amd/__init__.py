@@ -85,8 +85,8 @@ def _load() -> ctypes.CDLL:
                           "`python causal_attention_rope_amd/build.py`") from e
     vp, i32, f32, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
     cache_p = ctypes.POINTER(_CarKVCache)
-    prefill = [vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, vp, f32, i32, f32, cache_p, vp, sz,
-               vp]
+    prefill = [vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, vp, vp, f32, i32, f32, cache_p, vp,
+               sz, vp]
     cached = [vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, vp, vp, i32, f32, i32, f32, cache_p,
               vp]
     decode = [vp, vp, vp, vp, i32, i32, i32, i32, i32, vp, i32, f32, i32, f32, cache_p, vp, sz,
@@ -340,12 +340,15 @@ def attn_prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, positions: t
                  theta: float = 10000.0, scale: Optional[float] = None,
                  cache: Optional[KVCache] = None, out: Optional[torch.Tensor] = None,
                  workspace: Optional[torch.Tensor] = None,
-                 rope_pairing: str = "adjacent", timing=None) -> torch.Tensor:
+                 rope_pairing: str = "adjacent", timing=None,
+                 seq_lens: Optional[torch.Tensor] = None) -> torch.Tensor:
     """Causal attention over a prompt with RoPE on q and k (see car_attn_prefill).
 
     q [B, Hq, S, D]; k, v [B, Hkv, S, D]; positions int32 [B, S], strictly
     increasing per sequence.  With ``cache`` the rotated keys and the values
-    are also stored at index == position.  Returns out [B, Hq, S, D].
+    are also stored at index == position.  ``seq_lens`` int32 [B] (optional):
+    prompt b is its first seq_lens[b] rows, the rest padding (zero output
+    rows, not stored).  Returns out [B, Hq, S, D].
     """
     _need(q, "q", dim=4)
     _need(k, "k", dtype=q.dtype, dim=4, device=q.device)
@@ -357,6 +360,10 @@ def attn_prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, positions: t
     _need(positions, "positions", dtype=torch.int32, dim=2, device=q.device)
     if tuple(positions.shape) != (B, S):
         raise ValueError("positions must be [B, S]")
+    if seq_lens is not None:
+        _need(seq_lens, "seq_lens", dtype=torch.int32, dim=1, device=q.device)
+        if seq_lens.shape[0] != B:
+            raise ValueError("seq_lens must be [B]")
     if out is None:
         out = torch.empty_like(q)
     _need(out, "out", dtype=q.dtype, dim=4, device=q.device)
@@ -376,7 +383,7 @@ def attn_prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, positions: t
     need = int(_lib.car_attn_prefill_workspace_bytes(dt, B, Hkv, S, D, None))
     ws = _workspace(need, q.device, workspace)
     args = [_ptr(q), _ptr(k), _ptr(v), _ptr(out), dt, B, Hq, Hkv, S, D, _ptr(positions),
-            float(theta), _pairing(rope_pairing), float(scale),
+            _ptr(seq_lens), float(theta), _pairing(rope_pairing), float(scale),
             ctypes.byref(c) if c is not None else None, _ptr(ws),
             ws.numel() * ws.element_size(), _stream(q)]
     ev = _events(timing)

@@ -155,7 +155,8 @@ size_t car_attn_prefill_workspace_bytes(car_dtype dtype, int B, int Hkv, int S, 
 
 car_status car_attn_prefill_timed(const void* q, const void* k, const void* v, void* out,
                                   car_dtype dtype, int B, int Hq, int Hkv, int S, int D,
-                                  const int32_t* positions, float theta,
+                                  const int32_t* positions, const int32_t* seq_lens,
+                                  float theta,
                                   car_rope_pairing pairing, float scale,
                                   const car_kv_cache* cache, void* workspace,
                                   size_t workspace_bytes, hipStream_t stream,
@@ -195,20 +196,21 @@ car_status car_attn_prefill_timed(const void* q, const void* k, const void* v, v
   const bool keys_in_cache = cache != nullptr && !paged && !is_int8(cache) && dt == BF16;
   hipError_t e = launch_prefill_prep(dt, D, paged, is_int8(cache),
                                      cache != nullptr ? &c : nullptr, k, v, workspace, B, Hkv,
-                                     S, positions, fr, keys_in_cache, stream);
+                                     S, positions, seq_lens, fr, keys_in_cache, stream);
   if (e != hipSuccess) return CAR_ERR_HIP;
   return from_hip(launch_prefill_attention(dt, D, q, workspace, v, out, B, Hq, Hkv, S,
-                                           positions, fr, scale, keys_in_cache ? &c : nullptr,
-                                           stream, timed(kernel_start, kernel_stop)));
+                                           positions, seq_lens, fr, scale,
+                                           keys_in_cache ? &c : nullptr, stream,
+                                           timed(kernel_start, kernel_stop)));
 }
 
 car_status car_attn_prefill(const void* q, const void* k, const void* v, void* out,
                             car_dtype dtype, int B, int Hq, int Hkv, int S, int D,
-                            const int32_t* positions, float theta, car_rope_pairing pairing,
-                            float scale, const car_kv_cache* cache, void* workspace,
-                            size_t workspace_bytes, hipStream_t stream) {
-  return car_attn_prefill_timed(q, k, v, out, dtype, B, Hq, Hkv, S, D, positions, theta,
-                                pairing, scale, cache, workspace, workspace_bytes, stream,
+                            const int32_t* positions, const int32_t* seq_lens, float theta,
+                            car_rope_pairing pairing, float scale, const car_kv_cache* cache,
+                            void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  return car_attn_prefill_timed(q, k, v, out, dtype, B, Hq, Hkv, S, D, positions, seq_lens,
+                                theta, pairing, scale, cache, workspace, workspace_bytes, stream,
                                 nullptr, nullptr);
 }
 

@@ -272,17 +272,18 @@ __device__ __forceinline__ int cache_last_slot(const CacheArgs& c) {
   return PAGED ? c.mbps * 16 - 1 : c.max_seq - 1;
 }
 
-// Whether prompt b's S positions are p0, p0+1, ..., p0+S-1 with every one a
-// slot of a contiguous cache of max_seq slots.  Positions strictly increase,
-// so the first and the last decide it.  Then the prompt's rotated keys, once
-// stored at their positions, are rows p0..p0+S-1 of each head in the cache,
-// and the attention reads them there.
+// Whether the n >= 1 tokens of prompt b (positions rows of S entries) sit at
+// positions p0, p0+1, ..., p0+n-1 with every one a slot of a contiguous cache
+// of max_seq slots.  Positions strictly increase over a prompt's tokens, so
+// the first and the last decide it.  Then the prompt's rotated keys, once
+// stored at their positions, are rows p0..p0+n-1 of each head in the cache,
+// and the attention reads them there.  An empty prompt (n = 0) gives false.
 __device__ __forceinline__ bool prompt_rows_in_cache(const int32_t* positions, int b, int S,
-                                                     int max_seq, int* p0) {
+                                                     int n, int max_seq, int* p0) {
   const int first = positions[(int64_t)b * S];
-  const int last = positions[(int64_t)b * S + S - 1];
+  const int last = positions[(int64_t)b * S + max(n, 1) - 1];
   *p0 = first;
-  return first >= 0 && last <= max_seq - 1 && last - first == S - 1;
+  return n >= 1 && first >= 0 && last <= max_seq - 1 && last - first == n - 1;
 }
 
 // ---------------------------------------------------------------------------

@@ -55,13 +55,15 @@ hipError_t launch_kv_append(Dtype dt, int D, bool paged, bool i8, const CacheArg
 
 // Rotates k into k_rot (dense [B,Hkv,S,D]) and, if cache != nullptr, also
 // stores the rotated keys and raw values into the cache (as int8 codes if i8).
+// lens (nullable): tokens of each prompt; rows from there on are padding,
+// neither rotated nor stored.
 // keys_in_cache (contiguous native cache only): sequences whose positions
 // are consecutive cache slots (prompt_rows_in_cache) skip k_rot, and the
 // attention must then be given the cache to read their keys from.
 hipError_t launch_prefill_prep(Dtype dt, int D, bool paged, bool i8, const CacheArgs* cache,
                                const void* k, const void* v, void* k_rot, int B, int Hkv,
-                               int S, const int32_t* positions, const RopeFreq& fr,
-                               bool keys_in_cache, hipStream_t s);
+                               int S, const int32_t* positions, const int32_t* lens,
+                               const RopeFreq& fr, bool keys_in_cache, hipStream_t s);
 
 // Per-(KV head, channel) absmax / 127 of the rotated keys and of the values
 // of a calibration batch, into k_scale / v_scale (fp32 [Hkv, D]).
@@ -78,12 +80,13 @@ hipError_t launch_chunk_prep(Dtype dt, int D, bool paged, const CacheArgs& c, co
 // ---- prefill.hip -----------------------------------------------------------
 // kcache (nullable; bf16 only): the contiguous cache that the K pass filled
 // with keys_in_cache; sequences whose positions are consecutive cache slots
-// read their rotated keys from it instead of k_rot.
+// read their rotated keys from it instead of k_rot.  lens (nullable): tokens
+// of each prompt; padding rows are written as zeros.
 hipError_t launch_prefill_attention(Dtype dt, int D, const void* q, const void* k_rot,
                                     const void* v, void* out, int B, int Hq, int Hkv, int S,
-                                    const int32_t* positions, const RopeFreq& fr, float scale,
-                                    const CacheArgs* kcache, hipStream_t s,
-                                    const TimedLaunch& tl);
+                                    const int32_t* positions, const int32_t* lens,
+                                    const RopeFreq& fr, float scale, const CacheArgs* kcache,
+                                    hipStream_t s, const TimedLaunch& tl);
 
 // Attention of a chunk over cache rows 0..P+S-1 (after launch_chunk_prep).
 // chunk_lens (nullable): tokens of each sequence's chunk; the rest is padding.

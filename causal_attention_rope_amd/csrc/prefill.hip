@@ -40,12 +40,12 @@ constexpr int KEYS_PROMPT = 0;  // the prompt's own K' and V, [B, Hkv, S, D]
 constexpr int KEYS_CONTIG = 1;  // a contiguous cache holding the prefix and the chunk
 constexpr int KEYS_PAGED = 2;   // a paged cache holding the prefix and the chunk
 
-// Tokens of sequence b's chunk: S for a prompt or a full chunk, else
-// chunk_lens[b] (a padded batch of chunks of different lengths).
+// Tokens of sequence b's prompt or chunk: S, or with per-sequence lengths
+// (a padded batch of prompts or chunks of different lengths) lens[b]; rows
+// from there on are padding.
 template <int SRC>
-__device__ __forceinline__ int chunk_len(const int32_t* chunk_lens, int b, int S) {
-  if constexpr (SRC == KEYS_PROMPT) return S;
-  else return chunk_lens == nullptr ? S : min(max(chunk_lens[b], 0), S);
+__device__ __forceinline__ int chunk_len(const int32_t* lens, int b, int S) {
+  return lens == nullptr ? S : min(max(lens[b], 0), S);
 }
 
 // Tokens cached before the chunk (0 for a prompt): seq_lens[b], kept small
@@ -154,7 +154,7 @@ __global__ __launch_bounds__(F32_ROWS) void prefill_f32_kernel(
     m = m_new;
   }
   if (i < S) {
-    const bool pad = SRC != KEYS_PROMPT && i >= Sb;  // padding rows: zeros
+    const bool pad = i >= Sb;  // padding rows: zeros
     const float inv = 1.f / l;
     float* orow = out + (((int64_t)b * Hq + hq) * S + i) * D;
 #pragma unroll
@@ -342,7 +342,7 @@ __global__ __launch_bounds__((Tile<D, 8>::THREADS), 2) void prefill_bf16_kernel(
     kbase = kr + ((int64_t)b * Hkv + hk) * S * D;
     vbase = v + ((int64_t)b * Hkv + hk) * S * D;
     int p0;  // keys the K pass left in the cache only (at consecutive slots p0..)
-    if (c.k != nullptr && prompt_rows_in_cache(positions, b, S, c.max_seq, &p0))
+    if (c.k != nullptr && prompt_rows_in_cache(positions, b, S, Sb, c.max_seq, &p0))
       kbase = static_cast<const bf16_t*>(c.k) + (((int64_t)b * Hkv + hk) * c.max_seq + p0) * D;
   }
 
@@ -447,7 +447,7 @@ __global__ __launch_bounds__((Tile<D, 8>::THREADS), 2) void prefill_bf16_kernel(
     const int q0 = qt * C::BM;
     const int qw = q0 + wq * 32;               // first query row of this wave
     const int qrow = qw + l32;                 // this lane's query row
-    if (SRC != KEYS_PROMPT && q0 >= Sb) {  // padding rows only (uniform): zeros
+    if (q0 >= Sb) {  // padding rows only (uniform): zeros
       if (grp == 0 && qrow < S) {
         bf16_t* op = out + ((int64_t)bh * S + qrow) * D;
   #pragma unroll
@@ -716,7 +716,7 @@ __global__ __launch_bounds__((Tile<D, 8>::THREADS), 2) void prefill_bf16_kernel(
     // ---- normalise and store: lane holds query qrow, dims db*32+8*(r/4)+4g+r%4 ----
     const float l_tot = l_run + swap_halves(l_run);
     if (qrow < S) {
-      const bool pad = SRC != KEYS_PROMPT && qrow >= Sb;  // padding rows: zeros
+      const bool pad = qrow >= Sb;  // padding rows: zeros
       const float inv = 1.f / l_tot;
       bf16_t* op = out + ((int64_t)bh * S + qrow) * D;
   #pragma unroll
@@ -821,12 +821,12 @@ hipError_t prefill_dispatch(Dtype dt, int D, const void* q, const KeySource& ks,
 
 hipError_t launch_prefill_attention(Dtype dt, int D, const void* q, const void* k_rot,
                                     const void* v, void* out, int B, int Hq, int Hkv, int S,
-                                    const int32_t* positions, const RopeFreq& fr, float scale,
-                                    const CacheArgs* kcache, hipStream_t s,
-                                    const TimedLaunch& tl) {
+                                    const int32_t* positions, const int32_t* lens,
+                                    const RopeFreq& fr, float scale, const CacheArgs* kcache,
+                                    hipStream_t s, const TimedLaunch& tl) {
   // the fp32 kernel always reads k_rot (its K pass never skips it)
   const KeySource ks{k_rot, v, kcache != nullptr && dt == BF16 ? *kcache : CacheArgs{}, nullptr,
-                     nullptr};
+                     lens};
   return prefill_dispatch<KEYS_PROMPT>(dt, D, q, ks, out, B, Hq, Hkv, S, positions, fr, scale, s,
                                        tl);
 }

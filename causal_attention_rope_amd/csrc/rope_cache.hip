@@ -104,7 +104,8 @@ __global__ __launch_bounds__(kThreads) void kv_append_kernel(CacheArgs c,
 template <typename T, int D, bool PAGED, bool CACHE, bool I8, bool KEYS_IN_CACHE = false>
 __global__ __launch_bounds__(kThreads) void prefill_prep_kernel(
     CacheArgs c, const T* __restrict__ k, const T* __restrict__ v, T* __restrict__ k_rot,
-    int Hkv, int S, const int32_t* __restrict__ positions, int64_t nvec, RopeFreq fr) {
+    int Hkv, int S, const int32_t* __restrict__ positions, const int32_t* __restrict__ lens,
+    int64_t nvec, RopeFreq fr) {
   constexpr int N = Vec16<T>::N;
   constexpr int VPR = D / N;
   for (int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x; i < nvec;
@@ -114,12 +115,14 @@ __global__ __launch_bounds__(kThreads) void prefill_prep_kernel(
     const int s = (int)(row % S);
     const int64_t bh = row / S;
     const int b = (int)(bh / Hkv);
+    const int n = lens == nullptr ? S : min(max(lens[b], 0), S);
+    if (s >= n) continue;  // padding: neither rotated nor stored
     const int pos = positions[(int64_t)b * S + s];
     float f[N];
     load16<T>(k + row * D + col, f);
     rope_rotate_chunk<T, N>(f, k + row * D, col, D, pos, fr);
     int p0;
-    if (!KEYS_IN_CACHE || !prompt_rows_in_cache(positions, b, S, c.max_seq, &p0))
+    if (!KEYS_IN_CACHE || !prompt_rows_in_cache(positions, b, S, n, c.max_seq, &p0))
       store16<T>(k_rot + row * D + col, f);
     if (CACHE && pos >= 0 && pos <= cache_last_slot<PAGED>(c)) {  // else not stored
       const int hk = (int)(bh % Hkv);
@@ -303,7 +306,8 @@ hipError_t kv_append_t(bool paged, const CacheArgs& c, const void* k, const void
 template <typename T, int D, bool I8>
 hipError_t prefill_prep_t(bool paged, const CacheArgs* cache, const void* k, const void* v,
                           void* k_rot, int B, int Hkv, int S, const int32_t* positions,
-                          const RopeFreq& fr, bool keys_in_cache, hipStream_t st) {
+                          const int32_t* lens, const RopeFreq& fr, bool keys_in_cache,
+                          hipStream_t st) {
   const int64_t nvec = (int64_t)B * Hkv * S * (D / Vec16<T>::N);
   const T* kk = static_cast<const T*>(k);
   const T* vv = static_cast<const T*>(v);
@@ -312,16 +316,16 @@ hipError_t prefill_prep_t(bool paged, const CacheArgs* cache, const void* k, con
   if (cache == nullptr) {
     CacheArgs none{};
     hipLaunchKernelGGL((prefill_prep_kernel<T, D, false, false, false>), grid, block, 0, st,
-                       none, kk, vv, kr, Hkv, S, positions, nvec, fr);
+                       none, kk, vv, kr, Hkv, S, positions, lens, nvec, fr);
   } else if (paged) {
     hipLaunchKernelGGL((prefill_prep_kernel<T, D, true, true, I8>), grid, block, 0, st, *cache,
-                       kk, vv, kr, Hkv, S, positions, nvec, fr);
+                       kk, vv, kr, Hkv, S, positions, lens, nvec, fr);
   } else if (!I8 && keys_in_cache) {
     hipLaunchKernelGGL((prefill_prep_kernel<T, D, false, true, false, true>), grid, block, 0, st,
-                       *cache, kk, vv, kr, Hkv, S, positions, nvec, fr);
+                       *cache, kk, vv, kr, Hkv, S, positions, lens, nvec, fr);
   } else {
     hipLaunchKernelGGL((prefill_prep_kernel<T, D, false, true, I8>), grid, block, 0, st,
-                       *cache, kk, vv, kr, Hkv, S, positions, nvec, fr);
+                       *cache, kk, vv, kr, Hkv, S, positions, lens, nvec, fr);
   }
   return hipGetLastError();
 }
@@ -384,10 +388,11 @@ hipError_t launch_kv_append(Dtype dt, int D, bool paged, bool i8, const CacheArg
 
 hipError_t launch_prefill_prep(Dtype dt, int D, bool paged, bool i8, const CacheArgs* cache,
                                const void* k, const void* v, void* k_rot, int B, int Hkv,
-                               int S, const int32_t* positions, const RopeFreq& fr,
-                               bool keys_in_cache, hipStream_t s) {
-#define CAR_PREP(T, DD, I)                                                                    \
-  prefill_prep_t<T, DD, I>(paged, cache, k, v, k_rot, B, Hkv, S, positions, fr, keys_in_cache, s)
+                               int S, const int32_t* positions, const int32_t* lens,
+                               const RopeFreq& fr, bool keys_in_cache, hipStream_t s) {
+#define CAR_PREP(T, DD, I)                                                             \
+  prefill_prep_t<T, DD, I>(paged, cache, k, v, k_rot, B, Hkv, S, positions, lens, fr, \
+                           keys_in_cache, s)
   if (i8 && cache != nullptr) {
     if (dt == F32) return D == 64 ? CAR_PREP(float, 64, true) : CAR_PREP(float, 128, true);
     return D == 64 ? CAR_PREP(bf16_t, 64, true) : CAR_PREP(bf16_t, 128, true);

@@ -197,12 +197,20 @@ size_t car_attn_prefill_workspace_bytes(car_dtype dtype, int B, int Hkv, int S, 
  * each key block) and never stores the S x S score matrix.
  *   q          [B, Hq, S, D] device;   k, v  [B, Hkv, S, D] device (k not rotated).
  *   out        [B, Hq, S, D] device, written.
- *   positions  int32 [B, S] device, strictly increasing along s for every b
- *              (so that the position order equals the index order).
+ *   positions  int32 [B, S] device, strictly increasing along s over each
+ *              prompt's tokens (so that the position order equals the index
+ *              order); entries of padding rows are not read.
+ *   seq_lens   NULL: every prompt has S tokens.  Otherwise int32 [B] device:
+ *              prompt b is its first seq_lens[b] rows (0..S; values outside
+ *              are clamped), a padded batch of prompts of different lengths
+ *              ([Scratch] §3.3 names the padding mask).  Padding rows are
+ *              neither attended to nor stored in the cache, and their output
+ *              rows are written as zeros.
  *   scale      multiplies the scores before the softmax; 1/sqrt(D) on the
  *              pages ([Intuition] §4).
  *   cache      NULL: nothing is stored.  Otherwise every rotated key and raw
- *              value is also stored at index positions[b][s], as by
+ *              value of a prompt token is also stored at index
+ *              positions[b][s], as by
  *              car_kv_cache_append.  With an INT8 cache only the stored
  *              copy is quantized: the prompt attends to its own keys and
  *              values at full precision.
@@ -215,7 +223,8 @@ size_t car_attn_prefill_workspace_bytes(car_dtype dtype, int B, int Hkv, int S, 
  */
 car_status car_attn_prefill(const void* q, const void* k, const void* v, void* out,
                             car_dtype dtype, int B, int Hq, int Hkv, int S, int D,
-                            const int32_t* positions, float theta, car_rope_pairing pairing,
+                            const int32_t* positions, const int32_t* seq_lens, float theta,
+                            car_rope_pairing pairing,
                             float scale,
                             const car_kv_cache* cache, void* workspace,
                             size_t workspace_bytes, hipStream_t stream);
@@ -305,7 +314,8 @@ car_status car_attn_decode(const void* q, const void* k_new, const void* v_new,
  */
 car_status car_attn_prefill_timed(const void* q, const void* k, const void* v, void* out,
                                   car_dtype dtype, int B, int Hq, int Hkv, int S, int D,
-                                  const int32_t* positions, float theta,
+                                  const int32_t* positions, const int32_t* seq_lens,
+                                  float theta,
                                   car_rope_pairing pairing, float scale,
                                   const car_kv_cache* cache, void* workspace,
                                   size_t workspace_bytes, hipStream_t stream,

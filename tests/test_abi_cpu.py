@@ -104,13 +104,14 @@ def test_prefill_rejects(car, lib):
     need = lib.car_attn_prefill_workspace_bytes(BF16, 2, 2, 8, 64, None)
     assert need == 2 * 2 * 8 * 64 * 2
     args = dict(q=FAKE, k=FAKE, v=FAKE, out=FAKE, dt=BF16, B=2, Hq=4, Hkv=2, S=8, D=64,
-                pos=FAKE, theta=1e4, pair=0, scale=0.125, cache=None, ws=FAKE, wsb=need)
+                pos=FAKE, lens=None, theta=1e4, pair=0, scale=0.125, cache=None, ws=FAKE,
+                wsb=need)
 
     def call(**kw):
         a = dict(args, **kw)
         return f(a["q"], a["k"], a["v"], a["out"], a["dt"], a["B"], a["Hq"], a["Hkv"], a["S"],
-                 a["D"], a["pos"], a["theta"], a["pair"], a["scale"], a["cache"], a["ws"],
-                 a["wsb"], None)
+                 a["D"], a["pos"], a["lens"], a["theta"], a["pair"], a["scale"], a["cache"],
+                 a["ws"], a["wsb"], None)
 
     assert call(D=80) == UNSUPPORTED
     assert call(pair=5) == UNSUPPORTED               # unknown RoPE pairing
@@ -250,8 +251,8 @@ def test_prefill_launch_limits_fail_before_any_launch(car, lib):
     ws = 1 << 40  # the workspace check passes; nothing is dereferenced
 
     def call(dt, B, Hq, Hkv, S, D, cache=None):
-        return f(FAKE, FAKE, FAKE, FAKE, dt, B, Hq, Hkv, S, D, FAKE, 1e4, 0, 0.1, cache, FAKE,
-                 ws, None)
+        return f(FAKE, FAKE, FAKE, FAKE, dt, B, Hq, Hkv, S, D, FAKE, None, 1e4, 0, 0.1, cache,
+                 FAKE, ws, None)
 
     assert call(F32, 65536, 1, 1, 4, 64) == UNSUPPORTED      # fp32 grid z
     assert call(F32, 1, 65536, 1, 4, 64) == UNSUPPORTED      # fp32 grid y
@@ -277,8 +278,8 @@ def test_timed_variants_check_like_the_plain_calls(car, lib):
               ctypes.byref(c), FAKE)
     assert lib.car_attn_decode_timed(*common, need - 16, None, None, None) == WORKSPACE
     assert lib.car_attn_decode_timed(*common, need - 16, None, FAKE, FAKE) == WORKSPACE
-    pre = (FAKE, FAKE, FAKE, FAKE, BF16, 1, 4, 4, 8, 96, FAKE, 1e4, 0, 0.1, None, FAKE, 1 << 20,
-           None)
+    pre = (FAKE, FAKE, FAKE, FAKE, BF16, 1, 4, 4, 8, 96, FAKE, FAKE, 1e4, 0, 0.1, None, FAKE,
+           1 << 20, None)
     assert lib.car_attn_prefill_timed(*pre, None, None) == UNSUPPORTED
     assert lib.car_attn_prefill(*pre) == UNSUPPORTED
     cached = (FAKE, FAKE, FAKE, FAKE, BF16, 1, 4, 3, 8, 128, FAKE, None, 64, 1e4, 0, 0.1,

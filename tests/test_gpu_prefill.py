@@ -212,3 +212,72 @@ def test_qwen_workload_prefill_every_head(car):
     (one head at a time), every cached row checked, and no other row of the
     NaN-filled cache written."""
     check_prefill(car, W.qwen_prefill(DEV), cap=4096)
+
+
+def check_varlen(car, B, Hq, Hkv, S, D, dtype, lens, offsets, cache_kind, cap, seed):
+    """A padded batch of prompts: prompt b is its first lens[b] rows at
+    positions offsets[b] + 0.., the padding rows hold NaN (q, k, v) and
+    position -7.  Rows of each prompt match the oracle, padding rows are
+    exactly zero, and only prompt tokens reach the NaN-filled cache."""
+    case = W.prefill_case("varlen", B, Hq, Hkv, S, D, dtype, seed, DEV)
+    pos = torch.full((B, S), -7, dtype=torch.int32)
+    for b, n in enumerate(lens):
+        pos[b, :n] = torch.arange(n, dtype=torch.int32) + offsets[b]
+        case.q[b, :, n:] = float("nan")
+        case.k[b, :, n:] = float("nan")
+        case.v[b, :, n:] = float("nan")
+    pos = pos.to(DEV)
+    seq_lens = torch.tensor(lens, dtype=torch.int32, device=DEV)
+    cache, table = (None, None) if cache_kind == "none" else \
+        make_cache(car, case, cache_kind == "paged", cap)
+    out = car.attn_prefill(case.q, case.k, case.v, pos, theta=case.theta, scale=case.scale,
+                           cache=cache, seq_lens=seq_lens)
+    torch.cuda.synchronize()
+    want, k_rot = oracle.attn_prefill(f64(case.q), f64(case.k), f64(case.v), pos.cpu().numpy(),
+                                      case.theta, case.scale, seq_lens=np.array(lens))
+    got = f64(out)
+    tol = TOL[dtype]
+    err = 0.0
+    for b, n in enumerate(lens):
+        err = max(err, max_abs(got[b, :, :n], want[b, :, :n]))
+        assert torch.equal(out[b, :, n:].float().cpu(), torch.zeros_like(out[b, :, n:].float().cpu())), \
+            f"padding rows of sequence {b} are not zero"
+    if cache is not None:
+        for b, n in enumerate(lens):
+            for s in range(n):
+                t = offsets[b] + s
+                if table is None:
+                    gk, gv = cache.k[b, :, t], cache.v[b, :, t]
+                else:
+                    gk, gv = cache.k[int(table[b, t // 16]), :, t % 16], \
+                        cache.v[int(table[b, t // 16]), :, t % 16]
+                err = max(err, max_abs(f64(gk), k_rot[b, :, s]))
+                assert torch.equal(bits(gv.cpu()), bits(case.v[b, :, s].cpu())), "cached V"
+        written = sum(lens) * Hkv
+        for name, t in (("K", cache.k), ("V", cache.v)):
+            rows = (~torch.isnan(t.float()).all(dim=-1)).sum().item()
+            assert rows == written, f"cache {name}: {rows} rows written, expected {written}"
+    log_case(f"varlen prefill {cache_kind} {dtype} D={D} lens={lens}: max-abs error {err:.3e}")
+    assert err <= tol
+
+
+@pytest.mark.parametrize("cache_kind", ["none", "contiguous", "paged"])
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16], ids=["f32", "bf16"])
+@pytest.mark.parametrize("D", [64, 128])
+def test_prefill_varlen(car, cache_kind, dtype, D):
+    """Lengths 333 (full), 0, 1, 130 and 64 padded to S = 333, GQA 4/2;
+    prompt 4 starts at position 100 (its keys then sit at consecutive cache
+    slots 100..163)."""
+    log_case(f"prefill varlen {cache_kind} {dtype} D={D}")
+    check_varlen(car, 5, 4, 2, 333, D, dtype, [333, 0, 1, 130, 64], [0, 0, 5, 2, 100],
+                 cache_kind, 448, 900 + D)
+
+
+@pytest.mark.parametrize("cache_kind", ["none", "contiguous"])
+def test_prefill_varlen_paired_form(car, cache_kind):
+    """Enough query-tile pairs (4 x 32 heads x 2) for the 8-wave paired form:
+    lengths 1024, 700, 1 and 513 padded to 1024, 32 query heads on 8 KV heads,
+    bf16, D = 128."""
+    log_case(f"prefill varlen paired form {cache_kind}")
+    check_varlen(car, 4, 32, 8, 1024, 128, torch.bfloat16, [1024, 700, 1, 513], [0, 0, 0, 0],
+                 cache_kind, 1024, 950)

@@ -356,3 +356,17 @@ def paged_decode(device="cpu", poison_unused=False):
     return decode_case("paged_decode", 64, 32, 8, 128, torch.bfloat16, lens,
                        BASE_SEED + 4, device, paged=True, poison_unused=poison_unused,
                        blocks_per_seq=513)
+
+
+def varlen_prefill_lens():
+    """Prompt lengths of the padded batch: 8 draws from U{128..2048}."""
+    return [int(x) for x in host_rng(BASE_SEED + 50).integers(128, 2049, size=8)]
+
+
+def varlen_prefill(device="cpu"):
+    """A padded batch of whole prompts: B=8, H=32, D=128, S=2048 rows per
+    prompt of which the first varlen_prefill_lens()[b] are tokens, bf16,
+    positions 0.. (a [8, 32, 2048, 128] cache holds them)."""
+    case = prefill_case("varlen_prefill", 8, 32, 32, 2048, 128, torch.bfloat16,
+                        BASE_SEED + 50, device, cache_max_seq=2048)
+    return case, varlen_prefill_lens()
