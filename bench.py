@@ -21,9 +21,11 @@ cores on a bounded sample of the same workloads, is reported as a baseline.
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--only NAME] [--no-cpu-baseline]
                     [--stat-iters N]
 
-Every stage and extra is also timed over N (default 100) further iterations
-for its median, p10 and p90; the decode kernels once more after 512 MiB of
-writes before each iteration (cold Infinity Cache).
+Before the W warmup steps the stages run untimed for 0.3 s more, so that the
+timed steps do not start at idle clocks.  Every stage and extra is also timed
+over N (default 100) further iterations for its median, p10 and p90; the
+decode kernels once more after 512 MiB of writes before each iteration (cold
+Infinity Cache).
 """
 
 from __future__ import annotations
@@ -95,6 +97,7 @@ KERNEL_SOURCES = ["rope_cache.hip", "decode.hip", "decode_i8.hip", "prefill.hip"
                   "decode_common.hpp", "launch.hpp"]
 COPY_BYTES = 1 << 30
 FLUSH_BYTES = 512 << 20
+CLOCK_WARM_S = 0.3
 
 
 def kernel_source_sha() -> str:
@@ -547,6 +550,13 @@ def main(argv=None) -> int:
         torch.cuda.synchronize()
         del src, dst
 
+    # clocks: the same stages, untimed, for CLOCK_WARM_S seconds before the
+    # warmup steps, so that the timed steps do not start at idle clocks
+    t_end = time.perf_counter() + CLOCK_WARM_S
+    while time.perf_counter() < t_end:
+        for s in stages:
+            run_stage(s)
+        torch.cuda.synchronize()
     for _ in range(args.warmup):
         for s in stages:
             run_stage(s)

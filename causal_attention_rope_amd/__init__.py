@@ -341,14 +341,17 @@ def attn_prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, positions: t
                  cache: Optional[KVCache] = None, out: Optional[torch.Tensor] = None,
                  workspace: Optional[torch.Tensor] = None,
                  rope_pairing: str = "adjacent", timing=None,
-                 seq_lens: Optional[torch.Tensor] = None) -> torch.Tensor:
+                 seq_lens: Optional[torch.Tensor] = None,
+                 no_workspace: bool = False) -> torch.Tensor:
     """Causal attention over a prompt with RoPE on q and k (see car_attn_prefill).
 
     q [B, Hq, S, D]; k, v [B, Hkv, S, D]; positions int32 [B, S], strictly
     increasing per sequence.  With ``cache`` the rotated keys and the values
     are also stored at index == position.  ``seq_lens`` int32 [B] (optional):
     prompt b is its first seq_lens[b] rows, the rest padding (zero output
-    rows, not stored).  Returns out [B, Hq, S, D].
+    rows, not stored).  ``no_workspace``: pass no workspace, so that the keys
+    are read back from ``cache`` (bf16, contiguous, native; each prompt's
+    positions consecutive slots).  Returns out [B, Hq, S, D].
     """
     _need(q, "q", dim=4)
     _need(k, "k", dtype=q.dtype, dim=4, device=q.device)
@@ -381,11 +384,17 @@ def attn_prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, positions: t
         c = cache._c()
     dt = _dtype_code(q)
     need = int(_lib.car_attn_prefill_workspace_bytes(dt, B, Hkv, S, D, None))
-    ws = _workspace(need, q.device, workspace)
+    if no_workspace:
+        # keys read back from a contiguous bf16 cache (consecutive positions only)
+        if workspace is not None:
+            raise ValueError("no_workspace and workspace are exclusive")
+        ws, ws_bytes = None, 0
+    else:
+        ws = _workspace(need, q.device, workspace)
+        ws_bytes = ws.numel() * ws.element_size()
     args = [_ptr(q), _ptr(k), _ptr(v), _ptr(out), dt, B, Hq, Hkv, S, D, _ptr(positions),
             _ptr(seq_lens), float(theta), _pairing(rope_pairing), float(scale),
-            ctypes.byref(c) if c is not None else None, _ptr(ws),
-            ws.numel() * ws.element_size(), _stream(q)]
+            ctypes.byref(c) if c is not None else None, _ptr(ws), ws_bytes, _stream(q)]
     ev = _events(timing)
     if ev is None:
         _check(_lib.car_attn_prefill(*args), "attn_prefill")

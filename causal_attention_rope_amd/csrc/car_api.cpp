@@ -78,6 +78,14 @@ int64_t prefill_ws_bytes(car_dtype dt, int B, int Hkv, int S, int D) {
   return (int64_t)B * Hkv * S * D * (int64_t)elem_bytes(dt);
 }
 
+// bf16 into a contiguous native cache: prompts at consecutive slots keep
+// their rotated keys in the cache only, and the attention reads them there
+// (then no workspace is needed for prompts that fit the cache).
+bool keys_go_to_cache(car_dtype dt, const car_kv_cache* c) {
+  return dt == CAR_DTYPE_BF16 && c != nullptr && c->block_table == nullptr &&
+         c->format == CAR_CACHE_NATIVE;
+}
+
 int decode_nsplit(int max_seq_len) { return (max_seq_len + DECODE_SPLIT - 1) / DECODE_SPLIT; }
 
 bool is_int8(const car_kv_cache* c) { return c != nullptr && c->format == CAR_CACHE_INT8; }
@@ -148,8 +156,8 @@ car_status car_kv_int8_calibrate(const void* k, const void* v, car_dtype dtype, 
 
 size_t car_attn_prefill_workspace_bytes(car_dtype dtype, int B, int Hkv, int S, int D,
                                         const car_kv_cache* cache) {
-  (void)cache;
   if (!dtype_ok(dtype) || !head_dim_ok(D) || B < 0 || Hkv < 0 || S < 0) return 0;
+  if (keys_go_to_cache(dtype, cache) && S <= cache->max_seq) return 0;
   return (size_t)prefill_ws_bytes(dtype, B, Hkv, S, D);
 }
 
@@ -184,21 +192,23 @@ car_status car_attn_prefill_timed(const void* q, const void* k, const void* v, v
   if (B > 65535 || Hq > 65535 || (int64_t)B * Hq * ((S + 63) / 64) > INT32_MAX ||
       (S > cap ? (int64_t)S : cap) * D * 4 > (int64_t)UINT32_MAX)
     return CAR_ERR_UNSUPPORTED;
-  const int64_t need = prefill_ws_bytes(dtype, B, Hkv, S, D);
-  if (workspace == nullptr || !aligned16(workspace) || (int64_t)workspace_bytes < need)
-    return CAR_ERR_WORKSPACE;
+  // A workspace of the full size holds the rotated keys of every prompt;
+  // without one (allowed when the keys go to a contiguous native cache) the
+  // attention reads every prompt's keys back from the cache.
+  const int64_t full = prefill_ws_bytes(dtype, B, Hkv, S, D);
+  const bool keys_in_cache = keys_go_to_cache(dtype, cache);
+  void* k_rot = workspace != nullptr && (int64_t)workspace_bytes >= full ? workspace : nullptr;
+  if (k_rot == nullptr && (!keys_in_cache || S > cap)) return CAR_ERR_WORKSPACE;
+  if (k_rot != nullptr && !aligned16(k_rot)) return CAR_ERR_WORKSPACE;
 
   const Dtype dt = dtype == CAR_DTYPE_F32 ? F32 : BF16;
   const RopeFreq fr = make_freq(D, theta, pairing);
   const bool paged = cache != nullptr && cache->block_table != nullptr;
-  // bf16 into a contiguous native cache: prompts at consecutive slots keep
-  // their rotated keys in the cache only, and the attention reads them there
-  const bool keys_in_cache = cache != nullptr && !paged && !is_int8(cache) && dt == BF16;
   hipError_t e = launch_prefill_prep(dt, D, paged, is_int8(cache),
-                                     cache != nullptr ? &c : nullptr, k, v, workspace, B, Hkv,
+                                     cache != nullptr ? &c : nullptr, k, v, k_rot, B, Hkv,
                                      S, positions, seq_lens, fr, keys_in_cache, stream);
   if (e != hipSuccess) return CAR_ERR_HIP;
-  return from_hip(launch_prefill_attention(dt, D, q, workspace, v, out, B, Hq, Hkv, S,
+  return from_hip(launch_prefill_attention(dt, D, q, k_rot, v, out, B, Hq, Hkv, S,
                                            positions, seq_lens, fr, scale,
                                            keys_in_cache ? &c : nullptr, stream,
                                            timed(kernel_start, kernel_stop)));

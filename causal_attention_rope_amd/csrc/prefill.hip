@@ -341,9 +341,15 @@ __global__ __launch_bounds__((Tile<D, 8>::THREADS), 2) void prefill_bf16_kernel(
   } else if constexpr (SRC == KEYS_PROMPT) {
     kbase = kr + ((int64_t)b * Hkv + hk) * S * D;
     vbase = v + ((int64_t)b * Hkv + hk) * S * D;
-    int p0;  // keys the K pass left in the cache only (at consecutive slots p0..)
-    if (c.k != nullptr && prompt_rows_in_cache(positions, b, S, Sb, c.max_seq, &p0))
+    // keys the K pass left in the cache only (at consecutive slots p0..), and
+    // without k_rot every prompt's: rows p0.. of the cache, kept inside it
+    // (positions that are not consecutive slots then give unspecified output)
+    int p0;
+    if (c.k != nullptr &&
+        (prompt_rows_in_cache(positions, b, S, Sb, c.max_seq, &p0) || kr == nullptr)) {
+      p0 = min(max(p0, 0), max(c.max_seq - Sb, 0));
       kbase = static_cast<const bf16_t*>(c.k) + (((int64_t)b * Hkv + hk) * c.max_seq + p0) * D;
+    }
   }
 
   // ---- direct buffer -> LDS loads of K and V tiles ----

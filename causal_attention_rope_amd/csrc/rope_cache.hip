@@ -122,7 +122,8 @@ __global__ __launch_bounds__(kThreads) void prefill_prep_kernel(
     load16<T>(k + row * D + col, f);
     rope_rotate_chunk<T, N>(f, k + row * D, col, D, pos, fr);
     int p0;
-    if (!KEYS_IN_CACHE || !prompt_rows_in_cache(positions, b, S, n, c.max_seq, &p0))
+    if (k_rot != nullptr &&
+        (!KEYS_IN_CACHE || !prompt_rows_in_cache(positions, b, S, n, c.max_seq, &p0)))
       store16<T>(k_rot + row * D + col, f);
     if (CACHE && pos >= 0 && pos <= cache_last_slot<PAGED>(c)) {  // else not stored
       const int hk = (int)(bh % Hkv);

@@ -180,8 +180,9 @@ car_status car_kv_int8_calibrate(const void* k, const void* v, car_dtype dtype, 
 
 /*
  * Bytes of device workspace car_attn_prefill needs for these sizes: room for
- * the rotated keys [B, Hkv, S, D] in `dtype`.  Returns 0 for invalid sizes.
- * `cache` may be NULL; the size does not depend on it.
+ * the rotated keys [B, Hkv, S, D] in `dtype`, or 0 when they need none: bf16
+ * into a contiguous native cache (`cache` non-NULL, no block table, format
+ * native) with S at most its capacity.  Also 0 for invalid sizes.
  */
 size_t car_attn_prefill_workspace_bytes(car_dtype dtype, int B, int Hkv, int S, int D,
                                         const car_kv_cache* cache);
@@ -214,8 +215,16 @@ size_t car_attn_prefill_workspace_bytes(car_dtype dtype, int B, int Hkv, int S, 
  *              car_kv_cache_append.  With an INT8 cache only the stored
  *              copy is quantized: the prompt attends to its own keys and
  *              values at full precision.
- *   workspace  device scratch of at least car_attn_prefill_workspace_bytes();
- *              its contents on entry are ignored and on exit unspecified.
+ *   workspace  device scratch for the rotated keys; its contents on entry are
+ *              ignored and on exit unspecified.  With B*Hkv*S*D elements or
+ *              more it is used.  Otherwise (NULL or smaller; allowed only when
+ *              car_attn_prefill_workspace_bytes() is 0) the attention reads
+ *              each prompt's rotated keys back from the cache rows p0.. where
+ *              p0 is its first position: each prompt's positions must then be
+ *              consecutive (p0, p0+1, ...) inside the cache, or its output is
+ *              unspecified (the cache store stays correct, and no read leaves
+ *              the cache).  With a workspace, prompts at consecutive slots
+ *              read their keys from the cache too; others read the workspace.
  * S == 0 is a no-op returning CAR_OK.  Sizes one launch cannot cover (B or
  * Hq above 65535, B * Hq * ceil(S / 64) above 2^31 - 1, or S, or a cache's
  * capacity, times D * 4 bytes above 2^32 - 1) return CAR_ERR_UNSUPPORTED

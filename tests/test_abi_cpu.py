@@ -233,6 +233,31 @@ def test_int8_calibrate_rejects(lib):
     assert f(None, None, BF16, 1, 0, 8, 64, None, 1e4, 0, None, None, None) == OK   # no heads
 
 
+def test_prefill_workspace_not_needed_for_a_contiguous_bf16_cache(car, lib):
+    """Keys into a contiguous native bf16 cache need no workspace (they are
+    read back from the cache) when the prompt fits it; every other case
+    needs B*Hkv*S*D elements."""
+    full_bf16 = 2 * 4 * 128 * 64 * 2
+    cont = _cache(car, max_seq=128)
+    assert lib.car_attn_prefill_workspace_bytes(BF16, 2, 4, 128, 64, ctypes.byref(cont)) == 0
+    assert lib.car_attn_prefill_workspace_bytes(BF16, 2, 4, 128, 64, None) == full_bf16
+    short = _cache(car, max_seq=127)   # the prompt does not fit: keys need the workspace
+    assert lib.car_attn_prefill_workspace_bytes(BF16, 2, 4, 128, 64, ctypes.byref(short)) == full_bf16
+    paged = _cache(car, paged=True)
+    assert lib.car_attn_prefill_workspace_bytes(BF16, 2, 4, 128, 64, ctypes.byref(paged)) == full_bf16
+    i8 = _cache(car, max_seq=128, fmt=1, ks=FAKE, vs=FAKE)
+    assert lib.car_attn_prefill_workspace_bytes(BF16, 2, 4, 128, 64, ctypes.byref(i8)) == full_bf16
+    assert lib.car_attn_prefill_workspace_bytes(F32, 2, 4, 128, 64, ctypes.byref(cont)) == 2 * full_bf16
+    # without a workspace the host checks refuse every case but the first
+    f = lib.car_attn_prefill
+
+    def call(dt, cache):
+        return f(FAKE, FAKE, FAKE, FAKE, dt, 2, 4, 4, 128, 64, FAKE, None, 1e4, 0, 0.1, cache,
+                 None, 0, None)
+    for dt, c in ((BF16, None), (BF16, short), (BF16, paged), (F32, cont)):
+        assert call(dt, ctypes.byref(c) if c is not None else None) == WORKSPACE
+
+
 def test_workspace_sizes(lib):
     assert lib.car_attn_decode_workspace_bytes(32, 32, 128, 4096) == 32 * 32 * 16 * 132 * 4
     assert lib.car_attn_decode_workspace_bytes(64, 32, 128, 8193) == 64 * 32 * 33 * 132 * 4

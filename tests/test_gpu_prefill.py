@@ -281,3 +281,59 @@ def test_prefill_varlen_paired_form(car, cache_kind):
     log_case(f"prefill varlen paired form {cache_kind}")
     check_varlen(car, 4, 32, 8, 1024, 128, torch.bfloat16, [1024, 700, 1, 513], [0, 0, 0, 0],
                  cache_kind, 1024, 950)
+
+
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("varlen", [False, True], ids=["full", "varlen"])
+def test_prefill_without_workspace(car, D, varlen):
+    """bf16 into a contiguous cache with no workspace: the rotated keys are
+    read back from the cache.  Prompts start at positions 7, 0 and 30 (each
+    consecutive); with varlen their lengths are 200, 1 and 77 of S = 200."""
+    log_case(f"prefill without workspace D={D} varlen={varlen}")
+    B, H, S, cap = 3, 4, 200, 240
+    assert car._lib.car_attn_prefill_workspace_bytes(1, B, 2, S, D, None) > 0
+    case = W.prefill_case("nows", B, H, 2, S, D, torch.bfloat16, 990 + D, DEV)
+    offs = [7, 0, 30]
+    lens = [200, 1, 77] if varlen else [S] * B
+    pos = torch.stack([torch.arange(S, dtype=torch.int32) + o for o in offs]).to(DEV)
+    ck = torch.full((B, 2, cap, D), float("nan"), dtype=torch.bfloat16, device=DEV)
+    cache = car.KVCache(ck, ck.clone())
+    sl = torch.tensor(lens, dtype=torch.int32, device=DEV) if varlen else None
+    out = car.attn_prefill(case.q, case.k, case.v, pos, theta=case.theta, scale=case.scale,
+                           cache=cache, seq_lens=sl, no_workspace=True)
+    torch.cuda.synchronize()
+    want, k_rot = oracle.attn_prefill(f64(case.q), f64(case.k), f64(case.v), pos.cpu().numpy(),
+                                      case.theta, case.scale, seq_lens=np.array(lens))
+    err = 0.0
+    for b, n in enumerate(lens):
+        err = max(err, max_abs(f64(out[b, :, :n]), want[b, :, :n]))
+        assert not out[b, :, n:].float().any()
+        err = max(err, max_abs(f64(cache.k[b, :, offs[b]:offs[b] + n]), k_rot[b, :, :n]))
+        assert torch.equal(bits(cache.v[b, :, offs[b]:offs[b] + n].cpu()),
+                           bits(case.v[b, :, :n].cpu()))
+    rows = (~torch.isnan(cache.k.float()).all(dim=-1)).sum().item()
+    assert rows == 2 * sum(lens)
+    log_case(f"max-abs error {err:.3e}")
+    assert err <= TOL[torch.bfloat16]
+
+
+def test_prefill_without_workspace_gapped_positions_stay_in_bounds(car):
+    """Without a workspace, positions that are not consecutive slots give an
+    unspecified output, but the cache store is still exact and nothing
+    outside the prompt's rows is written."""
+    log_case("prefill without workspace, gapped positions")
+    B, H, S, D, cap = 2, 2, 40, 64, 100
+    case = W.prefill_case("nows_gap", B, H, H, S, D, torch.bfloat16, 996, DEV)
+    pos = (torch.arange(S, dtype=torch.int32) * 2 + 3).repeat(B, 1).to(DEV)  # 3, 5, .., 81
+    ck = torch.full((B, H, cap, D), float("nan"), dtype=torch.bfloat16, device=DEV)
+    cache = car.KVCache(ck, ck.clone())
+    car.attn_prefill(case.q, case.k, case.v, pos, theta=case.theta, scale=case.scale,
+                     cache=cache, no_workspace=True)
+    torch.cuda.synchronize()
+    _, k_rot = oracle.attn_prefill(f64(case.q), f64(case.k), f64(case.v), pos.cpu().numpy(),
+                                   case.theta, case.scale)
+    p = pos[0].long()
+    assert max_abs(f64(cache.k[:, :, p]), k_rot) <= TOL[torch.bfloat16]
+    assert torch.equal(bits(cache.v[:, :, p].cpu()), bits(case.v.cpu()))
+    rows = (~torch.isnan(cache.k.float()).all(dim=-1)).sum().item()
+    assert rows == B * H * S
