@@ -31,7 +31,9 @@ __all__ = [
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-library_path = os.path.join(_HERE, "libcar.so")
+# CAR_LIBRARY selects another build of the same library (the sanitized
+# host-only build that the ABI tests run against); default: the in-tree one.
+library_path = os.environ.get("CAR_LIBRARY") or os.path.join(_HERE, "libcar.so")
 
 F32, BF16 = 0, 1
 _DTYPES = {torch.float32: F32, torch.bfloat16: BF16}

@@ -1,12 +1,19 @@
 """Build libcar.so (the HIP kernels and the C-ABI shim) for gfx950, in-tree.
 
-    python causal_attention_rope_amd/build.py
+    python causal_attention_rope_amd/build.py [--sanitize]
 
 (Run as a script: importing the package loads libcar.so, which the build
 creates.)
 
 Compiles every source under ``csrc/`` with hipcc for ``--offload-arch=gfx950``
 into ``_build/`` and links ``libcar.so`` next to this file.  Always rebuilds.
+
+``--sanitize`` builds ``libcar_san.so`` instead: the same sources with the
+host code under AddressSanitizer and UndefinedBehaviorSanitizer (device code
+unsanitized and unoptimised: this build is for the host-side ABI checks on a
+machine without a GPU and is never launched).  The package loads it when
+CAR_LIBRARY names it, with the sanitizer runtime (``asan_runtime()``)
+preloaded.
 """
 
 from __future__ import annotations
@@ -73,6 +80,61 @@ def check_defined(lib: str) -> None:
         raise RuntimeError("libcar.so has undefined symbols:\n" + "\n".join(missing))
 
 
+SAN_BUILD = os.path.join(HERE, "_build_san")
+SAN_LIB = os.path.join(HERE, "libcar_san.so")
+# host code: ASan + UBSan (every -fsanitize= for the host pass only)
+SAN_FLAGS = [
+    f"--offload-arch={ARCH}", "-O1", "-Xarch_device", "-O0", "-fPIC", "-std=c++17",
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-I", INCLUDE, "-I", CSRC,
+    "-Xarch_host", "-fsanitize=address",
+    "-Xarch_host", "-fsanitize=undefined",
+    "-Xarch_host", "-fno-sanitize-recover=undefined",
+    "-Xarch_host", "-fno-omit-frame-pointer",
+]
+SAN_LINK = ["-fsanitize=address,undefined", "-shared-libsan"]
+
+
+def clangxx() -> str:
+    rocm = os.path.dirname(os.path.dirname(os.path.realpath(hipcc())))
+    cand = os.path.join(rocm, "llvm", "bin", "clang++")
+    if not os.path.exists(cand):
+        raise RuntimeError(f"{cand} not found (ROCm's clang links the sanitized build)")
+    return cand
+
+
+def asan_runtime() -> str:
+    """Path of the shared ASan runtime the sanitized library links against."""
+    r = subprocess.run([clangxx(), "-print-file-name=libclang_rt.asan-x86_64.so"],
+                       capture_output=True, text=True, check=True)
+    return r.stdout.strip()
+
+
+def build_sanitized(verbose: bool = False) -> str:
+    os.makedirs(SAN_BUILD, exist_ok=True)
+
+    def one(src: str) -> str:
+        obj = os.path.join(SAN_BUILD, os.path.basename(src) + ".o")
+        cmd = [hipcc(), *SAN_FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+        r = subprocess.run(cmd, capture_output=True, text=True)
+        if r.returncode != 0:
+            raise RuntimeError(f"hipcc failed for {src}:\n{' '.join(cmd)}\n{r.stderr}")
+        return obj
+    with concurrent.futures.ThreadPoolExecutor(max_workers=len(SOURCES)) as ex:
+        objs = list(ex.map(one, SOURCES))
+    rocm_lib = os.path.join(os.path.dirname(os.path.dirname(os.path.realpath(hipcc()))), "lib")
+    tmp = SAN_LIB + ".tmp"
+    link = [clangxx(), "-shared", "-fPIC", *SAN_LINK, *objs, "-L", rocm_lib,
+            f"-Wl,-rpath,{rocm_lib}", "-lamdhip64", "-o", tmp]
+    r = subprocess.run(link, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"link failed:\n{' '.join(link)}\n{r.stderr}")
+    os.replace(tmp, SAN_LIB)
+    if verbose:
+        print(f"built {SAN_LIB}")
+    return SAN_LIB
+
+
 def build(verbose: bool = False, extra_flags=()) -> str:
     os.makedirs(BUILD, exist_ok=True)
     with concurrent.futures.ThreadPoolExecutor(max_workers=len(SOURCES)) as ex:
@@ -90,4 +152,7 @@ def build(verbose: bool = False, extra_flags=()) -> str:
 
 
 if __name__ == "__main__":
-    build(verbose=True, extra_flags=sys.argv[1:])
+    if sys.argv[1:] == ["--sanitize"]:
+        build_sanitized(verbose=True)
+    else:
+        build(verbose=True, extra_flags=sys.argv[1:])

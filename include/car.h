@@ -55,7 +55,17 @@
 extern "C" {
 #endif
 
-typedef enum car_dtype {
+/* The enums below are int32 in C and in C++.  C++ sees them with a fixed
+ * int32_t underlying type, so that any int32 a caller passes is a valid
+ * value of the type: values not listed are rejected by the checks, never
+ * undefined behaviour. */
+#ifdef __cplusplus
+#define CAR_ENUM(name) enum name : int32_t
+#else
+#define CAR_ENUM(name) enum name
+#endif
+
+typedef CAR_ENUM(car_dtype) {
   CAR_DTYPE_F32 = 0,
   CAR_DTYPE_BF16 = 1
 } car_dtype;
@@ -66,7 +76,7 @@ typedef enum car_dtype {
  * name ([Guide] §6.1) pair each element of the first half with its twin in
  * the second).  Pair i has angle m * theta^(-2i/D) in both layouts.
  */
-typedef enum car_rope_pairing {
+typedef CAR_ENUM(car_rope_pairing) {
   CAR_ROPE_ADJACENT = 0,  /* pair i = elements (2i, 2i+1) */
   CAR_ROPE_HALF = 1       /* pair i = elements (i, i + D/2) */
 } car_rope_pairing;
@@ -93,12 +103,12 @@ typedef enum car_rope_pairing {
  *     car_attn_decode accept an INT8 cache; car_attn_prefill_cached returns
  *     CAR_ERR_UNSUPPORTED for one.
  */
-typedef enum car_cache_format {
+typedef CAR_ENUM(car_cache_format) {
   CAR_CACHE_NATIVE = 0,
   CAR_CACHE_INT8 = 1
 } car_cache_format;
 
-typedef enum car_status {
+typedef CAR_ENUM(car_status) {
   CAR_OK = 0,
   CAR_ERR_INVALID_ARGUMENT = 1, /* null pointer, negative size, Hq % Hkv != 0,
                                    pointer not 16-byte aligned, bad cache shape */
