@@ -48,4 +48,5 @@ from .int8_cache import (  # noqa: F401
     int8_calibrate,
     kv_cache_append_int8,
     attn_decode_int8,
+    attn_prefill_cached_int8,
 )

@@ -33,9 +33,12 @@ Readings where the pages leave a step open (each one is a pin below):
   values rounded once to float32 equals float32 division: 53 >= 2*24 + 2.)
 * Attention reads the dequantized cache, code * scale, in float64; the new
   token of a decode step is quantized when it is appended and attended to in
-  its quantized form, like every other cached token.  A prefill's own
-  attention uses its full-precision keys and values; only what it stores is
-  quantized.
+  its quantized form, like every other cached token.  A chunk continuing a
+  cached prefix does the same for all of its tokens: they are stored first
+  and every key and value the chunk attends to is read back from the cache
+  (so a one-token chunk is a decode step, and a chunk equals the same tokens
+  taken as two chunks).  A whole-prompt prefill's own attention uses its
+  full-precision keys and values; only what it stores is quantized.
 
 Pins (``tests/test_oracle_int8.py``, none reuses this code): a channel's
 absolute maximum maps to +-127 and dequantizes back to itself within float32
@@ -46,6 +49,11 @@ that channel's scale and leaves all codes unchanged; a decode over an INT8
 cache whose values lie on the grid equals the float decode of ``attention``
 over the dequantized cache, with different K and V scales per channel; the
 bound |O_int8 - O_float| <= max scale_v / 2 when only V is off the grid.
+A chunk over an INT8 cache: with the prefix on the grid, zero chunk keys and
+chunk values on the V grid it equals the float chunk over the dequantized
+cache (contiguous and paged, with padding); a one-token chunk equals a
+decode step; a chunk equals the same tokens taken as two chunks (outputs
+and codes); padding rows are zero and padding tokens are not stored.
 """
 
 from __future__ import annotations
@@ -61,6 +69,7 @@ __all__ = [
     "int8_calibrate",
     "kv_cache_append_int8",
     "attn_decode_int8",
+    "attn_prefill_cached_int8",
 ]
 
 
@@ -186,4 +195,56 @@ def attn_decode_int8(q, k_new, v_new, cache_k, cache_v, seq_lens, k_scale, v_sca
             vals = _rows_int8(cache_v, v_scale[hk], b, hk, L + 1, block_table, block_size)
             out[b, hq] = causal_attention(q_rot[hq][None, :], keys, vals,
                                           (np.array([L]), pos), scale)[0]
+    return out
+
+
+def attn_prefill_cached_int8(q, k, v, cache_k, cache_v, seq_lens, k_scale, v_scale,
+                             theta: float = 10000.0, scale: float | None = None,
+                             block_table=None, block_size: int = 16, chunk_lens=None,
+                             pairing: str = "adjacent"):
+    """A prompt chunk continuing a cached prefix, over an INT8 cache.
+
+    As ``attention.attn_prefill_cached`` ([Scratch] §3.2-§3.3): with P =
+    seq_lens[b] tokens cached, chunk token s sits at position and cache
+    index P + s; q and k are rotated there; the rotated keys and raw values
+    are quantized and stored at P..P+n-1 (n = chunk_lens[b], or S); chunk
+    query i then attends over the dequantized rows 0..P+i, its own chunk's
+    tokens included in their quantized form.  Padding rows of the output are
+    zero and padding tokens are not stored.  The int8 caches are updated in
+    place.  Returns out [B, Hq, S, D] in float64.
+    """
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    k_scale = np.asarray(k_scale, dtype=np.float32)
+    v_scale = np.asarray(v_scale, dtype=np.float32)
+    B, Hq, S, D = q.shape
+    Hkv = k.shape[1]
+    group = Hq // Hkv
+    if scale is None:
+        scale = 1.0 / np.sqrt(D)
+    seq_lens = np.asarray(seq_lens)
+    out = np.zeros((B, Hq, S, D))
+    for b in range(B):
+        P = int(seq_lens[b])
+        n = S if chunk_lens is None else int(chunk_lens[b])
+        if n == 0:
+            continue
+        pos = P + np.arange(n)
+        q_rot = rope_rotate(q[b, :, :n], pos, theta, pairing)    # [Hq, n, D]
+        k_rot = rope_rotate(k[b, :, :n], pos, theta, pairing)    # [Hkv, n, D]
+        v_b = v[b:b + 1, :, :n]
+        if block_table is None:
+            kv_cache_append_int8(cache_k[b:b + 1], cache_v[b:b + 1], k_rot[None], v_b,
+                                 pos[None, :], k_scale, v_scale)
+        else:
+            kv_cache_append_int8(cache_k, cache_v, k_rot[None], v_b, pos[None, :], k_scale,
+                                 v_scale, block_table=block_table[b:b + 1],
+                                 block_size=block_size)
+        kpos = np.arange(P + n)
+        for hq in range(Hq):
+            hk = hq // group
+            keys = _rows_int8(cache_k, k_scale[hk], b, hk, P + n, block_table, block_size)
+            vals = _rows_int8(cache_v, v_scale[hk], b, hk, P + n, block_table, block_size)
+            out[b, hq, :n] = causal_attention(q_rot[hq], keys, vals, (pos, kpos), scale)
     return out

@@ -361,3 +361,167 @@ def _decode_transposed_scales(q, kn, vn, ck, cv, lens, ks, vs, block_table=None)
 def test_int8_decode_pins_catch_planted_mistakes(bad):
     assert not (check_decode_on_grid_equals_float_decode(bad)
                 and check_decode_v_error_bound(bad))
+
+
+# ==========================================================================
+# A chunk over an INT8 cache ([Scratch] §3.2-§3.3, every key read from the cache)
+# ==========================================================================
+
+def _chunk_grid_case(B, Hq, Hkv, D, S, lens, seed, paged):
+    """Random codes in every slot, distinct per-channel scales, zero chunk
+    keys (rotation keeps them zero, so their codes are exact) and chunk
+    values on the V grid."""
+    r = rng(seed)
+    n = int(max(lens)) + S
+    ks = r.uniform(0.01, 0.05, size=(Hkv, D)).astype(np.float32)
+    vs = r.uniform(0.02, 0.08, size=(Hkv, D)).astype(np.float32)
+    q = r.standard_normal((B, Hq, S, D))
+    k = np.zeros((B, Hkv, S, D))
+    v = r.integers(-127, 128, size=(B, Hkv, S, D)) * vs.astype(np.float64)[None, :, None, :]
+    if paged:
+        mbps = (n + 15) // 16
+        nb = B * mbps + 2
+        table = r.permutation(nb)[: B * mbps].reshape(B, mbps)
+        shape = (nb, Hkv, 16, D)
+    else:
+        table = None
+        shape = (B, Hkv, n, D)
+    ck = r.integers(-127, 128, size=shape).astype(np.int8)
+    cv = r.integers(-127, 128, size=shape).astype(np.int8)
+    return q, k, v, ck, cv, ks, vs, table
+
+
+def check_chunk_on_grid_equals_float_chunk(chunk, paged=False):
+    """Prefix, chunk keys and chunk values on the code grid: the INT8 chunk
+    is the float chunk over the dequantized cache (padding included)."""
+    lens = np.array([0, 5, 17, 33])
+    n = np.array([6, 1, 6, 3])
+    q, k, v, ck, cv, ks, vs, table = _chunk_grid_case(4, 4, 2, 8, 6, lens, 11, paged)
+    fk, fv = _dequantized(ck, ks, paged), _dequantized(cv, vs, paged)
+    got = chunk(q, k, v, ck.copy(), cv.copy(), lens, ks, vs, block_table=table, chunk_lens=n)
+    want = A.attn_prefill_cached(q, k, v, fk, fv, lens, block_table=table, chunk_lens=n)
+    return np.allclose(got, want, atol=1e-12, rtol=0)
+
+
+def check_one_token_chunk_is_a_decode_step(chunk):
+    r = rng(12)
+    B, Hq, Hkv, D, n = 2, 4, 2, 8, 20
+    lens = np.array([4, 13])
+    ks = r.uniform(0.01, 0.05, size=(Hkv, D)).astype(np.float32)
+    vs = r.uniform(0.02, 0.08, size=(Hkv, D)).astype(np.float32)
+    q = r.standard_normal((B, Hq, D))
+    kn, vn = r.standard_normal((B, Hkv, D)), r.standard_normal((B, Hkv, D))
+    ck = r.integers(-127, 128, size=(B, Hkv, n, D)).astype(np.int8)
+    cv = r.integers(-127, 128, size=(B, Hkv, n, D)).astype(np.int8)
+    ck2, cv2 = ck.copy(), cv.copy()
+    got = chunk(q[:, :, None], kn[:, :, None], vn[:, :, None], ck, cv, lens, ks, vs)[:, :, 0]
+    want = Q.attn_decode_int8(q, kn, vn, ck2, cv2, lens, ks, vs)
+    return (np.allclose(got, want, atol=1e-13, rtol=0) and np.array_equal(ck, ck2)
+            and np.array_equal(cv, cv2))
+
+
+def check_chunk_equals_two_chunks(chunk):
+    """Off-grid keys and values: a chunk of 9 tokens equals its first 4
+    then its last 5 as two chunks (outputs and stored codes)."""
+    r = rng(13)
+    B, Hq, Hkv, D, S, n = 2, 4, 2, 8, 9, 24
+    lens = np.array([0, 7])
+    ks = r.uniform(0.02, 0.05, size=(Hkv, D)).astype(np.float32)
+    vs = r.uniform(0.02, 0.05, size=(Hkv, D)).astype(np.float32)
+    q = r.standard_normal((B, Hq, S, D))
+    k, v = r.standard_normal((B, Hkv, S, D)), r.standard_normal((B, Hkv, S, D))
+    ck = r.integers(-127, 128, size=(B, Hkv, n, D)).astype(np.int8)
+    cv = r.integers(-127, 128, size=(B, Hkv, n, D)).astype(np.int8)
+    ck2, cv2 = ck.copy(), cv.copy()
+    whole = chunk(q, k, v, ck, cv, lens, ks, vs)
+    first = chunk(q[:, :, :4], k[:, :, :4], v[:, :, :4], ck2, cv2, lens, ks, vs)
+    second = chunk(q[:, :, 4:], k[:, :, 4:], v[:, :, 4:], ck2, cv2, lens + 4, ks, vs)
+    both = np.concatenate([first, second], axis=2)
+    return (np.allclose(whole, both, atol=1e-13, rtol=0) and np.array_equal(ck, ck2)
+            and np.array_equal(cv, cv2))
+
+
+@pytest.mark.parametrize("paged", [False, True], ids=["contiguous", "paged"])
+def test_int8_chunk_on_grid_equals_float_chunk(paged):
+    assert check_chunk_on_grid_equals_float_chunk(Q.attn_prefill_cached_int8, paged)
+
+
+def test_int8_one_token_chunk_is_a_decode_step():
+    assert check_one_token_chunk_is_a_decode_step(Q.attn_prefill_cached_int8)
+
+
+def test_int8_chunk_equals_two_chunks():
+    assert check_chunk_equals_two_chunks(Q.attn_prefill_cached_int8)
+
+
+def test_int8_chunk_stores_codes_and_zero_padding_rows():
+    """Chunk tokens' codes land at P..P+n-1 and nowhere else; padding rows
+    are zero."""
+    r = rng(14)
+    B, Hq, Hkv, D, S, cap = 2, 2, 1, 8, 5, 16
+    lens, n = np.array([3, 9]), np.array([5, 2])
+    q = r.standard_normal((B, Hq, S, D))
+    k, v = r.standard_normal((B, Hkv, S, D)), r.standard_normal((B, Hkv, S, D))
+    ks = np.full((Hkv, D), 0.02, np.float32)
+    vs = np.full((Hkv, D), 0.03, np.float32)
+    ck = np.full((B, Hkv, cap, D), 99, np.int8)
+    cv = np.full((B, Hkv, cap, D), 99, np.int8)
+    out = Q.attn_prefill_cached_int8(q, k, v, ck, cv, lens, ks, vs, chunk_lens=n)
+    for b in range(B):
+        P, m = int(lens[b]), int(n[b])
+        pos = P + np.arange(m)
+        kr = A.rope_rotate(k[b, :, :m], pos)
+        assert np.array_equal(ck[b, :, P:P + m], Q.int8_quantize(kr, ks[:, None, :]))
+        assert np.array_equal(cv[b, :, P:P + m], Q.int8_quantize(v[b, :, :m], vs[:, None, :]))
+        others = [t for t in range(cap) if not P <= t < P + m]
+        assert np.all(ck[b, :, others] == 99) and np.all(cv[b, :, others] == 99)
+        assert not np.any(out[b, :, m:])
+
+
+def _chunk_own_tokens_full_precision(q, k, v, ck, cv, lens, ks, vs, block_table=None,
+                                     chunk_lens=None):
+    """Planted mistake: the chunk attends to its own tokens at full precision
+    (only the prefix read from the cache), then stores their codes."""
+    B, Hq, S, D = q.shape
+    Hkv = k.shape[1]
+    out = np.zeros((B, Hq, S, D))
+    for b in range(B):
+        P = int(lens[b])
+        m = S if chunk_lens is None else int(chunk_lens[b])
+        if m == 0:
+            continue
+        pos = P + np.arange(m)
+        qr, kr = A.rope_rotate(q[b, :, :m], pos), A.rope_rotate(k[b, :, :m], pos)
+        for hq in range(Hq):
+            hk = hq // (Hq // Hkv)
+            if block_table is None:
+                pk = Q.int8_dequantize(ck[b, hk, :P], ks[hk][None])
+                pv = Q.int8_dequantize(cv[b, hk, :P], vs[hk][None])
+            else:
+                t = np.arange(P)
+                blk = block_table[b, t // 16]
+                pk = Q.int8_dequantize(ck[blk, hk, t % 16], ks[hk][None])
+                pv = Q.int8_dequantize(cv[blk, hk, t % 16], vs[hk][None])
+            keys = np.concatenate([pk, kr[hk]])
+            vals = np.concatenate([pv, v[b, hk, :m]])
+            out[b, hq, :m] = A.causal_attention(qr[hq], keys, vals, (pos, np.arange(P + m)),
+                                                1 / np.sqrt(D))
+        if block_table is None:
+            Q.kv_cache_append_int8(ck[b:b + 1], cv[b:b + 1], kr[None], v[b:b + 1, :, :m],
+                                   pos[None], ks, vs)
+        else:
+            Q.kv_cache_append_int8(ck, cv, kr[None], v[b:b + 1, :, :m], pos[None], ks, vs,
+                                   block_table=block_table[b:b + 1])
+    return out
+
+
+def _chunk_swapped_scales(q, k, v, ck, cv, lens, ks, vs, block_table=None, chunk_lens=None):
+    return Q.attn_prefill_cached_int8(q, k, v, ck, cv, lens, vs, ks, block_table=block_table,
+                                      chunk_lens=chunk_lens)
+
+
+@pytest.mark.parametrize("bad", [_chunk_own_tokens_full_precision, _chunk_swapped_scales])
+def test_int8_chunk_pins_catch_planted_mistakes(bad):
+    assert not (check_chunk_on_grid_equals_float_chunk(bad)
+                and check_one_token_chunk_is_a_decode_step(bad)
+                and check_chunk_equals_two_chunks(bad))
