@@ -265,6 +265,46 @@ def measure_chunked(car, W, dev, stream, new_event, iters: int = 100) -> dict:
     return out
 
 
+def measure_int8_chunk(car, W, dev, stream, new_event, iters: int = 100) -> dict:
+    """The contiguous chunk workload (1024 tokens after 3072 cached, 32 heads,
+    D = 128, bf16 q/k/v) over an INT8 cache [1, 32, 4096, 128] with
+    per-(head, channel) scales: attention kernel and whole call (chunk store
+    as codes, the rows dequantized to codes in bf16, attention)."""
+    import torch
+    P, S = 3072, 1024
+    case = W.chunk_case("chunk_int8", 1, 32, 32, S, 128, torch.bfloat16, [P], 571, dev,
+                        paged=False, max_seq=P + S)
+    ck = W.randcodes((1, 32, P + S, 128), dev, 572, 0)
+    cv = W.randcodes((1, 32, P + S, 128), dev, 572, 1)
+    cache = car.KVCache(ck, cv, k_scale=W.randscales((32, 128), dev, 572, 2),
+                        v_scale=W.randscales((32, 128), dev, 572, 3))
+    o = torch.empty_like(case.q)
+    ws = torch.empty(car.prefill_cached_workspace_bytes(torch.bfloat16, 1, 32, 128, P + S, cache),
+                     dtype=torch.uint8, device=dev)
+
+    def call(timing=None):
+        car.attn_prefill_cached(case.q, case.k, case.v, case.seq_lens, cache, P + S,
+                                case.theta, case.scale, out=o, timing=timing, workspace=ws)
+    for _ in range(3):
+        call()
+    pairs_k, pairs_c = timed_calls(car, call, stream, new_event, iters)
+    if not torch.isfinite(o.float()).all():
+        raise RuntimeError("non-finite output in the INT8 chunk")
+    ksp = spread([a.elapsed_time(b) for a, b in pairs_k])
+    csp = spread([a.elapsed_time(b) for a, b in pairs_c])
+    fl = chunk_flops(1, 32, P, S, 128)
+    return {"chunked_prefill_int8_contiguous": {
+        "workload": f"B=1,Hq=32,Hkv=32,D=128,cached={P},chunk={S},bf16 q/k/v, INT8 contiguous "
+                    "cache 4096 with per-(head, channel) scales",
+        "kernel_ms": sum(a.elapsed_time(b) for a, b in pairs_k) / iters,
+        "call_ms": sum(a.elapsed_time(b) for a, b in pairs_c) / iters,
+        "kernel_spread_ms": ksp, "call_spread_ms": csp,
+        "TFLOPs_kernel_median": fl / (ksp["median"] * 1e-3) / 1e12,
+        "TFLOPs_call_median": fl / (csp["median"] * 1e-3) / 1e12,
+        "mfma_frac_kernel_median": fl / (ksp["median"] * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
+        "per_launch": f"{fl} flops (4*B*H*D*(S*P + S(S+1)/2))"}}
+
+
 def measure_int8_decode(car, W, dev, stream, new_event, iters: int = 100) -> dict:
     """The two decode workloads with INT8 caches of the same shapes (codes in
     [-127, 127], per-(KV head, channel) fp32 scales): event times of the
@@ -619,6 +659,7 @@ def main(argv=None) -> int:
     if args.only is None and not args.no_extras:
         extras = measure_chunked(car, W, dev, stream, new_event, n_stat)
         extras.update(measure_int8_decode(car, W, dev, stream, new_event, n_stat))
+        extras.update(measure_int8_chunk(car, W, dev, stream, new_event, n_stat))
         extras.update(measure_small_prefills(car, W, dev, stream, new_event, n_stat))
         extras.update(measure_varlen_prefill(car, W, dev, stream, new_event, n_stat))
         extras.update(measure_rope_append(car, pf, dev, stream, new_event, n_stat))

@@ -27,7 +27,8 @@ __all__ = [
     "CarError", "KVCache", "rope_apply", "kv_cache_append", "attn_prefill", "attn_decode",
     "attn_prefill_cached", "kv_int8_calibrate",
     "attn_decode_noalloc", "DECODE_NOALLOC_MAX_BYTES",
-    "prefill_workspace_bytes", "decode_workspace_bytes", "library_path",
+    "prefill_workspace_bytes", "prefill_cached_workspace_bytes", "decode_workspace_bytes",
+    "library_path",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -90,7 +91,7 @@ def _load() -> ctypes.CDLL:
     prefill = [vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, vp, vp, f32, i32, f32, cache_p, vp,
                sz, vp]
     cached = [vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, vp, vp, i32, f32, i32, f32, cache_p,
-              vp]
+              vp, sz, vp]
     decode = [vp, vp, vp, vp, i32, i32, i32, i32, i32, vp, i32, f32, i32, f32, cache_p, vp, sz,
               vp]
     sigs = {
@@ -104,6 +105,7 @@ def _load() -> ctypes.CDLL:
         "car_attn_prefill_cached": (i32, cached),
         "car_attn_prefill_cached_timed": (i32, cached + [vp, vp]),
         "car_attn_decode_workspace_bytes": (sz, [i32, i32, i32, i32]),
+        "car_attn_prefill_cached_workspace_bytes": (sz, [i32, i32, i32, i32, i32, cache_p]),
         "car_attn_decode": (i32, decode),
         "car_attn_decode_timed": (i32, decode + [vp, vp]),
         "car_attn_decode_noalloc": (i32, decode[:15] + [vp]),
@@ -325,6 +327,15 @@ def prefill_workspace_bytes(dtype: torch.dtype, B: int, Hkv: int, S: int, D: int
     return int(_lib.car_attn_prefill_workspace_bytes(_DTYPES[dtype], B, Hkv, S, D, None))
 
 
+def prefill_cached_workspace_bytes(dtype: torch.dtype, B: int, Hkv: int, D: int,
+                                   max_seq_len: int, cache: KVCache) -> int:
+    """Workspace of attn_prefill_cached: 0 for a native cache, the dequantized
+    rows for an INT8 one."""
+    c = cache._c()
+    return int(_lib.car_attn_prefill_cached_workspace_bytes(_DTYPES[dtype], B, Hkv, D,
+                                                            max_seq_len, ctypes.byref(c)))
+
+
 def decode_workspace_bytes(B: int, Hq: int, D: int, max_seq_len: int) -> int:
     return int(_lib.car_attn_decode_workspace_bytes(B, Hq, D, max_seq_len))
 
@@ -410,7 +421,8 @@ def attn_prefill_cached(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
                         theta: float = 10000.0, scale: Optional[float] = None,
                         out: Optional[torch.Tensor] = None,
                         chunk_lens: Optional[torch.Tensor] = None,
-                        rope_pairing: str = "adjacent", timing=None) -> torch.Tensor:
+                        rope_pairing: str = "adjacent", timing=None,
+                        workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
     """A prompt chunk continuing a cached prefix (see car_attn_prefill_cached).
 
     q [B, Hq, S, D]; k, v [B, Hkv, S, D] (k not rotated); seq_lens int32 [B]
@@ -419,6 +431,7 @@ def attn_prefill_cached(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
     chunk_lens[b] rows, the rest is padding (zero output rows);
     ``max_seq_len`` is a host bound on seq_lens + chunk length.  Writes the
     chunk's keys and values into the cache and returns out [B, Hq, S, D].
+    An INT8 cache needs a workspace (allocated here unless given).
     """
     _need(q, "q", dim=4)
     _need(k, "k", dtype=q.dtype, dim=4, device=q.device)
@@ -447,9 +460,17 @@ def attn_prefill_cached(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
     if scale is None:
         scale = 1.0 / math.sqrt(D)
     c = cache._c()
+    need = int(_lib.car_attn_prefill_cached_workspace_bytes(_dtype_code(q), B, Hkv, D,
+                                                            int(max_seq_len), ctypes.byref(c)))
+    if need == 0 and workspace is None:
+        ws, ws_bytes = None, 0
+    else:
+        ws = _workspace(need, q.device, workspace)
+        ws_bytes = ws.numel() * ws.element_size()
     args = [_ptr(q), _ptr(k), _ptr(v), _ptr(out), _dtype_code(q), B, Hq, Hkv, S, D,
             _ptr(seq_lens), _ptr(chunk_lens), int(max_seq_len), float(theta),
-            _pairing(rope_pairing), float(scale), ctypes.byref(c), _stream(q)]
+            _pairing(rope_pairing), float(scale), ctypes.byref(c), _ptr(ws), ws_bytes,
+            _stream(q)]
     ev = _events(timing)
     if ev is None:
         _check(_lib.car_attn_prefill_cached(*args), "attn_prefill_cached")

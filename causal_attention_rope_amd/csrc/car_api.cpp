@@ -90,6 +90,13 @@ int decode_nsplit(int max_seq_len) { return (max_seq_len + DECODE_SPLIT - 1) / D
 
 bool is_int8(const car_kv_cache* c) { return c != nullptr && c->format == CAR_CACHE_INT8; }
 
+// A chunk over an INT8 cache: bytes of one dequantized copy (K or V) of
+// [B, Hkv, max_seq_len, D] in the call's dtype, rounded up to 256 bytes.
+int64_t chunk_dequant_half_bytes(car_dtype dt, int B, int Hkv, int D, int max_seq_len) {
+  const int64_t n = (int64_t)B * Hkv * max_seq_len * D * (int64_t)elem_bytes(dt);
+  return (n + 255) / 256 * 256;
+}
+
 }  // namespace
 
 extern "C" {
@@ -224,12 +231,20 @@ car_status car_attn_prefill(const void* q, const void* k, const void* v, void* o
                                 nullptr, nullptr);
 }
 
+size_t car_attn_prefill_cached_workspace_bytes(car_dtype dtype, int B, int Hkv, int D,
+                                               int max_seq_len, const car_kv_cache* cache) {
+  if (!dtype_ok(dtype) || !head_dim_ok(D) || B < 0 || Hkv < 0 || max_seq_len < 0) return 0;
+  if (!is_int8(cache)) return 0;
+  return 2 * (size_t)chunk_dequant_half_bytes(dtype, B, Hkv, D, max_seq_len);
+}
+
 car_status car_attn_prefill_cached_timed(const void* q, const void* k, const void* v,
                                          void* out, car_dtype dtype, int B, int Hq, int Hkv,
                                          int S, int D, const int32_t* seq_lens,
                                          const int32_t* chunk_lens, int max_seq_len,
                                          float theta, car_rope_pairing pairing, float scale,
-                                         const car_kv_cache* cache, hipStream_t stream,
+                                         const car_kv_cache* cache, void* workspace,
+                                         size_t workspace_bytes, hipStream_t stream,
                                          hipEvent_t kernel_start, hipEvent_t kernel_stop) {
   if (!dtype_ok(dtype) || !head_dim_ok(D) || !pairing_ok(pairing)) return CAR_ERR_UNSUPPORTED;
   if (cache != nullptr && cache->block_table != nullptr && cache->block_size != 16)
@@ -246,23 +261,49 @@ car_status car_attn_prefill_cached_timed(const void* q, const void* k, const voi
   int64_t cap = 0;
   const car_status cs = check_cache(cache, &c, &cap);
   if (cs != CAR_OK) return cs;
-  if (is_int8(cache)) return CAR_ERR_UNSUPPORTED;  // the chunk kernel reads a native cache
   // every sequence's chunk fits: S tokens, or up to S with chunk_lens
   if (max_seq_len < (chunk_lens == nullptr ? S : 1) || max_seq_len > cap)
     return CAR_ERR_INVALID_ARGUMENT;
-  // launch grids (fp32: B and Hq in grid y, z; bf16: query-tile pairs x B x Hq
-  // in x) and 32-bit byte offsets within one head of a contiguous cache
-  if (B > 65535 || Hq > 65535 || (int64_t)B * Hq * ((S + 511) / 512) > INT32_MAX ||
+  // launch grids (fp32: B and Hq in grid y, z; bf16: query tiles of at least
+  // 64 rows x B x Hq in x) and 32-bit byte offsets within one head of a
+  // contiguous cache
+  if (B > 65535 || Hq > 65535 || (int64_t)B * Hq * ((S + 63) / 64) > INT32_MAX ||
       cap * D * 4 > (int64_t)UINT32_MAX)
     return CAR_ERR_UNSUPPORTED;
+  const bool i8 = is_int8(cache);
+  if (i8) {
+    const size_t need = car_attn_prefill_cached_workspace_bytes(dtype, B, Hkv, D, max_seq_len,
+                                                                cache);
+    if (workspace == nullptr || !aligned16(workspace) || workspace_bytes < need)
+      return CAR_ERR_WORKSPACE;
+  }
 
   const Dtype dt = dtype == CAR_DTYPE_F32 ? F32 : BF16;
   const RopeFreq fr = make_freq(D, theta, pairing);
   const bool paged = cache->block_table != nullptr;
-  hipError_t e =
-      launch_chunk_prep(dt, D, paged, c, k, v, B, Hkv, S, seq_lens, chunk_lens, fr, stream);
+  hipError_t e = launch_chunk_prep(dt, D, paged, i8, c, k, v, B, Hkv, S, seq_lens, chunk_lens,
+                                   fr, stream);
   if (e != hipSuccess) return CAR_ERR_HIP;
-  return from_hip(launch_prefill_cached(dt, D, paged, q, out, B, Hq, Hkv, S, c, seq_lens,
+  if (!i8)
+    return from_hip(launch_prefill_cached(dt, D, paged, q, out, B, Hq, Hkv, S, c, seq_lens,
+                                          chunk_lens, fr, scale, stream,
+                                          timed(kernel_start, kernel_stop)));
+  // INT8: the rows the chunk attends to, copied into the workspace and read
+  // by the same attention kernel as a contiguous cache of max_seq_len slots:
+  // dequantized values for fp32; for bf16 the codes, with the scales passed
+  // on for the kernel to apply
+  CacheArgs dq{};
+  dq.k = workspace;
+  dq.v = static_cast<char*>(workspace) + chunk_dequant_half_bytes(dtype, B, Hkv, D, max_seq_len);
+  dq.max_seq = max_seq_len;
+  if (dt == BF16) {
+    dq.k_scale = c.k_scale;
+    dq.v_scale = c.v_scale;
+  }
+  e = launch_int8_dequant(dt, D, paged, c, dq.k, dq.v, B, Hkv, S, max_seq_len, seq_lens,
+                          chunk_lens, stream);
+  if (e != hipSuccess) return CAR_ERR_HIP;
+  return from_hip(launch_prefill_cached(dt, D, false, q, out, B, Hq, Hkv, S, dq, seq_lens,
                                         chunk_lens, fr, scale, stream,
                                         timed(kernel_start, kernel_stop)));
 }
@@ -271,10 +312,11 @@ car_status car_attn_prefill_cached(const void* q, const void* k, const void* v, 
                                    car_dtype dtype, int B, int Hq, int Hkv, int S, int D,
                                    const int32_t* seq_lens, const int32_t* chunk_lens,
                                    int max_seq_len, float theta, car_rope_pairing pairing,
-                                   float scale, const car_kv_cache* cache, hipStream_t stream) {
+                                   float scale, const car_kv_cache* cache, void* workspace,
+                                   size_t workspace_bytes, hipStream_t stream) {
   return car_attn_prefill_cached_timed(q, k, v, out, dtype, B, Hq, Hkv, S, D, seq_lens,
                                        chunk_lens, max_seq_len, theta, pairing, scale, cache,
-                                       stream, nullptr, nullptr);
+                                       workspace, workspace_bytes, stream, nullptr, nullptr);
 }
 
 size_t car_attn_decode_workspace_bytes(int B, int Hq, int D, int max_seq_len) {

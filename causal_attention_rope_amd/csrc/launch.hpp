@@ -72,10 +72,20 @@ hipError_t launch_int8_calibrate(Dtype dt, int D, const void* k, const void* v, 
                                  float* k_scale, float* v_scale, hipStream_t s);
 
 // A chunk continuing a cached prefix (P = seq_lens[b] tokens): rotates k at
-// positions P..P+S-1 and stores the rotated keys and raw values there.
-hipError_t launch_chunk_prep(Dtype dt, int D, bool paged, const CacheArgs& c, const void* k,
-                             const void* v, int B, int Hkv, int S, const int32_t* seq_lens,
-                             const int32_t* chunk_lens, const RopeFreq& fr, hipStream_t s);
+// positions P..P+S-1 and stores the rotated keys and raw values there (as
+// int8 codes if i8).
+hipError_t launch_chunk_prep(Dtype dt, int D, bool paged, bool i8, const CacheArgs& c,
+                             const void* k, const void* v, int B, int Hkv, int S,
+                             const int32_t* seq_lens, const int32_t* chunk_lens,
+                             const RopeFreq& fr, hipStream_t s);
+
+// Rows 0..P+n-1 of each sequence of an INT8 cache, dequantized into dense
+// [B, Hkv, max_seq, D] arrays dk, dv of the call's dtype, for the chunk
+// attention to read as a contiguous cache of max_seq slots.
+hipError_t launch_int8_dequant(Dtype dt, int D, bool paged, const CacheArgs& c, void* dk,
+                               void* dv, int B, int Hkv, int S, int max_seq,
+                               const int32_t* seq_lens, const int32_t* chunk_lens,
+                               hipStream_t s);
 
 // ---- prefill.hip -----------------------------------------------------------
 // kcache (nullable; bf16 only): the contiguous cache that the K pass filled
@@ -90,6 +100,8 @@ hipError_t launch_prefill_attention(Dtype dt, int D, const void* q, const void* 
 
 // Attention of a chunk over cache rows 0..P+S-1 (after launch_chunk_prep).
 // chunk_lens (nullable): tokens of each sequence's chunk; the rest is padding.
+// bf16 with a contiguous c whose k_scale is set: c holds INT8 codes as bf16
+// (launch_int8_dequant) and the kernel applies the scales.
 hipError_t launch_prefill_cached(Dtype dt, int D, bool paged, const void* q, void* out, int B,
                                  int Hq, int Hkv, int S, const CacheArgs& c,
                                  const int32_t* seq_lens, const int32_t* chunk_lens,

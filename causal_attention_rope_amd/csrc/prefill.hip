@@ -39,6 +39,9 @@ namespace {
 constexpr int KEYS_PROMPT = 0;  // the prompt's own K' and V, [B, Hkv, S, D]
 constexpr int KEYS_CONTIG = 1;  // a contiguous cache holding the prefix and the chunk
 constexpr int KEYS_PAGED = 2;   // a paged cache holding the prefix and the chunk
+// (bf16 only) a contiguous array of INT8 codes as bf16, the rows of an INT8
+// cache, with the cache's per-(KV head, channel) scales in c.k_scale, c.v_scale
+constexpr int KEYS_CODES = 3;
 
 // Tokens of sequence b's prompt or chunk: S, or with per-sequence lengths
 // (a padded batch of prompts or chunks of different lengths) lens[b]; rows
@@ -333,9 +336,12 @@ __global__ __launch_bounds__((Tile<D, 8>::THREADS), 2) void prefill_bf16_kernel(
   const int Sb = chunk_len<SRC>(chunk_lens, b, S);  // query rows >= Sb are padding
   const int P = chunk_start<SRC>(c, seq_lens, b, Sb);
   const int nkeys = P + Sb;
+  // Keys and values that are INT8 codes: the key scales go into the query
+  // and the value scales into the output, both in fp32.
+  constexpr bool codes = SRC == KEYS_CODES;
   const bf16_t* kbase = nullptr;  // the head's key rows (paged: per block, below)
   const bf16_t* vbase = nullptr;
-  if constexpr (SRC == KEYS_CONTIG) {
+  if constexpr (SRC == KEYS_CONTIG || SRC == KEYS_CODES) {
     kbase = static_cast<const bf16_t*>(c.k) + ((int64_t)b * Hkv + hk) * c.max_seq * D;
     vbase = static_cast<const bf16_t*>(c.v) + ((int64_t)b * Hkv + hk) * c.max_seq * D;
   } else if constexpr (SRC == KEYS_PROMPT) {
@@ -477,6 +483,10 @@ __global__ __launch_bounds__((Tile<D, 8>::THREADS), 2) void prefill_bf16_kernel(
         float f[8];
         load16<bf16_t>(qp + d0, f);
         rope_rotate_chunk<bf16_t, 8, HALF>(f, qp, d0, D, pos, fr);
+        if constexpr (codes) {  // keys are codes: q'.(code * s) = (q' * s).code
+  #pragma unroll
+          for (int e = 0; e < 8; ++e) f[e] *= c.k_scale[hk * D + d0 + e];
+        }
         const u32x4_t u = {cvt_pk_bf16(f[0], f[1]), cvt_pk_bf16(f[2], f[3]),
                            cvt_pk_bf16(f[4], f[5]), cvt_pk_bf16(f[6], f[7])};
         qf[ks] = __builtin_bit_cast(bf16x8_t, u);
@@ -729,9 +739,16 @@ __global__ __launch_bounds__((Tile<D, 8>::THREADS), 2) void prefill_bf16_kernel(
       for (int db = 0; db < C::NDB; ++db)
   #pragma unroll
         for (int r4 = 0; r4 < 4; ++r4) {
+          float o[4];
+  #pragma unroll
+          for (int j = 0; j < 4; ++j) o[j] = oacc[db][4 * r4 + j] * inv;
+          if constexpr (codes) {  // values are codes: sum p * (code * s) = s * sum p * code
+  #pragma unroll
+            for (int j = 0; j < 4; ++j) o[j] *= c.v_scale[hk * D + db * 32 + 8 * r4 + 4 * g + j];
+          }
           u32x2_t u;
-          u[0] = cvt_pk_bf16(oacc[db][4 * r4] * inv, oacc[db][4 * r4 + 1] * inv);
-          u[1] = cvt_pk_bf16(oacc[db][4 * r4 + 2] * inv, oacc[db][4 * r4 + 3] * inv);
+          u[0] = cvt_pk_bf16(o[0], o[1]);
+          u[1] = cvt_pk_bf16(o[2], o[3]);
           if (pad) u = u32x2_t{0u, 0u};
           *reinterpret_cast<u32x2_t*>(op + db * 32 + 8 * r4 + 4 * g) = u;
         }
@@ -843,6 +860,17 @@ hipError_t launch_prefill_cached(Dtype dt, int D, bool paged, const void* q, voi
                                  const RopeFreq& fr, float scale, hipStream_t s,
                                  const TimedLaunch& tl) {
   const KeySource ks{nullptr, nullptr, c, seq_lens, chunk_lens};
+  if (dt == BF16 && !paged && c.k_scale != nullptr) {  // a dense copy of INT8 codes
+    if (D == 64)
+      return fr.half ? prefill_bf16_t<64, KEYS_CODES, 1>(q, ks, out, B, Hq, Hkv, S, nullptr, fr,
+                                                         scale, s, tl)
+                     : prefill_bf16_t<64, KEYS_CODES, 0>(q, ks, out, B, Hq, Hkv, S, nullptr, fr,
+                                                         scale, s, tl);
+    return fr.half ? prefill_bf16_t<128, KEYS_CODES, 1>(q, ks, out, B, Hq, Hkv, S, nullptr, fr,
+                                                        scale, s, tl)
+                   : prefill_bf16_t<128, KEYS_CODES, 0>(q, ks, out, B, Hq, Hkv, S, nullptr, fr,
+                                                        scale, s, tl);
+  }
   return paged ? prefill_dispatch<KEYS_PAGED>(dt, D, q, ks, out, B, Hq, Hkv, S, nullptr, fr,
                                               scale, s, tl)
                : prefill_dispatch<KEYS_CONTIG>(dt, D, q, ks, out, B, Hq, Hkv, S, nullptr, fr,

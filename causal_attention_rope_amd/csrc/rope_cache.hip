@@ -148,7 +148,8 @@ __global__ __launch_bounds__(kThreads) void prefill_prep_kernel(
 // chunk that does not fit the cache is not stored (the attention kernel then
 // reads clamped rows and its output is unspecified).
 // With chunk_lens, tokens s >= chunk_lens[b] are padding and are not stored.
-template <typename T, int D, bool PAGED>
+// I8: an INT8 cache; the fp32 rotated key and the value are stored as codes.
+template <typename T, int D, bool PAGED, bool I8>
 __global__ __launch_bounds__(kThreads) void chunk_prep_kernel(
     CacheArgs c, const T* __restrict__ k, const T* __restrict__ v, int Hkv, int S,
     const int32_t* __restrict__ seq_lens, const int32_t* __restrict__ chunk_lens, int64_t nvec,
@@ -173,9 +174,69 @@ __global__ __launch_bounds__(kThreads) void chunk_prep_kernel(
     load16<T>(k + row * D + col, f);
     rope_rotate_chunk<T, N>(f, k + row * D, col, D, pos, fr);
     const int64_t dst = cache_row<PAGED>(c, b, hk, Hkv, pos) * D + col;
-    store16<T>(static_cast<T*>(c.k) + dst, f);
-    *reinterpret_cast<uint4*>(static_cast<T*>(c.v) + dst) =
-        *reinterpret_cast<const uint4*>(v + row * D + col);
+    if constexpr (I8) {
+      float vf[N];
+      load16<T>(v + row * D + col, vf);
+      store_int8<N>(static_cast<int8_t*>(c.k) + dst, f, c.k_scale + hk * D + col);
+      store_int8<N>(static_cast<int8_t*>(c.v) + dst, vf, c.v_scale + hk * D + col);
+    } else {
+      store16<T>(static_cast<T*>(c.k) + dst, f);
+      *reinterpret_cast<uint4*>(static_cast<T*>(c.v) + dst) =
+          *reinterpret_cast<const uint4*>(v + row * D + col);
+    }
+  }
+}
+
+// A chunk over an INT8 cache reads its keys and values through a dense copy:
+// rows 0..P+n-1 of each sequence into contiguous [B, Hkv, max_seq, D] arrays
+// dk, dv, which the chunk attention kernel then reads as its cache.  fp32:
+// the dequantized values code * scale.  bf16: the codes themselves, exact in
+// bf16 (integers of magnitude <= 127); the bf16 attention kernel applies the
+// scales in fp32 instead (k_scale to the query, v_scale to the output), so
+// that no dequantized value is rounded to bf16.  n is the chunk length
+// (chunk_lens[b] or S) and P = seq_lens[b] lowered so that P + n <= max_seq:
+// the same rows the attention kernel takes for a cache of max_seq slots.
+// Rows from P+n on are not written (the attention never reads them).
+template <typename T, int D, bool PAGED>
+__global__ __launch_bounds__(kThreads) void int8_dequant_rows_kernel(
+    CacheArgs c, T* __restrict__ dk, T* __restrict__ dv, int Hkv, int S, int max_seq,
+    const int32_t* __restrict__ seq_lens, const int32_t* __restrict__ chunk_lens,
+    int64_t nvec) {
+  constexpr int N = Vec16<T>::N;  // elements per 16 bytes of T (4 or 8 codes)
+  constexpr int VPR = D / N;
+  for (int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x; i < nvec;
+       i += (int64_t)gridDim.x * kThreads) {
+    const int64_t row = i / VPR;  // (b*Hkv + hk)*max_seq + t
+    const int col = (int)(i % VPR) * N;
+    const int t = (int)(row % max_seq);
+    const int64_t bh = row / max_seq;
+    const int hk = (int)(bh % Hkv);
+    const int b = (int)(bh / Hkv);
+    const int n = chunk_lens == nullptr ? S : min(max(chunk_lens[b], 0), S);
+    const int P = max(min(max(seq_lens[b], 0), max_seq - n), 0);
+    if (t >= P + n) continue;
+    const int64_t src = cache_row<PAGED>(c, b, hk, Hkv, t) * D + col;
+    uint32_t wk[N / 4], wv[N / 4];
+    if constexpr (N == 4) {
+      wk[0] = *reinterpret_cast<const uint32_t*>(static_cast<const int8_t*>(c.k) + src);
+      wv[0] = *reinterpret_cast<const uint32_t*>(static_cast<const int8_t*>(c.v) + src);
+    } else {
+      const uint2 a = *reinterpret_cast<const uint2*>(static_cast<const int8_t*>(c.k) + src);
+      const uint2 e = *reinterpret_cast<const uint2*>(static_cast<const int8_t*>(c.v) + src);
+      wk[0] = a.x, wk[1] = a.y, wv[0] = e.x, wv[1] = e.y;
+    }
+    float fk[N], fv[N];
+#pragma unroll
+    for (int j = 0; j < N; ++j) {
+      fk[j] = int8_elem(wk[j / 4], j % 4);
+      fv[j] = int8_elem(wv[j / 4], j % 4);
+      if constexpr (sizeof(T) == 4) {
+        fk[j] *= c.k_scale[hk * D + col + j];
+        fv[j] *= c.v_scale[hk * D + col + j];
+      }
+    }
+    store16<T>(dk + row * D + col, fk);
+    store16<T>(dv + row * D + col, fv);
   }
 }
 
@@ -332,33 +393,69 @@ hipError_t prefill_prep_t(bool paged, const CacheArgs* cache, const void* k, con
 }
 
 template <typename T, int D>
-hipError_t chunk_prep_t(bool paged, const CacheArgs& c, const void* k, const void* v, int B,
-                        int Hkv, int S, const int32_t* seq_lens, const int32_t* chunk_lens,
-                        const RopeFreq& fr, hipStream_t st) {
+hipError_t chunk_prep_t(bool paged, bool i8, const CacheArgs& c, const void* k, const void* v,
+                        int B, int Hkv, int S, const int32_t* seq_lens,
+                        const int32_t* chunk_lens, const RopeFreq& fr, hipStream_t st) {
   const int64_t nvec = (int64_t)B * Hkv * S * (D / Vec16<T>::N);
   const T* kk = static_cast<const T*>(k);
   const T* vv = static_cast<const T*>(v);
+  const dim3 grid(grid_for(nvec)), block(kThreads);
+  if (i8) {
+    if (paged)
+      hipLaunchKernelGGL((chunk_prep_kernel<T, D, true, true>), grid, block, 0, st, c, kk, vv,
+                         Hkv, S, seq_lens, chunk_lens, nvec, fr);
+    else
+      hipLaunchKernelGGL((chunk_prep_kernel<T, D, false, true>), grid, block, 0, st, c, kk, vv,
+                         Hkv, S, seq_lens, chunk_lens, nvec, fr);
+  } else if (paged) {
+    hipLaunchKernelGGL((chunk_prep_kernel<T, D, true, false>), grid, block, 0, st, c, kk, vv,
+                       Hkv, S, seq_lens, chunk_lens, nvec, fr);
+  } else {
+    hipLaunchKernelGGL((chunk_prep_kernel<T, D, false, false>), grid, block, 0, st, c, kk, vv,
+                       Hkv, S, seq_lens, chunk_lens, nvec, fr);
+  }
+  return hipGetLastError();
+}
+
+template <typename T, int D>
+hipError_t int8_dequant_t(bool paged, const CacheArgs& c, void* dk, void* dv, int B, int Hkv,
+                          int S, int max_seq, const int32_t* seq_lens,
+                          const int32_t* chunk_lens, hipStream_t st) {
+  const int64_t nvec = (int64_t)B * Hkv * max_seq * (D / Vec16<T>::N);
+  const dim3 grid(grid_for(nvec)), block(kThreads);
   if (paged)
-    hipLaunchKernelGGL((chunk_prep_kernel<T, D, true>), dim3(grid_for(nvec)), dim3(kThreads), 0,
-                       st, c, kk, vv, Hkv, S, seq_lens, chunk_lens, nvec, fr);
+    hipLaunchKernelGGL((int8_dequant_rows_kernel<T, D, true>), grid, block, 0, st, c,
+                       static_cast<T*>(dk), static_cast<T*>(dv), Hkv, S, max_seq, seq_lens,
+                       chunk_lens, nvec);
   else
-    hipLaunchKernelGGL((chunk_prep_kernel<T, D, false>), dim3(grid_for(nvec)), dim3(kThreads), 0,
-                       st, c, kk, vv, Hkv, S, seq_lens, chunk_lens, nvec, fr);
+    hipLaunchKernelGGL((int8_dequant_rows_kernel<T, D, false>), grid, block, 0, st, c,
+                       static_cast<T*>(dk), static_cast<T*>(dv), Hkv, S, max_seq, seq_lens,
+                       chunk_lens, nvec);
   return hipGetLastError();
 }
 
 }  // namespace
 
-hipError_t launch_chunk_prep(Dtype dt, int D, bool paged, const CacheArgs& c, const void* k,
-                             const void* v, int B, int Hkv, int S, const int32_t* seq_lens,
-                             const int32_t* chunk_lens, const RopeFreq& fr, hipStream_t s) {
-  if (dt == F32)
-    return D == 64 ? chunk_prep_t<float, 64>(paged, c, k, v, B, Hkv, S, seq_lens, chunk_lens, fr, s)
-                   : chunk_prep_t<float, 128>(paged, c, k, v, B, Hkv, S, seq_lens, chunk_lens, fr,
-                                              s);
-  return D == 64 ? chunk_prep_t<bf16_t, 64>(paged, c, k, v, B, Hkv, S, seq_lens, chunk_lens, fr, s)
-                 : chunk_prep_t<bf16_t, 128>(paged, c, k, v, B, Hkv, S, seq_lens, chunk_lens, fr,
-                                             s);
+hipError_t launch_chunk_prep(Dtype dt, int D, bool paged, bool i8, const CacheArgs& c,
+                             const void* k, const void* v, int B, int Hkv, int S,
+                             const int32_t* seq_lens, const int32_t* chunk_lens,
+                             const RopeFreq& fr, hipStream_t s) {
+#define CAR_CHUNK(T, DD) \
+  chunk_prep_t<T, DD>(paged, i8, c, k, v, B, Hkv, S, seq_lens, chunk_lens, fr, s)
+  if (dt == F32) return D == 64 ? CAR_CHUNK(float, 64) : CAR_CHUNK(float, 128);
+  return D == 64 ? CAR_CHUNK(bf16_t, 64) : CAR_CHUNK(bf16_t, 128);
+#undef CAR_CHUNK
+}
+
+hipError_t launch_int8_dequant(Dtype dt, int D, bool paged, const CacheArgs& c, void* dk,
+                               void* dv, int B, int Hkv, int S, int max_seq,
+                               const int32_t* seq_lens, const int32_t* chunk_lens,
+                               hipStream_t s) {
+#define CAR_DEQ(T, DD) \
+  int8_dequant_t<T, DD>(paged, c, dk, dv, B, Hkv, S, max_seq, seq_lens, chunk_lens, s)
+  if (dt == F32) return D == 64 ? CAR_DEQ(float, 64) : CAR_DEQ(float, 128);
+  return D == 64 ? CAR_DEQ(bf16_t, 64) : CAR_DEQ(bf16_t, 128);
+#undef CAR_DEQ
 }
 
 hipError_t launch_rope_apply(Dtype dt, int D, void* x, int B, int H, int S,

@@ -99,9 +99,7 @@ typedef CAR_ENUM(car_rope_pairing) {
  *     with x / s one IEEE fp32 division, ties rounded away from zero, and
  *     code 0 where s == 0; the cached value is code * s.  Keys are quantized
  *     from their fp32 rotated values.  car_kv_int8_calibrate computes the
- *     scales.  car_kv_cache_append, car_attn_prefill (its cache store) and
- *     car_attn_decode accept an INT8 cache; car_attn_prefill_cached returns
- *     CAR_ERR_UNSUPPORTED for one.
+ *     scales.  Every call that takes a cache accepts an INT8 one.
  */
 typedef CAR_ENUM(car_cache_format) {
   CAR_CACHE_NATIVE = 0,
@@ -271,19 +269,34 @@ car_status car_attn_prefill(const void* q, const void* k, const void* v, void* o
  *                to, and their output rows are written as zeros.
  *   max_seq_len  host bound on seq_lens[b] + (chunk length) over the batch; at
  *                most the cache capacity, and at least S when chunk_lens is NULL.
- *   cache        contiguous or paged, native format (an INT8 cache returns
- *                CAR_ERR_UNSUPPORTED); rows 0..P-1 must hold the prefix (as
- *                written by earlier calls), rows P..P+S-1 are written.
- * No workspace: the keys are rotated straight into the cache.  S == 0 or an
- * empty batch is a no-op returning CAR_OK.  Sizes one launch cannot cover
- * return CAR_ERR_UNSUPPORTED.
+ *   cache        contiguous or paged, native or INT8; rows 0..P-1 must hold the
+ *                prefix (as written by earlier calls), rows P..P+S-1 are written.
+ *                With an INT8 cache the chunk's keys and values are stored as
+ *                codes first, and every key and value the chunk attends to,
+ *                its own tokens included, is read back dequantized (code *
+ *                scale), as a decode step reads its new token.
+ *   workspace    native cache: unused (may be NULL).  INT8 cache: device scratch
+ *                of at least car_attn_prefill_cached_workspace_bytes(), which
+ *                receives the dequantized rows; contents on entry ignored, on
+ *                exit unspecified.
+ * S == 0 or an empty batch is a no-op returning CAR_OK.  Sizes one launch
+ * cannot cover return CAR_ERR_UNSUPPORTED.
  */
 car_status car_attn_prefill_cached(const void* q, const void* k, const void* v, void* out,
                                    car_dtype dtype, int B, int Hq, int Hkv, int S, int D,
                                    const int32_t* seq_lens, const int32_t* chunk_lens,
                                    int max_seq_len, float theta, car_rope_pairing pairing,
-                                   float scale,
-                                   const car_kv_cache* cache, hipStream_t stream);
+                                   float scale, const car_kv_cache* cache, void* workspace,
+                                   size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * Bytes of device workspace car_attn_prefill_cached needs: 0 for a native
+ * cache; for an INT8 cache two dense copies (K and V) of [B, Hkv,
+ * max_seq_len, D] in `dtype`, each rounded up to 256 bytes.  Also 0 for
+ * invalid sizes.
+ */
+size_t car_attn_prefill_cached_workspace_bytes(car_dtype dtype, int B, int Hkv, int D,
+                                               int max_seq_len, const car_kv_cache* cache);
 
 /*
  * Bytes of device workspace car_attn_decode needs: per (sequence, query head)
@@ -344,7 +357,8 @@ car_status car_attn_prefill_cached_timed(const void* q, const void* k, const voi
                                          int S, int D, const int32_t* seq_lens,
                                          const int32_t* chunk_lens, int max_seq_len,
                                          float theta, car_rope_pairing pairing, float scale,
-                                         const car_kv_cache* cache, hipStream_t stream,
+                                         const car_kv_cache* cache, void* workspace,
+                                         size_t workspace_bytes, hipStream_t stream,
                                          hipEvent_t kernel_start, hipEvent_t kernel_stop);
 car_status car_attn_decode_timed(const void* q, const void* k_new, const void* v_new,
                                  void* out, car_dtype dtype, int B, int Hq, int Hkv, int D,

@@ -167,13 +167,13 @@ def test_prefill_cached_rejects(car, lib):
     c = _cache(car, max_seq=512)
     args = dict(q=FAKE, k=FAKE, v=FAKE, out=FAKE, dt=BF16, B=2, Hq=8, Hkv=2, S=100, D=128,
                 lens=FAKE, clens=None, msl=300, theta=1e4, pair=0, scale=0.088,
-                cache=ctypes.byref(c))
+                cache=ctypes.byref(c), ws=None, wsb=0)
 
     def call(**kw):
         a = dict(args, **kw)
         return f(a["q"], a["k"], a["v"], a["out"], a["dt"], a["B"], a["Hq"], a["Hkv"], a["S"],
                  a["D"], a["lens"], a["clens"], a["msl"], a["theta"], a["pair"], a["scale"],
-                 a["cache"], None)
+                 a["cache"], a["ws"], a["wsb"], None)
 
     assert call(D=96) == UNSUPPORTED
     assert call(dt=7) == UNSUPPORTED
@@ -197,7 +197,8 @@ def test_prefill_cached_rejects(car, lib):
 
 def test_int8_cache_rejects(car, lib):
     """An INT8 cache needs both scale arrays, 16-byte aligned; an unknown
-    format is unsupported; the chunked prefill does not read INT8 caches."""
+    format is unsupported; a chunk over an INT8 cache needs its workspace
+    (two dequantized copies of [B, Hkv, max_seq_len, D])."""
     app = lib.car_kv_cache_append
     for c, want in ((_cache(car, fmt=1), INVALID),                          # no scales
                     (_cache(car, fmt=1, ks=FAKE), INVALID),                 # no v_scale
@@ -205,9 +206,18 @@ def test_int8_cache_rejects(car, lib):
                     (_cache(car, fmt=2, ks=FAKE, vs=FAKE), UNSUPPORTED)):   # unknown format
         assert app(ctypes.byref(c), BF16, FAKE, FAKE, 1, 1, 1, 64, FAKE, None) == want
     good = _cache(car, max_seq=512, fmt=1, ks=FAKE, vs=FAKE)
-    chunk = lib.car_attn_prefill_cached(FAKE, FAKE, FAKE, FAKE, BF16, 2, 8, 2, 100, 128, FAKE,
-                                        None, 300, 1e4, 0, 0.088, ctypes.byref(good), None)
-    assert chunk == UNSUPPORTED
+    need = lib.car_attn_prefill_cached_workspace_bytes(BF16, 2, 2, 128, 300, ctypes.byref(good))
+    assert need == 2 * 2 * 2 * 300 * 128 * 2
+    assert lib.car_attn_prefill_cached_workspace_bytes(F32, 2, 2, 128, 300,
+                                                       ctypes.byref(good)) == 2 * need
+    native = _cache(car, max_seq=512)
+    assert lib.car_attn_prefill_cached_workspace_bytes(BF16, 2, 2, 128, 300,
+                                                       ctypes.byref(native)) == 0
+    for ws, wsb in ((None, need), (FAKE, need - 1), (FAKE + 8, need)):
+        chunk = lib.car_attn_prefill_cached(FAKE, FAKE, FAKE, FAKE, BF16, 2, 8, 2, 100, 128, FAKE,
+                                            None, 300, 1e4, 0, 0.088, ctypes.byref(good), ws, wsb,
+                                            None)
+        assert chunk == WORKSPACE
     noscale = _cache(car, max_seq=512, fmt=1)
     dec = lib.car_attn_decode(FAKE, FAKE, FAKE, FAKE, BF16, 2, 8, 2, 128, FAKE, 300, 1e4, 0,
                               0.088, ctypes.byref(noscale), FAKE, 1 << 20, None)
@@ -308,7 +318,7 @@ def test_timed_variants_check_like_the_plain_calls(car, lib):
     assert lib.car_attn_prefill_timed(*pre, None, None) == UNSUPPORTED
     assert lib.car_attn_prefill(*pre) == UNSUPPORTED
     cached = (FAKE, FAKE, FAKE, FAKE, BF16, 1, 4, 3, 8, 128, FAKE, None, 64, 1e4, 0, 0.1,
-              ctypes.byref(c), None)
+              ctypes.byref(c), None, 0, None)
     assert lib.car_attn_prefill_cached_timed(*cached, None, None) == INVALID   # Hq % Hkv
     assert lib.car_attn_prefill_cached(*cached) == INVALID
 

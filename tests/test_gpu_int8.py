@@ -443,3 +443,107 @@ def test_paged_decode_workload_int8(car):
     log_case(case.name)
     order = np.argsort(case.lens_host)
     run_and_check(car, case, bsel=[int(order[0]), int(order[-1])], poison=False)
+
+
+# ==========================================================================
+# A chunk continuing a prefix held in an INT8 cache
+# ==========================================================================
+
+def int8_chunk_inputs(B, Hq, Hkv, S, D, dtype, lens, n, seed, paged, cap, unambiguous=True):
+    """Prefix codes, chunk q/k/v and per-(KV head, channel) scales.  With
+    ``unambiguous`` the seed is advanced until no chunk key's quotient lies
+    near a rounding tie, so the kernel's fp32 rotation stores exactly the
+    oracle's codes."""
+    for tries in range(64 if unambiguous else 1):
+        s = seed + 1000 * tries
+        q = W.randn((B, Hq, S, D), dtype, DEV, s, 0)
+        k = W.randn((B, Hkv, S, D), dtype, DEV, s, 1)
+        v = W.randn((B, Hkv, S, D), dtype, DEV, s, 2)
+        ks = W.randscales((Hkv, D), DEV, s, 3)   # [0.01, 0.03]: values within +-3.81,
+        vs = W.randscales((Hkv, D), DEV, s, 4)   # as in the decode tests
+        kr = np.concatenate([oracle.rope_rotate(f64(k[b, :, :n[b]]), lens[b] + np.arange(n[b]))
+                             for b in range(B)], axis=1)
+        if not unambiguous or not ambiguous(kr, f64(ks)[:, None, :]).any():
+            break
+    else:
+        raise AssertionError("no seed without an ambiguous key code")
+    if paged:
+        mbps = cap // 16
+        nb = B * mbps + 3
+        table = np.random.default_rng(seed).permutation(nb)[: B * mbps].reshape(B, mbps)
+        table = table.astype(np.int32)
+        shape = (nb, Hkv, 16, D)
+    else:
+        table = None
+        shape = (B, Hkv, cap, D)
+    ck = W.randcodes(shape, DEV, s, 5)
+    cv = W.randcodes(shape, DEV, s, 6)
+    return q, k, v, ks, vs, ck, cv, table
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16], ids=["f32", "bf16"])
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("paged", [False, True], ids=["contiguous", "paged"])
+def test_chunk_int8(car, dtype, D, paged):
+    """A padded batch of chunks (lengths 70, 1, 33 of S = 70) after cached
+    prefixes of 0, 37 and 100 tokens in an INT8 cache, 8 query heads on 2 KV
+    heads: outputs against the oracle's INT8 chunk (padding rows zero), the
+    chunk's codes stored exactly at P..P+n-1 and every other slot unchanged."""
+    B, Hq, Hkv, S, cap = 3, 8, 2, 70, 176
+    lens, n = [0, 37, 100], [70, 1, 33]
+    log_case(f"int8 chunk {dtype} D={D} paged={paged}")
+    q, k, v, ks, vs, ck, cv, table = int8_chunk_inputs(B, Hq, Hkv, S, D, dtype, lens, n,
+                                                       700 + D, paged, cap)
+    before_k, before_v = np_i8(ck), np_i8(cv)
+    cache = car.KVCache(ck, cv, None if table is None else torch.from_numpy(table).to(DEV),
+                        k_scale=ks, v_scale=vs)
+    seq_lens = torch.tensor(lens, dtype=torch.int32, device=DEV)
+    chunk_lens = torch.tensor(n, dtype=torch.int32, device=DEV)
+    out = car.attn_prefill_cached(q, k, v, seq_lens, cache, max(l + m for l, m in zip(lens, n)),
+                                  chunk_lens=chunk_lens)
+    torch.cuda.synchronize()
+    ok, ov = before_k.copy(), before_v.copy()
+    want = oracle.attn_prefill_cached_int8(f64(q), f64(k), f64(v), ok, ov, np.array(lens),
+                                           f64(ks), f64(vs), block_table=table,
+                                           chunk_lens=np.array(n))
+    err = max_abs(f64(out), want)
+    log_case(f"max-abs error {err:.3e}")
+    assert err <= TOL[dtype]
+    for b in range(B):
+        assert not out[b, :, n[b]:].float().any(), "padding rows"
+    assert np.array_equal(np_i8(ck), ok), "key codes"
+    assert np.array_equal(np_i8(cv), ov), "value codes"
+
+
+def test_chunk_int8_long_prefix_bf16(car):
+    """bf16 on the matrix cores over several key tiles: a 300-token chunk
+    after 1000 cached tokens, 16 query heads on 4 KV heads, D = 128, paged."""
+    B, Hq, Hkv, S, D, cap = 1, 16, 4, 300, 128, 1312
+    lens, n = [1000], [300]
+    log_case("int8 chunk bf16 long prefix")
+    q, k, v, ks, vs, ck, cv, table = int8_chunk_inputs(B, Hq, Hkv, S, D, torch.bfloat16, lens,
+                                                       n, 777, True, cap, unambiguous=False)
+    ok, ov = np_i8(ck), np_i8(cv)
+    cache = car.KVCache(ck, cv, torch.from_numpy(table).to(DEV), k_scale=ks, v_scale=vs)
+    out = car.attn_prefill_cached(q, k, v, torch.tensor(lens, dtype=torch.int32, device=DEV),
+                                  cache, 1300)
+    torch.cuda.synchronize()
+    want = oracle.attn_prefill_cached_int8(f64(q), f64(k), f64(v), ok, ov, np.array(lens),
+                                           f64(ks), f64(vs), block_table=table)
+    err = max_abs(f64(out), want)
+    log_case(f"max-abs error {err:.3e}")
+    assert err <= TOL[torch.bfloat16]
+    # value codes exact everywhere; key codes exact, or one apart at a rounding
+    # tie of a chunk token's rotated key (slots outside the chunk unchanged)
+    assert np.array_equal(np_i8(cv), ov)
+    t = lens[0] + np.arange(n[0])
+    blk, off = table[0, t // 16], t % 16
+    kr = oracle.rope_rotate(f64(k[0]), t)                       # [Hkv, n, D]
+    got_rows = np_i8(ck)[blk, :, off].transpose(1, 0, 2)        # [Hkv, n, D]
+    want_rows = ok[blk, :, off].transpose(1, 0, 2)
+    flips = check_key_codes(got_rows, want_rows, kr, f64(ks)[:, None, :])
+    log_case(f"key codes one apart at ties: {flips}")
+    rest_got, rest_want = np_i8(ck).copy(), ok.copy()
+    rest_got[blk, :, off] = 0
+    rest_want[blk, :, off] = 0
+    assert np.array_equal(rest_got, rest_want)
