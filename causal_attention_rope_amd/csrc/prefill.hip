@@ -472,16 +472,50 @@ __global__ __launch_bounds__((Tile<D, 8>::THREADS), 2) void prefill_bf16_kernel(
     }
     const int qrc = min(qrow, Sb - 1);
 
+    // ---- Q rows, raw: their loads are issued before the first tiles' ----
+    u32x4_t qraw[C::QKS];
+    const bf16_t* qp = q + ((int64_t)bh * S + qrc) * D;
+  #pragma unroll
+    for (int ks = 0; ks < C::QKS; ++ks)
+      qraw[ks] = *reinterpret_cast<const u32x4_t*>(qp + ks * 16 + g * 8);
+
+    const int q_end = min(q0 + C::BM, Sb);  // exclusive
+    const int ntiles = (P + q_end + C::BN - 1) / C::BN;
+    // tiles 0..wlast hold keys visible to this wave (uniform per wave)
+    const int wlast = min(ntiles - 1, (P + qw + 31) / C::BN);
+    // this wave's group walks tiles tbeg .. tbeg+tcnt-1; the lambdas below
+    // take the local index t - tbeg, which also picks the LDS buffers
+    const int nt0 = KSPLIT ? (ntiles + 1) >> 1 : ntiles;  // steps of the launch
+    const int tbeg = grp == 0 ? 0 : nt0;
+    const int tcnt = grp == 0 ? nt0 : ntiles - nt0;
+    const int ulast = min(wlast - tbeg, tcnt - 1);  // local index of the last visible tile
+
+    int ids_v = 0, ids_k = 0;
+    // first tiles K(0), V(0) and K(1), issued while the Q rows are in flight
+    if (tcnt > 0) {
+      const int ids0 = block_ids(tbeg * C::BN);
+      issue(krs, c.k, tbeg * C::BN, kbuf, ids0);
+      issue(vrs, c.v, tbeg * C::BN, vbuf, ids0);
+      if (tcnt > 1) {
+        ids_v = block_ids((tbeg + 1) * C::BN);
+        issue(krs, c.k, (tbeg + 1) * C::BN, kbuf + C::TILEB, ids_v);
+      }
+      if (tcnt > 2) ids_k = block_ids((tbeg + 2) * C::BN);
+    }
+
     // ---- Q fragments (B operand of S^T = K Q^T), rotated, bf16 ----
     bf16x8_t qf[C::QKS];
     {
-      const bf16_t* qp = q + ((int64_t)bh * S + qrc) * D;
       const int pos = SRC == KEYS_PROMPT ? positions[(int64_t)b * S + qrc] : P + qrc;
   #pragma unroll
       for (int ks = 0; ks < C::QKS; ++ks) {
         const int d0 = ks * 16 + g * 8;
         float f[8];
-        load16<bf16_t>(qp + d0, f);
+  #pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          f[2 * e] = bf16_lo(qraw[ks][e]);
+          f[2 * e + 1] = bf16_hi(qraw[ks][e]);
+        }
         rope_rotate_chunk<bf16_t, 8, HALF>(f, qp, d0, D, pos, fr);
         if constexpr (codes) {  // keys are codes: q'.(code * s) = (q' * s).code
   #pragma unroll
@@ -500,17 +534,6 @@ __global__ __launch_bounds__((Tile<D, 8>::THREADS), 2) void prefill_bf16_kernel(
       for (int r = 0; r < 16; ++r) oacc[db][r] = 0.f;
     float m_run = -INFINITY, l_run = 0.f;
     f32x16_t sacc[2][C::NKB];  // S^T of the tile being consumed and of the next one
-
-    const int q_end = min(q0 + C::BM, Sb);  // exclusive
-    const int ntiles = (P + q_end + C::BN - 1) / C::BN;
-    // tiles 0..wlast hold keys visible to this wave (uniform per wave)
-    const int wlast = min(ntiles - 1, (P + qw + 31) / C::BN);
-    // this wave's group walks tiles tbeg .. tbeg+tcnt-1; the lambdas below
-    // take the local index t - tbeg, which also picks the LDS buffers
-    const int nt0 = KSPLIT ? (ntiles + 1) >> 1 : ntiles;  // steps of the launch
-    const int tbeg = grp == 0 ? 0 : nt0;
-    const int tcnt = grp == 0 ? nt0 : ntiles - nt0;
-    const int ulast = min(wlast - tbeg, tcnt - 1);  // local index of the last visible tile
 
     // S^T = K Q^T for the tile in K buffer kb_i: lane holds keys
     // kb*32 + 8*(r/4) + 4*g + r%4 of query qrow.  The two 32-key blocks are
@@ -661,7 +684,6 @@ __global__ __launch_bounds__((Tile<D, 8>::THREADS), 2) void prefill_bf16_kernel(
     // Paged: block ids of tiles t+1 (V loads of step t), t+2 (K loads) and
     // t+3 (read during step t for the next step).
     // (t is the group's local tile index throughout.)
-    int ids_v = 0, ids_k = 0;
     auto step = [&](int t, auto SC, auto SN) {
       __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's loads landed
       __syncthreads();                     // everyone's loads landed; old buffers free
@@ -679,16 +701,6 @@ __global__ __launch_bounds__((Tile<D, 8>::THREADS), 2) void prefill_bf16_kernel(
 
     using S0 = std::integral_constant<int, 0>;
     using S1 = std::integral_constant<int, 1>;
-    if (tcnt > 0) {
-      const int ids0 = block_ids(tbeg * C::BN);
-      issue(krs, c.k, tbeg * C::BN, kbuf, ids0);
-      issue(vrs, c.v, tbeg * C::BN, vbuf, ids0);
-      if (tcnt > 1) {
-        ids_v = block_ids((tbeg + 1) * C::BN);
-        issue(krs, c.k, (tbeg + 1) * C::BN, kbuf + C::TILEB, ids_v);
-      }
-      if (tcnt > 2) ids_k = block_ids((tbeg + 2) * C::BN);
-    }
     __builtin_amdgcn_s_waitcnt(0x0F70);
     __syncthreads();
     // K(0) is visible; K(1) and V(0) may still be in flight (waited for in step 0)
