@@ -213,7 +213,8 @@ car_status car_attn_prefill_timed(const void* q, const void* k, const void* v, v
   const bool paged = cache != nullptr && cache->block_table != nullptr;
   hipError_t e = launch_prefill_prep(dt, D, paged, is_int8(cache),
                                      cache != nullptr ? &c : nullptr, k, v, k_rot, B, Hkv,
-                                     S, positions, seq_lens, fr, keys_in_cache, stream);
+                                     S, positions, seq_lens, fr, keys_in_cache, out,
+                                     Hq / Hkv, stream);
   if (e != hipSuccess) return CAR_ERR_HIP;
   return from_hip(launch_prefill_attention(dt, D, q, k_rot, v, out, B, Hq, Hkv, S,
                                            positions, seq_lens, fr, scale,

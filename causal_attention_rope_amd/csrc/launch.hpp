@@ -56,14 +56,16 @@ hipError_t launch_kv_append(Dtype dt, int D, bool paged, bool i8, const CacheArg
 // Rotates k into k_rot (dense [B,Hkv,S,D]) and, if cache != nullptr, also
 // stores the rotated keys and raw values into the cache (as int8 codes if i8).
 // lens (nullable): tokens of each prompt; rows from there on are padding,
-// neither rotated nor stored.
+// neither rotated nor stored, and their rows of out ([B, Hkv*G, S, D]) are
+// zeroed here.
 // keys_in_cache (contiguous native cache only): sequences whose positions
 // are consecutive cache slots (prompt_rows_in_cache) skip k_rot, and the
 // attention must then be given the cache to read their keys from.
 hipError_t launch_prefill_prep(Dtype dt, int D, bool paged, bool i8, const CacheArgs* cache,
                                const void* k, const void* v, void* k_rot, int B, int Hkv,
                                int S, const int32_t* positions, const int32_t* lens,
-                               const RopeFreq& fr, bool keys_in_cache, hipStream_t s);
+                               const RopeFreq& fr, bool keys_in_cache, void* out, int G,
+                               hipStream_t s);
 
 // Per-(KV head, channel) absmax / 127 of the rotated keys and of the values
 // of a calibration batch, into k_scale / v_scale (fp32 [Hkv, D]).

@@ -305,15 +305,24 @@ __global__ __launch_bounds__((Tile<D, 8>::THREADS), 2) void prefill_bf16_kernel(
   // workgroup takes the pair (nqt-1-p, p): every pair costs nqt+1 tile rows
   // (the middle tile of an odd nqt runs alone) and all workgroups of a launch
   // finish together.  Workgroups go to the 8 XCDs round-robin by id; when the
-  // head count is a multiple of 8, XCD x owns the consecutive heads
-  // [x*hpx, (x+1)*hpx), so query heads of one KV group share its L2.
+  // query head count is a multiple of 8, XCD x owns the consecutive heads
+  // [x*hpx, (x+1)*hpx) of every sequence (else of the flattened batch), so
+  // query heads of one KV group share its L2.
   // With a cached prefix every query tile costs about the same (the prefix
   // dominates), so a workgroup then takes a single tile: twice the workgroups.
   const int npair = PAIRED ? (nqt + 1) >> 1 : nqt;
   const int nbh = gridDim.x / npair;
   const int bid = blockIdx.x;
   int bh, pr;
-  if ((nbh & 7) == 0) {
+  if ((Hq & 7) == 0) {
+    // XCD x owns query heads [x*hpx, (x+1)*hpx) of every sequence, so that
+    // sequences of different lengths load all XCDs alike
+    const int hpx = Hq >> 3, nb = nbh / Hq;
+    const int xcd = bid & 7, slot = bid >> 3;
+    const int rest = slot / hpx;  // sequence fastest, then the pair
+    bh = (rest % nb) * Hq + xcd * hpx + slot % hpx;
+    pr = rest / nb;
+  } else if ((nbh & 7) == 0) {
     const int hpx = nbh >> 3;
     const int xcd = bid & 7, slot = bid >> 3;
     bh = xcd * hpx + slot % hpx;
@@ -324,6 +333,20 @@ __global__ __launch_bounds__((Tile<D, 8>::THREADS), 2) void prefill_bf16_kernel(
   }
   const int b = bh / Hq, hq = bh % Hq;
   const int hk = hq / (Hq / Hkv);
+  // Prompts of their own lengths (a padded batch): the pairs are formed over
+  // each prompt's own query tiles (nqt_b of them), so that every working
+  // workgroup of a prompt costs the same; workgroups past its pairs have
+  // nothing to do (the K pass writes the padding rows' zeros), and the pair
+  // index runs backwards, so that the highest pairs, which only the longest
+  // prompts have, are dispatched first.
+  int nqt_b = nqt;
+  if constexpr (PAIRED && SRC == KEYS_PROMPT) {
+    if (chunk_lens != nullptr) {
+      nqt_b = (min(max(chunk_lens[b], 0), S) + C::BM - 1) / C::BM;
+      pr = npair - 1 - pr;
+      if (pr >= ((nqt_b + 1) >> 1)) return;  // uniform over the workgroup
+    }
+  }
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -451,9 +474,9 @@ __global__ __launch_bounds__((Tile<D, 8>::THREADS), 2) void prefill_bf16_kernel(
   // ---- the pair's two query tiles, longest first ----
 #pragma nounroll
   for (int pass = 0; pass < 2; ++pass) {
-    const int qt = !PAIRED ? pr : (pass == 0 ? nqt - 1 - pr : pr);
+    const int qt = !PAIRED ? pr : (pass == 0 ? nqt_b - 1 - pr : pr);
     if (pass == 1) {
-      if (!PAIRED || qt == nqt - 1 - pr) break;  // one tile, or no partner
+      if (!PAIRED || qt == nqt_b - 1 - pr) break;  // one tile, or no partner
       __syncthreads();                // every wave is done with the LDS tiles
     }
     const int q0 = qt * C::BM;

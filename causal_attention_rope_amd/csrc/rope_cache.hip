@@ -105,7 +105,7 @@ template <typename T, int D, bool PAGED, bool CACHE, bool I8, bool KEYS_IN_CACHE
 __global__ __launch_bounds__(kThreads) void prefill_prep_kernel(
     CacheArgs c, const T* __restrict__ k, const T* __restrict__ v, T* __restrict__ k_rot,
     int Hkv, int S, const int32_t* __restrict__ positions, const int32_t* __restrict__ lens,
-    int64_t nvec, RopeFreq fr) {
+    int64_t nvec, RopeFreq fr, T* __restrict__ out, int G) {
   constexpr int N = Vec16<T>::N;
   constexpr int VPR = D / N;
   for (int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x; i < nvec;
@@ -116,7 +116,16 @@ __global__ __launch_bounds__(kThreads) void prefill_prep_kernel(
     const int64_t bh = row / S;
     const int b = (int)(bh / Hkv);
     const int n = lens == nullptr ? S : min(max(lens[b], 0), S);
-    if (s >= n) continue;  // padding: neither rotated nor stored
+    if (s >= n) {
+      // padding: neither rotated nor stored; its output rows (the G query
+      // heads of this KV head) are written as zeros here, since the attention
+      // kernel visits only the query tiles that hold prompt tokens
+      const int64_t hq0 = (int64_t)b * Hkv * G + (bh % Hkv) * G;
+#pragma unroll 1
+      for (int g = 0; g < G; ++g)
+        *reinterpret_cast<uint4*>(out + ((hq0 + g) * S + s) * D + col) = make_uint4(0u, 0u, 0u, 0u);
+      continue;
+    }
     const int pos = positions[(int64_t)b * S + s];
     float f[N];
     load16<T>(k + row * D + col, f);
@@ -369,7 +378,8 @@ template <typename T, int D, bool I8>
 hipError_t prefill_prep_t(bool paged, const CacheArgs* cache, const void* k, const void* v,
                           void* k_rot, int B, int Hkv, int S, const int32_t* positions,
                           const int32_t* lens, const RopeFreq& fr, bool keys_in_cache,
-                          hipStream_t st) {
+                          void* out, int G, hipStream_t st) {
+  T* const oo = static_cast<T*>(out);
   const int64_t nvec = (int64_t)B * Hkv * S * (D / Vec16<T>::N);
   const T* kk = static_cast<const T*>(k);
   const T* vv = static_cast<const T*>(v);
@@ -378,16 +388,16 @@ hipError_t prefill_prep_t(bool paged, const CacheArgs* cache, const void* k, con
   if (cache == nullptr) {
     CacheArgs none{};
     hipLaunchKernelGGL((prefill_prep_kernel<T, D, false, false, false>), grid, block, 0, st,
-                       none, kk, vv, kr, Hkv, S, positions, lens, nvec, fr);
+                       none, kk, vv, kr, Hkv, S, positions, lens, nvec, fr, oo, G);
   } else if (paged) {
     hipLaunchKernelGGL((prefill_prep_kernel<T, D, true, true, I8>), grid, block, 0, st, *cache,
-                       kk, vv, kr, Hkv, S, positions, lens, nvec, fr);
+                       kk, vv, kr, Hkv, S, positions, lens, nvec, fr, oo, G);
   } else if (!I8 && keys_in_cache) {
     hipLaunchKernelGGL((prefill_prep_kernel<T, D, false, true, false, true>), grid, block, 0, st,
-                       *cache, kk, vv, kr, Hkv, S, positions, lens, nvec, fr);
+                       *cache, kk, vv, kr, Hkv, S, positions, lens, nvec, fr, oo, G);
   } else {
     hipLaunchKernelGGL((prefill_prep_kernel<T, D, false, true, I8>), grid, block, 0, st,
-                       *cache, kk, vv, kr, Hkv, S, positions, lens, nvec, fr);
+                       *cache, kk, vv, kr, Hkv, S, positions, lens, nvec, fr, oo, G);
   }
   return hipGetLastError();
 }
@@ -487,10 +497,11 @@ hipError_t launch_kv_append(Dtype dt, int D, bool paged, bool i8, const CacheArg
 hipError_t launch_prefill_prep(Dtype dt, int D, bool paged, bool i8, const CacheArgs* cache,
                                const void* k, const void* v, void* k_rot, int B, int Hkv,
                                int S, const int32_t* positions, const int32_t* lens,
-                               const RopeFreq& fr, bool keys_in_cache, hipStream_t s) {
+                               const RopeFreq& fr, bool keys_in_cache, void* out, int G,
+                               hipStream_t s) {
 #define CAR_PREP(T, DD, I)                                                             \
   prefill_prep_t<T, DD, I>(paged, cache, k, v, k_rot, B, Hkv, S, positions, lens, fr, \
-                           keys_in_cache, s)
+                           keys_in_cache, out, G, s)
   if (i8 && cache != nullptr) {
     if (dt == F32) return D == 64 ? CAR_PREP(float, 64, true) : CAR_PREP(float, 128, true);
     return D == 64 ? CAR_PREP(bf16_t, 64, true) : CAR_PREP(bf16_t, 128, true);
