@@ -542,8 +542,9 @@ def main(argv=None) -> int:
     pf_cache = car.KVCache(torch.zeros((1, 32, 4096, 128), dtype=torch.bfloat16, device=dev),
                            torch.zeros((1, 32, 4096, 128), dtype=torch.bfloat16, device=dev))
     pf_out = torch.empty_like(pf.q)
-    pf_ws = torch.empty(car.prefill_workspace_bytes(torch.bfloat16, 1, 32, 4096, 128),
-                        dtype=torch.uint8, device=dev)
+    # keys into a contiguous bf16 cache the prompt fits: no workspace (the
+    # attention reads the rotated keys back from the cache)
+    assert car.prefill_workspace_bytes(torch.bfloat16, 1, 32, 4096, 128, cache=pf_cache) == 0
     c4_cache = car.KVCache(c4.cache_k, c4.cache_v)
     c5_cache = car.KVCache(c5.cache_k, c5.cache_v, c5.block_table)
     c4_out, c5_out = torch.empty_like(c4.q), torch.empty_like(c5.q)
@@ -564,7 +565,7 @@ def main(argv=None) -> int:
     def stage_call(s, timing=None):
         if s == "prefill":
             car.attn_prefill(pf.q, pf.k, pf.v, pf.positions, pf.theta, pf.scale,
-                             cache=pf_cache, out=pf_out, workspace=pf_ws, timing=timing)
+                             cache=pf_cache, out=pf_out, no_workspace=True, timing=timing)
         elif s == "contiguous":
             car.attn_decode(c4.q, c4.k_new, c4.v_new, c4.seq_lens, c4_cache, c4.max_seq_len,
                             c4.theta, c4.scale, out=c4_out, workspace=c4_ws, timing=timing)

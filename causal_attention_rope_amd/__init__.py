@@ -323,8 +323,15 @@ def kv_int8_calibrate(k: torch.Tensor, v: torch.Tensor, positions: torch.Tensor,
     return ks, vs
 
 
-def prefill_workspace_bytes(dtype: torch.dtype, B: int, Hkv: int, S: int, D: int) -> int:
-    return int(_lib.car_attn_prefill_workspace_bytes(_DTYPES[dtype], B, Hkv, S, D, None))
+def prefill_workspace_bytes(dtype: torch.dtype, B: int, Hkv: int, S: int, D: int,
+                            cache: Optional[KVCache] = None) -> int:
+    """Workspace of attn_prefill; with a cache given, 0 where the attention can
+    read the rotated keys back from it (bf16, contiguous, S <= max_seq)."""
+    if cache is None:
+        return int(_lib.car_attn_prefill_workspace_bytes(_DTYPES[dtype], B, Hkv, S, D, None))
+    c = cache._c()
+    return int(_lib.car_attn_prefill_workspace_bytes(_DTYPES[dtype], B, Hkv, S, D,
+                                                     ctypes.byref(c)))
 
 
 def prefill_cached_workspace_bytes(dtype: torch.dtype, B: int, Hkv: int, D: int,

@@ -30,7 +30,9 @@
  *   ([Scratch] §3.2); positions are 0-based.
  * Ownership.  The caller owns every buffer.  The library never allocates,
  *   frees or keeps a pointer after a call returns, and holds no state
- *   between calls.
+ *   between calls, with one exception: car_attn_decode_noalloc keeps its
+ *   partials in a fixed device array per GPU (allocated when the library's
+ *   code is loaded) and remembers that array's address per device.
  * Asynchrony.  Each call only enqueues kernels on `stream` (0 = the null
  *   stream) and returns; results are ready when the stream reaches them.
  * Errors.  Everything the host can check (null pointers, sizes, D, Hq/Hkv,

@@ -268,6 +268,23 @@ def test_prefill_workspace_not_needed_for_a_contiguous_bf16_cache(car, lib):
         assert call(dt, ctypes.byref(c) if c is not None else None) == WORKSPACE
 
 
+def test_python_workspace_size_helper_passes_the_cache(car):
+    """The binding's prefill_workspace_bytes forwards an optional cache (a
+    stand-in that only describes a contiguous 128-slot cache; nothing is
+    launched)."""
+    import torch
+
+    class Cont:
+        def _c(self):
+            return _cache(car, max_seq=128)
+    cont = Cont()
+    full = 2 * 4 * 128 * 64 * 2
+    assert car.prefill_workspace_bytes(torch.bfloat16, 2, 4, 128, 64) == full
+    assert car.prefill_workspace_bytes(torch.bfloat16, 2, 4, 128, 64, cache=cont) == 0
+    assert car.prefill_workspace_bytes(torch.bfloat16, 2, 4, 129, 64, cache=cont) == full // 128 * 129
+    assert car.prefill_workspace_bytes(torch.float32, 2, 4, 128, 64, cache=cont) == 2 * full
+
+
 def test_workspace_sizes(lib):
     assert lib.car_attn_decode_workspace_bytes(32, 32, 128, 4096) == 32 * 32 * 16 * 132 * 4
     assert lib.car_attn_decode_workspace_bytes(64, 32, 128, 8193) == 64 * 32 * 33 * 132 * 4
