@@ -211,10 +211,12 @@ car_status car_attn_prefill_timed(const void* q, const void* k, const void* v, v
   const Dtype dt = dtype == CAR_DTYPE_F32 ? F32 : BF16;
   const RopeFreq fr = make_freq(D, theta, pairing);
   const bool paged = cache != nullptr && cache->block_table != nullptr;
+  const bool values_by_attention =
+      keys_in_cache && prefill_attention_stores_values(dt, B, Hq, S, &c);
   hipError_t e = launch_prefill_prep(dt, D, paged, is_int8(cache),
                                      cache != nullptr ? &c : nullptr, k, v, k_rot, B, Hkv,
-                                     S, positions, seq_lens, fr, keys_in_cache, out,
-                                     Hq / Hkv, stream);
+                                     S, positions, seq_lens, fr, keys_in_cache,
+                                     !values_by_attention, out, Hq / Hkv, stream);
   if (e != hipSuccess) return CAR_ERR_HIP;
   return from_hip(launch_prefill_attention(dt, D, q, k_rot, v, out, B, Hq, Hkv, S,
                                            positions, seq_lens, fr, scale,

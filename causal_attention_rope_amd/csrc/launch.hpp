@@ -61,11 +61,13 @@ hipError_t launch_kv_append(Dtype dt, int D, bool paged, bool i8, const CacheArg
 // keys_in_cache (contiguous native cache only): sequences whose positions
 // are consecutive cache slots (prompt_rows_in_cache) skip k_rot, and the
 // attention must then be given the cache to read their keys from.
+// store_v (only read with keys_in_cache): false when the attention kernel
+// stores the values into the cache (prefill_attention_stores_values).
 hipError_t launch_prefill_prep(Dtype dt, int D, bool paged, bool i8, const CacheArgs* cache,
                                const void* k, const void* v, void* k_rot, int B, int Hkv,
                                int S, const int32_t* positions, const int32_t* lens,
-                               const RopeFreq& fr, bool keys_in_cache, void* out, int G,
-                               hipStream_t s);
+                               const RopeFreq& fr, bool keys_in_cache, bool store_v, void* out,
+                               int G, hipStream_t s);
 
 // Per-(KV head, channel) absmax / 127 of the rotated keys and of the values
 // of a calibration batch, into k_scale / v_scale (fp32 [Hkv, D]).
@@ -90,6 +92,11 @@ hipError_t launch_int8_dequant(Dtype dt, int D, bool paged, const CacheArgs& c, 
                                hipStream_t s);
 
 // ---- prefill.hip -----------------------------------------------------------
+// Whether launch_prefill_attention, given the contiguous native bf16 cache
+// kcache of a prompt of this shape, stores the prompt's values into it (the
+// paired form does; the K pass then stores only the keys).
+bool prefill_attention_stores_values(Dtype dt, int B, int Hq, int S, const CacheArgs* kcache);
+
 // kcache (nullable; bf16 only): the contiguous cache that the K pass filled
 // with keys_in_cache; sequences whose positions are consecutive cache slots
 // read their rotated keys from it instead of k_rot.  lens (nullable): tokens

@@ -289,7 +289,7 @@ __global__ __launch_bounds__((Tile<D, 8>::THREADS), 2) void prefill_bf16_kernel(
     const bf16_t* __restrict__ q, const bf16_t* __restrict__ kr, const bf16_t* __restrict__ v,
     bf16_t* __restrict__ out, const int32_t* __restrict__ positions, int Hq, int Hkv, int S,
     int nqt, RopeFreq fr, float sm_scale_log2, CacheArgs c, const int32_t* __restrict__ seq_lens,
-    const int32_t* __restrict__ chunk_lens) {
+    const int32_t* __restrict__ chunk_lens, int vstore) {
   constexpr bool PAIRED = FORM == FORM_PAIR;
   // FORM_SPLIT: waves 0..3 take the first half of the query tile's key tiles
   // and waves 4..7 the second, each group with its own double-buffered K and
@@ -470,6 +470,52 @@ __global__ __launch_bounds__((Tile<D, 8>::THREADS), 2) void prefill_bf16_kernel(
         voff[db][h] = row * C::ROWB + (phys_chunk<C::CPR>(chunk, row) << 4) + ((col & 7) << 1);
       }
   }
+
+  // ---- values into the cache (paired form, vstore != 0) ----
+  // The K pass then stores only the keys: each 64- or 128-key value tile of
+  // a KV head goes from LDS to the cache rows at the prompt's positions,
+  // written by one workgroup, from the first query head of the KV group, in
+  // its first (long) pass, while the tile sits in LDS anyway.  Pair p's long
+  // pass reaches tiles [0, reach(p)), reach falling with p: tiles every pair
+  // reaches go round-robin, and each higher tile to the last pair that still
+  // reaches it, so that every pair stores about the same number.  Rows past
+  // the prompt (padding, the clamped rows of a partial tile) and positions
+  // outside the cache are not stored; prompts at consecutive slots p0.. need
+  // no position reads.
+  const int npair_b = PAIRED ? (nqt_b + 1) >> 1 : 1;
+  const bool store_values = PAIRED && SRC == KEYS_PROMPT && vstore != 0 &&
+                            hq % (Hq / Hkv) == 0;
+  constexpr int TPQ = C::BM / C::BN;  // key tiles per query tile
+  auto value_owner = [&](int t) {
+    const int all = (nqt_b - npair_b + 1) * TPQ;  // tiles every pair's long pass reaches
+    return t < all ? t % npair_b : nqt_b - 1 - t / TPQ;
+  };
+  int vp0 = 0;
+  const bool v_consecutive = store_values && c.v != nullptr &&
+                             prompt_rows_in_cache(positions, b, S, Sb, c.max_seq, &vp0);
+  auto store_value_tile = [&](int t) {
+    const char* vt = vbuf + (t & 1) * C::TILEB;
+    bf16_t* const vc = static_cast<bf16_t*>(c.v) + ((int64_t)b * Hkv + hk) * c.max_seq * D;
+    // the lane's chunk indices are formed here from a copy of the thread id
+    // the compiler cannot see through, so that they hold no registers across
+    // the key loop
+    int tcopy = tid;
+    asm volatile("" : "+v"(tcopy));
+#pragma unroll
+    for (int i = 0; i < C::TILEB / 16 / C::THREADS; ++i) {
+      const int e = tcopy + i * C::THREADS;  // 16-byte chunk e of the tile
+      const int r = e / C::CPR, ch = e % C::CPR;
+      const int j = t * C::BN + r;
+      if (j < Sb) {
+        const int pos = v_consecutive ? vp0 + j : positions[(int64_t)b * S + j];
+        if (pos >= 0 && pos < c.max_seq) {
+          const u32x4_t x = *reinterpret_cast<const u32x4_t*>(
+              vt + r * C::ROWB + (phys_chunk<C::CPR>(ch, r) << 4));
+          *reinterpret_cast<u32x4_t*>(vc + (int64_t)pos * D + ch * 8) = x;
+        }
+      }
+    }
+  };
 
   // ---- the pair's two query tiles, longest first ----
 #pragma nounroll
@@ -710,6 +756,9 @@ __global__ __launch_bounds__((Tile<D, 8>::THREADS), 2) void prefill_bf16_kernel(
     auto step = [&](int t, auto SC, auto SN) {
       __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's loads landed
       __syncthreads();                     // everyone's loads landed; old buffers free
+      if constexpr (PAIRED && SRC == KEYS_PROMPT) {
+        if (store_values && pass == 0 && value_owner(t) == pr) store_value_tile(t);
+      }
       if (t + 2 < tcnt)
         issue(krs, c.k, (tbeg + t + 2) * C::BN, kbuf + (t & 1) * C::TILEB, ids_k);
       if (t + 1 < tcnt)
@@ -798,6 +847,7 @@ struct KeySource {
   CacheArgs c;
   const int32_t* seq_lens;
   const int32_t* chunk_lens;
+  bool vstore;  // the paired form stores the values into c (contiguous, native bf16)
 };
 
 template <int D, int SRC, int HALF>
@@ -816,7 +866,7 @@ hipError_t prefill_f32_t(const void* q, const KeySource& ks, void* out, int B, i
 template <int D, int SRC, int HALF, int FORM>
 hipError_t prefill_bf16_w(const void* q, const KeySource& ks, void* out, int B, int Hq, int Hkv,
                           int S, const int32_t* positions, const RopeFreq& fr, float scale,
-                          hipStream_t st, const TimedLaunch& tl) {
+                          hipStream_t st, const TimedLaunch& tl, bool vstore = false) {
   using C = Tile<D, FORM == FORM_SPLIT ? 4 : 8>;  // BM query rows per workgroup
   const int nqt = (S + C::BM - 1) / C::BM;
   const int npair = FORM == FORM_PAIR ? (nqt + 1) / 2 : nqt;  // workgroups per head
@@ -824,7 +874,8 @@ hipError_t prefill_bf16_w(const void* q, const KeySource& ks, void* out, int B, 
                         st, tl.start, tl.stop, 0, static_cast<const bf16_t*>(q),
                         static_cast<const bf16_t*>(ks.k_rot), static_cast<const bf16_t*>(ks.v),
                         static_cast<bf16_t*>(out), positions, Hq, Hkv, S, nqt, fr,
-                        scale * 1.4426950408889634f, ks.c, ks.seq_lens, ks.chunk_lens);
+                        scale * 1.4426950408889634f, ks.c, ks.seq_lens, ks.chunk_lens,
+                        vstore ? 1 : 0);
   return hipGetLastError();
 }
 
@@ -832,15 +883,21 @@ hipError_t prefill_bf16_w(const void* q, const KeySource& ks, void* out, int B, 
 // than this runs in the split form instead.
 constexpr int kComputeUnits = 256;
 
+// Whether a bf16 prompt of this shape runs in the paired form.
+bool paired_form(int B, int Hq, int S) {
+  const int64_t pairs = (int64_t)((S + Tile<128, 8>::BM - 1) / Tile<128, 8>::BM + 1) / 2 * B * Hq;
+  static_assert(Tile<128, 8>::BM == Tile<64, 8>::BM, "one query tile height");
+  return pairs >= kComputeUnits;
+}
+
 template <int D, int SRC, int HALF>
 hipError_t prefill_bf16_t(const void* q, const KeySource& ks, void* out, int B, int Hq, int Hkv,
                           int S, const int32_t* positions, const RopeFreq& fr, float scale,
                           hipStream_t st, const TimedLaunch& tl) {
   if constexpr (SRC == KEYS_PROMPT) {
-    const int64_t pairs = (int64_t)((S + Tile<D, 8>::BM - 1) / Tile<D, 8>::BM + 1) / 2 * B * Hq;
-    if (pairs >= kComputeUnits)
+    if (paired_form(B, Hq, S))
       return prefill_bf16_w<D, SRC, HALF, FORM_PAIR>(q, ks, out, B, Hq, Hkv, S, positions, fr,
-                                                     scale, st, tl);
+                                                     scale, st, tl, ks.vstore);
   }
   return prefill_bf16_w<D, SRC, HALF, FORM_SPLIT>(q, ks, out, B, Hq, Hkv, S, positions, fr, scale,
                                                   st, tl);
@@ -877,6 +934,10 @@ hipError_t prefill_dispatch(Dtype dt, int D, const void* q, const KeySource& ks,
 
 }  // namespace
 
+bool prefill_attention_stores_values(Dtype dt, int B, int Hq, int S, const CacheArgs* kcache) {
+  return dt == BF16 && kcache != nullptr && paired_form(B, Hq, S);
+}
+
 hipError_t launch_prefill_attention(Dtype dt, int D, const void* q, const void* k_rot,
                                     const void* v, void* out, int B, int Hq, int Hkv, int S,
                                     const int32_t* positions, const int32_t* lens,
@@ -884,7 +945,7 @@ hipError_t launch_prefill_attention(Dtype dt, int D, const void* q, const void* 
                                     hipStream_t s, const TimedLaunch& tl) {
   // the fp32 kernel always reads k_rot (its K pass never skips it)
   const KeySource ks{k_rot, v, kcache != nullptr && dt == BF16 ? *kcache : CacheArgs{}, nullptr,
-                     lens};
+                     lens, prefill_attention_stores_values(dt, B, Hq, S, kcache)};
   return prefill_dispatch<KEYS_PROMPT>(dt, D, q, ks, out, B, Hq, Hkv, S, positions, fr, scale, s,
                                        tl);
 }
@@ -894,7 +955,7 @@ hipError_t launch_prefill_cached(Dtype dt, int D, bool paged, const void* q, voi
                                  const int32_t* seq_lens, const int32_t* chunk_lens,
                                  const RopeFreq& fr, float scale, hipStream_t s,
                                  const TimedLaunch& tl) {
-  const KeySource ks{nullptr, nullptr, c, seq_lens, chunk_lens};
+  const KeySource ks{nullptr, nullptr, c, seq_lens, chunk_lens, false};
   if (dt == BF16 && !paged && c.k_scale != nullptr) {  // a dense copy of INT8 codes
     if (D == 64)
       return fr.half ? prefill_bf16_t<64, KEYS_CODES, 1>(q, ks, out, B, Hq, Hkv, S, nullptr, fr,

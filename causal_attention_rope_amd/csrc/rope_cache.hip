@@ -100,12 +100,13 @@ __global__ __launch_bounds__(kThreads) void kv_append_kernel(CacheArgs c,
 // with a cache, store rotated keys and raw values at their positions.
 // KEYS_IN_CACHE (contiguous native cache): a prompt whose positions are
 // consecutive slots of the cache gets no dense copy; the attention kernel
-// reads its rotated keys from the cache rows instead.
+// reads its rotated keys from the cache rows instead.  store_v = 0 there:
+// the attention kernel stores the values (it stages them in LDS anyway).
 template <typename T, int D, bool PAGED, bool CACHE, bool I8, bool KEYS_IN_CACHE = false>
 __global__ __launch_bounds__(kThreads) void prefill_prep_kernel(
     CacheArgs c, const T* __restrict__ k, const T* __restrict__ v, T* __restrict__ k_rot,
     int Hkv, int S, const int32_t* __restrict__ positions, const int32_t* __restrict__ lens,
-    int64_t nvec, RopeFreq fr, T* __restrict__ out, int G) {
+    int64_t nvec, RopeFreq fr, T* __restrict__ out, int G, int store_v) {
   constexpr int N = Vec16<T>::N;
   constexpr int VPR = D / N;
   for (int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x; i < nvec;
@@ -145,8 +146,9 @@ __global__ __launch_bounds__(kThreads) void prefill_prep_kernel(
         store_int8<N>(static_cast<int8_t*>(c.v) + dst, vf, c.v_scale + hk * D + col);
       } else {
         store16<T>(static_cast<T*>(c.k) + dst, f);
-        *reinterpret_cast<uint4*>(static_cast<T*>(c.v) + dst) =
-            *reinterpret_cast<const uint4*>(v + row * D + col);
+        if (store_v)
+          *reinterpret_cast<uint4*>(static_cast<T*>(c.v) + dst) =
+              *reinterpret_cast<const uint4*>(v + row * D + col);
       }
     }
   }
@@ -378,7 +380,7 @@ template <typename T, int D, bool I8>
 hipError_t prefill_prep_t(bool paged, const CacheArgs* cache, const void* k, const void* v,
                           void* k_rot, int B, int Hkv, int S, const int32_t* positions,
                           const int32_t* lens, const RopeFreq& fr, bool keys_in_cache,
-                          void* out, int G, hipStream_t st) {
+                          bool store_v, void* out, int G, hipStream_t st) {
   T* const oo = static_cast<T*>(out);
   const int64_t nvec = (int64_t)B * Hkv * S * (D / Vec16<T>::N);
   const T* kk = static_cast<const T*>(k);
@@ -388,16 +390,17 @@ hipError_t prefill_prep_t(bool paged, const CacheArgs* cache, const void* k, con
   if (cache == nullptr) {
     CacheArgs none{};
     hipLaunchKernelGGL((prefill_prep_kernel<T, D, false, false, false>), grid, block, 0, st,
-                       none, kk, vv, kr, Hkv, S, positions, lens, nvec, fr, oo, G);
+                       none, kk, vv, kr, Hkv, S, positions, lens, nvec, fr, oo, G, 1);
   } else if (paged) {
     hipLaunchKernelGGL((prefill_prep_kernel<T, D, true, true, I8>), grid, block, 0, st, *cache,
-                       kk, vv, kr, Hkv, S, positions, lens, nvec, fr, oo, G);
+                       kk, vv, kr, Hkv, S, positions, lens, nvec, fr, oo, G, 1);
   } else if (!I8 && keys_in_cache) {
     hipLaunchKernelGGL((prefill_prep_kernel<T, D, false, true, false, true>), grid, block, 0, st,
-                       *cache, kk, vv, kr, Hkv, S, positions, lens, nvec, fr, oo, G);
+                       *cache, kk, vv, kr, Hkv, S, positions, lens, nvec, fr, oo, G,
+                       store_v ? 1 : 0);
   } else {
     hipLaunchKernelGGL((prefill_prep_kernel<T, D, false, true, I8>), grid, block, 0, st,
-                       *cache, kk, vv, kr, Hkv, S, positions, lens, nvec, fr, oo, G);
+                       *cache, kk, vv, kr, Hkv, S, positions, lens, nvec, fr, oo, G, 1);
   }
   return hipGetLastError();
 }
@@ -497,11 +500,11 @@ hipError_t launch_kv_append(Dtype dt, int D, bool paged, bool i8, const CacheArg
 hipError_t launch_prefill_prep(Dtype dt, int D, bool paged, bool i8, const CacheArgs* cache,
                                const void* k, const void* v, void* k_rot, int B, int Hkv,
                                int S, const int32_t* positions, const int32_t* lens,
-                               const RopeFreq& fr, bool keys_in_cache, void* out, int G,
-                               hipStream_t s) {
+                               const RopeFreq& fr, bool keys_in_cache, bool store_v,
+                               void* out, int G, hipStream_t s) {
 #define CAR_PREP(T, DD, I)                                                             \
   prefill_prep_t<T, DD, I>(paged, cache, k, v, k_rot, B, Hkv, S, positions, lens, fr, \
-                           keys_in_cache, out, G, s)
+                           keys_in_cache, store_v, out, G, s)
   if (i8 && cache != nullptr) {
     if (dt == F32) return D == 64 ? CAR_PREP(float, 64, true) : CAR_PREP(float, 128, true);
     return D == 64 ? CAR_PREP(bf16_t, 64, true) : CAR_PREP(bf16_t, 128, true);

@@ -169,6 +169,49 @@ def test_prefill_many_tiles_bf16(car):
 
 
 @pytest.mark.parametrize("D", [64, 128])
+def test_prefill_paired_form_stores_values_gqa_gapped(car, D):
+    """The paired form (2 x 64 query heads x 2 query-tile pairs) into a
+    contiguous cache, where the attention kernel stores the values and the
+    K pass only the keys: GQA (16 KV heads), sequence 0 at consecutive slots
+    5..604 (keys read back from the cache), sequence 1 at sorted random
+    positions whose last 20 lie past the cache (those rows are not stored).
+    Every stored K and V row is checked, and no other row of the NaN-filled
+    cache is written."""
+    log_case(f"prefill paired form stores values, GQA, gapped positions D={D}")
+    B, Hq, Hkv, S, cap = 2, 64, 16, 600, 1000
+    case = W.prefill_case("paired_values", B, Hq, Hkv, S, D, torch.bfloat16, 4200 + D, DEV)
+    rng = np.random.default_rng(4200 + D)
+    p1 = np.concatenate([np.sort(rng.choice(cap, S - 20, replace=False)), cap + np.arange(20)])
+    pos = np.stack([np.arange(S) + 5, p1]).astype(np.int32)
+    case.positions = torch.from_numpy(pos).to(DEV)
+    ck = torch.full((B, Hkv, cap, D), float("nan"), dtype=torch.bfloat16, device=DEV)
+    cache = car.KVCache(ck, ck.clone())
+    out = car.attn_prefill(case.q, case.k, case.v, case.positions, theta=case.theta,
+                           scale=case.scale, cache=cache)
+    torch.cuda.synchronize()
+    worst = 0.0
+    group = Hq // Hkv
+    for b in range(B):
+        for hq in (0, 37, 63):
+            o, _ = oracle.attn_prefill(f64(case.q[b:b + 1, hq:hq + 1]),
+                                       f64(case.k[b:b + 1, hq // group:hq // group + 1]),
+                                       f64(case.v[b:b + 1, hq // group:hq // group + 1]),
+                                       pos[b:b + 1], case.theta, case.scale)
+            worst = max(worst, max_abs(f64(out[b:b + 1, hq:hq + 1]), o))
+        valid = pos[b] < cap
+        sel = torch.as_tensor(pos[b][valid], device=DEV, dtype=torch.long)
+        k_rot = oracle.rope_rotate(f64(case.k[b:b + 1]), pos[b:b + 1][:, None, :], case.theta)
+        worst = max(worst, max_abs(f64(cache.k[b][:, sel]), k_rot[0][:, valid]))
+        assert torch.equal(bits(cache.v[b][:, sel].cpu()), bits(case.v[b][:, valid].cpu())), \
+            "cached V"
+    for name, t in (("K", cache.k), ("V", cache.v)):
+        rows = (~torch.isnan(t.float()).all(dim=-1)).sum().item()
+        assert rows == Hkv * (2 * S - 20), f"cache {name}: {rows} rows written"
+    log_case(f"paired form values D={D}: max-abs error {worst:.3e}")
+    assert worst <= TOL[torch.bfloat16]
+
+
+@pytest.mark.parametrize("D", [64, 128])
 def test_prefill_short_prompt_split_form(car, D):
     """A prompt whose query-tile pairs would fill few compute units (B=3,
     H=8, S=700: 48 pairs) runs in the split form: one 128-row query tile per
