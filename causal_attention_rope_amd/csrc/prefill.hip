@@ -196,14 +196,22 @@ __device__ __forceinline__ uint32_t cvt_pk_bf16(float a, float b) {
 
 // One direct buffer -> LDS load: every lane moves the 16 bytes at
 // rsrc.base + soff + voff to lds_base + 16 * lane (lds_base and soff uniform
-// over the wave).  Kept in a separate device function: a kernel body that
-// names the builtin directly loses its host-side launch stub in the host
-// compilation pass.
+// over the wave).  Issued from inline assembly (it has no register outputs):
+// the compiler would count the builtin's load as a pending LDS write and
+// wait for it before every later LDS read of the wave, which keeps loads
+// issued in the middle of a step from overlapping that step's LDS work.
+// Every wait for these loads is explicit (vmcnt before the step barriers).
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
 __device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t rsrc, uint32_t voff, uint32_t soff,
                                       void* lds_base) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (__attribute__((address_space(3))) void*)lds_base,
-                                           16, voff, soff, 0, 0);
+  const uint32_t lds_addr = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)lds_base);
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
+               :
+               : "s"(lds_addr), "v"(voff), "s"(rsrc), "s"(soff)
+               : "memory", "m0");
 }
+#pragma clang diagnostic pop
 
 // Buffer resource over `bytes` bytes at `base` (raw addressing, no stride);
 // the fourth descriptor word is the gfx9-family default data format.
@@ -748,8 +756,8 @@ __global__ __launch_bounds__((Tile<D, 8>::THREADS), 2) void prefill_bf16_kernel(
     };
 
     // One pipeline step for tile t (S^T of tile t already issued into
-    // sacc[SC]): make K(t+1) and V(t) visible, start the loads of K(t+2) and
-    // V(t+1), issue QK^T of tile t+1 into sacc[SN], then softmax and P V of t.
+    // sacc[SC]): make K(t+1) and V(t) visible, issue QK^T of tile t+1 into
+    // sacc[SN], start the loads of K(t+2) and V(t+1), then softmax and P V of t.
     // Paged: block ids of tiles t+1 (V loads of step t), t+2 (K loads) and
     // t+3 (read during step t for the next step).
     // (t is the group's local tile index throughout.)
@@ -759,6 +767,10 @@ __global__ __launch_bounds__((Tile<D, 8>::THREADS), 2) void prefill_bf16_kernel(
       if constexpr (PAIRED && SRC == KEYS_PROMPT) {
         if (store_values && pass == 0 && value_owner(t) == pr) store_value_tile(t);
       }
+      // the next tiles' loads go out after the QK^T MFMAs: issued right
+      // after the barrier, every wave's loads at once queue up in front of
+      // the texture unit and stall the waves' issue
+      if (t + 1 <= ulast) qk((t + 1) & 1, SN);
       if (t + 2 < tcnt)
         issue(krs, c.k, (tbeg + t + 2) * C::BN, kbuf + (t & 1) * C::TILEB, ids_k);
       if (t + 1 < tcnt)
@@ -767,7 +779,6 @@ __global__ __launch_bounds__((Tile<D, 8>::THREADS), 2) void prefill_bf16_kernel(
         ids_v = ids_k;
         if (t + 3 < tcnt) ids_k = block_ids((tbeg + t + 3) * C::BN);
       }
-      if (t + 1 <= ulast) qk((t + 1) & 1, SN);
       if (t <= ulast) softmax_pv(t, SC);
     };
 
