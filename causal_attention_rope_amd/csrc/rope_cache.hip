@@ -102,53 +102,78 @@ __global__ __launch_bounds__(kThreads) void kv_append_kernel(CacheArgs c,
 // consecutive slots of the cache gets no dense copy; the attention kernel
 // reads its rotated keys from the cache rows instead.  store_v = 0 there:
 // the attention kernel stores the values (it stages them in LDS anyway).
+//
+// Grid: (chunk blocks, groups of kPrepHeads KV heads, sequence).  A thread
+// takes one 16-byte chunk of one token in each KV head of its group: the
+// rotation angles depend only on the position and the chunk, so they are
+// computed once for all those heads, and the row and chunk come from shifts
+// instead of divisions by run-time sizes.
+constexpr int kPrepHeads = 8;  // 2, 4 and 16 were slower at workload 3's shape
 template <typename T, int D, bool PAGED, bool CACHE, bool I8, bool KEYS_IN_CACHE = false>
 __global__ __launch_bounds__(kThreads) void prefill_prep_kernel(
     CacheArgs c, const T* __restrict__ k, const T* __restrict__ v, T* __restrict__ k_rot,
     int Hkv, int S, const int32_t* __restrict__ positions, const int32_t* __restrict__ lens,
-    int64_t nvec, RopeFreq fr, T* __restrict__ out, int G, int store_v) {
+    RopeFreq fr, T* __restrict__ out, int G, int store_v) {
   constexpr int N = Vec16<T>::N;
   constexpr int VPR = D / N;
-  for (int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x; i < nvec;
-       i += (int64_t)gridDim.x * kThreads) {
-    const int64_t row = i / VPR;
-    const int col = (int)(i % VPR) * N;
-    const int s = (int)(row % S);
-    const int64_t bh = row / S;
-    const int b = (int)(bh / Hkv);
-    const int n = lens == nullptr ? S : min(max(lens[b], 0), S);
+  const int hk0 = blockIdx.y * kPrepHeads, b = blockIdx.z;
+  const int nh = min(kPrepHeads, Hkv - hk0);  // KV heads of this group
+  const int n = lens == nullptr ? S : min(max(lens[b], 0), S);
+  bool dense = k_rot != nullptr;  // the rotated keys also go to the dense copy
+  if constexpr (KEYS_IN_CACHE) {
+    int p0;
+    if (dense && prompt_rows_in_cache(positions, b, S, n, c.max_seq, &p0)) dense = false;
+  }
+  const int items = S * VPR;
+  for (int i = blockIdx.x * kThreads + threadIdx.x; i < items; i += gridDim.x * kThreads) {
+    const int s = i / VPR;
+    const int col = (i % VPR) * N;
     if (s >= n) {
       // padding: neither rotated nor stored; its output rows (the G query
-      // heads of this KV head) are written as zeros here, since the attention
+      // heads of each KV head) are written as zeros here, since the attention
       // kernel visits only the query tiles that hold prompt tokens
-      const int64_t hq0 = (int64_t)b * Hkv * G + (bh % Hkv) * G;
 #pragma unroll 1
-      for (int g = 0; g < G; ++g)
-        *reinterpret_cast<uint4*>(out + ((hq0 + g) * S + s) * D + col) = make_uint4(0u, 0u, 0u, 0u);
+      for (int g = 0; g < nh * G; ++g) {
+        const int64_t hq = ((int64_t)b * Hkv + hk0) * G + g;
+        *reinterpret_cast<uint4*>(out + (hq * S + s) * D + col) = make_uint4(0u, 0u, 0u, 0u);
+      }
       continue;
     }
     const int pos = positions[(int64_t)b * S + s];
-    float f[N];
-    load16<T>(k + row * D + col, f);
-    rope_rotate_chunk<T, N>(f, k + row * D, col, D, pos, fr);
-    int p0;
-    if (k_rot != nullptr &&
-        (!KEYS_IN_CACHE || !prompt_rows_in_cache(positions, b, S, n, c.max_seq, &p0)))
-      store16<T>(k_rot + row * D + col, f);
-    if (CACHE && pos >= 0 && pos <= cache_last_slot<PAGED>(c)) {  // else not stored
-      const int hk = (int)(bh % Hkv);
-      const int64_t dst = cache_row<PAGED>(c, b, hk, Hkv, pos) * D + col;
-      if constexpr (I8) {
-        // the fp32 rotated key is quantized (not its rounded copy in k_rot)
-        float vf[N];
-        load16<T>(v + row * D + col, vf);
-        store_int8<N>(static_cast<int8_t*>(c.k) + dst, f, c.k_scale + hk * D + col);
-        store_int8<N>(static_cast<int8_t*>(c.v) + dst, vf, c.v_scale + hk * D + col);
-      } else {
-        store16<T>(static_cast<T*>(c.k) + dst, f);
-        if (store_v)
-          *reinterpret_cast<uint4*>(static_cast<T*>(c.v) + dst) =
-              *reinterpret_cast<const uint4*>(v + row * D + col);
+    // every head's chunk is loaded before any store (a store to the cache
+    // could alias the next head's keys for all the compiler knows, which
+    // would leave one load in flight per thread)
+    uint4 raw[kPrepHeads];
+#pragma unroll
+    for (int j = 0; j < kPrepHeads; ++j)
+      if (j < nh)
+        raw[j] = *reinterpret_cast<const uint4*>(k + (((int64_t)b * Hkv + hk0 + j) * S + s) * D + col);
+    const RopeChunk<N> rot = rope_prepare<N, -1>(pos, col, D, fr);
+    const bool in_cache = CACHE && pos >= 0 && pos <= cache_last_slot<PAGED>(c);
+#pragma unroll
+    for (int j = 0; j < kPrepHeads; ++j) {
+      if (j >= nh) break;  // uniform over the block
+      const int hk = hk0 + j;
+      const int64_t row = ((int64_t)b * Hkv + hk) * S + s;
+      float f[N];
+#pragma unroll
+      for (int e = 0; e < N; ++e) f[e] = elem<T>(raw[j], e);
+      rope_apply_prepared<T, N, -1>(f, k + row * D, D, rot, fr);
+      if (dense) store16<T>(k_rot + row * D + col, f);
+      if (in_cache) {  // else not stored
+        const int64_t dst = cache_row<PAGED>(c, b, hk, Hkv, pos) * D + col;
+        if constexpr (I8) {
+          // the fp32 rotated key is quantized (not its rounded copy in k_rot)
+          float vf[N];
+          load16<T>(v + row * D + col, vf);
+          store_int8<N>(static_cast<int8_t*>(c.k) + dst, f, c.k_scale + hk * D + col);
+          store_int8<N>(static_cast<int8_t*>(c.v) + dst, vf, c.v_scale + hk * D + col);
+        } else {
+          store16<T>(static_cast<T*>(c.k) + dst, f);
+          if (store_v)
+            *reinterpret_cast<uint4*>(static_cast<T*>(c.v) + dst) =
+                *reinterpret_cast<const uint4*>(v + row * D + col);
+        }
       }
     }
   }
@@ -382,25 +407,29 @@ hipError_t prefill_prep_t(bool paged, const CacheArgs* cache, const void* k, con
                           const int32_t* lens, const RopeFreq& fr, bool keys_in_cache,
                           bool store_v, void* out, int G, hipStream_t st) {
   T* const oo = static_cast<T*>(out);
-  const int64_t nvec = (int64_t)B * Hkv * S * (D / Vec16<T>::N);
   const T* kk = static_cast<const T*>(k);
   const T* vv = static_cast<const T*>(v);
   T* kr = static_cast<T*>(k_rot);
-  const dim3 grid(grid_for(nvec)), block(kThreads);
+  if ((int64_t)B * Hkv * S == 0) return hipSuccess;
+  // (B and Hkv <= Hq are at most 65535: the call checks them)
+  const int64_t items = (int64_t)S * (D / Vec16<T>::N);
+  const int64_t gx = (items + kThreads - 1) / kThreads;
+  const dim3 grid((unsigned)(gx < 4096 ? gx : 4096), (Hkv + kPrepHeads - 1) / kPrepHeads, B);
+  const dim3 block(kThreads);
   if (cache == nullptr) {
     CacheArgs none{};
     hipLaunchKernelGGL((prefill_prep_kernel<T, D, false, false, false>), grid, block, 0, st,
-                       none, kk, vv, kr, Hkv, S, positions, lens, nvec, fr, oo, G, 1);
+                       none, kk, vv, kr, Hkv, S, positions, lens, fr, oo, G, 1);
   } else if (paged) {
     hipLaunchKernelGGL((prefill_prep_kernel<T, D, true, true, I8>), grid, block, 0, st, *cache,
-                       kk, vv, kr, Hkv, S, positions, lens, nvec, fr, oo, G, 1);
+                       kk, vv, kr, Hkv, S, positions, lens, fr, oo, G, 1);
   } else if (!I8 && keys_in_cache) {
     hipLaunchKernelGGL((prefill_prep_kernel<T, D, false, true, false, true>), grid, block, 0, st,
-                       *cache, kk, vv, kr, Hkv, S, positions, lens, nvec, fr, oo, G,
+                       *cache, kk, vv, kr, Hkv, S, positions, lens, fr, oo, G,
                        store_v ? 1 : 0);
   } else {
     hipLaunchKernelGGL((prefill_prep_kernel<T, D, false, true, I8>), grid, block, 0, st,
-                       *cache, kk, vv, kr, Hkv, S, positions, lens, nvec, fr, oo, G, 1);
+                       *cache, kk, vv, kr, Hkv, S, positions, lens, fr, oo, G, 1);
   }
   return hipGetLastError();
 }
