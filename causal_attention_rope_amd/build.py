@@ -82,9 +82,11 @@ def check_defined(lib: str) -> None:
 
 SAN_BUILD = os.path.join(HERE, "_build_san")
 SAN_LIB = os.path.join(HERE, "libcar_san.so")
-# host code: ASan + UBSan (every -fsanitize= for the host pass only)
+# host code: ASan + UBSan (every -fsanitize= for the host pass only); the
+# device code is optimized as usual (its inline assembly needs the operands
+# that optimization keeps in scalar registers)
 SAN_FLAGS = [
-    f"--offload-arch={ARCH}", "-O1", "-Xarch_device", "-O0", "-fPIC", "-std=c++17",
+    f"--offload-arch={ARCH}", "-O1", "-Xarch_device", "-O3", "-fPIC", "-std=c++17",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-I", INCLUDE, "-I", CSRC,
     "-Xarch_host", "-fsanitize=address",
