@@ -109,6 +109,9 @@ __global__ __launch_bounds__(kThreads) void kv_append_kernel(CacheArgs c,
 // computed once for all those heads, and the row and chunk come from shifts
 // instead of divisions by run-time sizes.
 constexpr int kPrepHeads = 8;  // 2, 4 and 16 were slower at workload 3's shape
+// chunk prep: a chunk has fewer tokens than a prompt, and one KV head per
+// thread (more workgroups) measured faster than groups of 2, 4 or 8
+constexpr int kChunkHeads = 1;
 template <typename T, int D, bool PAGED, bool CACHE, bool I8, bool KEYS_IN_CACHE = false>
 __global__ __launch_bounds__(kThreads) void prefill_prep_kernel(
     CacheArgs c, const T* __restrict__ k, const T* __restrict__ v, T* __restrict__ k_rot,
@@ -143,13 +146,17 @@ __global__ __launch_bounds__(kThreads) void prefill_prep_kernel(
     // every head's chunk is loaded before any store (a store to the cache
     // could alias the next head's keys for all the compiler knows, which
     // would leave one load in flight per thread)
-    uint4 raw[kPrepHeads];
+    uint4 raw[kPrepHeads], vraw[kPrepHeads];
+    const bool in_cache = CACHE && pos >= 0 && pos <= cache_last_slot<PAGED>(c);
+    const bool copy_v = in_cache && (I8 || store_v);  // the values are read here
 #pragma unroll
     for (int j = 0; j < kPrepHeads; ++j)
-      if (j < nh)
-        raw[j] = *reinterpret_cast<const uint4*>(k + (((int64_t)b * Hkv + hk0 + j) * S + s) * D + col);
+      if (j < nh) {
+        const int64_t e0 = (((int64_t)b * Hkv + hk0 + j) * S + s) * D + col;
+        raw[j] = *reinterpret_cast<const uint4*>(k + e0);
+        if (copy_v) vraw[j] = *reinterpret_cast<const uint4*>(v + e0);
+      }
     const RopeChunk<N> rot = rope_prepare<N, -1>(pos, col, D, fr);
-    const bool in_cache = CACHE && pos >= 0 && pos <= cache_last_slot<PAGED>(c);
 #pragma unroll
     for (int j = 0; j < kPrepHeads; ++j) {
       if (j >= nh) break;  // uniform over the block
@@ -165,14 +172,13 @@ __global__ __launch_bounds__(kThreads) void prefill_prep_kernel(
         if constexpr (I8) {
           // the fp32 rotated key is quantized (not its rounded copy in k_rot)
           float vf[N];
-          load16<T>(v + row * D + col, vf);
+#pragma unroll
+          for (int e = 0; e < N; ++e) vf[e] = elem<T>(vraw[j], e);
           store_int8<N>(static_cast<int8_t*>(c.k) + dst, f, c.k_scale + hk * D + col);
           store_int8<N>(static_cast<int8_t*>(c.v) + dst, vf, c.v_scale + hk * D + col);
         } else {
           store16<T>(static_cast<T*>(c.k) + dst, f);
-          if (store_v)
-            *reinterpret_cast<uint4*>(static_cast<T*>(c.v) + dst) =
-                *reinterpret_cast<const uint4*>(v + row * D + col);
+          if (store_v) *reinterpret_cast<uint4*>(static_cast<T*>(c.v) + dst) = vraw[j];
         }
       }
     }
@@ -188,37 +194,54 @@ __global__ __launch_bounds__(kThreads) void prefill_prep_kernel(
 template <typename T, int D, bool PAGED, bool I8>
 __global__ __launch_bounds__(kThreads) void chunk_prep_kernel(
     CacheArgs c, const T* __restrict__ k, const T* __restrict__ v, int Hkv, int S,
-    const int32_t* __restrict__ seq_lens, const int32_t* __restrict__ chunk_lens, int64_t nvec,
-    RopeFreq fr) {
+    const int32_t* __restrict__ seq_lens, const int32_t* __restrict__ chunk_lens, RopeFreq fr) {
+  // grid and per-thread work as prefill_prep_kernel: one chunk of one token
+  // in each of kChunkHeads KV heads, with the angles computed once
   constexpr int N = Vec16<T>::N;
   constexpr int VPR = D / N;
+  constexpr int kPrepHeads = kChunkHeads;
+  const int hk0 = blockIdx.y * kPrepHeads, b = blockIdx.z;
+  const int nh = min(kPrepHeads, Hkv - hk0);
   const int last = cache_last_slot<PAGED>(c);
-  for (int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x; i < nvec;
+  const int Sb = chunk_lens == nullptr ? S : min(max(chunk_lens[b], 0), S);
+  const int P = seq_lens[b];
+  if (P < 0 || P + Sb > last + 1) return;  // the chunk does not fit: not stored
+  const int64_t items = (int64_t)Sb * VPR;  // padding rows s >= Sb are skipped
+  for (int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x; i < items;
        i += (int64_t)gridDim.x * kThreads) {
-    const int64_t row = i / VPR;
+    const int s = (int)(i / VPR);
     const int col = (int)(i % VPR) * N;
-    const int s = (int)(row % S);
-    const int64_t bh = row / S;
-    const int hk = (int)(bh % Hkv);
-    const int b = (int)(bh / Hkv);
-    const int Sb = chunk_lens == nullptr ? S : min(max(chunk_lens[b], 0), S);
-    if (s >= Sb) continue;  // padding
-    const int P = seq_lens[b];
-    if (P < 0 || P + Sb > last + 1) continue;  // the chunk does not fit: not stored
     const int pos = P + s;
-    float f[N];
-    load16<T>(k + row * D + col, f);
-    rope_rotate_chunk<T, N>(f, k + row * D, col, D, pos, fr);
-    const int64_t dst = cache_row<PAGED>(c, b, hk, Hkv, pos) * D + col;
-    if constexpr (I8) {
-      float vf[N];
-      load16<T>(v + row * D + col, vf);
-      store_int8<N>(static_cast<int8_t*>(c.k) + dst, f, c.k_scale + hk * D + col);
-      store_int8<N>(static_cast<int8_t*>(c.v) + dst, vf, c.v_scale + hk * D + col);
-    } else {
-      store16<T>(static_cast<T*>(c.k) + dst, f);
-      *reinterpret_cast<uint4*>(static_cast<T*>(c.v) + dst) =
-          *reinterpret_cast<const uint4*>(v + row * D + col);
+    // every head's key and value chunks are loaded before any store
+    uint4 raw[kPrepHeads], vraw[kPrepHeads];
+#pragma unroll
+    for (int j = 0; j < kPrepHeads; ++j)
+      if (j < nh) {
+        const int64_t e0 = (((int64_t)b * Hkv + hk0 + j) * S + s) * D + col;
+        raw[j] = *reinterpret_cast<const uint4*>(k + e0);
+        vraw[j] = *reinterpret_cast<const uint4*>(v + e0);
+      }
+    const RopeChunk<N> rot = rope_prepare<N, -1>(pos, col, D, fr);
+#pragma unroll
+    for (int j = 0; j < kPrepHeads; ++j) {
+      if (j >= nh) break;  // uniform over the block
+      const int hk = hk0 + j;
+      const int64_t row = ((int64_t)b * Hkv + hk) * S + s;
+      float f[N];
+#pragma unroll
+      for (int e = 0; e < N; ++e) f[e] = elem<T>(raw[j], e);
+      rope_apply_prepared<T, N, -1>(f, k + row * D, D, rot, fr);
+      const int64_t dst = cache_row<PAGED>(c, b, hk, Hkv, pos) * D + col;
+      if constexpr (I8) {
+        float vf[N];
+#pragma unroll
+        for (int e = 0; e < N; ++e) vf[e] = elem<T>(vraw[j], e);
+        store_int8<N>(static_cast<int8_t*>(c.k) + dst, f, c.k_scale + hk * D + col);
+        store_int8<N>(static_cast<int8_t*>(c.v) + dst, vf, c.v_scale + hk * D + col);
+      } else {
+        store16<T>(static_cast<T*>(c.k) + dst, f);
+        *reinterpret_cast<uint4*>(static_cast<T*>(c.v) + dst) = vraw[j];
+      }
     }
   }
 }
@@ -438,23 +461,26 @@ template <typename T, int D>
 hipError_t chunk_prep_t(bool paged, bool i8, const CacheArgs& c, const void* k, const void* v,
                         int B, int Hkv, int S, const int32_t* seq_lens,
                         const int32_t* chunk_lens, const RopeFreq& fr, hipStream_t st) {
-  const int64_t nvec = (int64_t)B * Hkv * S * (D / Vec16<T>::N);
   const T* kk = static_cast<const T*>(k);
   const T* vv = static_cast<const T*>(v);
-  const dim3 grid(grid_for(nvec)), block(kThreads);
+  if ((int64_t)B * Hkv * S == 0) return hipSuccess;
+  // (B and Hkv <= Hq are at most 65535: the call checks them)
+  const int64_t gx = ((int64_t)S * (D / Vec16<T>::N) + kThreads - 1) / kThreads;
+  const dim3 grid((unsigned)(gx < 4096 ? gx : 4096), (Hkv + kChunkHeads - 1) / kChunkHeads, B);
+  const dim3 block(kThreads);
   if (i8) {
     if (paged)
       hipLaunchKernelGGL((chunk_prep_kernel<T, D, true, true>), grid, block, 0, st, c, kk, vv,
-                         Hkv, S, seq_lens, chunk_lens, nvec, fr);
+                         Hkv, S, seq_lens, chunk_lens, fr);
     else
       hipLaunchKernelGGL((chunk_prep_kernel<T, D, false, true>), grid, block, 0, st, c, kk, vv,
-                         Hkv, S, seq_lens, chunk_lens, nvec, fr);
+                         Hkv, S, seq_lens, chunk_lens, fr);
   } else if (paged) {
     hipLaunchKernelGGL((chunk_prep_kernel<T, D, true, false>), grid, block, 0, st, c, kk, vv,
-                       Hkv, S, seq_lens, chunk_lens, nvec, fr);
+                       Hkv, S, seq_lens, chunk_lens, fr);
   } else {
     hipLaunchKernelGGL((chunk_prep_kernel<T, D, false, false>), grid, block, 0, st, c, kk, vv,
-                       Hkv, S, seq_lens, chunk_lens, nvec, fr);
+                       Hkv, S, seq_lens, chunk_lens, fr);
   }
   return hipGetLastError();
 }
