@@ -112,7 +112,7 @@ constexpr int kPrepHeads = 8;  // 2, 4 and 16 were slower at workload 3's shape
 // chunk prep: a chunk has fewer tokens than a prompt, and one KV head per
 // thread (more workgroups) measured faster than groups of 2, 4 or 8
 constexpr int kChunkHeads = 1;
-template <typename T, int D, bool PAGED, bool CACHE, bool I8, bool KEYS_IN_CACHE = false>
+template <typename T, int D, bool PAGED, bool CACHE, bool I8, bool KEYS_IN_CACHE, int HALF>
 __global__ __launch_bounds__(kThreads) void prefill_prep_kernel(
     CacheArgs c, const T* __restrict__ k, const T* __restrict__ v, T* __restrict__ k_rot,
     int Hkv, int S, const int32_t* __restrict__ positions, const int32_t* __restrict__ lens,
@@ -150,13 +150,12 @@ __global__ __launch_bounds__(kThreads) void prefill_prep_kernel(
     const bool in_cache = CACHE && pos >= 0 && pos <= cache_last_slot<PAGED>(c);
     const bool copy_v = in_cache && (I8 || store_v);  // the values are read here
 #pragma unroll
-    for (int j = 0; j < kPrepHeads; ++j)
-      if (j < nh) {
-        const int64_t e0 = (((int64_t)b * Hkv + hk0 + j) * S + s) * D + col;
-        raw[j] = *reinterpret_cast<const uint4*>(k + e0);
-        if (copy_v) vraw[j] = *reinterpret_cast<const uint4*>(v + e0);
-      }
-    const RopeChunk<N> rot = rope_prepare<N, -1>(pos, col, D, fr);
+    for (int j = 0; j < kPrepHeads; ++j) {  // (heads past the group's last read that one)
+      const int64_t e0 = (((int64_t)b * Hkv + hk0 + min(j, nh - 1)) * S + s) * D + col;
+      raw[j] = *reinterpret_cast<const uint4*>(k + e0);
+      vraw[j] = copy_v ? *reinterpret_cast<const uint4*>(v + e0) : make_uint4(0u, 0u, 0u, 0u);
+    }
+    const RopeChunk<N> rot = rope_prepare<N, HALF>(pos, col, D, fr);
 #pragma unroll
     for (int j = 0; j < kPrepHeads; ++j) {
       if (j >= nh) break;  // uniform over the block
@@ -165,7 +164,7 @@ __global__ __launch_bounds__(kThreads) void prefill_prep_kernel(
       float f[N];
 #pragma unroll
       for (int e = 0; e < N; ++e) f[e] = elem<T>(raw[j], e);
-      rope_apply_prepared<T, N, -1>(f, k + row * D, D, rot, fr);
+      rope_apply_prepared<T, N, HALF>(f, k + row * D, D, rot, fr);
       if (dense) store16<T>(k_rot + row * D + col, f);
       if (in_cache) {  // else not stored
         const int64_t dst = cache_row<PAGED>(c, b, hk, Hkv, pos) * D + col;
@@ -191,7 +190,7 @@ __global__ __launch_bounds__(kThreads) void prefill_prep_kernel(
 // reads clamped rows and its output is unspecified).
 // With chunk_lens, tokens s >= chunk_lens[b] are padding and are not stored.
 // I8: an INT8 cache; the fp32 rotated key and the value are stored as codes.
-template <typename T, int D, bool PAGED, bool I8>
+template <typename T, int D, bool PAGED, bool I8, int HALF>
 __global__ __launch_bounds__(kThreads) void chunk_prep_kernel(
     CacheArgs c, const T* __restrict__ k, const T* __restrict__ v, int Hkv, int S,
     const int32_t* __restrict__ seq_lens, const int32_t* __restrict__ chunk_lens, RopeFreq fr) {
@@ -215,13 +214,12 @@ __global__ __launch_bounds__(kThreads) void chunk_prep_kernel(
     // every head's key and value chunks are loaded before any store
     uint4 raw[kPrepHeads], vraw[kPrepHeads];
 #pragma unroll
-    for (int j = 0; j < kPrepHeads; ++j)
-      if (j < nh) {
-        const int64_t e0 = (((int64_t)b * Hkv + hk0 + j) * S + s) * D + col;
-        raw[j] = *reinterpret_cast<const uint4*>(k + e0);
-        vraw[j] = *reinterpret_cast<const uint4*>(v + e0);
-      }
-    const RopeChunk<N> rot = rope_prepare<N, -1>(pos, col, D, fr);
+    for (int j = 0; j < kPrepHeads; ++j) {  // (heads past the group's last read that one)
+      const int64_t e0 = (((int64_t)b * Hkv + hk0 + min(j, nh - 1)) * S + s) * D + col;
+      raw[j] = *reinterpret_cast<const uint4*>(k + e0);
+      vraw[j] = *reinterpret_cast<const uint4*>(v + e0);
+    }
+    const RopeChunk<N> rot = rope_prepare<N, HALF>(pos, col, D, fr);
 #pragma unroll
     for (int j = 0; j < kPrepHeads; ++j) {
       if (j >= nh) break;  // uniform over the block
@@ -230,7 +228,7 @@ __global__ __launch_bounds__(kThreads) void chunk_prep_kernel(
       float f[N];
 #pragma unroll
       for (int e = 0; e < N; ++e) f[e] = elem<T>(raw[j], e);
-      rope_apply_prepared<T, N, -1>(f, k + row * D, D, rot, fr);
+      rope_apply_prepared<T, N, HALF>(f, k + row * D, D, rot, fr);
       const int64_t dst = cache_row<PAGED>(c, b, hk, Hkv, pos) * D + col;
       if constexpr (I8) {
         float vf[N];
@@ -424,8 +422,9 @@ hipError_t kv_append_t(bool paged, const CacheArgs& c, const void* k, const void
   return hipGetLastError();
 }
 
-template <typename T, int D, bool I8>
-hipError_t prefill_prep_t(bool paged, const CacheArgs* cache, const void* k, const void* v,
+// (HALF: the pair layout, a compile-time choice of the prep kernels)
+template <typename T, int D, bool I8, int HALF>
+hipError_t prefill_prep_h(bool paged, const CacheArgs* cache, const void* k, const void* v,
                           void* k_rot, int B, int Hkv, int S, const int32_t* positions,
                           const int32_t* lens, const RopeFreq& fr, bool keys_in_cache,
                           bool store_v, void* out, int G, hipStream_t st) {
@@ -441,24 +440,35 @@ hipError_t prefill_prep_t(bool paged, const CacheArgs* cache, const void* k, con
   const dim3 block(kThreads);
   if (cache == nullptr) {
     CacheArgs none{};
-    hipLaunchKernelGGL((prefill_prep_kernel<T, D, false, false, false>), grid, block, 0, st,
+    hipLaunchKernelGGL((prefill_prep_kernel<T, D, false, false, false, false, HALF>), grid, block, 0, st,
                        none, kk, vv, kr, Hkv, S, positions, lens, fr, oo, G, 1);
   } else if (paged) {
-    hipLaunchKernelGGL((prefill_prep_kernel<T, D, true, true, I8>), grid, block, 0, st, *cache,
+    hipLaunchKernelGGL((prefill_prep_kernel<T, D, true, true, I8, false, HALF>), grid, block, 0, st, *cache,
                        kk, vv, kr, Hkv, S, positions, lens, fr, oo, G, 1);
   } else if (!I8 && keys_in_cache) {
-    hipLaunchKernelGGL((prefill_prep_kernel<T, D, false, true, false, true>), grid, block, 0, st,
+    hipLaunchKernelGGL((prefill_prep_kernel<T, D, false, true, false, true, HALF>), grid, block, 0, st,
                        *cache, kk, vv, kr, Hkv, S, positions, lens, fr, oo, G,
                        store_v ? 1 : 0);
   } else {
-    hipLaunchKernelGGL((prefill_prep_kernel<T, D, false, true, I8>), grid, block, 0, st,
+    hipLaunchKernelGGL((prefill_prep_kernel<T, D, false, true, I8, false, HALF>), grid, block, 0, st,
                        *cache, kk, vv, kr, Hkv, S, positions, lens, fr, oo, G, 1);
   }
   return hipGetLastError();
 }
 
-template <typename T, int D>
-hipError_t chunk_prep_t(bool paged, bool i8, const CacheArgs& c, const void* k, const void* v,
+template <typename T, int D, bool I8>
+hipError_t prefill_prep_t(bool paged, const CacheArgs* cache, const void* k, const void* v,
+                          void* k_rot, int B, int Hkv, int S, const int32_t* positions,
+                          const int32_t* lens, const RopeFreq& fr, bool keys_in_cache,
+                          bool store_v, void* out, int G, hipStream_t st) {
+  return fr.half ? prefill_prep_h<T, D, I8, 1>(paged, cache, k, v, k_rot, B, Hkv, S, positions,
+                                                lens, fr, keys_in_cache, store_v, out, G, st)
+                 : prefill_prep_h<T, D, I8, 0>(paged, cache, k, v, k_rot, B, Hkv, S, positions,
+                                                lens, fr, keys_in_cache, store_v, out, G, st);
+}
+
+template <typename T, int D, int HALF>
+hipError_t chunk_prep_h(bool paged, bool i8, const CacheArgs& c, const void* k, const void* v,
                         int B, int Hkv, int S, const int32_t* seq_lens,
                         const int32_t* chunk_lens, const RopeFreq& fr, hipStream_t st) {
   const T* kk = static_cast<const T*>(k);
@@ -470,19 +480,27 @@ hipError_t chunk_prep_t(bool paged, bool i8, const CacheArgs& c, const void* k, 
   const dim3 block(kThreads);
   if (i8) {
     if (paged)
-      hipLaunchKernelGGL((chunk_prep_kernel<T, D, true, true>), grid, block, 0, st, c, kk, vv,
+      hipLaunchKernelGGL((chunk_prep_kernel<T, D, true, true, HALF>), grid, block, 0, st, c, kk, vv,
                          Hkv, S, seq_lens, chunk_lens, fr);
     else
-      hipLaunchKernelGGL((chunk_prep_kernel<T, D, false, true>), grid, block, 0, st, c, kk, vv,
+      hipLaunchKernelGGL((chunk_prep_kernel<T, D, false, true, HALF>), grid, block, 0, st, c, kk, vv,
                          Hkv, S, seq_lens, chunk_lens, fr);
   } else if (paged) {
-    hipLaunchKernelGGL((chunk_prep_kernel<T, D, true, false>), grid, block, 0, st, c, kk, vv,
+    hipLaunchKernelGGL((chunk_prep_kernel<T, D, true, false, HALF>), grid, block, 0, st, c, kk, vv,
                        Hkv, S, seq_lens, chunk_lens, fr);
   } else {
-    hipLaunchKernelGGL((chunk_prep_kernel<T, D, false, false>), grid, block, 0, st, c, kk, vv,
+    hipLaunchKernelGGL((chunk_prep_kernel<T, D, false, false, HALF>), grid, block, 0, st, c, kk, vv,
                        Hkv, S, seq_lens, chunk_lens, fr);
   }
   return hipGetLastError();
+}
+
+template <typename T, int D>
+hipError_t chunk_prep_t(bool paged, bool i8, const CacheArgs& c, const void* k, const void* v,
+                        int B, int Hkv, int S, const int32_t* seq_lens,
+                        const int32_t* chunk_lens, const RopeFreq& fr, hipStream_t st) {
+  return fr.half ? chunk_prep_h<T, D, 1>(paged, i8, c, k, v, B, Hkv, S, seq_lens, chunk_lens, fr, st)
+                 : chunk_prep_h<T, D, 0>(paged, i8, c, k, v, B, Hkv, S, seq_lens, chunk_lens, fr, st);
 }
 
 template <typename T, int D>
