@@ -355,6 +355,9 @@ car_status car_attn_decode_timed(const void* q, const void* k_new, const void* v
   int64_t cap = 0;
   const car_status cs = check_cache(cache, &c, &cap);
   if (cs != CAR_OK) return cs;
+  // a contiguous head's rows are addressed with 32-bit byte offsets
+  if (cache->block_table == nullptr && cap * D * 4 > (int64_t)UINT32_MAX)
+    return CAR_ERR_UNSUPPORTED;
   if (max_seq_len > cap) return CAR_ERR_INVALID_ARGUMENT;
   const size_t need = car_attn_decode_workspace_bytes(B, Hq, D, max_seq_len);
   if (workspace == nullptr || !aligned16(workspace) || workspace_bytes < need)

@@ -14,7 +14,8 @@
 // LPR = D*sizeof(T)/16 lanes covering one row, so a
 // wave load instruction moves 64/LPR whole rows (4 rows of 256 bytes for
 // bf16, D = 128).  All G = Hq/Hkv query heads of a KV head are served from the
-// same loads (GQA).  Dot products are reduced across the LPR lanes of a row
+// same loads (GQA); with G > 1 the loads write straight into a per-wave LDS
+// ring two rounds deep, so no registers wait on loads in flight.  Dot products are reduced across the LPR lanes of a row
 // with DPP moves; the softmax maximum and sums are combined across the rows
 // of a wave with lane shuffles and across the waves (4, or 8 with GQA)
 // through LDS.  Each
@@ -53,6 +54,39 @@ __device__ __forceinline__ uint32_t perm_hi(uint32_t a, uint32_t b) {
 }
 
 constexpr uint32_t kOnePair = 0x3F803F80u;  // (1.0, 1.0) in bf16
+
+// One non-temporal buffer -> LDS load: every lane moves the 16 bytes at
+// rsrc.base + voff to lds_base + 16 * lane (lds_base uniform over the wave).
+// Inline assembly without register outputs; the caller waits for it with an
+// explicit vmcnt before reading the LDS it wrote.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ __forceinline__ void dma16_nt(__amdgpu_buffer_rsrc_t rsrc, uint32_t voff,
+                                         void* lds_base) {
+  const uint32_t lds_addr = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)lds_base);
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen nt lds"
+               :
+               : "s"(lds_addr), "v"(voff), "s"(rsrc), "s"(0u)
+               : "memory", "m0");
+}
+#pragma clang diagnostic pop
+
+// Buffer resource over `bytes` bytes at `base` (raw addressing, no stride).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t raw_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
+                                           0x00020000);
+}
+
+// Waits for all but N of this wave's vector memory operations (loads into
+// LDS included), and keeps the compiler from moving memory accesses across.
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N < 16, "vmcnt immediate");
+  if constexpr (N == 0) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  if constexpr (N == 4) asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
+  if constexpr (N == 8) asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+  static_assert(N == 0 || N == 4 || N == 8, "vmcnt values in use");
+}
 
 // Per-lane geometry of the decode split kernel.  A lane holds C chunks of
 // 16 bytes of a cache row, chunks c*LPR + lane%LPR for c < C, so LPR =
@@ -115,7 +149,25 @@ __attribute__((amdgpu_waves_per_eu(G <= 4 ? 4 : 2))) void decode_split_kernel(
   constexpr bool BF = sizeof(T) == 2;
 
   constexpr int kWaves = Gm::WAVES, kThreads = 64 * kWaves;
-  __shared__ float sm_acc[kWaves][G][D];
+  // With several query heads (G > 1) the rows go from memory straight into a
+  // per-wave LDS ring of two rounds, so that two rounds are in flight while
+  // one is consumed from registers, and no registers wait for loads: at that
+  // register count four waves per SIMD are all that fit, and the bytes in
+  // flight per CU set the bandwidth.  A wave's partial sums later reuse its
+  // own ring.
+  constexpr bool DMA = G > 1;
+  constexpr int NOPS = 2 * R * C;      // 1 KB wave loads per round (K and V)
+  constexpr int ROUNDB = NOPS * 1024;  // bytes of one round
+  constexpr int WAVEB = DMA ? 2 * ROUNDB : 16;
+  static_assert(!DMA || (G * D * 4 <= WAVEB && ROUNDS >= 2), "ring geometry");
+  __shared__ __align__(16) char ring[DMA ? kWaves * WAVEB : 16];
+  __shared__ float sm_acc_w[DMA ? 1 : kWaves][DMA ? 1 : G][DMA ? 1 : D];
+  auto sm_acc = [&](int w, int g, int d) -> float& {
+    if constexpr (DMA)
+      return reinterpret_cast<float*>(ring + w * WAVEB)[g * D + d];
+    else
+      return sm_acc_w[w][g][d];
+  };
   __shared__ float sm_ml[kWaves][G][2];
 
   // Workgroups are numbered split-major with (sequence, KV head) fastest:
@@ -346,10 +398,73 @@ __attribute__((amdgpu_waves_per_eu(G <= 4 ? 4 : 2))) void decode_split_kernel(
       }
     };
 
-    // Double-buffered rounds: round r+1's loads are in flight while round r
-    // is consumed.
     using B0 = std::integral_constant<int, 0>;
     using B1 = std::integral_constant<int, 1>;
+    if constexpr (DMA) {
+      // Round r goes to ring slot r % 2 (its K rows, then its V rows, each
+      // step's 1 KB loads in order); lane l's 16 bytes land at 16 * l of a
+      // load's kilobyte and the lane reads them back from there.  The rows
+      // are those of the register path: paged steps stay in one block (one
+      // resource per block), contiguous rows are clamped to L.
+      char* const wring = ring + wave * WAVEB;
+      auto issue_dma = [&](int r, int slot) {
+        char* const dst = wring + slot * ROUNDB;
+#pragma unroll
+        for (int st = 0; st < R; ++st) {
+          const int x = r * R + st;
+          int64_t e0;  // first element of the resource
+          uint32_t bytes;
+          int row;  // the lane's row within it
+          if constexpr (PAGED) {
+            const int blk = __builtin_amdgcn_readlane(myblk, (x * NG) >> 4);  // uniform index
+            e0 = (((int64_t)blk * Hkv + hk) << 4) * D;
+            bytes = 16 * D * sizeof(T);
+            row = ((x * NG) & 15) + grp;
+          } else {
+            e0 = ((int64_t)b * Hkv + hk) * c.max_seq * D;
+            bytes = (uint32_t)c.max_seq * D * sizeof(T);
+            row = min(tw + x * NG + grp, L);
+          }
+          const __amdgpu_buffer_rsrc_t krs = raw_rsrc(Kc + e0, bytes);
+          const __amdgpu_buffer_rsrc_t vrs = raw_rsrc(Vc + e0, bytes);
+#pragma unroll
+          for (int ch = 0; ch < C; ++ch) {
+            const uint32_t voff = (uint32_t)(row * D + col[ch]) * sizeof(T);
+            dma16_nt(krs, voff, dst + (st * C + ch) * 2048);
+            dma16_nt(vrs, voff, dst + (st * C + ch) * 2048 + 1024);
+          }
+        }
+      };
+      auto read_round = [&](int slot) {
+        const char* const src = wring + slot * ROUNDB + lane * 16;
+#pragma unroll
+        for (int st = 0; st < R; ++st)
+#pragma unroll
+          for (int ch = 0; ch < C; ++ch) {
+            kb[0][st][ch] = *reinterpret_cast<const u32x4_t*>(src + (st * C + ch) * 2048);
+            vb[0][st][ch] = *reinterpret_cast<const u32x4_t*>(src + (st * C + ch) * 2048 + 1024);
+          }
+        // the slot is loaded again next: its reads must have returned
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+      };
+      issue_dma(0, 0);
+      issue_dma(1, 1);
+#pragma unroll 1
+      for (int r = 0; r < ROUNDS - 2; ++r) {
+        wait_vm<NOPS>();  // round r landed; round r + 1 may still be in flight
+        read_round(r & 1);
+        issue_dma(r + 2, r & 1);
+        consume(r, B0{});
+      }
+      wait_vm<NOPS>();
+      read_round(0);  // ROUNDS is even
+      consume(ROUNDS - 2, B0{});
+      wait_vm<0>();
+      read_round(1);
+      consume(ROUNDS - 1, B0{});
+    } else {
+    // Double-buffered rounds: round r+1's loads are in flight while round r
+    // is consumed.
     // The steady-state loop issues its loads unconditionally, so that each
     // wait covers only the round being consumed; the last two rounds follow.
     issue(0, B0{});
@@ -366,6 +481,7 @@ __attribute__((amdgpu_waves_per_eu(G <= 4 ? 4 : 2))) void decode_split_kernel(
       issue(ROUNDS - 1, B1{});
       consume(ROUNDS - 2, B0{});
       consume(ROUNDS - 1, B1{});
+    }
     }
   }
 
@@ -384,7 +500,7 @@ __attribute__((amdgpu_waves_per_eu(G <= 4 ? 4 : 2))) void decode_split_kernel(
 #pragma unroll
       for (int ch = 0; ch < C; ++ch)
 #pragma unroll
-        for (int e = 0; e < N; ++e) sm_acc[wave][g][col[ch] + e] = acc[g][ch][e];
+        for (int e = 0; e < N; ++e) sm_acc(wave, g, col[ch] + e) = acc[g][ch][e];
       if (lane == 0) {
         sm_ml[wave][g][0] = m_run[g];
         sm_ml[wave][g][1] = l_run[g];
@@ -404,7 +520,7 @@ __attribute__((amdgpu_waves_per_eu(G <= 4 ? 4 : 2))) void decode_split_kernel(
     for (int w = 0; w < kWaves; ++w) {
       const float mw = sm_ml[w][g][0];
       const float f = mw == -INFINITY ? 0.f : fast_exp2(mw - M);
-      a = fmaf(f, sm_acc[w][g][d], a);
+      a = fmaf(f, sm_acc(w, g, d), a);
       l = fmaf(f, sm_ml[w][g][1], l);
     }
     float* dst = part + (((int64_t)b * Hq + hk * G + g) * nsplit + split) * PW;

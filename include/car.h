@@ -328,8 +328,9 @@ size_t car_attn_decode_workspace_bytes(int B, int Hq, int D, int max_seq_len);
  *   workspace   device scratch of at least car_attn_decode_workspace_bytes();
  *               contents on entry ignored, on exit unspecified.
  * Calls that share a workspace must be ordered on one stream.
- * Sizes one launch cannot cover (B * Hq above 2^31 - 1, or max_seq_len above
- * 65535 * 256 tokens) return CAR_ERR_UNSUPPORTED before any work is queued.
+ * Sizes one launch cannot cover (B * Hq above 2^31 - 1, max_seq_len above
+ * 65535 * 256 tokens, or a contiguous cache whose capacity times D * 4 bytes
+ * is above 2^32 - 1) return CAR_ERR_UNSUPPORTED before any work is queued.
  */
 car_status car_attn_decode(const void* q, const void* k_new, const void* v_new,
                            void* out, car_dtype dtype, int B, int Hq, int Hkv, int D,

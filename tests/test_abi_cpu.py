@@ -160,6 +160,8 @@ def test_decode_rejects(car, lib):
     assert call(B=0, q=None, ws=None) == OK          # empty batch: no-op
     assert call(B=1 << 30) == UNSUPPORTED            # B * Hkv workgroups exceed the grid
     assert call(msl=65535 * 256 + 1) == UNSUPPORTED  # more than 65535 splits
+    huge = _cache(car, max_seq=(1 << 23) + 1)        # a head's rows past 32-bit offsets
+    assert call(cache=ctypes.byref(huge)) == UNSUPPORTED
 
 
 def test_prefill_cached_rejects(car, lib):
