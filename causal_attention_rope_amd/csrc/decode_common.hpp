@@ -16,9 +16,11 @@ namespace {
 constexpr float kRescaleLog2 = 8.f;
 
 // One wave per (sequence, query head): merge the partials of the splits that
-// hold tokens 0..L (log-sum-exp rule) and write the normalised output.  Lane s
-// reads split s's maximum and sum; the accumulators are read split by split,
-// 4 splits at a time.
+// hold tokens 0..L (log-sum-exp rule) and write the normalised output.  The
+// splits are taken 8 at a time with a running maximum, so that every load of
+// a group (each split's maximum, sum and the lane's accumulators) is issued
+// at once: one memory round trip per group instead of a pass for the maxima
+// before the accumulators.
 template <typename T, int D>
 __global__ __launch_bounds__(64) void decode_combine_kernel(const float* __restrict__ part,
                                                             const int32_t* __restrict__ seq_lens,
@@ -27,48 +29,43 @@ __global__ __launch_bounds__(64) void decode_combine_kernel(const float* __restr
                                                             int last_slot) {
   constexpr int PW = decode_partial_words(D);
   constexpr int E = D / 64;
+  constexpr int U = 8;  // splits per group
   const int bh = blockIdx.x;
   const int b = bh / Hq;
   const int lane = threadIdx.x;
   const int L = min(max(seq_lens[b], 0), last_slot);
-  const int n = min(L / split_tokens + 1, nsplit);
+  const int n = min(L / split_tokens + 1, nsplit);  // >= 1; every split holds a token
   const float* p = part + (int64_t)bh * nsplit * PW;
 
-  // max and weighted sum over splits, 64 splits per pass
-  float M = -INFINITY;
-  for (int s = lane; s < n; s += 64) M = fmaxf(M, p[(int64_t)s * PW]);
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) M = fmaxf(M, __shfl_xor(M, o));
-  float l = 0.f;
-  for (int s = lane; s < n; s += 64) l += fast_exp2(p[(int64_t)s * PW] - M) * p[(int64_t)s * PW + 1];
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) l += __shfl_xor(l, o);
-
-  float a[E];
+  float M = -INFINITY, l = 0.f, a[E];
 #pragma unroll
   for (int e = 0; e < E; ++e) a[e] = 0.f;
-  int s = 0;
-  for (; s + 4 <= n; s += 4) {
-    float w[4], v[4][E];
+  for (int s = 0; s < n; s += U) {
+    float w[U], lw[U], v[U][E];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const float* ps = p + (int64_t)(s + u) * PW;
-      w[u] = ps[0];
+    for (int u = 0; u < U; ++u) {
+      // splits past n read split n - 1 and weigh nothing
+      const float* ps = p + (int64_t)min(s + u, n - 1) * PW;
+      w[u] = s + u < n ? ps[0] : -INFINITY;
+      lw[u] = ps[1];
 #pragma unroll
       for (int e = 0; e < E; ++e) v[u][e] = ps[4 + lane + 64 * e];
     }
+    float m_new = M;
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
+    for (int u = 0; u < U; ++u) m_new = fmaxf(m_new, w[u]);  // finite: split s holds a token
+    const float r = fast_exp2(M - m_new);  // 0 on the first group
+    l *= r;
+#pragma unroll
+    for (int e = 0; e < E; ++e) a[e] *= r;
+    M = m_new;
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
       const float f = fast_exp2(w[u] - M);
+      l = fmaf(f, lw[u], l);
 #pragma unroll
       for (int e = 0; e < E; ++e) a[e] = fmaf(f, v[u][e], a[e]);
     }
-  }
-  for (; s < n; ++s) {
-    const float* ps = p + (int64_t)s * PW;
-    const float f = fast_exp2(ps[0] - M);
-#pragma unroll
-    for (int e = 0; e < E; ++e) a[e] = fmaf(f, ps[4 + lane + 64 * e], a[e]);
   }
   const float inv = 1.f / l;
 #pragma unroll
