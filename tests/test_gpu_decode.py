@@ -80,13 +80,16 @@ def test_decode_gqa_groups(car, dtype, group, paged):
     run_and_check(car, case)
 
 
-@pytest.mark.parametrize("group", [2, 4])
-def test_decode_gqa_lengths_d64(car, group):
-    """D = 64 with groups (16-row load steps, 1024-token splits)."""
-    log_case(f"decode gqa D=64 group={group}")
-    lens = [0, 1, 127, 255, 511, 700, 1023, 1024, 1025]
+@pytest.mark.parametrize("group", [2, 4, 8])
+@pytest.mark.parametrize("paged", [False, True], ids=["contiguous", "paged"])
+def test_decode_gqa_lengths_d64(car, group, paged):
+    """D = 64 with groups (8-row load steps, 1024-token splits, rows streamed
+    through the per-wave LDS ring): lengths inside the first rounds, at the
+    wave and split edges."""
+    log_case(f"decode gqa D=64 group={group} paged={paged}")
+    lens = [0, 1, 7, 8, 17, 127, 255, 511, 700, 1023, 1024, 1025]
     case = W.decode_case("gqa64", len(lens), 8, 8 // group, 64, torch.bfloat16, lens,
-                         450 + group, DEV, paged=True, poison_unused=True, extra_blocks=2)
+                         450 + group, DEV, paged=paged, poison_unused=True, extra_blocks=2)
     run_and_check(car, case)
 
 
