@@ -314,7 +314,9 @@ def test_decode_int8_mha(car, dtype, D, paged):
     run_and_check(car, case)
 
 
-GQA_LENS = [0, 3, 127, 1023, 1024, 1025, 2047, 2049]
+# several query heads: 2048-token splits over 8 waves of 256 tokens; lengths
+# at the wave and split edges
+GQA_LENS = [0, 3, 127, 255, 256, 1023, 1024, 1025, 2047, 2048, 2049, 4097]
 
 
 @pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16], ids=["f32", "bf16"])
